@@ -1,0 +1,293 @@
+"""ctypes front of the plain CPU oracle (``oracle/oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the test-suite, the package smoke check and the
+benchmark's CPU-baseline leg are the only callers.  The product path (the HIP
+library and its binding) never imports this package.
+
+Arrays are numpy arrays.  Two-dimensional operands may be row-strided views
+(leading dimension = ``strides[0] / itemsize``) but must have unit element
+stride.  Each wrapper names the C function it forwards to; the C source states
+the definition each one follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+_c_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"oracle library missing: {LIB_PATH}; build it with __graft_entry__.build()")
+        _lib = ctypes.CDLL(LIB_PATH)
+        _lib.oracle_f16_to_f64.restype = ctypes.c_double
+        _lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+        _lib.oracle_bf16_to_f64.restype = ctypes.c_double
+        _lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        _lib.oracle_e4m3_to_f64.restype = ctypes.c_double
+        _lib.oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+        _lib.oracle_f32_to_bf16_rne.restype = ctypes.c_uint16
+        _lib.oracle_f32_to_bf16_rne.argtypes = [ctypes.c_float]
+        for name in ("oracle_decode_f16", "oracle_decode_bf16", "oracle_decode_e4m3",
+                     "oracle_round_bf16"):
+            fn = getattr(_lib, name)
+            fn.restype = None
+            fn.argtypes = [_vp, _vp, _c_i64]
+        for name in ("oracle_gemm_f16", "oracle_gemm_bf16"):
+            fn = getattr(_lib, name)
+            fn.restype = ctypes.c_int
+            fn.argtypes = [_c_i64] * 3 + [_vp, _c_i64, _vp, _c_i64, _vp, _c_i64, _vp, _vp]
+        for name in ("oracle_gemm_f16_at", "oracle_gemm_bf16_at"):
+            fn = getattr(_lib, name)
+            fn.restype = ctypes.c_int
+            fn.argtypes = ([_c_i64] * 3 + [_vp, _c_i64, _vp, _c_i64, _vp, _c_i64]
+                           + [_c_i64, _vp, _vp, _vp, _vp])
+        _lib.oracle_gemm_f16_intexact.restype = ctypes.c_int
+        _lib.oracle_gemm_f16_intexact.argtypes = ([_c_i64] * 3
+                                                  + [_vp, _c_i64, _vp, _c_i64, _vp, _c_i64, _vp])
+        _lib.oracle_gemm_i8_i32.restype = ctypes.c_int
+        _lib.oracle_gemm_i8_i32.argtypes = [_c_i64] * 3 + [_vp, _c_i64, _vp, _c_i64, _vp, _c_i64,
+                                                           _vp]
+        _lib.oracle_gemm_i8_i32_at.restype = ctypes.c_int
+        _lib.oracle_gemm_i8_i32_at.argtypes = ([_c_i64] * 3
+                                               + [_vp, _c_i64, _vp, _c_i64, _vp, _c_i64]
+                                               + [_c_i64, _vp, _vp, _vp])
+        _lib.oracle_gemm_fp8_blockscaled.restype = ctypes.c_int
+        _lib.oracle_gemm_fp8_blockscaled.argtypes = ([_c_i64] * 3
+                                                     + [_vp, _c_i64, _vp, _c_i64]
+                                                     + [_vp, _c_i64, _vp, _c_i64, _vp, _vp])
+        _lib.oracle_gemm_fp8_blockscaled_at.restype = ctypes.c_int
+        _lib.oracle_gemm_fp8_blockscaled_at.argtypes = ([_c_i64] * 3
+                                                        + [_vp, _c_i64, _vp, _c_i64]
+                                                        + [_vp, _c_i64, _vp, _c_i64]
+                                                        + [_c_i64, _vp, _vp, _vp, _vp])
+        _lib.oracle_gemv_w8a8.restype = ctypes.c_int
+        _lib.oracle_gemv_w8a8.argtypes = [_c_i64, _c_i64, _vp, ctypes.c_float, _vp, _c_i64, _vp,
+                                          _vp, _vp]
+    return _lib
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+_ERRORS = {1: "invalid argument", 2: "non-finite input", 3: "INT32 overflow",
+           4: "non-integer input"}
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise OracleError(f"{what}: {_ERRORS.get(rc, rc)}")
+
+
+def _mat(x: np.ndarray, dtype) -> tuple[int, int]:
+    """Pointer and leading dimension (elements) of a row-major 2-D operand."""
+    if x.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {x.dtype}")
+    if x.ndim != 2:
+        raise ValueError("expected a 2-D array")
+    item = x.itemsize
+    if x.size == 0:
+        return x.ctypes.data, max(int(x.shape[1]), 1)
+    if x.shape[1] > 1 and x.strides[1] != item:
+        raise ValueError("unit element stride required")
+    ld = x.strides[0] // item if x.shape[0] > 1 else max(x.shape[1], 1)
+    if x.shape[0] > 1 and x.strides[0] % item:
+        raise ValueError("row stride must be a whole number of elements")
+    return x.ctypes.data, int(ld)
+
+
+def _ptr(x):
+    return None if x is None else x.ctypes.data
+
+
+# ---------------------------------------------------------------- formats --
+def f16_to_f64(bits: np.ndarray) -> np.ndarray:
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(bits.shape, np.float64)
+    _load().oracle_decode_f16(bits.ctypes.data, out.ctypes.data, bits.size)
+    return out
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(bits.shape, np.float64)
+    _load().oracle_decode_bf16(bits.ctypes.data, out.ctypes.data, bits.size)
+    return out
+
+
+def e4m3_to_f64(bits: np.ndarray) -> np.ndarray:
+    bits = np.ascontiguousarray(bits, dtype=np.uint8)
+    out = np.empty(bits.shape, np.float64)
+    _load().oracle_decode_e4m3(bits.ctypes.data, out.ctypes.data, bits.size)
+    return out
+
+
+def f32_to_bf16_rne(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint16)
+    _load().oracle_round_bf16(x.ctypes.data, out.ctypes.data, x.size)
+    return out
+
+
+# ------------------------------------------------------------------ GEMMs --
+def _gemm16(fn_name, A, B, C):
+    lib = _load()
+    M, K = A.shape
+    K2, N = B.shape
+    assert K == K2
+    pa, lda = _mat(A, np.uint16)
+    pb, ldb = _mat(B, np.uint16)
+    pc, ldc = (None, 0) if C is None else _mat(C, np.float32)
+    R = np.empty((M, N), np.float64)
+    S = np.empty((M, N), np.float64)
+    _check(getattr(lib, fn_name)(M, N, K, pa, lda, pb, ldb, pc, ldc, R.ctypes.data,
+                                 S.ctypes.data), fn_name)
+    return R, S
+
+
+def gemm_f16(A, B, C=None):
+    """``oracle_gemm_f16``: (R, S) with R = A.B + C in FP64 and S = sum |a.b|."""
+    return _gemm16("oracle_gemm_f16", A, B, C)
+
+
+def gemm_bf16(A, B, C=None):
+    """``oracle_gemm_bf16``: (R, S) as :func:`gemm_f16` for BF16 bit patterns."""
+    return _gemm16("oracle_gemm_bf16", A, B, C)
+
+
+def _gemm16_at(fn_name, A, B, C, ii, jj):
+    lib = _load()
+    M, K = A.shape
+    N = B.shape[1]
+    pa, lda = _mat(A, np.uint16)
+    pb, ldb = _mat(B, np.uint16)
+    pc, ldc = (None, 0) if C is None else _mat(C, np.float32)
+    ii = np.ascontiguousarray(ii, np.int64)
+    jj = np.ascontiguousarray(jj, np.int64)
+    R = np.empty(ii.shape, np.float64)
+    S = np.empty(ii.shape, np.float64)
+    _check(getattr(lib, fn_name)(M, N, K, pa, lda, pb, ldb, pc, ldc, ii.size, ii.ctypes.data,
+                                 jj.ctypes.data, R.ctypes.data, S.ctypes.data), fn_name)
+    return R, S
+
+
+def gemm_f16_at(A, B, C, ii, jj):
+    """``oracle_gemm_f16_at``: R, S at output positions (ii[p], jj[p])."""
+    return _gemm16_at("oracle_gemm_f16_at", A, B, C, ii, jj)
+
+
+def gemm_bf16_at(A, B, C, ii, jj):
+    """``oracle_gemm_bf16_at``: R, S at output positions (ii[p], jj[p])."""
+    return _gemm16_at("oracle_gemm_bf16_at", A, B, C, ii, jj)
+
+
+def gemm_f16_intexact(A, B, C=None):
+    """``oracle_gemm_f16_intexact``: FP32 D = fl32(exact integer sum + C)."""
+    lib = _load()
+    M, K = A.shape
+    N = B.shape[1]
+    pa, lda = _mat(A, np.uint16)
+    pb, ldb = _mat(B, np.uint16)
+    pc, ldc = (None, 0) if C is None else _mat(C, np.float32)
+    D = np.empty((M, N), np.float32)
+    _check(lib.oracle_gemm_f16_intexact(M, N, K, pa, lda, pb, ldb, pc, ldc, D.ctypes.data),
+           "oracle_gemm_f16_intexact")
+    return D
+
+
+def gemm_i8_i32(A, B, C=None):
+    """``oracle_gemm_i8_i32``: exact INT32 D = A.B + C."""
+    lib = _load()
+    M, K = A.shape
+    N = B.shape[1]
+    pa, lda = _mat(A, np.int8)
+    pb, ldb = _mat(B, np.int8)
+    pc, ldc = (None, 0) if C is None else _mat(C, np.int32)
+    D = np.empty((M, N), np.int32)
+    _check(lib.oracle_gemm_i8_i32(M, N, K, pa, lda, pb, ldb, pc, ldc, D.ctypes.data),
+           "oracle_gemm_i8_i32")
+    return D
+
+
+def gemm_i8_i32_at(A, B, C, ii, jj):
+    """``oracle_gemm_i8_i32_at``: exact INT32 D at output positions (ii[p], jj[p])."""
+    lib = _load()
+    M, K = A.shape
+    N = B.shape[1]
+    pa, lda = _mat(A, np.int8)
+    pb, ldb = _mat(B, np.int8)
+    pc, ldc = (None, 0) if C is None else _mat(C, np.int32)
+    ii = np.ascontiguousarray(ii, np.int64)
+    jj = np.ascontiguousarray(jj, np.int64)
+    D = np.empty(ii.shape, np.int32)
+    _check(lib.oracle_gemm_i8_i32_at(M, N, K, pa, lda, pb, ldb, pc, ldc, ii.size,
+                                     ii.ctypes.data, jj.ctypes.data, D.ctypes.data),
+           "oracle_gemm_i8_i32_at")
+    return D
+
+
+def gemm_fp8_blockscaled(A, sA, B, sB):
+    """``oracle_gemm_fp8_blockscaled``: (R, S) in FP64 for E4M3 bytes with
+    1x128 A scales and 128x128 B scales."""
+    lib = _load()
+    M, K = A.shape
+    N = B.shape[1]
+    pa, lda = _mat(A, np.uint8)
+    pb, ldb = _mat(B, np.uint8)
+    psa, ldsa = _mat(sA, np.float32)
+    psb, ldsb = _mat(sB, np.float32)
+    R = np.empty((M, N), np.float64)
+    S = np.empty((M, N), np.float64)
+    _check(lib.oracle_gemm_fp8_blockscaled(M, N, K, pa, lda, psa, ldsa, pb, ldb, psb, ldsb,
+                                           R.ctypes.data, S.ctypes.data),
+           "oracle_gemm_fp8_blockscaled")
+    return R, S
+
+
+def gemm_fp8_blockscaled_at(A, sA, B, sB, ii, jj):
+    """``oracle_gemm_fp8_blockscaled_at``: R, S at output positions (ii[p], jj[p])."""
+    lib = _load()
+    M, K = A.shape
+    N = B.shape[1]
+    pa, lda = _mat(A, np.uint8)
+    pb, ldb = _mat(B, np.uint8)
+    psa, ldsa = _mat(sA, np.float32)
+    psb, ldsb = _mat(sB, np.float32)
+    ii = np.ascontiguousarray(ii, np.int64)
+    jj = np.ascontiguousarray(jj, np.int64)
+    R = np.empty(ii.shape, np.float64)
+    S = np.empty(ii.shape, np.float64)
+    _check(lib.oracle_gemm_fp8_blockscaled_at(M, N, K, pa, lda, psa, ldsa, pb, ldb, psb, ldsb,
+                                              ii.size, ii.ctypes.data, jj.ctypes.data,
+                                              R.ctypes.data, S.ctypes.data),
+           "oracle_gemm_fp8_blockscaled_at")
+    return R, S
+
+
+def gemv_w8a8(x, s_x, W, s_w):
+    """``oracle_gemv_w8a8``: (z INT32 [N], y BF16 bits [N]) for W stored N x K."""
+    lib = _load()
+    N, K = W.shape
+    x = np.ascontiguousarray(x, np.int8)
+    assert x.size == K
+    pw, ldw = _mat(W, np.int8)
+    s_w = np.ascontiguousarray(s_w, np.float32)
+    z = np.empty(N, np.int32)
+    y = np.empty(N, np.uint16)
+    _check(lib.oracle_gemv_w8a8(N, K, x.ctypes.data, float(np.float32(s_x)), pw, ldw,
+                                s_w.ctypes.data, z.ctypes.data, y.ctypes.data),
+           "oracle_gemv_w8a8")
+    return z, y

@@ -1,0 +1,115 @@
+/*
+ * oracle.h -- plain CPU oracle for the tiled mixed-precision multiply-accumulate
+ * D = A x B + C and the batch-1 W8A8 linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link or
+ * call this library.  Its only users are the test-suite, the smoke check of the
+ * package entry point and the CPU-baseline leg of the benchmark.  It shares no
+ * source with the HIP kernels: it has its own number-format decoders, its own
+ * BF16 rounding and its own loops.
+ *
+ * What it computes (each function below names the passage it follows):
+ *   - GEMMs are the textbook sum D[i][j] = sum_k A[i][k] * B[k][j] + C[i][j]
+ *     ("Tensor Core" handbook page, section "What a Tensor Core does": one
+ *     instruction computes D = A x B + C on small matrices; the wmma_gemm.cu
+ *     program indexes A and B row-major with leading dimension = row length).
+ *     Floating point is accumulated in FP64 (exact products for FP16/BF16/E4M3
+ *     inputs), integers in INT64.  Every floating-point GEMM also returns the
+ *     bound matrix S[i][j] = sum_k |A[i][k] * B[k][j]| used by the tolerance.
+ *   - Number formats FP16 (1/5/10), BF16 (1/8/7) and FP8 E4M3 (1/4/3) follow
+ *     the format table of the same page, section "Precision: FP16, BF16, TF32,
+ *     FP8".  E4M3 is the OCP "FN" variant (bias 7, no infinities, only
+ *     S.1111.111 is NaN, largest finite 448).
+ *   - The W8A8 linear layer follows "NVIDIA A100: from chip to SIMT", sections
+ *     5.1 and 5.2: symmetric INT8 x INT8 products summed exactly in INT32, then
+ *     one dequantisation in the epilogue, (float(z) * s_x) * s_w[o], in that
+ *     left-to-right order; the weights are stored [N][K] row-major (one output
+ *     channel per row).  Output is rounded to BF16 (round to nearest even).
+ *
+ * All matrices are row-major with explicit leading dimensions (in elements).
+ * Output arrays R and S are dense M x N row-major (leading dimension N).
+ *
+ * Return codes: 0 ok, 1 invalid argument, 2 non-finite input, 3 integer
+ * overflow of the INT32 result, 4 non-integer input to an exact-integer path.
+ */
+#ifndef MPDT_ORACLE_H
+#define MPDT_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- number formats: exact decode to double, and FP32 -> BF16 RNE ---- */
+double   oracle_f16_to_f64(uint16_t h);
+double   oracle_bf16_to_f64(uint16_t b);
+double   oracle_e4m3_to_f64(uint8_t q);
+uint16_t oracle_f32_to_bf16_rne(float x);
+
+void oracle_decode_f16(const uint16_t* in, double* out, int64_t n);
+void oracle_decode_bf16(const uint16_t* in, double* out, int64_t n);
+void oracle_decode_e4m3(const uint8_t* in, double* out, int64_t n);
+void oracle_round_bf16(const float* in, uint16_t* out, int64_t n);
+
+/* ---- FP16 / BF16 GEMM, FP64 accumulation.  C may be NULL (= 0). ---- */
+int oracle_gemm_f16(int64_t M, int64_t N, int64_t K,
+                    const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                    const float* C, int64_t ldc, double* R, double* S);
+int oracle_gemm_bf16(int64_t M, int64_t N, int64_t K,
+                     const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                     const float* C, int64_t ldc, double* R, double* S);
+
+/* Same sum at P listed output positions (rows ii[p], columns jj[p]). */
+int oracle_gemm_f16_at(int64_t M, int64_t N, int64_t K,
+                       const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                       const float* C, int64_t ldc,
+                       int64_t P, const int64_t* ii, const int64_t* jj, double* R, double* S);
+int oracle_gemm_bf16_at(int64_t M, int64_t N, int64_t K,
+                        const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                        const float* C, int64_t ldc,
+                        int64_t P, const int64_t* ii, const int64_t* jj, double* R, double* S);
+
+/* FP16 GEMM whose inputs are all integers: the product sum is formed exactly
+ * in INT64 (must fit 2^24 in magnitude) and C is added with ONE IEEE FP32
+ * addition.  D is M x N FP32 (leading dimension N). */
+int oracle_gemm_f16_intexact(int64_t M, int64_t N, int64_t K,
+                             const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                             const float* C, int64_t ldc, float* D);
+
+/* ---- INT8 x INT8 -> INT32 GEMM, exact (INT64 sum, checked to fit INT32). ---- */
+int oracle_gemm_i8_i32(int64_t M, int64_t N, int64_t K,
+                       const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb,
+                       const int32_t* C, int64_t ldc, int32_t* D);
+int oracle_gemm_i8_i32_at(int64_t M, int64_t N, int64_t K,
+                          const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb,
+                          const int32_t* C, int64_t ldc,
+                          int64_t P, const int64_t* ii, const int64_t* jj, int32_t* D);
+
+/* ---- FP8 E4M3 block-scaled GEMM (block 128 along K; B scales per 128x128).
+ * R[i][j] = sum_kb (sA[i][kb] * sB[kb][j/128]) * sum_{k in block kb} a[i][k]*b[k][j]
+ * S[i][j] = sum_k |a[i][k]*sA[i][k/128]| * |b[k][j]*sB[k/128][j/128]|
+ * sA is M x ceil(K/128) (leading dimension ld_sa), sB is ceil(K/128) x
+ * ceil(N/128) (leading dimension ld_sb). ---- */
+int oracle_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K,
+                                const uint8_t* A, int64_t lda, const float* sA, int64_t ld_sa,
+                                const uint8_t* B, int64_t ldb, const float* sB, int64_t ld_sb,
+                                double* R, double* S);
+int oracle_gemm_fp8_blockscaled_at(int64_t M, int64_t N, int64_t K,
+                                   const uint8_t* A, int64_t lda, const float* sA, int64_t ld_sa,
+                                   const uint8_t* B, int64_t ldb, const float* sB, int64_t ld_sb,
+                                   int64_t P, const int64_t* ii, const int64_t* jj,
+                                   double* R, double* S);
+
+/* ---- batch-1 W8A8 linear layer.
+ * z[o] = sum_k x[k] * W[o][k] (exact), y[o] = bf16_rne((float(z[o]) * s_x) * s_w[o]).
+ * W is N x K row-major with leading dimension ldw; z and y have N entries.
+ * z may be NULL. ---- */
+int oracle_gemv_w8a8(int64_t N, int64_t K, const int8_t* x, float s_x,
+                     const int8_t* W, int64_t ldw, const float* s_w,
+                     int32_t* z, uint16_t* y);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MPDT_ORACLE_H */
