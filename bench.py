@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Benchmark of the tiled mixed-precision GEMM / W8A8 GEMV library on one
+MI355X.
+
+A step is one call of the headline workload, the BF16 GEMM D = A . B + C at
+M = N = K = 4096 (row-major, FP32 C and D), on inputs already resident in
+HBM.  The other workloads of the suite (W8A8 batch-1 GEMV 1 x 4096 . 4096 x
+14336 with a cold cache, FP8 block-scaled 4096 x 7168 x 7168, ragged FP16
+8191 x 8193 x 4099, FP16 64^3, INT8 4096^3) are timed the same way and
+reported under "extra", each with its own roofline figure.
+
+Prints ONE JSON line.  Kernel durations come from HIP events recorded on the
+stream the kernels run on (torch's current stream).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2500.0      # TFLOP/s, dense
+PEAK_FP16 = 2500.0
+PEAK_FP8 = 5000.0
+PEAK_INT8 = 5000.0      # TOP/s
+PEAK_HBM = 8000.0       # GB/s
+
+METRIC = "TFLOP/s & % MFMA peak (BF16 4096³); GB/s & % HBM peak (W8A8 GEMV)"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--only", default="all",
+                   choices=["all", "bf16", "gemv", "fp8", "f16_ragged", "f16_64", "i8", "copy"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the bounded oracle sample")
+    return p.parse_args()
+
+
+def source_digest(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "mixed_precision_dense_tiled_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, digest: str, per_launch_units: float = 1.0):
+    """Counter-measured HBM bytes per launch from profiles/traffic.json, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel)
+    if not e or e.get("source_digest") != digest:
+        return None
+    return e.get("bytes_per_launch")
+
+
+def timed(fn, steps, warmup, stream, rotate=None):
+    """Run fn(i) warmup + steps times; returns (region_ms, per-launch ms list)."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    r0.record(stream)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fn(warmup + i)
+        ev[i][1].record(stream)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in ev]
+    return r0.elapsed_time(r1), per
+
+
+def stats(per):
+    s = sorted(per)
+    n = len(s)
+    return {"mean_us": 1e3 * sum(s) / n, "median_us": 1e3 * s[n // 2], "min_us": 1e3 * s[0],
+            "max_us": 1e3 * s[-1]}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import mixed_precision_dense_tiled_amd as mp
+    from mixed_precision_dense_tiled_amd import inputs
+
+    if not os.path.exists(mp.lib_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    def to_dev(x):
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.uint16:
+            x = x.view(np.int16)
+        return torch.from_numpy(x).to(dev)
+
+    extra = {}
+    result = None
+
+    # ---------------- headline: BF16 4096^3 -----------------------------------
+    if args.only in ("all", "bf16"):
+        M = N = K = 4096
+        A, B, C = inputs.gemm16_operands(M, N, K, dist="normal", fmt="bf16")
+        tA, tB, tC = to_dev(A), to_dev(B), to_dev(C)
+        tD = torch.empty((M, N), dtype=torch.float32, device=dev)
+        region, per = timed(lambda i: mp.gemm_bf16(tA, tB, tC, out=tD), args.steps, args.warmup,
+                            stream)
+        st = stats(per)
+        flop = 2.0 * M * N * K
+        avg_s = st["mean_us"] * 1e-6
+        achieved = flop / avg_s / 1e12
+        digest = source_digest("gemm.hip", "device_common.hpp")
+        traffic = traffic_for("gemm_bf16_4096", digest)
+        result = {
+            "metric": METRIC,
+            "value": flop * args.steps / (region * 1e-3) / 1e12,
+            "unit": "TFLOP/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": region / args.steps,
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": "gemm_bf16 D=A*B+C, M=N=K=4096, row-major, A,B~N(0,1) as BF16, "
+                                   "C~N(0,1) FP32, FP32 accumulate and output",
+                       "M": M, "N": N, "K": K, "parallelism": "single GPU"},
+            "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16,
+                         "unit": "TFLOP/s", "frac": achieved / PEAK_BF16, "traffic": traffic,
+                         "kernel": "gemm_kernel<BF16,256x256>", "launch_us": st},
+        }
+        del tA, tB, tC, tD
+
+    # ---------------- W8A8 GEMV, cold cache ------------------------------------
+    if args.only in ("all", "gemv"):
+        N, K = 14336, 4096
+        x, s_x, W, s_w = inputs.w8a8_operands(N, K)
+        copies = 8  # 8 x 58.7 MB rotated: larger than the 256 MB Infinity Cache
+        tWs = [to_dev(W) for _ in range(copies)]
+        tx, tsw = to_dev(x), to_dev(s_w)
+        ty = torch.empty(N, dtype=torch.bfloat16, device=dev)
+        region, per = timed(lambda i: mp.gemv_w8a8(tx, float(s_x), tWs[i % copies], tsw, out=ty),
+                            args.steps, args.warmup, stream)
+        st = stats(per)
+        nbytes = N * K + K + 4 * N + 4 + 2 * N      # W + x + s_w + s_x + y (algorithmic)
+        gbs = nbytes / (st["mean_us"] * 1e-6) / 1e9
+        _, per_w = timed(lambda i: mp.gemv_w8a8(tx, float(s_x), tWs[0], tsw, out=ty),
+                         args.steps, args.warmup, stream)
+        stw = stats(per_w)
+        digest = source_digest("gemv_w8a8.hip", "device_common.hpp")
+        extra["gemv_w8a8"] = {
+            "workload": "batch-1 W8A8 linear, x int8 [4096], W int8 [14336 x 4096] (stored N x K), "
+                        "BF16 out; cold: 8 rotating W copies",
+            "GB_s": gbs, "algorithmic_bytes": nbytes, "launch_us": st,
+            "region_ms_per_step": region / args.steps,
+            "warm_same_W_GB_s": nbytes / (stw["mean_us"] * 1e-6) / 1e9,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM,
+                         "traffic": traffic_for("gemv_w8a8_14336x4096", digest)},
+        }
+        del tWs
+
+    # ---------------- FP8 block-scaled 4096 x 7168 x 7168 ----------------------
+    if args.only in ("all", "fp8"):
+        M, N, K = 4096, 7168, 7168
+        qa, sa, qb, sb = inputs.fp8_operands(M, N, K)
+        ta, tsa, tb, tsb = to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb)
+        td = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        steps = max(args.steps // 2, 5)
+        _, per = timed(lambda i: mp.gemm_fp8_blockscaled(ta, tsa, tb, tsb, out=td), steps,
+                       args.warmup, stream)
+        st = stats(per)
+        tf = 2.0 * M * N * K / (st["mean_us"] * 1e-6) / 1e12
+        extra["gemm_fp8_blockscaled"] = {
+            "workload": "FP8 E4M3 4096x7168x7168, 1x128 A / 128x128 B FP32 scales, BF16 out",
+            "TFLOP_s": tf, "launch_us": st,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP8, "unit": "TFLOP/s",
+                         "frac": tf / PEAK_FP8}}
+        del ta, tb, td
+
+    # ---------------- FP16 ragged 8191 x 8193 x 4099 ---------------------------
+    if args.only in ("all", "f16_ragged"):
+        M, N, K = 8191, 8193, 4099
+        A, B, C = inputs.gemm16_operands(M, N, K, dist="uniform", fmt="f16", c_zero=True)
+        tA, tB, tC = to_dev(A), to_dev(B), to_dev(C)
+        tD = torch.empty((M, N), dtype=torch.float32, device=dev)
+        steps = max(args.steps // 4, 5)
+        _, per = timed(lambda i: mp.gemm_f16(tA, tB, tC, out=tD), steps, args.warmup, stream)
+        st = stats(per)
+        tf = 2.0 * M * N * K / (st["mean_us"] * 1e-6) / 1e12
+        extra["gemm_f16_ragged"] = {
+            "workload": "FP16 8191x8193x4099 tight leading dims, C=0, FP32 out",
+            "TFLOP_s": tf, "launch_us": st,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP16, "unit": "TFLOP/s",
+                         "frac": tf / PEAK_FP16}}
+        del tA, tB, tC, tD
+
+    # ---------------- FP16 64^3 (latency) --------------------------------------
+    if args.only in ("all", "f16_64"):
+        A, B, C = inputs.gemm16_operands(64, 64, 64, dist="uniform", fmt="f16")
+        tA, tB, tC = to_dev(A), to_dev(B), to_dev(C)
+        tD = torch.empty((64, 64), dtype=torch.float32, device=dev)
+        _, per = timed(lambda i: mp.gemm_f16(tA, tB, tC, out=tD), args.steps, args.warmup, stream)
+        extra["gemm_f16_64"] = {"workload": "FP16 64^3 with FP32 C (latency bound)",
+                                "launch_us": stats(per)}
+
+    # ---------------- INT8 4096^3 ----------------------------------------------
+    if args.only in ("all", "i8"):
+        M = N = K = 4096
+        A, B, C = inputs.i8_operands(M, N, K)
+        tA, tB, tC = to_dev(A), to_dev(B), to_dev(C)
+        tD = torch.empty((M, N), dtype=torch.int32, device=dev)
+        _, per = timed(lambda i: mp.gemm_i8_i32(tA, tB, tC, out=tD), args.steps, args.warmup,
+                       stream)
+        st = stats(per)
+        tops = 2.0 * M * N * K / (st["mean_us"] * 1e-6) / 1e12
+        extra["gemm_i8_i32"] = {"workload": "INT8 4096^3, INT32 C/D", "TOP_s": tops,
+                                "launch_us": st,
+                                "roofline": {"bound": "mfma", "achieved": tops, "peak": PEAK_INT8,
+                                             "unit": "TOP/s", "frac": tops / PEAK_INT8}}
+        del tA, tB, tC, tD
+
+    # ---------------- plain copy (counter calibration) -------------------------
+    if args.only == "copy":
+        n = 256 << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        _, per = timed(lambda i: dst.copy_(src), args.steps, args.warmup, stream)
+        extra["copy"] = {"bytes_read": n, "bytes_written": n, "launch_us": stats(per)}
+
+    # ---------------- CPU baseline: the oracle on a bounded sample -------------
+    if result is not None and not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+
+    if result is None:
+        result = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1,
+                  "steps": args.steps, "warmup": args.warmup, "only": args.only}
+    result["extra"] = extra
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(target_s):
+    """The CPU oracle (FP64 GEMM + bound matrix, OpenMP) timed on a row block
+    of the BF16 4096^3 workload; throughput scaled to TFLOP/s of the full
+    problem's FLOP convention (2 per multiply-add)."""
+    cores = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+    import oracle
+    from mixed_precision_dense_tiled_amd import inputs
+    N = K = 4096
+    A, B, C = inputs.gemm16_operands(4096, N, K, dist="normal", fmt="bf16")
+    rows = 8
+    t = 0.0
+    while True:
+        t0 = time.perf_counter()
+        oracle.gemm_bf16(A[:rows], B, C[:rows])
+        t = time.perf_counter() - t0
+        if t * 2 > target_s or rows >= 4096:
+            break
+        rows = min(4096, max(rows * 2, int(rows * target_s / max(t, 1e-3) * 0.9)))
+    flop = 2.0 * rows * N * K
+    return {"value": flop / t / 1e12, "unit": "TFLOP/s", "cores": int(os.environ["OMP_NUM_THREADS"]),
+            "kind": "oracle",
+            "sample": f"oracle_gemm_bf16 (FP64 sum and bound matrix) on the first {rows} rows of "
+                      f"A (all 4096 columns of the 4096^3 BF16 workload), {t:.2f} s wall"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,128 @@
+/*
+ * mpdt.h -- C ABI of libmpdt.so: tiled mixed-precision matrix
+ * multiply-accumulate and the batch-1 W8A8 linear layer on AMD MI355X
+ * (gfx950 / CDNA4).  Plain C: integers, device pointers, a stream handle.
+ *
+ * Operations and where they are defined:
+ *   D = A x B + C on small matrices, low-precision inputs, FP32 accumulation:
+ *     "Tensor Core" chapter of the CUDA advanced handbook, sections "What a
+ *     Tensor Core does" and "Precision: FP16, BF16, TF32, FP8" (FP32
+ *     accumulation because long low-precision sums lose accuracy quickly;
+ *     INT8 inputs accumulate in INT32; FP8 needs per-tensor, per-row or
+ *     per-block scale factors).  The handbook's wmma_gemm.cu program fixes
+ *     the row-major A[M][K], B[K][N], C[M][N] convention used here.
+ *   The batch-1 W8A8 linear layer: "NVIDIA A100: from chip to SIMT",
+ *     sections 5.1 (symmetric INT8 quantisation, per-token activation scale
+ *     s_x, per-output-channel weight scale s_w, zero point 0, INT32 sum,
+ *     dequantisation once in the epilogue; weights stored [N][K] row-major,
+ *     one output channel per row) and 5.2 (the launch wrapper takes the
+ *     quantised activation, the weights, the activation scale by value, the
+ *     weight-scale array, the output and a stream; dequantisation order is
+ *     float(z) * s_x, then * s_w[o]).
+ *
+ * Conventions shared by every entry point:
+ *   - Layout: all matrices row-major; ld* are leading dimensions in ELEMENTS
+ *     (distance between the starts of consecutive rows), ld >= row length.
+ *   - Memory: every pointer is a device pointer on the current HIP device.
+ *     The caller owns all buffers; the library never allocates, frees,
+ *     copies to the host or synchronises, and keeps no per-call state.
+ *   - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the
+ *     default stream) and the call returns.  Faults inside a kernel surface
+ *     at the caller's next synchronisation.
+ *   - Errors: every argument is validated on the host BEFORE anything is
+ *     launched; on any non-success status nothing is written or launched.
+ *     mpdt_last_error() returns a thread-local description of the last
+ *     failure.
+ *   - Sizes: M == 0 or N == 0 is a successful no-op.  K == 0 gives D = C
+ *     (or 0 when C is NULL) for the GEMMs with a C operand, D = 0 for the
+ *     FP8 GEMM and y = 0 (z = 0) for the GEMV.  Dimensions must be at most
+ *     2^30 and each operand must span fewer than 2^46 bytes.
+ *   - Alignment: only element alignment is required; faster 128-bit paths
+ *     are chosen internally from the alignment of pointers and leading
+ *     dimensions.
+ *   - Aliasing: D must not overlap A, B (or scales / x / W).  C may be
+ *     exactly D (same pointer, ldc == ldd) for an in-place update; any other
+ *     overlap of C and D is rejected.
+ *   - Threads: calls from several host threads are safe.
+ *   - Device: the current device must be gfx950.
+ */
+#ifndef MPDT_H
+#define MPDT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MPDT_SUCCESS = 0,
+    MPDT_ERROR_INVALID_VALUE = 1,      /* NULL required pointer, negative or too large dim,
+                                          ld smaller than the row, GEMV with M != 1 */
+    MPDT_ERROR_MISALIGNED = 2,         /* pointer not aligned to its element size */
+    MPDT_ERROR_ALIASING = 3,           /* output overlaps an input (other than D == C) */
+    MPDT_ERROR_NO_DEVICE = 4,          /* no HIP device available */
+    MPDT_ERROR_UNSUPPORTED_DEVICE = 5, /* current device is not gfx950 */
+    MPDT_ERROR_LAUNCH = 6              /* the HIP runtime reported an error at launch */
+} mpdt_status;
+
+/* D[M x N] (FP32) = A[M x K] . B[K x N] + C[M x N] (FP32), FP32 accumulation.
+ * A and B hold IEEE binary16 bit patterns.  The product sum starts from zero
+ * and C is added once at the end, so when every partial sum is exactly
+ * representable in FP32 (e.g. small integers) D is the correctly rounded
+ * FP32 value of the exact result.  C may be NULL (treated as zero). */
+mpdt_status gemm_f16(int64_t M, int64_t N, int64_t K,
+                     const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                     const float* C, int64_t ldc, float* D, int64_t ldd, void* stream);
+
+/* As gemm_f16 with bfloat16 bit patterns for A and B. */
+mpdt_status gemm_bf16(int64_t M, int64_t N, int64_t K,
+                      const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                      const float* C, int64_t ldc, float* D, int64_t ldd, void* stream);
+
+/* D[M x N] (INT32) = A[M x K] (INT8) . B[K x N] (INT8) + C (INT32), exact
+ * as long as no partial sum leaves the INT32 range (K * 128^2 + |C| < 2^31
+ * guarantees it).  C may be NULL. */
+mpdt_status gemm_i8_i32(int64_t M, int64_t N, int64_t K,
+                        const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb,
+                        const int32_t* C, int64_t ldc, int32_t* D, int64_t ldd, void* stream);
+
+/* D[M x N] (BF16 bits, round to nearest even) =
+ *     sum over 128-wide K blocks kb of (scale_a[i][kb] * scale_b[kb][j / 128]) *
+ *         sum_{k in kb} A[i][k] . B[k][j]
+ * A[M x K] and B[K x N] are OCP FP8 E4M3 ("FN": bias 7, max 448) bytes.
+ * scale_a is M x ceil(K/128) FP32 (leading dimension ld_sa), one dequantisation
+ * multiplier per row and 128-wide K block; scale_b is ceil(K/128) x
+ * ceil(N/128) FP32 (leading dimension ld_sb), one per 128 x 128 block of B.
+ * Partial blocks at the K and N edges use their own scale.  FP32
+ * accumulation; there is no C operand. */
+mpdt_status gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K,
+                                 const uint8_t* A, int64_t lda,
+                                 const float* scale_a, int64_t ld_sa,
+                                 const uint8_t* B, int64_t ldb,
+                                 const float* scale_b, int64_t ld_sb,
+                                 uint16_t* D, int64_t ldd, void* stream);
+
+/* Batch-1 W8A8 linear layer.  M must be 1.
+ *   z[o] = sum_k x[k] * W[o][k]                      (INT32, exact)
+ *   y[o] = bf16_rne( (float(z[o]) * x_scale) * w_scale[o] )   (two FP32 products,
+ *                                                     in this order)
+ * x: K INT8 values; W: N x K INT8 stored one output channel per row, leading
+ * dimension ldw >= K; w_scale: N FP32; y: N BF16 bit patterns; z_out
+ * (optional, may be NULL): N INT32 raw sums.  Exact while K * 128^2 < 2^31. */
+mpdt_status gemv_w8a8(int64_t M, int64_t N, int64_t K,
+                      const int8_t* x, float x_scale,
+                      const int8_t* W, int64_t ldw, const float* w_scale,
+                      uint16_t* y, int32_t* z_out, void* stream);
+
+/* Static text for a status code. */
+const char* mpdt_status_string(mpdt_status s);
+/* Thread-local description of the last non-success status on this thread. */
+const char* mpdt_last_error(void);
+/* Library version: major * 10000 + minor * 100 + patch. */
+int mpdt_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MPDT_H */

@@ -1,0 +1,181 @@
+"""Python binding of libmpdt.so, the gfx950 library of tiled mixed-precision
+multiply-accumulate kernels (see include/mpdt.h for the C ABI).
+
+The functions here only marshal arguments: they take torch tensors that live
+on the GPU, read their data pointers and leading dimensions, allocate outputs
+with torch when none is given, and call the C entry point of the same name on
+torch's current stream.  All arithmetic runs in the HIP kernels; there is no
+fallback of any kind.  If the native library is missing, every call raises.
+
+Bit-pattern operands may be passed with any 2-byte dtype (float16, bfloat16,
+int16, uint16) for the 16-bit GEMMs and any 1-byte dtype (uint8, int8,
+float8_e4m3fn) for FP8; only the bytes are used.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["gemm_f16", "gemm_bf16", "gemm_i8_i32", "gemm_fp8_blockscaled", "gemv_w8a8",
+           "MpdtError", "lib", "lib_path", "version"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmpdt.so")
+_lib = None
+
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+
+
+class MpdtError(RuntimeError):
+    """Raised when a libmpdt entry point returns a non-success status."""
+
+    def __init__(self, fn, status, detail):
+        super().__init__(f"{fn} failed with status {status}: {detail}")
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded native library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"native library not built: {_LIB_PATH} is missing "
+                "(run `python -m mixed_precision_dense_tiled_amd.build`)")
+        L = ctypes.CDLL(_LIB_PATH)
+        gemm_args = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]
+        for name in ("gemm_f16", "gemm_bf16", "gemm_i8_i32"):
+            getattr(L, name).argtypes = gemm_args
+            getattr(L, name).restype = ctypes.c_int
+        L.gemm_fp8_blockscaled.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+                                           _i64, _vp, _i64, _vp]
+        L.gemm_fp8_blockscaled.restype = ctypes.c_int
+        L.gemv_w8a8.argtypes = [_i64, _i64, _i64, _vp, ctypes.c_float, _vp, _i64, _vp, _vp, _vp,
+                                _vp]
+        L.gemv_w8a8.restype = ctypes.c_int
+        L.mpdt_status_string.argtypes = [ctypes.c_int]
+        L.mpdt_status_string.restype = ctypes.c_char_p
+        L.mpdt_last_error.argtypes = []
+        L.mpdt_last_error.restype = ctypes.c_char_p
+        L.mpdt_version.argtypes = []
+        L.mpdt_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def version() -> int:
+    return lib().mpdt_version()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise MpdtError(fn, status, lib().mpdt_last_error().decode())
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _mat(t: torch.Tensor, itemsize: int, name: str):
+    """(pointer, leading dimension in elements) of a row-major 2-D tensor."""
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.element_size() != itemsize:
+        raise TypeError(f"{name} must have {itemsize}-byte elements, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    rows, cols = t.shape
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit stride along its rows")
+    ld = t.stride(0) if rows > 1 else max(cols, 1)
+    return t.data_ptr(), int(ld)
+
+
+def _gemm16(fn, A, B, C, out):
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    pa, lda = _mat(A, 2, "A")
+    pb, ldb = _mat(B, 2, "B")
+    pc, ldc = (None, N) if C is None else _mat(C, 4, "C")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    pd, ldd = _mat(out, 4, "out")
+    _check(fn, getattr(lib(), fn)(M, N, K, pa, lda, pb, ldb, pc, ldc, pd, ldd, _stream(A)))
+    return out
+
+
+def gemm_f16(A, B, C=None, out=None):
+    """D = A . B + C; A [M,K], B [K,N] FP16 bits, C/D [M,N] FP32 (C optional)."""
+    return _gemm16("gemm_f16", A, B, C, out)
+
+
+def gemm_bf16(A, B, C=None, out=None):
+    """D = A . B + C; A [M,K], B [K,N] BF16 bits, C/D [M,N] FP32 (C optional)."""
+    return _gemm16("gemm_bf16", A, B, C, out)
+
+
+def gemm_i8_i32(A, B, C=None, out=None):
+    """D = A . B + C; A [M,K], B [K,N] INT8, C/D [M,N] INT32 (C optional)."""
+    M, K = A.shape
+    N = B.shape[1]
+    pa, lda = _mat(A, 1, "A")
+    pb, ldb = _mat(B, 1, "B")
+    pc, ldc = (None, N) if C is None else _mat(C, 4, "C")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.int32, device=A.device)
+    pd, ldd = _mat(out, 4, "out")
+    _check("gemm_i8_i32", lib().gemm_i8_i32(M, N, K, pa, lda, pb, ldb, pc, ldc, pd, ldd,
+                                            _stream(A)))
+    return out
+
+
+def gemm_fp8_blockscaled(A, scale_a, B, scale_b, out=None):
+    """BF16 D = block-scaled E4M3 A [M,K] . B [K,N]; scale_a [M, ceil(K/128)],
+    scale_b [ceil(K/128), ceil(N/128)] FP32.  Returns D as a bfloat16 tensor."""
+    M, K = A.shape
+    N = B.shape[1]
+    pa, lda = _mat(A, 1, "A")
+    pb, ldb = _mat(B, 1, "B")
+    psa, ldsa = _mat(scale_a, 4, "scale_a")
+    psb, ldsb = _mat(scale_b, 4, "scale_b")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    pd, ldd = _mat(out, 2, "out")
+    _check("gemm_fp8_blockscaled",
+           lib().gemm_fp8_blockscaled(M, N, K, pa, lda, psa, ldsa, pb, ldb, psb, ldsb, pd, ldd,
+                                      _stream(A)))
+    return out
+
+
+def gemv_w8a8(x, x_scale, W, w_scale, out=None, z_out=None, return_z=False):
+    """Batch-1 W8A8 layer: x INT8 [K], W INT8 [N, K] (one output channel per
+    row), w_scale FP32 [N]; returns y BF16 [N] (and the INT32 sums when
+    return_z or z_out is given)."""
+    K = x.numel()
+    pw, ldw = _mat(W, 1, "W")
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("W must be [N, K]")
+    if x.element_size() != 1 or not x.is_contiguous() or not x.is_cuda:
+        raise ValueError("x must be a contiguous 1-byte GPU tensor")
+    if w_scale.dtype != torch.float32 or w_scale.numel() != N or not w_scale.is_contiguous():
+        raise ValueError("w_scale must be a contiguous FP32 tensor of N entries")
+    if out is None:
+        out = torch.empty(N, dtype=torch.bfloat16, device=W.device)
+    if z_out is None and return_z:
+        z_out = torch.empty(N, dtype=torch.int32, device=W.device)
+    pz = None if z_out is None else z_out.data_ptr()
+    _check("gemv_w8a8", lib().gemv_w8a8(1, N, K, x.data_ptr(), float(x_scale), pw, ldw,
+                                        w_scale.data_ptr(), out.data_ptr(), pz, _stream(W)))
+    if return_z or z_out is not None:
+        return out, z_out
+    return out

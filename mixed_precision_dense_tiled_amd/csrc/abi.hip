@@ -1,0 +1,274 @@
+// abi.hip -- the C ABI of libmpdt.so (declared in include/mpdt.h): host-side
+// argument validation, device check, kernel selection and launch.  No device
+// code lives here.  Every check runs before anything is launched.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include <cstdio>
+#include <mutex>
+#include <string>
+
+#include "kernels.hpp"
+#include "mpdt.h"
+
+#define MPDT_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+constexpr int64_t kMaxSpanBytes = int64_t(1) << 46;
+
+thread_local std::string g_last_error;
+
+mpdt_status fail(mpdt_status s, const char* fn, const char* what) {
+    char buf[256];
+    snprintf(buf, sizeof buf, "%s: %s", fn, what);
+    g_last_error = buf;
+    return s;
+}
+
+struct Span {
+    uintptr_t lo = 0, hi = 0;   // [lo, hi) bytes; empty when lo == hi
+    bool overlaps(const Span& o) const { return lo < o.hi && o.lo < hi && lo != hi && o.lo != o.hi; }
+};
+
+// Byte span of a rows x cols operand with leading dimension ld (elements).
+// Returns false when it does not fit the size limit.
+bool span_of(const void* p, int64_t rows, int64_t cols, int64_t ld, int64_t es, Span* out) {
+    *out = Span{};
+    if (rows <= 0 || cols <= 0) return true;
+    const int64_t lim = kMaxSpanBytes / es;
+    if (ld > lim) return false;
+    if (rows > 1 && (ld > 0) && (rows - 1) > (lim - cols) / ld) return false;
+    const int64_t elems = (rows - 1) * ld + cols;
+    out->lo = reinterpret_cast<uintptr_t>(p);
+    out->hi = out->lo + (uintptr_t)(elems * es);
+    return true;
+}
+
+bool aligned_to(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Current device must be a gfx950; the answer is cached per device.
+constexpr int kMaxDevices = 64;
+std::once_flag g_once[kMaxDevices];
+int g_is_gfx950[kMaxDevices];
+
+mpdt_status check_device(const char* fn) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return fail(MPDT_ERROR_NO_DEVICE, fn, "no HIP device available");
+    }
+    if (dev >= kMaxDevices) return fail(MPDT_ERROR_UNSUPPORTED_DEVICE, fn, "device index too large");
+    std::call_once(g_once[dev], [dev] {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            g_is_gfx950[dev] = 0;
+            return;
+        }
+        g_is_gfx950[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    });
+    if (!g_is_gfx950[dev]) return fail(MPDT_ERROR_UNSUPPORTED_DEVICE, fn, "current device is not gfx950");
+    return MPDT_SUCCESS;
+}
+
+mpdt_status launched(hipError_t e, const char* fn) {
+    if (e == hipSuccess) return MPDT_SUCCESS;
+    return fail(MPDT_ERROR_LAUNCH, fn, hipGetErrorString(e));
+}
+
+bool dims_ok(int64_t M, int64_t N, int64_t K) {
+    return M >= 0 && N >= 0 && K >= 0 && M <= kMaxDim && N <= kMaxDim && K <= kMaxDim;
+}
+
+// Shared validation of the three GEMMs with A[MxK], B[KxN], optional C and D.
+mpdt_status check_gemm(const char* fn, int64_t M, int64_t N, int64_t K, const void* A,
+                       int64_t lda, int64_t esa, const void* B, int64_t ldb, int64_t esb,
+                       const void* C, int64_t ldc, int64_t esc, const void* D, int64_t ldd,
+                       int64_t esd, Span extra_inputs[], int n_extra) {
+    if (!dims_ok(M, N, K)) return fail(MPDT_ERROR_INVALID_VALUE, fn, "dimension out of range");
+    if (M == 0 || N == 0) return MPDT_SUCCESS;
+    if (!D) return fail(MPDT_ERROR_INVALID_VALUE, fn, "D is NULL");
+    if (ldd < N) return fail(MPDT_ERROR_INVALID_VALUE, fn, "ldd < N");
+    if (K > 0) {
+        if (!A || !B) return fail(MPDT_ERROR_INVALID_VALUE, fn, "A or B is NULL");
+        if (lda < K) return fail(MPDT_ERROR_INVALID_VALUE, fn, "lda < K");
+        if (ldb < N) return fail(MPDT_ERROR_INVALID_VALUE, fn, "ldb < N");
+    }
+    if (C && ldc < N) return fail(MPDT_ERROR_INVALID_VALUE, fn, "ldc < N");
+    if (!aligned_to(D, esd) || (C && !aligned_to(C, esc)) ||
+        (K > 0 && (!aligned_to(A, esa) || !aligned_to(B, esb))))
+        return fail(MPDT_ERROR_MISALIGNED, fn, "pointer not aligned to its element size");
+    Span sa, sb, sc, sd;
+    if (!span_of(D, M, N, ldd, esd, &sd) || !span_of(C, C ? M : 0, N, ldc, esc, &sc) ||
+        (K > 0 && (!span_of(A, M, K, lda, esa, &sa) || !span_of(B, K, N, ldb, esb, &sb))))
+        return fail(MPDT_ERROR_INVALID_VALUE, fn, "operand too large");
+    if (sd.overlaps(sa) || sd.overlaps(sb))
+        return fail(MPDT_ERROR_ALIASING, fn, "D overlaps A or B");
+    for (int i = 0; i < n_extra; ++i)
+        if (sd.overlaps(extra_inputs[i])) return fail(MPDT_ERROR_ALIASING, fn, "D overlaps a scale array");
+    if (C && sd.overlaps(sc) && !(C == D && ldc == ldd))
+        return fail(MPDT_ERROR_ALIASING, fn, "C overlaps D without being exactly D");
+    return MPDT_SUCCESS;
+}
+
+mpdt_status run_gemm16(const char* fn, mpdt::Kind kind, int64_t M, int64_t N, int64_t K,
+                       const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                       const float* C, int64_t ldc, float* D, int64_t ldd, void* stream) {
+    mpdt_status s = check_gemm(fn, M, N, K, A, lda, 2, B, ldb, 2, C, ldc, 4, D, ldd, 4, nullptr, 0);
+    if (s != MPDT_SUCCESS || M == 0 || N == 0) return s;
+    if ((s = check_device(fn)) != MPDT_SUCCESS) return s;
+    mpdt::GemmArgs a{};
+    a.A = (const char*)A;
+    a.B = (const char*)B;
+    a.C = C;
+    a.D = D;
+    a.lda_b = lda * 2;
+    a.ldb_b = ldb * 2;
+    a.ldc = ldc;
+    a.ldd = ldd;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    const bool al = aligned_to(A, 16) && aligned_to(B, 16) && (a.lda_b % 16 == 0) &&
+                    (a.ldb_b % 16 == 0);
+    return launched(mpdt::launch_gemm(kind, a, al, (hipStream_t)stream), fn);
+}
+
+}  // namespace
+
+MPDT_EXPORT mpdt_status gemm_f16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                                 const uint16_t* B, int64_t ldb, const float* C, int64_t ldc,
+                                 float* D, int64_t ldd, void* stream) {
+    return run_gemm16("gemm_f16", mpdt::Kind::F16, M, N, K, A, lda, B, ldb, C, ldc, D, ldd, stream);
+}
+
+MPDT_EXPORT mpdt_status gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                                  const uint16_t* B, int64_t ldb, const float* C, int64_t ldc,
+                                  float* D, int64_t ldd, void* stream) {
+    return run_gemm16("gemm_bf16", mpdt::Kind::BF16, M, N, K, A, lda, B, ldb, C, ldc, D, ldd,
+                      stream);
+}
+
+MPDT_EXPORT mpdt_status gemm_i8_i32(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda,
+                                    const int8_t* B, int64_t ldb, const int32_t* C, int64_t ldc,
+                                    int32_t* D, int64_t ldd, void* stream) {
+    const char* fn = "gemm_i8_i32";
+    mpdt_status s = check_gemm(fn, M, N, K, A, lda, 1, B, ldb, 1, C, ldc, 4, D, ldd, 4, nullptr, 0);
+    if (s != MPDT_SUCCESS || M == 0 || N == 0) return s;
+    if ((s = check_device(fn)) != MPDT_SUCCESS) return s;
+    mpdt::GemmArgs a{};
+    a.A = (const char*)A;
+    a.B = (const char*)B;
+    a.C = C;
+    a.D = D;
+    a.lda_b = lda;
+    a.ldb_b = ldb;
+    a.ldc = ldc;
+    a.ldd = ldd;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    const bool al = aligned_to(A, 16) && aligned_to(B, 16) && lda % 16 == 0 && ldb % 16 == 0;
+    return launched(mpdt::launch_gemm(mpdt::Kind::I8, a, al, (hipStream_t)stream), fn);
+}
+
+MPDT_EXPORT mpdt_status gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_t* A,
+                                             int64_t lda, const float* scale_a, int64_t ld_sa,
+                                             const uint8_t* B, int64_t ldb, const float* scale_b,
+                                             int64_t ld_sb, uint16_t* D, int64_t ldd,
+                                             void* stream) {
+    const char* fn = "gemm_fp8_blockscaled";
+    if (!dims_ok(M, N, K)) return fail(MPDT_ERROR_INVALID_VALUE, fn, "dimension out of range");
+    const int64_t kb = (K + 127) / 128, nb = (N + 127) / 128;
+    Span ssa, ssb;
+    if (M > 0 && N > 0 && K > 0) {
+        if (!scale_a || !scale_b) return fail(MPDT_ERROR_INVALID_VALUE, fn, "scale array is NULL");
+        if (ld_sa < kb) return fail(MPDT_ERROR_INVALID_VALUE, fn, "ld_sa < ceil(K/128)");
+        if (ld_sb < nb) return fail(MPDT_ERROR_INVALID_VALUE, fn, "ld_sb < ceil(N/128)");
+        if (!aligned_to(scale_a, 4) || !aligned_to(scale_b, 4))
+            return fail(MPDT_ERROR_MISALIGNED, fn, "scale array not 4-byte aligned");
+        if (!span_of(scale_a, M, kb, ld_sa, 4, &ssa) || !span_of(scale_b, kb, nb, ld_sb, 4, &ssb))
+            return fail(MPDT_ERROR_INVALID_VALUE, fn, "scale array too large");
+    }
+    Span extra[2] = {ssa, ssb};
+    mpdt_status s = check_gemm(fn, M, N, K, A, lda, 1, B, ldb, 1, nullptr, 0, 4, D, ldd, 2, extra, 2);
+    if (s != MPDT_SUCCESS || M == 0 || N == 0) return s;
+    if ((s = check_device(fn)) != MPDT_SUCCESS) return s;
+    mpdt::GemmArgs a{};
+    a.A = (const char*)A;
+    a.B = (const char*)B;
+    a.C = nullptr;
+    a.D = D;
+    a.lda_b = lda;
+    a.ldb_b = ldb;
+    a.ldc = 0;
+    a.ldd = ldd;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.sA = scale_a;
+    a.ld_sa = ld_sa;
+    a.sB = scale_b;
+    a.ld_sb = ld_sb;
+    const bool al = aligned_to(A, 16) && aligned_to(B, 16) && lda % 16 == 0 && ldb % 16 == 0;
+    return launched(mpdt::launch_gemm(mpdt::Kind::FP8, a, al, (hipStream_t)stream), fn);
+}
+
+MPDT_EXPORT mpdt_status gemv_w8a8(int64_t M, int64_t N, int64_t K, const int8_t* x, float x_scale,
+                                  const int8_t* W, int64_t ldw, const float* w_scale, uint16_t* y,
+                                  int32_t* z_out, void* stream) {
+    const char* fn = "gemv_w8a8";
+    if (!dims_ok(M, N, K)) return fail(MPDT_ERROR_INVALID_VALUE, fn, "dimension out of range");
+    if (M != 1) return fail(MPDT_ERROR_INVALID_VALUE, fn, "M must be 1 (batch-1 layer)");
+    if (N == 0) return MPDT_SUCCESS;
+    if (!y || !w_scale) return fail(MPDT_ERROR_INVALID_VALUE, fn, "y or w_scale is NULL");
+    if (K > 0) {
+        if (!x || !W) return fail(MPDT_ERROR_INVALID_VALUE, fn, "x or W is NULL");
+        if (ldw < K) return fail(MPDT_ERROR_INVALID_VALUE, fn, "ldw < K");
+    }
+    if (!aligned_to(y, 2) || !aligned_to(w_scale, 4) || (z_out && !aligned_to(z_out, 4)))
+        return fail(MPDT_ERROR_MISALIGNED, fn, "pointer not aligned to its element size");
+    Span sx, sw, ss, sy, sz;
+    if (!span_of(W, K > 0 ? N : 0, K, ldw, 1, &sw) || !span_of(x, K > 0 ? 1 : 0, K, K, 1, &sx) ||
+        !span_of(w_scale, 1, N, N, 4, &ss) || !span_of(y, 1, N, N, 2, &sy) ||
+        !span_of(z_out, z_out ? 1 : 0, N, N, 4, &sz))
+        return fail(MPDT_ERROR_INVALID_VALUE, fn, "operand too large");
+    if (sy.overlaps(sx) || sy.overlaps(sw) || sy.overlaps(ss) || sz.overlaps(sx) ||
+        sz.overlaps(sw) || sz.overlaps(ss) || sz.overlaps(sy))
+        return fail(MPDT_ERROR_ALIASING, fn, "an output overlaps an input or the other output");
+    mpdt_status s = check_device(fn);
+    if (s != MPDT_SUCCESS) return s;
+    mpdt::GemvArgs a{};
+    a.x = x;
+    a.W = W;
+    a.ldw = ldw;
+    a.w_scale = w_scale;
+    a.y = y;
+    a.z = z_out;
+    a.x_scale = x_scale;
+    a.N = (int)N;
+    a.K = (int)K;
+    const bool al = aligned_to(x, 16) && aligned_to(W, 16) && ldw % 16 == 0;
+    return launched(mpdt::launch_gemv_w8a8(a, al, (hipStream_t)stream), fn);
+}
+
+MPDT_EXPORT const char* mpdt_status_string(mpdt_status s) {
+    switch (s) {
+        case MPDT_SUCCESS: return "success";
+        case MPDT_ERROR_INVALID_VALUE: return "invalid value";
+        case MPDT_ERROR_MISALIGNED: return "misaligned pointer";
+        case MPDT_ERROR_ALIASING: return "output aliases an input";
+        case MPDT_ERROR_NO_DEVICE: return "no HIP device";
+        case MPDT_ERROR_UNSUPPORTED_DEVICE: return "unsupported device (gfx950 required)";
+        case MPDT_ERROR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+MPDT_EXPORT const char* mpdt_last_error(void) { return g_last_error.c_str(); }
+
+MPDT_EXPORT int mpdt_version(void) { return 100; }

@@ -1,0 +1,118 @@
+// gemv_w8a8.hip -- batch-1 W8A8 linear layer for gfx950, a streaming
+// wavefront-reduction kernel (no matrix instructions).
+//
+// The operation is the one of "NVIDIA A100: from chip to SIMT", sections 5.1
+// and 5.2: z[o] = sum_k x[k] * W[o][k] with symmetric INT8 operands summed
+// exactly in INT32, then y[o] = (float(z[o]) * s_x) * s_w[o] in the epilogue
+// (rounded here to BF16), with W stored one output channel per row.  That
+// page's teaching kernel pads the single activation row into 16-row matrix
+// tiles (about 16x wasted arithmetic, section 5.5) and notes the layer is
+// weight-bandwidth bound; this kernel instead streams W once at HBM rate:
+//
+//   * one wavefront owns R consecutive output rows; lane l reads the 16-byte
+//     chunks l, l + 64, l + 128, ... of each row (every load instruction moves
+//     1 KiB of one row, fully coalesced) and the matching chunks of x (4 KiB,
+//     shared by all waves through L2);
+//   * all R * (K / 1024) loads of a wave are issued before the first use, so
+//     a resident grid keeps the whole weight stream in flight;
+//   * v_dot4 accumulates 4 byte products per instruction into INT32;
+//   * a butterfly over the 64 lanes reduces each row; lane r writes row r.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace mpdt {
+
+constexpr int GEMV_WAVES = 4;        // wavefronts per workgroup
+constexpr int GEMV_ROWS = 4;         // output rows per wavefront
+constexpr int GEMV_U = 4;            // 16-byte chunks per lane per row per pass (K = 4096 in one pass)
+
+__device__ __forceinline__ int dot16(u32x4 w, u32x4 x, int acc) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_sdot4((int)w[q], (int)x[q], acc, false);
+    return acc;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+template <bool ALIGNED>
+__global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_w8a8_kernel(GemvArgs g) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int row0 = (blockIdx.x * GEMV_WAVES + wave) * GEMV_ROWS;
+    if (row0 >= g.N) return;                      // whole wave past the end: nothing to do
+
+    const int64_t kbytes = g.K;
+    const char* x = (const char*)g.x;
+    const char* xend = x + kbytes;
+    int acc[GEMV_ROWS];
+#pragma unroll
+    for (int r = 0; r < GEMV_ROWS; ++r) acc[r] = 0;
+
+    for (int64_t kb = 0; kb < kbytes; kb += 64 * 16 * GEMV_U) {
+        u32x4 xv[GEMV_U];
+        u32x4 wv[GEMV_ROWS][GEMV_U];
+#pragma unroll
+        for (int u = 0; u < GEMV_U; ++u) {
+            const int64_t off = kb + 16 * (lane + 64 * u);
+            xv[u] = (ALIGNED && off + 16 <= kbytes) ? load16_fast(x + off)
+                                                     : load16_row<ALIGNED>(x + off, xend);
+        }
+#pragma unroll
+        for (int r = 0; r < GEMV_ROWS; ++r) {
+            const int row = row0 + r;
+            const char* rowp = (const char*)g.W + (int64_t)row * g.ldw;
+#pragma unroll
+            for (int u = 0; u < GEMV_U; ++u) {
+                const int64_t off = kb + 16 * (lane + 64 * u);
+                const char* p = rowp + off;
+                if (row >= g.N)
+                    wv[r][u] = u32x4{0u, 0u, 0u, 0u};
+                else if (ALIGNED && off + 16 <= kbytes)
+                    wv[r][u] = load16_fast(p);
+                else
+                    wv[r][u] = load16_row<ALIGNED>(p, rowp + kbytes);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < GEMV_ROWS; ++r)
+#pragma unroll
+            for (int u = 0; u < GEMV_U; ++u) acc[r] = dot16(wv[r][u], xv[u], acc[r]);
+    }
+
+    int z[GEMV_ROWS];
+#pragma unroll
+    for (int r = 0; r < GEMV_ROWS; ++r) z[r] = wave_sum(acc[r]);
+
+#pragma unroll
+    for (int r = 0; r < GEMV_ROWS; ++r) {
+        const int row = row0 + r;
+        if (lane == r && row < g.N) {
+            if (g.z) g.z[row] = z[r];
+            // dequantise: two FP32 products, activation scale first
+            float v = (float)z[r];
+            v = v * g.x_scale;
+            v = v * g.w_scale[row];
+            g.y[row] = f32_to_bf16_bits(v);
+        }
+    }
+}
+
+hipError_t launch_gemv_w8a8(const GemvArgs& a, bool aligned, hipStream_t stream) {
+    if (a.N <= 0) return hipSuccess;
+    const int rows_per_wg = GEMV_WAVES * GEMV_ROWS;
+    dim3 grid((unsigned)((a.N + rows_per_wg - 1) / rows_per_wg)), block(64 * GEMV_WAVES);
+    if (aligned)
+        hipLaunchKernelGGL(gemv_w8a8_kernel<true>, grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL(gemv_w8a8_kernel<false>, grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace mpdt

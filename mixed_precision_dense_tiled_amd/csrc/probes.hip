@@ -1,0 +1,125 @@
+// probes.hip -- libmpdt_probes.so: single-wavefront kernels that pin the
+// gfx950 lane layouts the GEMM kernels rely on.  Used only by the test-suite;
+// every probe touches a fixed, small, in-bounds set of addresses.
+//
+//   mpdt_probe_tr(bits, lds_image, offsets, out): copies a 4 KiB image into
+//     LDS, then each of the 64 lanes issues one transposing read
+//     (ds_read_b64_tr_b16 when bits == 16, ds_read_b64_tr_b8 when bits == 8)
+//     at its byte offset and writes the 8 bytes it received to out[lane].
+//   mpdt_probe_mfma(kind, A, B, D): one MFMA of the GEMM kernels (kind 0 f16
+//     32x32x16, 1 bf16 32x32x16, 2 i8 32x32x32, 3 fp8 e4m3 32x32x64) with A
+//     (32 x KS, row-major) and B (KS x 32, row-major) loaded with the lane
+//     mapping the GEMM kernels use (lane l: row / column l % 32, K elements
+//     [KS/2 * (l/32), KS/2 * (l/32 + 1)) in order), D (32 x 32, row-major,
+//     FP32 or INT32) stored with the accumulator mapping the GEMM epilogue
+//     uses (register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.hpp"
+
+#define MPDT_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace mpdt {
+
+__global__ __launch_bounds__(64) void probe_tr_kernel(int bits, const u32x4* image,
+                                                      const uint32_t* offsets, u32x2* out) {
+    __shared__ __attribute__((aligned(16))) char smem[4096];
+    MPDT_LDS char* lds = lds_cast(smem);
+    const int lane = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_store16(lds, 16 * (lane + 64 * i), image[lane + 64 * i]);
+    __syncthreads();
+    const uint32_t off = offsets[lane] & (4096u - 8u);
+    out[lane] = (bits == 16) ? lds_read_tr16(lds, off) : lds_read_tr8(lds, off);
+}
+
+template <int KIND>
+__global__ __launch_bounds__(64) void probe_mfma_kernel(const char* A, const char* B, void* D) {
+    const int l = threadIdx.x;
+    const int row = l & 31, half = l >> 5;
+    if constexpr (KIND <= 2) {
+        // 16 bytes of K per lane: f16/bf16 8 elements, i8 16 elements
+        constexpr int ES = (KIND <= 1) ? 2 : 1;
+        constexpr int KS = 32 / ES;                 // K of the instruction
+        u32x4 a, b;
+        for (int w = 0; w < 4; ++w) {
+            uint32_t av = 0, bv = 0;
+            for (int q = 0; q < 4 / ES; ++q) {
+                const int k = half * (KS / 2) + w * (4 / ES) + q;
+                uint32_t ea = 0, eb = 0;
+                if (ES == 2) {
+                    ea = ((const uint16_t*)A)[row * KS + k];
+                    eb = ((const uint16_t*)B)[k * 32 + row];
+                } else {
+                    ea = ((const uint8_t*)A)[row * KS + k];
+                    eb = ((const uint8_t*)B)[k * 32 + row];
+                }
+                av |= ea << (8 * ES * q);
+                bv |= eb << (8 * ES * q);
+            }
+            a[w] = av;
+            b[w] = bv;
+        }
+        if constexpr (KIND == 0) {
+            f32x16 c = {};
+            c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+            for (int r = 0; r < 16; ++r)
+                ((float*)D)[(8 * (r >> 2) + 4 * half + (r & 3)) * 32 + row] = c[r];
+        } else if constexpr (KIND == 1) {
+            f32x16 c = {};
+            c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+            for (int r = 0; r < 16; ++r)
+                ((float*)D)[(8 * (r >> 2) + 4 * half + (r & 3)) * 32 + row] = c[r];
+        } else {
+            i32x16 c = {};
+            c = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
+                                                      __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+            for (int r = 0; r < 16; ++r)
+                ((int32_t*)D)[(8 * (r >> 2) + 4 * half + (r & 3)) * 32 + row] = c[r];
+        }
+    } else {
+        // FP8: 32 bytes of K per lane, K = 64
+        i32x8 a, b;
+        for (int w = 0; w < 8; ++w) {
+            uint32_t av = 0, bv = 0;
+            for (int q = 0; q < 4; ++q) {
+                const int k = half * 32 + w * 4 + q;
+                av |= (uint32_t)((const uint8_t*)A)[row * 64 + k] << (8 * q);
+                bv |= (uint32_t)((const uint8_t*)B)[k * 32 + row] << (8 * q);
+            }
+            a[w] = (int32_t)av;
+            b[w] = (int32_t)bv;
+        }
+        f32x16 c = {};
+        c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+        for (int r = 0; r < 16; ++r)
+            ((float*)D)[(8 * (r >> 2) + 4 * half + (r & 3)) * 32 + row] = c[r];
+    }
+}
+
+}  // namespace mpdt
+
+MPDT_EXPORT int mpdt_probe_tr(int bits, const void* image, const uint32_t* offsets, void* out,
+                              void* stream) {
+    if (bits != 8 && bits != 16) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(mpdt::probe_tr_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, bits,
+                       (const mpdt::u32x4*)image, offsets, (mpdt::u32x2*)out);
+    return (int)hipGetLastError();
+}
+
+MPDT_EXPORT int mpdt_probe_mfma(int kind, const void* A, const void* B, void* D, void* stream) {
+    const char* a = (const char*)A;
+    const char* b = (const char*)B;
+    hipStream_t s = (hipStream_t)stream;
+    switch (kind) {
+        case 0: hipLaunchKernelGGL(mpdt::probe_mfma_kernel<0>, dim3(1), dim3(64), 0, s, a, b, D); break;
+        case 1: hipLaunchKernelGGL(mpdt::probe_mfma_kernel<1>, dim3(1), dim3(64), 0, s, a, b, D); break;
+        case 2: hipLaunchKernelGGL(mpdt::probe_mfma_kernel<2>, dim3(1), dim3(64), 0, s, a, b, D); break;
+        case 3: hipLaunchKernelGGL(mpdt::probe_mfma_kernel<3>, dim3(1), dim3(64), 0, s, a, b, D); break;
+        default: return (int)hipErrorInvalidValue;
+    }
+    return (int)hipGetLastError();
+}

@@ -15,9 +15,9 @@ def pytest_configure(config):
 
 
 def _ensure_built():
-    need = [os.path.join(ROOT, "oracle", "liboracle.so")]
-    _later = [
-            os.path.join(ROOT, "mixed_precision_dense_tiled_amd", "libmpdt.so")]
+    pkg = os.path.join(ROOT, "mixed_precision_dense_tiled_amd")
+    need = [os.path.join(ROOT, "oracle", "liboracle.so"), os.path.join(pkg, "libmpdt.so"),
+            os.path.join(pkg, "libmpdt_probes.so")]
     if not all(os.path.exists(p) for p in need):
         import __graft_entry__
         __graft_entry__.build()

@@ -1,0 +1,209 @@
+"""GPU parity of the GEMM entry points against the CPU oracle, element by
+element, at sizes that span several 256x256 workgroup tiles with ragged M, N
+and K tails, plus the edge cases: odd leading dimensions, base pointers off
+16-byte alignment, C = NULL, in-place D == C, K = 0, M = 0, tiny shapes, and
+guard bands around D that must stay untouched.
+
+Bars: FP16/BF16 |D - R| <= 1e-3 * S + 1e-6 per element and relative Frobenius
+error <= 1e-5; integer-valued FP16 inputs bit-exact; INT8 bit-exact; FP8 the
+same per-element bound against the unrounded result and Frobenius <= 1e-2."""
+import numpy as np
+import pytest
+import torch
+
+import mixed_precision_dense_tiled_amd as mp
+import oracle
+from helpers import check_fp, dev, host
+from mixed_precision_dense_tiled_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+NAN16 = {"f16": 0x7E00, "bf16": 0x7FC0}
+FN16 = {"f16": (mp.gemm_f16, oracle.gemm_f16), "bf16": (mp.gemm_bf16, oracle.gemm_bf16)}
+
+
+def run16(fmt, A, B, C, lda=None, ldb=None, ldc=None, ldd=None, dist_check=True):
+    M, K = A.shape
+    N = B.shape[1]
+    gpu, orc = FN16[fmt]
+    tA = dev(A, lda, pad=NAN16[fmt])
+    tB = dev(B, ldb, pad=NAN16[fmt])
+    tC = None if C is None else dev(C, ldc, pad=np.float32(np.nan))
+    out = None
+    if ldd is not None:
+        out = dev(np.zeros((M, N), np.float32), ldd, pad=np.float32(-7.0))
+    D = gpu(tA, tB, tC, out=out)
+    torch.cuda.synchronize()
+    Dh = host(D)
+    R, S = orc(A, B, C)
+    return Dh, R, S, D
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("M,N,K", [(64, 64, 64), (300, 520, 200), (513, 257, 129),
+                                   (256, 256, 256), (1, 1, 1), (17, 300, 65), (260, 31, 1000)])
+def test_gemm16_parity(gpu_ok, fmt, M, N, K):
+    A, B, C = inputs.gemm16_operands(M, N, K, dist="uniform", fmt=fmt,
+                                     seeds=(M + 1, N + 2, K + 3))
+    D, R, S, _ = run16(fmt, A, B, C)
+    check_fp(D, R, S, 1e-5, f"{fmt} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_gemm16_normal_inputs(gpu_ok, fmt):
+    A, B, C = inputs.gemm16_operands(384, 640, 512, dist="normal", fmt=fmt)
+    D, R, S, _ = run16(fmt, A, B, C)
+    check_fp(D, R, S, 1e-5, fmt)
+
+
+def test_f16_64_integer_variant_bit_exact(gpu_ok):
+    A, B, C = inputs.gemm16_operands(64, 64, 64, dist="int4", fmt="f16")
+    D, _, _, _ = run16("f16", A, B, C)
+    ref = oracle.gemm_f16_intexact(A, B, C)
+    assert np.array_equal(D.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_integer_variant_bit_exact_multi_tile(gpu_ok, fmt):
+    # integer inputs keep every partial sum exact: D must be bit-exact at any size
+    A, B, C = inputs.gemm16_operands(300, 520, 400, dist="int4", fmt=fmt, seeds=(4, 5, 6))
+    D, R, _, _ = run16(fmt, A, B, C)
+    # R = exact integer sum + C in FP64 (exact here: |sum| <= 6400, C in [-1, 1])
+    assert np.array_equal(D, R.astype(np.float32))
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_unaligned_leading_dims_and_nan_padding(gpu_ok, fmt):
+    M, N, K = 301, 333, 203
+    A, B, C = inputs.gemm16_operands(M, N, K, fmt=fmt, seeds=(7, 8, 9))
+    D, R, S, _ = run16(fmt, A, B, C, lda=K + 1, ldb=N + 3, ldc=N + 5, ldd=N + 7)
+    check_fp(D, R, S, 1e-5, "odd ld")
+
+
+@pytest.mark.parametrize("shift", [2, 4, 8])
+def test_base_pointer_offsets(gpu_ok, shift):
+    M, N, K = 200, 300, 150
+    A, B, C = inputs.gemm16_operands(M, N, K, fmt="f16", seeds=(10, 11, 12))
+    e = shift // 2
+    tA = dev(np.concatenate([np.zeros(e, np.uint16), A.ravel()]))[e:].view(M, K)
+    tB = dev(np.concatenate([np.zeros(e, np.uint16), B.ravel()]))[e:].view(K, N)
+    ce = max(shift // 4, 1)
+    tC = dev(np.concatenate([np.zeros(ce, np.float32), C.ravel()]))[ce:].view(M, N)
+    D = host(mp.gemm_f16(tA, tB, tC))
+    R, S = oracle.gemm_f16(A, B, C)
+    check_fp(D, R, S, 1e-5, f"shift {shift}")
+
+
+def test_c_null_equals_zero_c_bitwise(gpu_ok):
+    A, B, _ = inputs.gemm16_operands(300, 270, 310, fmt="f16", with_c=False)
+    t0 = mp.gemm_f16(dev(A), dev(B), None)
+    tz = mp.gemm_f16(dev(A), dev(B), torch.zeros(300, 270, device=gpu_ok))
+    assert torch.equal(t0.view(torch.int32), tz.view(torch.int32))
+
+
+def test_in_place_d_equals_c(gpu_ok):
+    A, B, C = inputs.gemm16_operands(280, 290, 130, fmt="bf16", seeds=(13, 14, 15))
+    tC = dev(C)
+    D = mp.gemm_bf16(dev(A), dev(B), tC, out=tC)
+    assert D.data_ptr() == tC.data_ptr()
+    R, S = oracle.gemm_bf16(A, B, C)
+    check_fp(host(D), R, S, 1e-5, "in place")
+
+
+def test_k_zero_and_m_zero(gpu_ok):
+    C = inputs.uniform_f32((70, 90), 3)
+    A = torch.zeros((70, 0), dtype=torch.int16, device=gpu_ok)
+    B = torch.zeros((0, 90), dtype=torch.int16, device=gpu_ok)
+    D = host(mp.gemm_f16(A, B, dev(C)))
+    assert np.array_equal(D, C)
+    D = host(mp.gemm_f16(A, B, None))
+    assert not D.any()
+    e = torch.zeros((0, 90), dtype=torch.float32, device=gpu_ok)
+    mp.gemm_f16(torch.zeros((0, 5), dtype=torch.int16, device=gpu_ok),
+                torch.zeros((5, 90), dtype=torch.int16, device=gpu_ok), None, out=e)
+
+
+def test_guard_bands_untouched(gpu_ok):
+    M, N, K = 257, 259, 70
+    A, B, C = inputs.gemm16_operands(M, N, K, fmt="f16", seeds=(16, 17, 18))
+    ldd = N + 16
+    buf = torch.full((M + 8, ldd), -3.25, dtype=torch.float32, device=gpu_ok)
+    out = buf[4:4 + M, 3:3 + N]
+    mp.gemm_f16(dev(A), dev(B), dev(C), out=out)
+    h = host(buf)
+    R, S = oracle.gemm_f16(A, B, C)
+    check_fp(h[4:4 + M, 3:3 + N], R, S, 1e-5, "guarded")
+    mask = np.ones_like(h, bool)
+    mask[4:4 + M, 3:3 + N] = False
+    assert (h[mask] == -3.25).all()
+
+
+EDGE = [1, 15, 16, 17, 31, 33, 127, 128, 129, 255, 257]
+
+
+def test_edge_sweep(gpu_ok):
+    r = np.random.default_rng(2024)
+    cases = [(m, n, k) for m in EDGE for n in EDGE for k in EDGE]
+    pick = [cases[i] for i in r.choice(len(cases), 60, replace=False)]
+    pick += [(257, 257, 257), (1, 257, 1), (257, 1, 129), (129, 129, 1)]
+    for (M, N, K) in pick:
+        for fmt in ("f16", "bf16"):
+            A, B, C = inputs.gemm16_operands(M, N, K, fmt=fmt, seeds=(M, N, K))
+            D, R, S, _ = run16(fmt, A, B, C, lda=K + (M % 3), ldb=N + (K % 2))
+            check_fp(D, R, S, 1e-5, f"{fmt} {M}x{N}x{K}")
+
+
+# ------------------------------------------------------------------ INT8 --
+@pytest.mark.parametrize("M,N,K", [(64, 64, 64), (300, 520, 200), (513, 257, 129), (1, 1, 1),
+                                   (256, 256, 512)])
+def test_i8_bit_exact(gpu_ok, M, N, K):
+    A, B, C = inputs.i8_operands(M, N, K, seeds=(M, N, K))
+    D = host(mp.gemm_i8_i32(dev(A), dev(B), dev(C)))
+    assert np.array_equal(D, oracle.gemm_i8_i32(A, B, C))
+
+
+def test_i8_extremes_unaligned_and_null_c(gpu_ok):
+    M, N, K = 130, 270, 1031
+    A = np.full((M, K), -128, np.int8)
+    B = np.full((K, N), -128, np.int8)
+    B[:, ::3] = 127
+    D = host(mp.gemm_i8_i32(dev(A, K + 5, pad=99), dev(B, N + 3, pad=-99), None))
+    assert np.array_equal(D, oracle.gemm_i8_i32(A, B, None))
+    A, B, C = inputs.i8_operands(M, N, K, seeds=(1, 2, 3))
+    D = host(mp.gemm_i8_i32(dev(A, K + 7, pad=5), dev(B, N + 1, pad=5), dev(C, N + 2)))
+    assert np.array_equal(D, oracle.gemm_i8_i32(A, B, C))
+
+
+# ------------------------------------------------------------------- FP8 --
+def run_fp8(qa, sa, qb, sb, lda=None, ldb=None):
+    D = mp.gemm_fp8_blockscaled(dev(qa, lda, pad=0x7F), dev(sa), dev(qb, ldb, pad=0x7F), dev(sb))
+    torch.cuda.synchronize()
+    got = oracle.bf16_to_f64(host(D).view(np.uint16))
+    R, S = oracle.gemm_fp8_blockscaled(qa, sa, qb, sb)
+    return got, R, S
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 256, 256), (300, 520, 400), (129, 130, 131),
+                                   (1, 1, 1), (256, 512, 1024)])
+def test_fp8_parity(gpu_ok, M, N, K):
+    qa, sa, qb, sb = inputs.fp8_operands(M, N, K, seeds=(M, N))
+    got, R, S = run_fp8(qa, sa, qb, sb)
+    check_fp(got, R, S, 1e-2, f"fp8 {M}x{N}x{K}")
+
+
+def test_fp8_unaligned_and_unit_scales(gpu_ok):
+    M, N, K = 200, 300, 333
+    qa, sa, qb, sb = inputs.fp8_operands(M, N, K, seeds=(21, 22))
+    got, R, S = run_fp8(qa, sa, qb, sb, lda=K + 3, ldb=N + 5)
+    check_fp(got, R, S, 1e-2, "fp8 unaligned")
+    ones_a, ones_b = np.ones_like(sa), np.ones_like(sb)
+    got, R, S = run_fp8(qa, ones_a, qb, ones_b)
+    check_fp(got, R, S, 1e-2, "fp8 unit scales")
+
+
+def test_fp8_k_zero(gpu_ok):
+    D = mp.gemm_fp8_blockscaled(torch.zeros((40, 0), dtype=torch.uint8, device=gpu_ok),
+                                torch.zeros((40, 1), device=gpu_ok),
+                                torch.zeros((0, 50), dtype=torch.uint8, device=gpu_ok),
+                                torch.zeros((1, 1), device=gpu_ok))
+    assert not host(D).any()

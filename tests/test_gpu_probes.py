@@ -1,0 +1,95 @@
+"""gfx950 lane layouts the GEMM kernels rely on, pinned on the GPU with
+single-wavefront probes: the transposing LDS reads (ds_read_b64_tr_b16 /
+_b8) and the operand / accumulator mappings of each MFMA used, including the
+E4M3 decode of every non-NaN FP8 code inside the matrix core."""
+import numpy as np
+import pytest
+import torch
+
+from helpers import dev, host, probes
+
+pytestmark = pytest.mark.gpu
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+@pytest.mark.parametrize("bits", [16, 8])
+def test_transposing_read_layout(gpu_ok, bits):
+    r = np.random.default_rng(bits)
+    image = r.integers(0, 256, 4096, dtype=np.uint8)
+    offs = (r.integers(0, 4096 // 8, 64) * 8).astype(np.uint32)
+    out = torch.zeros(64 * 8, dtype=torch.uint8, device=gpu_ok)
+    t_img, t_off = dev(image), dev(offs.view(np.int32))
+    assert probes().mpdt_probe_tr(bits, t_img.data_ptr(), t_off.data_ptr(), out.data_ptr(),
+                                  _stream()) == 0
+    got = host(out).reshape(64, 8)
+    exp = np.zeros((64, 8), np.uint8)
+    for lane in range(64):
+        g, q = lane // 16, lane % 16
+        if bits == 16:
+            for e in range(4):   # element e of lane q: row e of column q of the 4x16 block
+                a = offs[16 * g + 4 * e + q // 4] + 2 * (q % 4)
+                exp[lane, 2 * e:2 * e + 2] = image[a:a + 2]
+        else:
+            for e in range(8):   # byte e of lane q: row e of column q of the 8x16 block
+                exp[lane, e] = image[offs[16 * g + 2 * e + q // 8] + q % 8]
+    assert np.array_equal(got, exp)
+
+
+def _run_mfma(kind, A, B, out_dtype):
+    D = torch.zeros((32, 32), dtype=out_dtype, device="cuda:0")
+    ta, tb = dev(A), dev(B)
+    assert probes().mpdt_probe_mfma(kind, ta.data_ptr(), tb.data_ptr(), D.data_ptr(), _stream()) == 0
+    return host(D)
+
+
+@pytest.mark.parametrize("kind,fmt", [(0, "f16"), (1, "bf16")])
+def test_mfma16_layout_exact(gpu_ok, kind, fmt):
+    r = np.random.default_rng(kind)
+    a = r.integers(-8, 9, (32, 16)).astype(np.float32)
+    b = r.integers(-8, 9, (16, 32)).astype(np.float32)
+    if fmt == "f16":
+        A, B = a.astype(np.float16).view(np.uint16), b.astype(np.float16).view(np.uint16)
+    else:
+        A = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        B = torch.from_numpy(b).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    D = _run_mfma(kind, A, B, torch.float32)
+    assert np.array_equal(D, (a.astype(np.int64) @ b.astype(np.int64)).astype(np.float32))
+
+
+def test_mfma_i8_layout_exact(gpu_ok):
+    r = np.random.default_rng(7)
+    A = r.integers(-128, 128, (32, 32)).astype(np.int8)
+    B = r.integers(-128, 128, (32, 32)).astype(np.int8)
+    D = _run_mfma(2, A, B, torch.int32)
+    assert np.array_equal(D, (A.astype(np.int64) @ B.astype(np.int64)).astype(np.int32))
+
+
+def _e4m3(q):
+    return torch.from_numpy(np.ascontiguousarray(q)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_mfma_fp8_layout_and_every_code(gpu_ok):
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)   # 254 finite codes
+    A = np.resize(codes, 32 * 64).reshape(32, 64).copy()
+    A[:, ::7] = np.random.default_rng(3).permutation(np.resize(codes, A[:, ::7].size)).reshape(
+        A[:, ::7].shape)
+    a = _e4m3(A)
+    one = np.uint8(0x38)   # 1.0
+    for t in range(2):     # B selects column k = j + 32 t of A: D[i][j] = a[i][j + 32 t]
+        B = np.zeros((64, 32), np.uint8)
+        B[np.arange(32) + 32 * t, np.arange(32)] = one
+        D = _run_mfma(3, A, B, torch.float32)
+        assert np.array_equal(D.astype(np.float64), a[:, 32 * t:32 * t + 32])
+    seen = set(A[:, :].ravel().tolist())
+    assert seen == set(codes.tolist())
+    # a general product
+    r = np.random.default_rng(11)
+    B = r.choice(codes, (64, 32)).astype(np.uint8)
+    D = _run_mfma(3, A, B, torch.float32)
+    b = _e4m3(B)
+    ref = a @ b
+    S = np.abs(a) @ np.abs(b)
+    assert (np.abs(D - ref) <= 2.0 ** -22 * S + 1e-30).all()
