@@ -356,7 +356,12 @@ void gemm_kernel(GemmArgs g) {
                     const uint32_t r = wm * C::WM + i * 32 + 8 * r4 + 4 * lhalf;
                     const u32x4 v = lds_load16((const MPDT_LDS char*)sa, r * 4);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) f[4 * r4 + q] = __builtin_bit_cast(float, v[q]) * sb;
+                    for (int q = 0; q < 4; ++q) {
+                        // (element to scalar first: bit-casting a vector element
+                        // directly reads element 0 with this compiler)
+                        const uint32_t bits = v[q];
+                        f[4 * r4 + q] = __uint_as_float(bits) * sb;
+                    }
                 }
 #pragma unroll
                 for (int j = 0; j < C::TN; ++j)

@@ -188,17 +188,17 @@ def run_fp8(qa, sa, qb, sb, lda=None, ldb=None):
 def test_fp8_parity(gpu_ok, M, N, K):
     qa, sa, qb, sb = inputs.fp8_operands(M, N, K, seeds=(M, N))
     got, R, S = run_fp8(qa, sa, qb, sb)
-    check_fp(got, R, S, 1e-2, f"fp8 {M}x{N}x{K}")
+    check_fp(got, R, S, 1e-2, f"fp8 {M}x{N}x{K}", bf16_out=True)
 
 
 def test_fp8_unaligned_and_unit_scales(gpu_ok):
     M, N, K = 200, 300, 333
     qa, sa, qb, sb = inputs.fp8_operands(M, N, K, seeds=(21, 22))
     got, R, S = run_fp8(qa, sa, qb, sb, lda=K + 3, ldb=N + 5)
-    check_fp(got, R, S, 1e-2, "fp8 unaligned")
+    check_fp(got, R, S, 1e-2, "fp8 unaligned", bf16_out=True)
     ones_a, ones_b = np.ones_like(sa), np.ones_like(sb)
     got, R, S = run_fp8(qa, ones_a, qb, ones_b)
-    check_fp(got, R, S, 1e-2, "fp8 unit scales")
+    check_fp(got, R, S, 1e-2, "fp8 unit scales", bf16_out=True)
 
 
 def test_fp8_k_zero(gpu_ok):

