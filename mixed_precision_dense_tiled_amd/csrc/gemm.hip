@@ -32,6 +32,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -81,11 +83,11 @@ template <> struct Fmt<Kind::FP8> {
 // ---------------------------------------------------------------------------
 // Tile geometry and LDS layout.
 // ---------------------------------------------------------------------------
-constexpr int KT_BYTES = 128;   // bytes of K per K tile
-
-template <Kind KD, int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+template <Kind KD, int BM_, int BN_, int WAVES_M_, int WAVES_N_, int KT_BYTES_, int STAGES_>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int KT_BYTES = KT_BYTES_;             // bytes of K per K tile
+    static constexpr int STAGES = STAGES_;                 // LDS stages (loads run STAGES-1 ahead)
     static constexpr int NT = 64 * WAVES_M * WAVES_N;
     static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     static constexpr int TM = WM / 32, TN = WN / 32;       // MFMA tiles per wave
@@ -93,25 +95,38 @@ struct Cfg {
     static constexpr int KROWS = KT_BYTES / ES;            // K elements per K tile
     static constexpr int STEPS = KT_BYTES / Fmt<KD>::STEP_BYTES;
     static constexpr int FRAG_BYTES = Fmt<KD>::STEP_BYTES / 2;  // per lane per operand
+    static constexpr int CPR_A = KT_BYTES / 16;            // 16-byte chunks per A row
     static constexpr int A_BYTES = BM * KT_BYTES;
     static constexpr int B_ROW = BN * ES;                  // bytes per K row of the B tile
     static constexpr int B_BYTES = KROWS * B_ROW;
-    static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int SA_BYTES = (KD == Kind::FP8) ? BM * 4 : 0;
-    static constexpr int LDS_BYTES = 2 * STAGE + 2 * SA_BYTES;
+    static constexpr int CPR_B = B_ROW / 16;               // 16-byte chunks per B row
+    static constexpr int SA_BYTES = (KD == Kind::FP8) ? BM * 4 : 0;   // A-row scales (FP8)
+    static constexpr int LDS_BYTES = STAGES * (A_BYTES + B_BYTES) + 2 * SA_BYTES;
     static constexpr int UA = A_BYTES / 16 / NT;           // 16-byte loads per thread, A
     static constexpr int UB = B_BYTES / 16 / NT;           // 16-byte loads per thread, B
-    static constexpr int CPR_B = B_ROW / 16;               // 16-byte chunks per B row
     static_assert(A_BYTES % (16 * NT) == 0 && B_BYTES % (16 * NT) == 0, "staging split");
+    static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "1 KiB load pieces");
     static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be 32-aligned");
+    static_assert(KT_BYTES == 64 || KT_BYTES == 128, "K tile of 64 or 128 bytes");
+    static_assert(STEPS >= 1, "at least one MFMA step per K tile");
+    static_assert(KD != Kind::FP8 || (KT_BYTES == 128 && STAGES == 2),
+                  "FP8: one K tile per 128-wide scale block, two stages");
+    static_assert(STAGES >= 2 && STAGES <= 5, "2..5 stages");
     static_assert(LDS_BYTES <= 163840, "LDS budget");
 };
 
-// A tile: row r (0..BM-1) holds the 8 16-byte chunks of its 128 K bytes; chunk
-// c is stored at c ^ swz_a(r).  Rows r..r+7 of one chunk land in 8 different
-// chunks and rows r, r+8 differ too, so the 32-row ds_read_b128 of an MFMA
-// operand meets no bank twice in a 128-byte or a 256-byte bank window.
-__device__ __forceinline__ uint32_t swz_a(uint32_t r) { return (r & 7u) ^ ((r >> 3) & 1u); }
+// A tile: row r (0..BM-1) holds the CPR_A 16-byte chunks of its K bytes; chunk
+// c is stored at c ^ swz_a(r).  An MFMA operand read (ds_read_b128) takes one
+// chunk from 32 consecutive rows; the swizzle puts rows r..r+7 in 8 distinct
+// 16-byte bank slots of a 128-byte bank window and rows r..r+15 in 16
+// distinct slots of a 256-byte window.
+//   8 chunks per row (128-byte rows): (r & 7) ^ ((r >> 3) & 1)
+//   4 chunks per row (64-byte rows, two rows per 128 bytes): ((r >> 1) ^ (r >> 2)) & 3
+template <int CPR>
+__device__ __forceinline__ uint32_t swz_a(uint32_t r) {
+    if constexpr (CPR == 8) return (r & 7u) ^ ((r >> 3) & 1u);
+    else return ((r >> 1) ^ (r >> 2)) & 3u;
+}
 
 // B tile: K row k holds CPR_B chunks; chunk c is stored at c ^ swz_b(k).
 //  16-bit: a transposing read touches 4 consecutive K rows x 2 (or 4) chunks;
@@ -129,8 +144,9 @@ __device__ __forceinline__ uint32_t swz_b(uint32_t k) {
     }
 }
 
+template <class C>
 __device__ __forceinline__ uint32_t a_off(uint32_t r, uint32_t c) {
-    return r * KT_BYTES + ((c ^ swz_a(r)) << 4);
+    return r * C::KT_BYTES + ((c ^ swz_a<C::CPR_A>(r)) << 4);
 }
 template <class C>
 __device__ __forceinline__ uint32_t b_off(uint32_t k, uint32_t c) {
@@ -164,15 +180,88 @@ __device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int& t
 // ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
+struct Stage {
+    MPDT_LDS char* A;
+    MPDT_LDS char* B;
+    MPDT_LDS float* S;   // FP8: per-row A scales of the staged K tile
+};
+
+// s_waitcnt vmcnt(N): at most N vector-memory operations of this wave
+// (direct-to-LDS loads included) are still in flight.  Memory reads retire in
+// issue order, so this waits for all but the N most recent.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// s_waitcnt lgkmcnt(0): this wave's LDS reads and writes have completed.
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier without a memory fence.  (A fence would make the compiler
+// drain every direct-to-LDS load in flight, defeating the multi-stage
+// pipeline.)  LDS visibility is managed explicitly: a wave waits for its own
+// LDS writes (wait_lds) or direct loads (wait_vmem) before the barrier.  The
+// signal fences keep the compiler from moving memory accesses across it and
+// sched_barrier keeps the scheduler from moving anything across it.
+__device__ __forceinline__ void wg_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Compile-time loop: f(integral_constant<int, I>) for I in [B, E).
+template <int B, int E, class Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 template <Kind KD, class C, bool ALIGNED>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::NT / 256, C::NT / 256)))
 void gemm_kernel(GemmArgs g) {
     using F = Fmt<KD>;
     using Acc = typename F::Acc;
     constexpr bool IS_FP8 = (KD == Kind::FP8);
+    constexpr int NS = C::STAGES;
+    constexpr int AHEAD = NS - 1;                 // K tiles loaded ahead of the one computed
 
-    __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
-    MPDT_LDS char* lds = lds_cast(smem);
+    // LDS stages, each its own object, so that the compiler can tell a
+    // direct-to-LDS load into one stage from the reads of another.  For FP8
+    // the A-row scales of stages 0 and 1 follow their A tiles.
+    __shared__ __attribute__((aligned(1024))) char sA0[C::A_BYTES + C::SA_BYTES];
+    __shared__ __attribute__((aligned(1024))) char sB0[C::B_BYTES];
+    __shared__ __attribute__((aligned(1024))) char sA1[C::A_BYTES + C::SA_BYTES];
+    __shared__ __attribute__((aligned(1024))) char sB1[C::B_BYTES];
+    __shared__ __attribute__((aligned(NS > 2 ? 1024 : 16))) char sA2[NS > 2 ? C::A_BYTES : 16];
+    __shared__ __attribute__((aligned(NS > 2 ? 1024 : 16))) char sB2[NS > 2 ? C::B_BYTES : 16];
+    __shared__ __attribute__((aligned(NS > 3 ? 1024 : 16))) char sA3[NS > 3 ? C::A_BYTES : 16];
+    __shared__ __attribute__((aligned(NS > 3 ? 1024 : 16))) char sB3[NS > 3 ? C::B_BYTES : 16];
+    __shared__ __attribute__((aligned(NS > 4 ? 1024 : 16))) char sA4[NS > 4 ? C::A_BYTES : 16];
+    __shared__ __attribute__((aligned(NS > 4 ? 1024 : 16))) char sB4[NS > 4 ? C::B_BYTES : 16];
+    // stage(I): the LDS buffers of stage I (a compile-time index, so that
+    // every access names its buffer object directly).
+    auto stage = [&](auto I) -> Stage {
+        constexpr int i = decltype(I)::value;
+        if constexpr (i == 0) return {lds_cast(sA0), lds_cast(sB0), (MPDT_LDS float*)(sA0 + C::A_BYTES)};
+        else if constexpr (i == 1) return {lds_cast(sA1), lds_cast(sB1), (MPDT_LDS float*)(sA1 + C::A_BYTES)};
+        else if constexpr (i == 2) return {lds_cast(sA2), lds_cast(sB2), nullptr};
+        else if constexpr (i == 3) return {lds_cast(sA3), lds_cast(sB3), nullptr};
+        else return {lds_cast(sA4), lds_cast(sB4), nullptr};
+    };
+    // Same with a run-time index (folds to a constant inside unrolled loops).
+    auto stage_rt = [&](int i) -> Stage {
+        return {i == 0 ? lds_cast(sA0) : i == 1 ? lds_cast(sA1) : i == 2 ? lds_cast(sA2)
+                : i == 3 ? lds_cast(sA3) : lds_cast(sA4),
+                i == 0 ? lds_cast(sB0) : i == 1 ? lds_cast(sB1) : i == 2 ? lds_cast(sB2)
+                : i == 3 ? lds_cast(sB3) : lds_cast(sB4),
+                (i & 1) ? (MPDT_LDS float*)(sA1 + C::A_BYTES) : (MPDT_LDS float*)(sA0 + C::A_BYTES)};
+    };
+    using I0 = std::integral_constant<int, 0>;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -187,52 +276,14 @@ void gemm_kernel(GemmArgs g) {
     const bool full_mn = (m0 + C::BM <= g.M) && (n0 + C::BN <= g.N);
 
     const int64_t k_bytes = (int64_t)g.K * C::ES;
-    const int ntk = (int)((k_bytes + KT_BYTES - 1) / KT_BYTES);
+    const int ntk = (int)((k_bytes + C::KT_BYTES - 1) / C::KT_BYTES);
 
-    // ---- staging: which 16-byte chunks this thread moves -------------------
+    // ---- register-staged loads (edge tiles, unaligned rows, K tail) --------
     u32x4 ra[C::UA];
     u32x4 rb[C::UB];
     float rsa = 0.0f;   // FP8: this thread's A-row scale of the staged K tile
 
-    auto load_tile = [&](int kt) {
-        const bool full_k = (int64_t)(kt + 1) * KT_BYTES <= k_bytes;
-        const int64_t kb0 = (int64_t)kt * KT_BYTES;   // byte offset along K (A) / row base (B)
-        if (ALIGNED && full_mn && full_k) {
-#pragma unroll
-            for (int u = 0; u < C::UA; ++u) {
-                const int slot = tid + C::NT * u;
-                const int r = slot >> 3, c = slot & 7;
-                ra[u] = load16_fast(g.A + (int64_t)(m0 + r) * g.lda_b + kb0 + c * 16);
-            }
-#pragma unroll
-            for (int u = 0; u < C::UB; ++u) {
-                const int slot = tid + C::NT * u;
-                const int k = slot / C::CPR_B, c = slot % C::CPR_B;
-                rb[u] = load16_fast(g.B + (int64_t)(kt * C::KROWS + k) * g.ldb_b +
-                                    (int64_t)n0 * C::ES + c * 16);
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < C::UA; ++u) {
-                const int slot = tid + C::NT * u;
-                const int r = slot >> 3, c = slot & 7;
-                const int row = m0 + r;
-                const char* rowp = g.A + (int64_t)row * g.lda_b;
-                const char* p = rowp + kb0 + c * 16;
-                const char* end = (row < g.M) ? rowp + k_bytes : p;
-                ra[u] = load16_row<ALIGNED>(p, end);
-            }
-#pragma unroll
-            for (int u = 0; u < C::UB; ++u) {
-                const int slot = tid + C::NT * u;
-                const int k = slot / C::CPR_B, c = slot % C::CPR_B;
-                const int krow = kt * C::KROWS + k;
-                const char* rowp = g.B + (int64_t)krow * g.ldb_b;
-                const char* p = rowp + (int64_t)n0 * C::ES + c * 16;
-                const char* end = (krow < g.K) ? rowp + (int64_t)g.N * C::ES : p;
-                rb[u] = load16_row<ALIGNED>(p, end);
-            }
-        }
+    auto load_scale = [&](int kt) {
         if constexpr (IS_FP8) {
             if (tid < C::BM) {
                 const int row = m0 + tid;
@@ -240,27 +291,82 @@ void gemm_kernel(GemmArgs g) {
             }
         }
     };
+    auto store_scale = [&](const Stage& s) {
+        if constexpr (IS_FP8) {
+            if (tid < C::BM) s.S[tid] = rsa;
+        }
+    };
 
-    auto store_tile = [&](int stage) {
-        MPDT_LDS char* As = lds + stage * C::STAGE;
-        MPDT_LDS char* Bs = As + C::A_BYTES;
+    auto reg_load = [&](int kt) {
+        const int64_t kb0 = (int64_t)kt * C::KT_BYTES;   // byte offset along K (A)
 #pragma unroll
         for (int u = 0; u < C::UA; ++u) {
             const int slot = tid + C::NT * u;
-            lds_store16(As, a_off(slot >> 3, slot & 7), ra[u]);
+            const int r = slot / C::CPR_A, c = slot % C::CPR_A;
+            const int row = m0 + r;
+            const char* rowp = g.A + (int64_t)row * g.lda_b;
+            const char* p = rowp + kb0 + c * 16;
+            const char* end = (row < g.M) ? rowp + k_bytes : p;
+            ra[u] = load16_row<ALIGNED>(p, end);
         }
 #pragma unroll
         for (int u = 0; u < C::UB; ++u) {
             const int slot = tid + C::NT * u;
-            lds_store16(Bs, b_off<C>(slot / C::CPR_B, slot % C::CPR_B), rb[u]);
+            const int k = slot / C::CPR_B, c = slot % C::CPR_B;
+            const int krow = kt * C::KROWS + k;
+            const char* rowp = g.B + (int64_t)krow * g.ldb_b;
+            const char* p = rowp + (int64_t)n0 * C::ES + c * 16;
+            const char* end = (krow < g.K) ? rowp + (int64_t)g.N * C::ES : p;
+            rb[u] = load16_row<ALIGNED>(p, end);
         }
-        if constexpr (IS_FP8) {
-            if (tid < C::BM) {
-                auto sa = (MPDT_LDS float*)(lds + 2 * C::STAGE + stage * C::SA_BYTES);
-                sa[tid] = rsa;
-            }
+        load_scale(kt);
+    };
+
+    auto reg_store = [&](const Stage& s) {
+#pragma unroll
+        for (int u = 0; u < C::UA; ++u) {
+            const int slot = tid + C::NT * u;
+            lds_store16(s.A, a_off<C>(slot / C::CPR_A, slot % C::CPR_A), ra[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < C::UB; ++u) {
+            const int slot = tid + C::NT * u;
+            lds_store16(s.B, b_off<C>(slot / C::CPR_B, slot % C::CPR_B), rb[u]);
+        }
+        store_scale(s);
+    };
+
+    // ---- direct global -> LDS loads (full interior K tiles, aligned rows) ---
+    // One wave instruction moves 1 KiB: lane l's 16 bytes land at byte 16*l of
+    // the wave's LDS piece.  The swizzle is applied on the global side: the
+    // lane that fills physical chunk pc of LDS row r fetches logical chunk
+    // pc ^ swz(r) from memory (XOR is its own inverse).  Each wave issues
+    // UA + UB of these per K tile.
+    auto dma_tile = [&](int kt, const Stage& s) {
+        const int64_t kb0 = (int64_t)kt * C::KT_BYTES;
+        constexpr int RPA = 1024 / C::KT_BYTES;              // A rows per 1 KiB piece
+#pragma unroll
+        for (int u = 0; u < C::UA; ++u) {
+            const int piece = wave * C::UA + u;
+            const int r = piece * RPA + lane / C::CPR_A;
+            const int c = (lane % C::CPR_A) ^ (int)swz_a<C::CPR_A>(r);
+            const char* gp = g.A + (int64_t)(m0 + r) * g.lda_b + kb0 + c * 16;
+            __builtin_amdgcn_global_load_lds((const void*)gp, (MPDT_LDS void*)(s.A + piece * 1024),
+                                             16, 0, 0);
+        }
+        constexpr int RPB = 1024 / C::B_ROW;                 // B rows per 1 KiB piece
+#pragma unroll
+        for (int u = 0; u < C::UB; ++u) {
+            const int piece = wave * C::UB + u;
+            const int k = piece * RPB + lane / C::CPR_B;
+            const int c = (lane % C::CPR_B) ^ (int)swz_b<C::ES>(k);
+            const char* gp = g.B + (int64_t)(kt * C::KROWS + k) * g.ldb_b +
+                             (int64_t)n0 * C::ES + c * 16;
+            __builtin_amdgcn_global_load_lds((const void*)gp, (MPDT_LDS void*)(s.B + piece * 1024),
+                                             16, 0, 0);
         }
     };
+    constexpr int DMA_PER_TILE = C::UA + C::UB;
 
     // ---- accumulators -------------------------------------------------------
     Acc acc[C::TM][C::TN];
@@ -277,144 +383,343 @@ void gemm_kernel(GemmArgs g) {
     const uint32_t grp = lane >> 4;         // 16-lane group of a transposing read
     const uint32_t gp = lane & 15;          // lane within that group
 
-    auto compute_tile = [&](int stage, int kt) {
-        const MPDT_LDS char* As = lds + stage * C::STAGE;
-        const MPDT_LDS char* Bs = As + C::A_BYTES;
-        Acc blk[IS_FP8 ? C::TM : 1][IS_FP8 ? C::TN : 1];
+    // Operand fragments of one K tile for this wave (all MFMA steps).
+    struct Frags {
+        u32x4 a[C::STEPS][C::TM][C::FRAG_BYTES / 16];
+        u32x2 b[C::STEPS][C::TN][C::FRAG_BYTES / 8];
+    };
+
+    auto load_step = [&](const Stage& st, Frags& f, int s) {
+        const MPDT_LDS char* As = st.A;
+        const MPDT_LDS char* Bs = st.B;
+        // A operand: FRAG_BYTES per lane, along K, from row lrow of each 32-row tile
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i) {
+            const uint32_t r = wm * C::WM + i * 32 + lrow;
+#pragma unroll
+            for (int q = 0; q < C::FRAG_BYTES / 16; ++q) {
+                const uint32_t c = s * (F::STEP_BYTES / 16) + lhalf * (C::FRAG_BYTES / 16) + q;
+                f.a[s][i][q] = lds_load16(As, a_off<C>(r, c));
+            }
+        }
+        // B operand: column lrow of each 32-column tile, FRAG_BYTES of K
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+            const uint32_t col16 = wn * C::WN + j * 32 + 16 * (grp & 1);  // element column
+#pragma unroll
+            for (int h = 0; h < C::FRAG_BYTES / 8; ++h) {
+                if constexpr (C::ES == 2) {
+                    const uint32_t k = s * 16 + 8 * (grp >> 1) + 4 * h + (gp >> 2);
+                    const uint32_t c = (col16 >> 3) + ((gp & 3) >> 1);
+                    f.b[s][j][h] = lds_read_tr16(Bs, b_off<C>(k, c) + 8 * (gp & 1));
+                } else {
+                    const uint32_t k = s * (F::STEP_BYTES) + (C::FRAG_BYTES) * (grp >> 1) +
+                                       8 * h + (gp >> 1);
+                    const uint32_t c = col16 >> 4;
+                    f.b[s][j][h] = lds_read_tr8(Bs, b_off<C>(k, c) + 8 * (gp & 1));
+                }
+            }
+        }
+    };
+
+    // MFMAs of one step into `out` (acc, or the FP8 block sums).
+    auto mma_step = [&](const Frags& f, int s, Acc (&out)[C::TM][C::TN]) {
         if constexpr (IS_FP8) {
+            i32x8 a8[C::TM], b8[C::TN];
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a8[i][e] = (int32_t)f.a[s][i][e >> 2][e & 3];
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) b8[j][e] = (int32_t)f.b[s][j][e >> 1][e & 1];
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j) out[i][j] = F::mma(a8[i], b8[j], out[i][j]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j) {
+                    const u32x4 b = {f.b[s][j][0][0], f.b[s][j][0][1], f.b[s][j][1][0],
+                                     f.b[s][j][1][1]};
+                    out[i][j] = F::mma(f.a[s][i][0], b, out[i][j]);
+                }
+        }
+    };
+
+    auto compute_tile = [&](const Stage& st, int kt) {
+        Frags f;
+        if constexpr (IS_FP8) {
+            Acc blk[C::TM][C::TN];
 #pragma unroll
             for (int i = 0; i < C::TM; ++i)
 #pragma unroll
                 for (int j = 0; j < C::TN; ++j)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) blk[i][j][r] = 0.0f;
-        }
 #pragma unroll
-        for (int s = 0; s < C::STEPS; ++s) {
-            // A operand: FRAG_BYTES per lane, along K, from row lrow of each 32-row tile
-            u32x4 af[C::TM][C::FRAG_BYTES / 16];
-#pragma unroll
-            for (int i = 0; i < C::TM; ++i) {
-                const uint32_t r = wm * C::WM + i * 32 + lrow;
-#pragma unroll
-                for (int q = 0; q < C::FRAG_BYTES / 16; ++q) {
-                    const uint32_t c = s * (F::STEP_BYTES / 16) + lhalf * (C::FRAG_BYTES / 16) + q;
-                    af[i][q] = lds_load16(As, a_off(r, c));
-                }
+            for (int s = 0; s < C::STEPS; ++s) {
+                load_step(st, f, s);
+                mma_step(f, s, blk);
             }
-            // B operand: column lrow of each 32-column tile, FRAG_BYTES of K
-            u32x2 bf[C::TN][C::FRAG_BYTES / 8];
-#pragma unroll
-            for (int j = 0; j < C::TN; ++j) {
-                const uint32_t col16 = wn * C::WN + j * 32 + 16 * (grp & 1);  // element column
-#pragma unroll
-                for (int h = 0; h < C::FRAG_BYTES / 8; ++h) {
-                    if constexpr (C::ES == 2) {
-                        const uint32_t k = s * 16 + 8 * (grp >> 1) + 4 * h + (gp >> 2);
-                        const uint32_t c = (col16 >> 3) + ((gp & 3) >> 1);
-                        bf[j][h] = lds_read_tr16(Bs, b_off<C>(k, c) + 8 * (gp & 1));
-                    } else {
-                        const uint32_t k = s * (F::STEP_BYTES) + (C::FRAG_BYTES) * (grp >> 1) +
-                                           8 * h + (gp >> 1);
-                        const uint32_t c = col16 >> 4;
-                        bf[j][h] = lds_read_tr8(Bs, b_off<C>(k, c) + 8 * (gp & 1));
-                    }
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-                for (int j = 0; j < C::TN; ++j) {
-                    if constexpr (IS_FP8) {
-                        uint32_t av[8] = {af[i][0][0], af[i][0][1], af[i][0][2], af[i][0][3],
-                                          af[i][1][0], af[i][1][1], af[i][1][2], af[i][1][3]};
-                        uint32_t bv[8] = {bf[j][0][0], bf[j][0][1], bf[j][1][0], bf[j][1][1],
-                                          bf[j][2][0], bf[j][2][1], bf[j][3][0], bf[j][3][1]};
-                        i32x8 a, b;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            a[e] = (int32_t)av[e];
-                            b[e] = (int32_t)bv[e];
-                        }
-                        blk[i][j] = F::mma(a, b, blk[i][j]);
-                    } else {
-                        u32x4 b = {bf[j][0][0], bf[j][0][1], bf[j][1][0], bf[j][1][1]};
-                        acc[i][j] = F::mma(af[i][0], b, acc[i][j]);
-                    }
-                }
-        }
-        if constexpr (IS_FP8) {
             // promote the block sums: acc += blk * (sA[row][kb] * sB[kb][n-block])
-            const auto sa = (const MPDT_LDS float*)(lds + 2 * C::STAGE + stage * C::SA_BYTES);
             const int nb = (n0 + wn * C::WN) / 128;
             const float sb = (nb < (g.N + 127) / 128) ? g.sB[(int64_t)kt * g.ld_sb + nb] : 0.0f;
 #pragma unroll
             for (int i = 0; i < C::TM; ++i) {
-                float f[16];
+                float fs[16];
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
                     const uint32_t r = wm * C::WM + i * 32 + 8 * r4 + 4 * lhalf;
-                    const u32x4 v = lds_load16((const MPDT_LDS char*)sa, r * 4);
+                    const u32x4 v = lds_load16((const MPDT_LDS char*)st.S, r * 4);
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         // (element to scalar first: bit-casting a vector element
                         // directly reads element 0 with this compiler)
                         const uint32_t bits = v[q];
-                        f[4 * r4 + q] = __uint_as_float(bits) * sb;
+                        fs[4 * r4 + q] = __uint_as_float(bits) * sb;
                     }
                 }
 #pragma unroll
                 for (int j = 0; j < C::TN; ++j)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(blk[i][j][r], f[r], acc[i][j][r]);
+                    for (int r = 0; r < 16; ++r)
+                        acc[i][j][r] = __builtin_fmaf(blk[i][j][r], fs[r], acc[i][j][r]);
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < C::STEPS; ++s) {
+                load_step(st, f, s);
+                mma_step(f, s, acc);
             }
         }
     };
 
-    // ---- pipelined K loop ---------------------------------------------------
-    if (ntk > 0) {
-        load_tile(0);
-        store_tile(0);
-        if (ntk > 1) load_tile(1);
-        __syncthreads();
-        for (int kt = 0; kt < ntk; ++kt) {
-            const int stage = kt & 1;
-            compute_tile(stage, kt);
-            if (kt + 1 < ntk) {
-                store_tile(stage ^ 1);
-                if (kt + 2 < ntk) load_tile(kt + 2);
+    // ---- K loop -------------------------------------------------------------
+    const bool pingpong = !IS_FP8 && C::WAVES_M == 2 && NS >= 3 && (k_bytes % C::KT_BYTES) == 0;
+    if (ALIGNED && full_mn && pingpong) {
+        if constexpr (ALIGNED && !IS_FP8 && C::WAVES_M == 2 && NS >= 3) {
+            // Interior tile, whole K tiles: two-group ping-pong.  The two
+            // wavefronts on each SIMD belong to different groups (group =
+            // wave / 4 = wm) and alternate roles between workgroup barriers:
+            // while one issues the MFMAs of a K tile from registers, the other
+            // reads its operand fragments of that tile from LDS; group 0 also
+            // issues all direct loads, AHEAD = NS-1 tiles ahead, into NS stages.
+            //   slot 2t:   group 0 reads frags(t), loads tile t+AHEAD | group 1 computes t-1
+            //   slot 2t+1: group 0 computes t                        | group 1 reads frags(t)
+            // A stage holding tile t is read in slots 2t and 2t+1 and refilled
+            // in slot 2t+2 with tile t+NS.  Before the barrier that opens slot
+            // 2t+2, group 0 waits for its loads of tile t+1.
+            const int nt = (int)(k_bytes / C::KT_BYTES);
+            const bool g0 = (wm == 0);
+            constexpr int PA = C::A_BYTES / 1024 / 4, PB = C::B_BYTES / 1024 / 4;
+            constexpr int PER_TILE = PA + PB;            // direct loads per group-0 wave per tile
+            Frags f;
+            auto dma_all = [&](int kt, const Stage& s) {   // one group moves the whole tile
+                const int64_t kb0 = (int64_t)kt * C::KT_BYTES;
+                constexpr int RPA = 1024 / C::KT_BYTES;
+                constexpr int RPB = 1024 / C::B_ROW;
+#pragma unroll
+                for (int u = 0; u < PA; ++u) {
+                    const int piece = wn * PA + u;
+                    const int r = piece * RPA + lane / C::CPR_A;
+                    const int c = (lane % C::CPR_A) ^ (int)swz_a<C::CPR_A>(r);
+                    const char* gpa = g.A + (int64_t)(m0 + r) * g.lda_b + kb0 + c * 16;
+                    __builtin_amdgcn_global_load_lds((const void*)gpa,
+                                                     (MPDT_LDS void*)(s.A + piece * 1024), 16, 0, 0);
+                }
+#pragma unroll
+                for (int u = 0; u < PB; ++u) {
+                    const int piece = wn * PB + u;
+                    const int k = piece * RPB + lane / C::CPR_B;
+                    const int c = (lane % C::CPR_B) ^ (int)swz_b<C::ES>(k);
+                    const char* gpb = g.B + (int64_t)(kt * C::KROWS + k) * g.ldb_b +
+                                      (int64_t)n0 * C::ES + c * 16;
+                    __builtin_amdgcn_global_load_lds((const void*)gpb,
+                                                     (MPDT_LDS void*)(s.B + piece * 1024), 16, 0, 0);
+                }
+            };
+            // wait until at most `later` tiles of loads (issued after the one
+            // wanted) are still in flight
+            auto wait_tiles = [&](int later) {
+                if (later >= 3) wait_vmem<3 * PER_TILE>();
+                else if (later == 2) wait_vmem<2 * PER_TILE>();
+                else if (later == 1) wait_vmem<PER_TILE>();
+                else wait_vmem<0>();
+            };
+            if (g0) {
+                static_for<0, AHEAD>([&](auto p) {
+                    if (decltype(p)::value < nt) dma_all(decltype(p)::value, stage(p));
+                });
+                wait_tiles(min(AHEAD - 1, nt - 1));
             }
-            __syncthreads();
+            wg_barrier();
+            if (!g0) wg_barrier();   // group 1 runs one slot behind
+            for (int t0 = 0; t0 < nt; t0 += NS) {
+                static_for<0, NS>([&](auto U) {
+                    constexpr int u = decltype(U)::value;
+                    const int t = t0 + u;
+                    if (t < nt) {
+                        // memory slot
+#pragma unroll
+                        for (int q = 0; q < C::STEPS; ++q) load_step(stage(U), f, q);
+                        if (g0 && t + AHEAD < nt)
+                            dma_all(t + AHEAD, stage(std::integral_constant<int, (u + AHEAD) % NS>{}));
+                        wait_lds();
+                        wg_barrier();
+                        // compute slot
+#pragma unroll
+                        for (int q = 0; q < C::STEPS; ++q) mma_step(f, q, acc);
+                        if (g0 && t + 1 < nt) wait_tiles(min(AHEAD - 1, nt - 2 - t));
+                        if (g0 || t + 1 < nt) wg_barrier();
+                    }
+                });
+            }
+        }
+    } else if (ALIGNED && full_mn) {
+        if constexpr (ALIGNED) {
+            // Interior tile: full K tiles stream through direct loads issued
+            // AHEAD tiles early into NS rotating stages; one barrier per K tile.
+            // At the top of iteration kt this wave waits for its own loads of
+            // tile kt (leaving the later tiles in flight), then the barrier
+            // publishes everyone's loads and retires the reads of tile kt-1,
+            // whose stage is refilled with tile kt+AHEAD.
+            const int nfull = (int)(k_bytes / C::KT_BYTES);
+#pragma unroll
+            for (int p = 0; p < AHEAD; ++p)
+                if (p < nfull) dma_tile(p, stage_rt(p));
+            load_scale(0);
+            for (int kt0 = 0; kt0 < nfull; kt0 += NS) {
+#pragma unroll
+                for (int u = 0; u < NS; ++u) {
+                    const int kt = kt0 + u;
+                    if (kt < nfull) {
+                        const int later = min(AHEAD - 1, nfull - 1 - kt);   // tiles issued after kt
+                        if (later >= 2) wait_vmem<2 * DMA_PER_TILE>();
+                        else if (later == 1) wait_vmem<DMA_PER_TILE>();
+                        else wait_vmem<0>();
+                        store_scale(stage_rt(u));
+                        wait_lds();
+                        wg_barrier();
+                        if (kt + AHEAD < nfull)
+                            dma_tile(kt + AHEAD, stage_rt((u + AHEAD) % NS));
+                        if (kt + 1 < nfull) load_scale(kt + 1);
+                        compute_tile(stage_rt(u), kt);
+                        wait_lds();
+                    }
+                }
+            }
+            if (nfull < ntk) {   // K tail: one partial tile through registers
+                reg_load(nfull);
+                wait_vmem<0>();
+                wg_barrier();   // every wave is past the reads of this stage's last tile
+                const Stage sT = stage_rt(nfull % NS);
+                reg_store(sT);
+                wait_lds();
+                wg_barrier();
+                compute_tile(sT, nfull);
+            }
+        }
+    } else if (ntk > 0) {
+        // Edge tile or rows not 16-byte aligned: guarded loads through
+        // registers, two stages, the loads of tile t+2 in flight while tile
+        // t+1 is computed.
+        reg_load(0);
+        reg_store(stage(I0{}));
+        if (ntk > 1) reg_load(1);
+        wait_lds();
+        wg_barrier();
+        for (int kt0 = 0; kt0 < ntk; kt0 += 2) {
+            static_for<0, 2>([&](auto U) {
+                constexpr int u = decltype(U)::value;
+                const int kt = kt0 + u;
+                if (kt < ntk) {
+                    compute_tile(stage(U), kt);
+                    if (kt + 1 < ntk) {
+                        reg_store(stage(std::integral_constant<int, u ^ 1>{}));
+                        if (kt + 2 < ntk) reg_load(kt + 2);
+                    }
+                    wait_lds();
+                    wg_barrier();
+                }
+            });
         }
     }
 
     // ---- epilogue -----------------------------------------------------------
     // Lane layout of a 32x32 accumulator: column lrow; register r holds row
     // 8*(r/4) + 4*lhalf + (r%4).
+    using OutT = typename std::conditional<KD == Kind::FP8, uint16_t,
+                 typename std::conditional<KD == Kind::I8, int32_t, float>::type>::type;
+    using CT = typename std::conditional<KD == Kind::I8, int32_t, float>::type;
+    OutT* const Dp = (OutT*)g.D;
+    const CT* const Cp = (const CT*)g.C;
+    const int row_base = m0 + wm * C::WM + 4 * (int)lhalf;
+    const int col_base = n0 + wn * C::WN + (int)lrow;
+    auto out_val = [&](float a, CT c) -> OutT {
+        if constexpr (KD == Kind::FP8) return f32_to_bf16_bits(a);
+        else return (OutT)(a + c);
+    };
+    constexpr int NTILE = C::TM * C::TN;
+    if (full_mn) {
+        // Interior tile: the wave's 32x32 tiles are written in turn, and C of
+        // the next tile is read before this one is stored, so the reads of C
+        // stream instead of costing one round trip per element.  (C is either
+        // exactly D or disjoint from it -- the C ABI rejects partial overlaps
+        // -- so reading C of other elements ahead of these stores is safe.)
+        // Row offsets (8*(r/4) + r%4) * ld are wave-uniform.
+        auto dtile = [&](int t) {
+            return Dp + (int64_t)(row_base + (t / C::TN) * 32) * g.ldd + col_base + (t % C::TN) * 32;
+        };
+        auto ctile = [&](int t) {
+            return Cp + (int64_t)(row_base + (t / C::TN) * 32) * g.ldc + col_base + (t % C::TN) * 32;
+        };
+        auto load_c = [&](int t, CT (&cv)[16]) {
+            const CT* cp = ctile(t);
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i)
+            for (int r = 0; r < 16; ++r) cv[r] = cp[(int64_t)(8 * (r >> 2) + (r & 3)) * g.ldc];
+        };
+        auto store_t = [&](int t, const CT (&cv)[16]) {
+            OutT* dp = dtile(t);
 #pragma unroll
-        for (int j = 0; j < C::TN; ++j) {
-            const int col = n0 + wn * C::WN + j * 32 + (int)lrow;
+            for (int r = 0; r < 16; ++r)
+                dp[(int64_t)(8 * (r >> 2) + (r & 3)) * g.ldd] =
+                    out_val(acc[t / C::TN][t % C::TN][r], cv[r]);
+        };
+        if (KD != Kind::FP8 && Cp) {
+            CT cbuf[2][16];
+            load_c(0, cbuf[0]);
+            static_for<0, NTILE>([&](auto T) {
+                constexpr int t = decltype(T)::value;
+                if constexpr (t + 1 < NTILE) load_c(t + 1, cbuf[(t + 1) & 1]);
+                store_t(t, cbuf[t & 1]);
+            });
+        } else {
+            CT zero[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm * C::WM + i * 32 + 8 * (r >> 2) + 4 * (int)lhalf + (r & 3);
-                if (full_mn || (row < g.M && col < g.N)) {
-                    if constexpr (KD == Kind::FP8) {
-                        uint16_t* D = (uint16_t*)g.D;
-                        D[(int64_t)row * g.ldd + col] = f32_to_bf16_bits(acc[i][j][r]);
-                    } else if constexpr (KD == Kind::I8) {
-                        int32_t v = acc[i][j][r];
-                        if (g.C) v += ((const int32_t*)g.C)[(int64_t)row * g.ldc + col];
-                        ((int32_t*)g.D)[(int64_t)row * g.ldd + col] = v;
-                    } else {
-                        float v = acc[i][j][r];
-                        if (g.C) v += ((const float*)g.C)[(int64_t)row * g.ldc + col];
-                        ((float*)g.D)[(int64_t)row * g.ldd + col] = v;
+            for (int r = 0; r < 16; ++r) zero[r] = (CT)0;
+            static_for<0, NTILE>([&](auto T) { store_t(decltype(T)::value, zero); });
+        }
+    } else {
+        // Edge tile: every element checked.
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j) {
+                const int col = col_base + j * 32;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
+                    if (row < g.M && col < g.N) {
+                        const CT c = (KD != Kind::FP8 && Cp) ? Cp[(int64_t)row * g.ldc + col] : (CT)0;
+                        Dp[(int64_t)row * g.ldd + col] = out_val(acc[i][j][r], c);
                     }
                 }
             }
-        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -435,10 +740,10 @@ static hipError_t launch_cfg(const GemmArgs& a0, bool aligned, hipStream_t strea
     return hipGetLastError();
 }
 
-using CfgF16 = Cfg<Kind::F16, 256, 256, 2, 4>;
-using CfgBF16 = Cfg<Kind::BF16, 256, 256, 2, 4>;
-using CfgI8 = Cfg<Kind::I8, 256, 256, 2, 4>;
-using CfgFP8 = Cfg<Kind::FP8, 128, 256, 2, 4>;
+using CfgF16 = Cfg<Kind::F16, 256, 256, 2, 4, 64, 4>;
+using CfgBF16 = Cfg<Kind::BF16, 256, 256, 2, 4, 64, 4>;
+using CfgI8 = Cfg<Kind::I8, 256, 256, 2, 4, 64, 4>;
+using CfgFP8 = Cfg<Kind::FP8, 128, 256, 2, 4, 128, 2>;
 
 hipError_t launch_gemm(Kind kind, const GemmArgs& a, bool aligned, hipStream_t stream) {
     switch (kind) {
