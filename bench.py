@@ -69,32 +69,42 @@ def traffic_for(kernel: str, digest: str, per_launch_units: float = 1.0):
     return e.get("bytes_per_launch")
 
 
-def timed(fn, steps, warmup, stream, rotate=None):
-    """Run fn(i) warmup + steps times; returns (region_ms, per-launch ms list)."""
+def timed(fn, steps, warmup, stream):
+    """warmup untimed calls, then `steps` back-to-back calls bracketed by HIP
+    events on the stream the kernels run on.  Returns (region_ms, per_launch_ms):
+    the average launch duration is region_ms / steps; per_launch_ms comes
+    from a separate, untimed pass with an event pair around each launch (its
+    spread only: the extra events there slow the launches down)."""
     import torch
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
     r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     r0.record(stream)
     for i in range(steps):
-        ev[i][0].record(stream)
         fn(warmup + i)
-        ev[i][1].record(stream)
     r1.record(stream)
     torch.cuda.synchronize()
-    per = [a.elapsed_time(b) for a, b in ev]
-    return r0.elapsed_time(r1), per
+    region = r0.elapsed_time(r1)
+    n = min(steps, 20)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for i in range(n):
+        ev[i][0].record(stream)
+        fn(warmup + steps + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return region, [a.elapsed_time(b) for a, b in ev]
 
 
-def stats(per):
+def stats(per, region_ms=None, steps=None):
     s = sorted(per)
     n = len(s)
-    return {"mean_us": 1e3 * sum(s) / n, "median_us": 1e3 * s[n // 2], "min_us": 1e3 * s[0],
-            "max_us": 1e3 * s[-1]}
+    out = {"median_us_eventpair": 1e3 * s[n // 2], "min_us_eventpair": 1e3 * s[0],
+           "max_us_eventpair": 1e3 * s[-1]}
+    if region_ms is not None:
+        out = {"mean_us": 1e3 * region_ms / steps, **out}
+    return out
 
 
 def main():
@@ -131,7 +141,7 @@ def main():
         tD = torch.empty((M, N), dtype=torch.float32, device=dev)
         region, per = timed(lambda i: mp.gemm_bf16(tA, tB, tC, out=tD), args.steps, args.warmup,
                             stream)
-        st = stats(per)
+        st = stats(per, region, args.steps)
         flop = 2.0 * M * N * K
         avg_s = st["mean_us"] * 1e-6
         achieved = flop / avg_s / 1e12
@@ -169,12 +179,12 @@ def main():
         ty = torch.empty(N, dtype=torch.bfloat16, device=dev)
         region, per = timed(lambda i: mp.gemv_w8a8(tx, float(s_x), tWs[i % copies], tsw, out=ty),
                             args.steps, args.warmup, stream)
-        st = stats(per)
+        st = stats(per, region, args.steps)
         nbytes = N * K + K + 4 * N + 4 + 2 * N      # W + x + s_w + s_x + y (algorithmic)
         gbs = nbytes / (st["mean_us"] * 1e-6) / 1e9
-        _, per_w = timed(lambda i: mp.gemv_w8a8(tx, float(s_x), tWs[0], tsw, out=ty),
-                         args.steps, args.warmup, stream)
-        stw = stats(per_w)
+        region_w, per_w = timed(lambda i: mp.gemv_w8a8(tx, float(s_x), tWs[0], tsw, out=ty),
+                                args.steps, args.warmup, stream)
+        stw = stats(per_w, region_w, args.steps)
         digest = source_digest("gemv_w8a8.hip", "device_common.hpp")
         extra["gemv_w8a8"] = {
             "workload": "batch-1 W8A8 linear, x int8 [4096], W int8 [14336 x 4096] (stored N x K), "
@@ -195,9 +205,9 @@ def main():
         ta, tsa, tb, tsb = to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb)
         td = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         steps = max(args.steps // 2, 5)
-        _, per = timed(lambda i: mp.gemm_fp8_blockscaled(ta, tsa, tb, tsb, out=td), steps,
-                       args.warmup, stream)
-        st = stats(per)
+        region, per = timed(lambda i: mp.gemm_fp8_blockscaled(ta, tsa, tb, tsb, out=td), steps,
+                            args.warmup, stream)
+        st = stats(per, region, steps)
         tf = 2.0 * M * N * K / (st["mean_us"] * 1e-6) / 1e12
         extra["gemm_fp8_blockscaled"] = {
             "workload": "FP8 E4M3 4096x7168x7168, 1x128 A / 128x128 B FP32 scales, BF16 out",
@@ -213,8 +223,8 @@ def main():
         tA, tB, tC = to_dev(A), to_dev(B), to_dev(C)
         tD = torch.empty((M, N), dtype=torch.float32, device=dev)
         steps = max(args.steps // 4, 5)
-        _, per = timed(lambda i: mp.gemm_f16(tA, tB, tC, out=tD), steps, args.warmup, stream)
-        st = stats(per)
+        region, per = timed(lambda i: mp.gemm_f16(tA, tB, tC, out=tD), steps, args.warmup, stream)
+        st = stats(per, region, steps)
         tf = 2.0 * M * N * K / (st["mean_us"] * 1e-6) / 1e12
         extra["gemm_f16_ragged"] = {
             "workload": "FP16 8191x8193x4099 tight leading dims, C=0, FP32 out",
@@ -228,9 +238,10 @@ def main():
         A, B, C = inputs.gemm16_operands(64, 64, 64, dist="uniform", fmt="f16")
         tA, tB, tC = to_dev(A), to_dev(B), to_dev(C)
         tD = torch.empty((64, 64), dtype=torch.float32, device=dev)
-        _, per = timed(lambda i: mp.gemm_f16(tA, tB, tC, out=tD), args.steps, args.warmup, stream)
+        region, per = timed(lambda i: mp.gemm_f16(tA, tB, tC, out=tD), args.steps, args.warmup,
+                            stream)
         extra["gemm_f16_64"] = {"workload": "FP16 64^3 with FP32 C (latency bound)",
-                                "launch_us": stats(per)}
+                                "launch_us": stats(per, region, args.steps)}
 
     # ---------------- INT8 4096^3 ----------------------------------------------
     if args.only in ("all", "i8"):
@@ -238,9 +249,9 @@ def main():
         A, B, C = inputs.i8_operands(M, N, K)
         tA, tB, tC = to_dev(A), to_dev(B), to_dev(C)
         tD = torch.empty((M, N), dtype=torch.int32, device=dev)
-        _, per = timed(lambda i: mp.gemm_i8_i32(tA, tB, tC, out=tD), args.steps, args.warmup,
-                       stream)
-        st = stats(per)
+        region, per = timed(lambda i: mp.gemm_i8_i32(tA, tB, tC, out=tD), args.steps, args.warmup,
+                            stream)
+        st = stats(per, region, args.steps)
         tops = 2.0 * M * N * K / (st["mean_us"] * 1e-6) / 1e12
         extra["gemm_i8_i32"] = {"workload": "INT8 4096^3, INT32 C/D", "TOP_s": tops,
                                 "launch_us": st,
@@ -253,8 +264,9 @@ def main():
         n = 256 << 20
         src = torch.ones(n // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
-        _, per = timed(lambda i: dst.copy_(src), args.steps, args.warmup, stream)
-        extra["copy"] = {"bytes_read": n, "bytes_written": n, "launch_us": stats(per)}
+        region, per = timed(lambda i: dst.copy_(src), args.steps, args.warmup, stream)
+        extra["copy"] = {"bytes_read": n, "bytes_written": n,
+                         "launch_us": stats(per, region, args.steps)}
 
     # ---------------- CPU baseline: the oracle on a bounded sample -------------
     if result is not None and not args.no_cpu_baseline:

@@ -453,23 +453,34 @@ void gemm_kernel(GemmArgs g) {
     auto compute_tile = [&](const Stage& st, int kt) {
         Frags f;
         if constexpr (IS_FP8) {
-            Acc blk[C::TM][C::TN];
+            // All steps' fragments first; then, one 32-row tile at a time, the
+            // block sums of its TN tiles (fresh accumulators, 2 MFMAs each)
+            // and their promotion, so only TN block accumulators are live.
 #pragma unroll
-            for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-                for (int j = 0; j < C::TN; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) blk[i][j][r] = 0.0f;
-#pragma unroll
-            for (int s = 0; s < C::STEPS; ++s) {
-                load_step(st, f, s);
-                mma_step(f, s, blk);
-            }
-            // promote the block sums: acc += blk * (sA[row][kb] * sB[kb][n-block])
+            for (int s = 0; s < C::STEPS; ++s) load_step(st, f, s);
             const int nb = (n0 + wn * C::WN) / 128;
             const float sb = (nb < (g.N + 127) / 128) ? g.sB[(int64_t)kt * g.ld_sb + nb] : 0.0f;
 #pragma unroll
             for (int i = 0; i < C::TM; ++i) {
+                Acc blk[C::TN];
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) blk[j][r] = 0.0f;
+#pragma unroll
+                for (int s = 0; s < C::STEPS; ++s) {
+                    i32x8 a8;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) a8[e] = (int32_t)f.a[s][i][e >> 2][e & 3];
+#pragma unroll
+                    for (int j = 0; j < C::TN; ++j) {
+                        i32x8 b8;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) b8[e] = (int32_t)f.b[s][j][e >> 1][e & 1];
+                        blk[j] = F::mma(a8, b8, blk[j]);
+                    }
+                }
+                // promote: acc += blk * (sA[row][kb] * sB[kb][n-block])
                 float fs[16];
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
@@ -487,7 +498,7 @@ void gemm_kernel(GemmArgs g) {
                 for (int j = 0; j < C::TN; ++j)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
-                        acc[i][j][r] = __builtin_fmaf(blk[i][j][r], fs[r], acc[i][j][r]);
+                        acc[i][j][r] = __builtin_fmaf(blk[j][r], fs[r], acc[i][j][r]);
             }
         } else {
 #pragma unroll

@@ -14,7 +14,9 @@
 //     1 KiB of one row, fully coalesced) and the matching chunks of x (4 KiB,
 //     shared by all waves through L2);
 //   * all R * (K / 1024) loads of a wave are issued before the first use, so
-//     a resident grid keeps the whole weight stream in flight;
+//     a resident grid keeps the whole weight stream in flight (R = 2 keeps
+//     the register count at 72, seven waves per SIMD: the 14336-row layer
+//     fits the chip in one round);
 //   * v_dot4 accumulates 4 byte products per instruction into INT32;
 //   * a butterfly over the 64 lanes reduces each row; lane r writes row r.
 #include <hip/hip_runtime.h>
@@ -26,7 +28,8 @@
 namespace mpdt {
 
 constexpr int GEMV_WAVES = 4;        // wavefronts per workgroup
-constexpr int GEMV_ROWS = 4;         // output rows per wavefront
+constexpr int GEMV_ROWS = 2;         // output rows per wavefront (72 VGPRs: 7 waves per SIMD,
+                                     // so the whole 14336-row layer is resident at once)
 constexpr int GEMV_U = 4;            // 16-byte chunks per lane per row per pass (K = 4096 in one pass)
 
 __device__ __forceinline__ int dot16(u32x4 w, u32x4 x, int acc) {
@@ -75,7 +78,8 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_w8a8_kernel(GemvArgs g) 
                 if (row >= g.N)
                     wv[r][u] = u32x4{0u, 0u, 0u, 0u};
                 else if (ALIGNED && off + 16 <= kbytes)
-                    wv[r][u] = load16_fast(p);
+                    // streamed once: non-temporal, so it does not displace x in the caches
+                    wv[r][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
                 else
                     wv[r][u] = load16_row<ALIGNED>(p, rowp + kbytes);
             }
