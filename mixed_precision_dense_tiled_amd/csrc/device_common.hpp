@@ -25,6 +25,21 @@ __device__ __forceinline__ MPDT_LDS char* lds_cast(void* p) {
     return (MPDT_LDS char*)(p);
 }
 
+// Buffer resource (CDNA raw buffer, stride 0) over `range` bytes from a
+// wave-uniform base: a buffer read at an offset at or past `range` returns
+// zero and touches no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t range) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)range,
+                                             0x00020000 /* 32-bit data format (gfx9 family) */);
+}
+
+// 16 bytes per lane from buffer offset voff + soff straight into LDS: lane l's
+// bytes land at dst + 16 * l (dst is wave-uniform).
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, MPDT_LDS char* dst,
+                                                uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (MPDT_LDS void*)dst, 16, (int)voff, (int)soff, 0, 0);
+}
+
 // Keep the bytes [0, nbytes) of a 16-byte chunk, zero the rest (nbytes 0..16).
 __device__ __forceinline__ u32x4 mask_tail(u32x4 v, int nbytes) {
 #pragma unroll

@@ -11,24 +11,27 @@
 // tiles, conflict-free shared-memory layout).  Everything below is designed
 // for CDNA4: 64-lane wavefronts, 32x32 MFMA tiles, a 160 KiB LDS, XCD-local L2.
 //
-// Structure of one workgroup (256 threads = 4 wavefronts, one per SIMD):
+// Structure of one workgroup (512 threads = 8 wavefronts, two per SIMD):
 //   * WG tile BM x BN of D; wave tile (BM / WAVES_M) x (BN / WAVES_N) held in
 //     MFMA accumulators for the whole K loop (acc starts at zero; C is added
 //     once in the epilogue).
-//   * K is walked in 128-byte tiles (64 FP16/BF16 or 128 INT8/FP8 elements; for
-//     FP8 one K tile is exactly one 128-wide scale block).
-//   * Global -> registers -> LDS staging with 16-byte loads, two LDS stages,
-//     one barrier per K tile; the loads of tile t+2 are in flight while tile
-//     t+1 is computed.
+//   * K is walked in K tiles of KT_BYTES bytes per row (32 FP16/BF16 or 64
+//     INT8 elements; 128 FP8 elements, exactly one scale block).
+//   * Interior tiles with 16-byte aligned rows: buffer loads that write LDS
+//     directly (no register round trip) fill NS rotating stages, issued
+//     NS-1 tiles ahead.  For FP16/BF16/INT8 the two wavefronts of each SIMD
+//     alternate between a compute slot (MFMAs) and a memory slot (operand
+//     reads from LDS, direct-load issue) between workgroup barriers.
+//   * Edge tiles, unaligned rows and the K tail: 16-byte global loads into
+//     registers (bounded: bytes past M, N or K read as zero, with an
+//     in-register re-alignment for rows that are not 16-byte aligned), then
+//     LDS stores; two stages; stores of D are masked.
 //   * LDS layouts are XOR-swizzled in 16-byte chunks.  A (row-major, K
 //     contiguous) is read with ds_read_b128 along K; B (row-major, N
 //     contiguous) is read with the gfx950 transposing reads ds_read_b64_tr_b16
 //     / _b8, which hand each lane one column of a small K x 16 block -- exactly
 //     the "column j, consecutive k" operand an MFMA lane needs, so B never has
 //     to be transposed in memory.
-//   * Edges: loads past M, N or K read zero (bounded 16-byte loads, with an
-//     in-register re-alignment for rows that are not 16-byte aligned); stores
-//     are masked.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -265,7 +268,7 @@ void gemm_kernel(GemmArgs g) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar registers
     const int wm = wave / C::WAVES_N;
     const int wn = wave % C::WAVES_N;
 
@@ -342,29 +345,46 @@ void gemm_kernel(GemmArgs g) {
     // lane that fills physical chunk pc of LDS row r fetches logical chunk
     // pc ^ swz(r) from memory (XOR is its own inverse).  Each wave issues
     // UA + UB of these per K tile.
+    // Each load reads through a buffer resource whose wave-uniform base is the
+    // K tile's first byte (A: row m0; B: K row kt*KROWS, column n0) and whose
+    // range ends at the operand's last byte (the hardware returns zeros for
+    // lane offsets past it; the interior-tile conditions keep every read of
+    // these paths inside the operand).  Lane offsets (row in the piece times
+    // ld, plus the swizzled chunk) are 32-bit and loop-invariant: the swizzles
+    // repeat every 16 rows and every wave starts its pieces on a multiple of
+    // 16 rows, so they take one or a few registers; piece offsets are scalar.
+    // Offsets stay below 2^31 when ld < 2^31 / BM (A) and < 2^31 / KROWS (B).
+    // rows per 1 KiB piece and the row periods of the two swizzles
+    constexpr int RPA = 1024 / C::KT_BYTES, RPB = 1024 / C::B_ROW;
+    constexpr int PERIOD_A = 16, PERIOD_B = C::ES == 2 ? 4 : 8;
+    static_assert((C::UA * RPA) % PERIOD_A == 0 && (C::UB * RPB) % PERIOD_B == 0,
+                  "each wave's pieces start on a swizzle period");
+    const int64_t span_a = (int64_t)(g.M - 1) * g.lda_b + k_bytes;
+    const int64_t span_b = (int64_t)(g.K - 1) * g.ldb_b + (int64_t)g.N * C::ES;
+    auto tile_rsrc = [](const char* base, int64_t rest) {
+        return buffer_rsrc(base, (uint32_t)min(rest, (int64_t)0x7fffffff));
+    };
+    auto dma_a = [&](int kt, MPDT_LDS char* dst, int wbase, int u) {
+        const int lr = lane / C::CPR_A;
+        const uint32_t c = (uint32_t)(lane % C::CPR_A) ^ swz_a<C::CPR_A>(u * RPA + lr);
+        const int64_t first = (int64_t)m0 * g.lda_b + (int64_t)kt * C::KT_BYTES;
+        const auto rs = tile_rsrc(g.A + first, span_a - first);
+        buffer_to_lds16(rs, dst + (wbase + u) * 1024, (uint32_t)lr * (uint32_t)g.lda_b + c * 16u,
+                        (uint32_t)((wbase + u) * RPA) * (uint32_t)g.lda_b);
+    };
+    auto dma_b = [&](int kt, MPDT_LDS char* dst, int wbase, int u) {
+        const int lr = lane / C::CPR_B;
+        const uint32_t c = (uint32_t)(lane % C::CPR_B) ^ swz_b<C::ES>(u * RPB + lr);
+        const int64_t first = (int64_t)kt * C::KROWS * g.ldb_b + (int64_t)n0 * C::ES;
+        const auto rs = tile_rsrc(g.B + first, span_b - first);
+        buffer_to_lds16(rs, dst + (wbase + u) * 1024, (uint32_t)lr * (uint32_t)g.ldb_b + c * 16u,
+                        (uint32_t)((wbase + u) * RPB) * (uint32_t)g.ldb_b);
+    };
     auto dma_tile = [&](int kt, const Stage& s) {
-        const int64_t kb0 = (int64_t)kt * C::KT_BYTES;
-        constexpr int RPA = 1024 / C::KT_BYTES;              // A rows per 1 KiB piece
 #pragma unroll
-        for (int u = 0; u < C::UA; ++u) {
-            const int piece = wave * C::UA + u;
-            const int r = piece * RPA + lane / C::CPR_A;
-            const int c = (lane % C::CPR_A) ^ (int)swz_a<C::CPR_A>(r);
-            const char* gp = g.A + (int64_t)(m0 + r) * g.lda_b + kb0 + c * 16;
-            __builtin_amdgcn_global_load_lds((const void*)gp, (MPDT_LDS void*)(s.A + piece * 1024),
-                                             16, 0, 0);
-        }
-        constexpr int RPB = 1024 / C::B_ROW;                 // B rows per 1 KiB piece
+        for (int u = 0; u < C::UA; ++u) dma_a(kt, s.A, wave * C::UA, u);
 #pragma unroll
-        for (int u = 0; u < C::UB; ++u) {
-            const int piece = wave * C::UB + u;
-            const int k = piece * RPB + lane / C::CPR_B;
-            const int c = (lane % C::CPR_B) ^ (int)swz_b<C::ES>(k);
-            const char* gp = g.B + (int64_t)(kt * C::KROWS + k) * g.ldb_b +
-                             (int64_t)n0 * C::ES + c * 16;
-            __builtin_amdgcn_global_load_lds((const void*)gp, (MPDT_LDS void*)(s.B + piece * 1024),
-                                             16, 0, 0);
-        }
+        for (int u = 0; u < C::UB; ++u) dma_b(kt, s.B, wave * C::UB, u);
     };
     constexpr int DMA_PER_TILE = C::UA + C::UB;
 
@@ -511,47 +531,37 @@ void gemm_kernel(GemmArgs g) {
 
     // ---- K loop -------------------------------------------------------------
     const bool pingpong = !IS_FP8 && C::WAVES_M == 2 && NS >= 3 && (k_bytes % C::KT_BYTES) == 0;
-    if (ALIGNED && full_mn && pingpong) {
+    const bool direct = ALIGNED && full_mn && g.lda_b < (int64_t(1) << 31) / C::BM &&
+                        g.ldb_b < (int64_t(1) << 31) / C::KROWS;
+    if (direct && pingpong) {
         if constexpr (ALIGNED && !IS_FP8 && C::WAVES_M == 2 && NS >= 3) {
             // Interior tile, whole K tiles: two-group ping-pong.  The two
             // wavefronts on each SIMD belong to different groups (group =
             // wave / 4 = wm) and alternate roles between workgroup barriers:
-            // while one issues the MFMAs of a K tile from registers, the other
-            // reads its operand fragments of that tile from LDS; group 0 also
-            // issues all direct loads, AHEAD = NS-1 tiles ahead, into NS stages.
-            //   slot 2t:   group 0 reads frags(t), loads tile t+AHEAD | group 1 computes t-1
-            //   slot 2t+1: group 0 computes t                        | group 1 reads frags(t)
-            // A stage holding tile t is read in slots 2t and 2t+1 and refilled
-            // in slot 2t+2 with tile t+NS.  Before the barrier that opens slot
-            // 2t+2, group 0 waits for its loads of tile t+1.
+            // a compute slot issues the MFMAs of a K tile from registers and,
+            // in between, reads step 0 of the next tile's operand fragments;
+            // a memory slot reads the remaining steps of the current tile
+            // (group 0 also issues all direct loads, AHEAD = NS-1 tiles
+            // ahead, into NS stages).  Splitting the LDS reads this way keeps
+            // both waves of a SIMD reading LDS, which sustains a higher LDS
+            // rate than one wave alone.
+            //   slot 2t:   group 0 memory(t), loads tile t+AHEAD | group 1 computes t-1, reads t/0
+            //   slot 2t+1: group 0 computes t, reads t+1/0      | group 1 memory(t)
+            // A stage holding tile t is read in slots 2t-1 .. 2t+1 and refilled
+            // from slot 2t+2 on.  Tile t+1 is first read in slot 2t+1: group 0
+            // waits for its loads of tile t+1 at the end of its memory slot 2t.
             const int nt = (int)(k_bytes / C::KT_BYTES);
             const bool g0 = (wm == 0);
             constexpr int PA = C::A_BYTES / 1024 / 4, PB = C::B_BYTES / 1024 / 4;
             constexpr int PER_TILE = PA + PB;            // direct loads per group-0 wave per tile
-            Frags f;
+            static_assert((PA * RPA) % PERIOD_A == 0 && (PB * RPB) % PERIOD_B == 0,
+                          "each wave's pieces start on a swizzle period");
+            Frags fr;
             auto dma_all = [&](int kt, const Stage& s) {   // one group moves the whole tile
-                const int64_t kb0 = (int64_t)kt * C::KT_BYTES;
-                constexpr int RPA = 1024 / C::KT_BYTES;
-                constexpr int RPB = 1024 / C::B_ROW;
 #pragma unroll
-                for (int u = 0; u < PA; ++u) {
-                    const int piece = wn * PA + u;
-                    const int r = piece * RPA + lane / C::CPR_A;
-                    const int c = (lane % C::CPR_A) ^ (int)swz_a<C::CPR_A>(r);
-                    const char* gpa = g.A + (int64_t)(m0 + r) * g.lda_b + kb0 + c * 16;
-                    __builtin_amdgcn_global_load_lds((const void*)gpa,
-                                                     (MPDT_LDS void*)(s.A + piece * 1024), 16, 0, 0);
-                }
+                for (int u = 0; u < PA; ++u) dma_a(kt, s.A, wn * PA, u);
 #pragma unroll
-                for (int u = 0; u < PB; ++u) {
-                    const int piece = wn * PB + u;
-                    const int k = piece * RPB + lane / C::CPR_B;
-                    const int c = (lane % C::CPR_B) ^ (int)swz_b<C::ES>(k);
-                    const char* gpb = g.B + (int64_t)(kt * C::KROWS + k) * g.ldb_b +
-                                      (int64_t)n0 * C::ES + c * 16;
-                    __builtin_amdgcn_global_load_lds((const void*)gpb,
-                                                     (MPDT_LDS void*)(s.B + piece * 1024), 16, 0, 0);
-                }
+                for (int u = 0; u < PB; ++u) dma_b(kt, s.B, wn * PB, u);
             };
             // wait until at most `later` tiles of loads (issued after the one
             // wanted) are still in flight
@@ -569,28 +579,36 @@ void gemm_kernel(GemmArgs g) {
             }
             wg_barrier();
             if (!g0) wg_barrier();   // group 1 runs one slot behind
+            load_step(stage(I0{}), fr, 0);
             for (int t0 = 0; t0 < nt; t0 += NS) {
                 static_for<0, NS>([&](auto U) {
                     constexpr int u = decltype(U)::value;
                     const int t = t0 + u;
                     if (t < nt) {
-                        // memory slot
-#pragma unroll
-                        for (int q = 0; q < C::STEPS; ++q) load_step(stage(U), f, q);
+                        // memory slot: remaining steps of tile t
                         if (g0 && t + AHEAD < nt)
                             dma_all(t + AHEAD, stage(std::integral_constant<int, (u + AHEAD) % NS>{}));
+#pragma unroll
+                        for (int q = 1; q < C::STEPS; ++q) load_step(stage(U), fr, q);
+                        if (g0 && t + 1 < nt) wait_tiles(min(AHEAD - 1, nt - 2 - t));
                         wait_lds();
                         wg_barrier();
-                        // compute slot
+                        // compute slot: MFMAs of tile t; once step 0's are
+                        // issued, its registers take step 0 of tile t+1
+                        mma_step(fr, 0, acc);
+                        if (t + 1 < nt)
+                            load_step(stage(std::integral_constant<int, (u + 1) % NS>{}), fr, 0);
 #pragma unroll
-                        for (int q = 0; q < C::STEPS; ++q) mma_step(f, q, acc);
-                        if (g0 && t + 1 < nt) wait_tiles(min(AHEAD - 1, nt - 2 - t));
-                        if (g0 || t + 1 < nt) wg_barrier();
+                        for (int q = 1; q < C::STEPS; ++q) mma_step(fr, q, acc);
+                        if (g0 || t + 1 < nt) {
+                            wait_lds();
+                            wg_barrier();
+                        }
                     }
                 });
             }
         }
-    } else if (ALIGNED && full_mn) {
+    } else if (direct) {
         if constexpr (ALIGNED) {
             // Interior tile: full K tiles stream through direct loads issued
             // AHEAD tiles early into NS rotating stages; one barrier per K tile.
