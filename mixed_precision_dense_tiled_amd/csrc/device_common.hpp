@@ -40,6 +40,32 @@ __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, MPDT_L
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (MPDT_LDS void*)dst, 16, (int)voff, (int)soff, 0, 0);
 }
 
+// Buffer resource words (raw buffer, stride 0, 32-bit data format) for
+// `range` bytes from `base`; reads at offsets >= range return zero and touch
+// no memory.
+__device__ __forceinline__ i32x4 rsrc_words(uint64_t base, uint32_t range) {
+    return i32x4{(int32_t)(uint32_t)base, (int32_t)((uint32_t)(base >> 32) & 0xffffu),
+                 (int32_t)range, 0x00020000};
+}
+
+// 16 bytes per lane from buffer offset voff + soff + OFF into LDS at
+// dst + OFF + 16 * lane (M0 = dst), written as inline assembly.  The compiler
+// does not see this LDS write, so it adds no waits of its own before later LDS
+// reads; the caller orders them with explicit vmcnt waits and workgroup
+// barriers.  (The compiler's own tracking of direct-to-LDS loads falls back to
+// waiting for every load in flight where control flow merges, which would
+// empty a multi-stage pipeline at each loop entry.)  OFF (0..4095) moves both
+// addresses, so several loads can share one M0 value.  The s_nop gives an M0
+// write just before it its one wait state.
+template <int OFF = 0>
+__device__ __forceinline__ void lds_dma16(i32x4 r, MPDT_LDS char* dst, uint32_t voff,
+                                          uint32_t soff) {
+    static_assert(OFF >= 0 && OFF < 4096, "12-bit instruction offset");
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen offset:%4 lds"
+                 :
+                 : "{m0}"((uint32_t)(uintptr_t)dst), "v"(voff), "s"(r), "s"(soff), "n"(OFF));
+}
+
 // Keep the bytes [0, nbytes) of a 16-byte chunk, zero the rest (nbytes 0..16).
 __device__ __forceinline__ u32x4 mask_tail(u32x4 v, int nbytes) {
 #pragma unroll

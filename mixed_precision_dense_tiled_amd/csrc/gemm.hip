@@ -232,11 +232,19 @@ void gemm_kernel(GemmArgs g) {
     constexpr bool IS_FP8 = (KD == Kind::FP8);
     constexpr int NS = C::STAGES;
     constexpr int AHEAD = NS - 1;                 // K tiles loaded ahead of the one computed
+    // ONE_WAVE: one wavefront per SIMD (4 per workgroup), each holding a large
+    // wave tile; its own instruction stream overlaps operand reads and direct
+    // loads with its MFMAs.  Otherwise two wavefronts per SIMD in ping-pong.
+    constexpr bool ONE_WAVE = !IS_FP8 && C::NT == 256;
 
     // LDS stages, each its own object, so that the compiler can tell a
     // direct-to-LDS load into one stage from the reads of another.  For FP8
     // the A-row scales of stages 0 and 1 follow their A tiles.
-    __shared__ __attribute__((aligned(1024))) char sA0[C::A_BYTES + C::SA_BYTES];
+    // One-wave tiles keep their NS stages in one array (stage i at i * STAGE_BYTES,
+    // A tile then B tile), so that the stage of a K tile can be a run-time index.
+    constexpr int STAGE_BYTES = C::A_BYTES + C::B_BYTES;
+    __shared__ __attribute__((aligned(1024))) char sA0[ONE_WAVE ? NS * STAGE_BYTES
+                                                                : C::A_BYTES + C::SA_BYTES];
     __shared__ __attribute__((aligned(1024))) char sB0[C::B_BYTES];
     __shared__ __attribute__((aligned(1024))) char sA1[C::A_BYTES + C::SA_BYTES];
     __shared__ __attribute__((aligned(1024))) char sB1[C::B_BYTES];
@@ -250,7 +258,10 @@ void gemm_kernel(GemmArgs g) {
     // every access names its buffer object directly).
     auto stage = [&](auto I) -> Stage {
         constexpr int i = decltype(I)::value;
-        if constexpr (i == 0) return {lds_cast(sA0), lds_cast(sB0), (MPDT_LDS float*)(sA0 + C::A_BYTES)};
+        if constexpr (ONE_WAVE)
+            return {lds_cast(sA0) + i * STAGE_BYTES, lds_cast(sA0) + i * STAGE_BYTES + C::A_BYTES,
+                    nullptr};
+        else if constexpr (i == 0) return {lds_cast(sA0), lds_cast(sB0), (MPDT_LDS float*)(sA0 + C::A_BYTES)};
         else if constexpr (i == 1) return {lds_cast(sA1), lds_cast(sB1), (MPDT_LDS float*)(sA1 + C::A_BYTES)};
         else if constexpr (i == 2) return {lds_cast(sA2), lds_cast(sB2), nullptr};
         else if constexpr (i == 3) return {lds_cast(sA3), lds_cast(sB3), nullptr};
@@ -364,21 +375,23 @@ void gemm_kernel(GemmArgs g) {
     auto tile_rsrc = [](const char* base, int64_t rest) {
         return buffer_rsrc(base, (uint32_t)min(rest, (int64_t)0x7fffffff));
     };
+    auto dma16 = [&](const char* base, int64_t rest, MPDT_LDS char* dst, uint32_t voff,
+                     uint32_t soff) { buffer_to_lds16(tile_rsrc(base, rest), dst, voff, soff); };
     auto dma_a = [&](int kt, MPDT_LDS char* dst, int wbase, int u) {
         const int lr = lane / C::CPR_A;
         const uint32_t c = (uint32_t)(lane % C::CPR_A) ^ swz_a<C::CPR_A>(u * RPA + lr);
         const int64_t first = (int64_t)m0 * g.lda_b + (int64_t)kt * C::KT_BYTES;
-        const auto rs = tile_rsrc(g.A + first, span_a - first);
-        buffer_to_lds16(rs, dst + (wbase + u) * 1024, (uint32_t)lr * (uint32_t)g.lda_b + c * 16u,
-                        (uint32_t)((wbase + u) * RPA) * (uint32_t)g.lda_b);
+        dma16(g.A + first, span_a - first, dst + (wbase + u) * 1024,
+              (uint32_t)lr * (uint32_t)g.lda_b + c * 16u,
+              (uint32_t)((wbase + u) * RPA) * (uint32_t)g.lda_b);
     };
     auto dma_b = [&](int kt, MPDT_LDS char* dst, int wbase, int u) {
         const int lr = lane / C::CPR_B;
         const uint32_t c = (uint32_t)(lane % C::CPR_B) ^ swz_b<C::ES>(u * RPB + lr);
         const int64_t first = (int64_t)kt * C::KROWS * g.ldb_b + (int64_t)n0 * C::ES;
-        const auto rs = tile_rsrc(g.B + first, span_b - first);
-        buffer_to_lds16(rs, dst + (wbase + u) * 1024, (uint32_t)lr * (uint32_t)g.ldb_b + c * 16u,
-                        (uint32_t)((wbase + u) * RPB) * (uint32_t)g.ldb_b);
+        dma16(g.B + first, span_b - first, dst + (wbase + u) * 1024,
+              (uint32_t)lr * (uint32_t)g.ldb_b + c * 16u,
+              (uint32_t)((wbase + u) * RPB) * (uint32_t)g.ldb_b);
     };
     auto dma_tile = [&](int kt, const Stage& s) {
 #pragma unroll
@@ -530,10 +543,181 @@ void gemm_kernel(GemmArgs g) {
     };
 
     // ---- K loop -------------------------------------------------------------
-    const bool pingpong = !IS_FP8 && C::WAVES_M == 2 && NS >= 3 && (k_bytes % C::KT_BYTES) == 0;
+    const bool whole_k = (k_bytes % C::KT_BYTES) == 0;
+    const bool pingpong = !IS_FP8 && !ONE_WAVE && C::WAVES_M == 2 && NS >= 3 && whole_k;
     const bool direct = ALIGNED && full_mn && g.lda_b < (int64_t(1) << 31) / C::BM &&
                         g.ldb_b < (int64_t(1) << 31) / C::KROWS;
-    if (direct && pingpong) {
+    if (ONE_WAVE && direct && whole_k && k_bytes >= (int64_t)NS * C::KT_BYTES) {
+        if constexpr (ALIGNED && ONE_WAVE && C::STEPS == 2 && C::TM == 4 && C::TN == 4) {
+            // Interior tile, whole K tiles (at least NS), one wavefront per
+            // SIMD with a 128 x 128 wave tile.  Per K tile t (two MFMA steps):
+            //   phase X: the 16 MFMAs of step 0, interleaved with the LDS
+            //            reads of step 1's fragments and the set-up of the
+            //            direct loads of tile t+NS;
+            //   wait for this wave's direct loads of tile t+1 and its LDS
+            //   reads, then workgroup barrier B(t+1): tile t+1 is in LDS and
+            //   no wave reads tile t's stage any more;
+            //   phase Y: the 16 MFMAs of step 1, interleaved with the 8 direct
+            //            loads of tile t+NS into tile t's stage and the reads
+            //            of tile t+1's step-0 fragments.
+            // All NS stages are filled before the loop.  Every K tile issues
+            // the same 8 direct loads (past the last tile they read through an
+            // empty buffer range: zeros, no memory traffic), so the vmcnt
+            // arithmetic is the same everywhere and the loop body is a single
+            // block.  The program order written here is pinned by scheduling
+            // barriers: a single wave per SIMD issues in order, so whatever
+            // sits between two MFMAs is issued while the first one runs.
+            static_assert(C::UA == 4 && C::UB == 4, "four A and four B pieces per wave and K tile");
+            const int nt = (int)(k_bytes / C::KT_BYTES);
+            constexpr int WAIT_AHEAD = (NS - 2) * DMA_PER_TILE;   // loads of tiles t+2..t+NS-1
+            MPDT_LDS char* const lds0 = lds_cast(sA0);
+
+            // Direct loads.  A piece u (16 rows of the K tile) and B piece u
+            // (RPB K rows) of this wave: lane offsets are loop-invariant (the
+            // swizzles repeat within a piece pair), scalar offsets per piece;
+            // the pieces of one operand share one M0 (piece u adds u KiB
+            // through the instruction offset, which also moves the global
+            // address, so the scalar offset takes u KiB back off).  The
+            // interior-tile conditions keep every live read inside A and B;
+            // offsets fit 32 bits (lda < 2^31 / BM, ldb < 2^31 / KROWS).
+            const int lra = lane / C::CPR_A, lrb = lane / C::CPR_B;
+            const uint32_t voffA = (uint32_t)lra * (uint32_t)g.lda_b +
+                                   (((uint32_t)(lane % C::CPR_A) ^ swz_a<C::CPR_A>(lra)) << 4);
+            const uint32_t voffB0 = (uint32_t)lrb * (uint32_t)g.ldb_b +
+                                    (((uint32_t)(lane % C::CPR_B) ^ swz_b<C::ES>(lrb)) << 4);
+            const uint32_t voffB1 = (uint32_t)lrb * (uint32_t)g.ldb_b +
+                                    (((uint32_t)(lane % C::CPR_B) ^ swz_b<C::ES>(RPB + lrb)) << 4);
+            auto soffA = [&](int u) {
+                return (uint32_t)((wave * C::UA + u) * RPA) * (uint32_t)g.lda_b - (uint32_t)u * 1024u;
+            };
+            auto soffB = [&](int u) {
+                return (uint32_t)((wave * C::UB + u) * RPB) * (uint32_t)g.ldb_b - (uint32_t)u * 1024u;
+            };
+            const uint64_t baseA = (uint64_t)(uintptr_t)g.A + (uint64_t)((int64_t)m0 * g.lda_b);
+            const uint64_t baseB = (uint64_t)(uintptr_t)g.B + (uint64_t)((int64_t)n0 * C::ES);
+            const int64_t restA0 = span_a - (int64_t)m0 * g.lda_b;   // bytes of A from baseA
+            const int64_t restB0 = span_b - (int64_t)n0 * C::ES;
+            const int64_t stepB = (int64_t)C::KROWS * g.ldb_b;          // bytes per K tile of B
+            auto clamp31 = [](int64_t r) { return (uint32_t)(r > 0x7fffffff ? 0x7fffffff : r); };
+            // resources of K tile kt (kA = kt * KT_BYTES, kB = kt * stepB)
+            auto rsA = [&](int64_t kA, bool live) {
+                return rsrc_words(baseA + (uint64_t)kA, live ? clamp31(restA0 - kA) : 0u);
+            };
+            auto rsB = [&](int64_t kB, bool live) {
+                return rsrc_words(baseB + (uint64_t)kB, live ? clamp31(restB0 - kB) : 0u);
+            };
+            auto dma_piece = [&](auto P, i32x4 ra, i32x4 rb, uint32_t stage_off) {
+                constexpr int p = decltype(P)::value;
+                if constexpr (p < C::UA)
+                    lds_dma16<p * 1024>(ra, lds0 + stage_off + wave * C::UA * 1024, voffA, soffA(p));
+                else
+                    lds_dma16<(p - C::UA) * 1024>(rb, lds0 + stage_off + C::A_BYTES + wave * C::UB * 1024,
+                                                  (p & 1) ? voffB1 : voffB0, soffB(p - C::UA));
+            };
+
+            // Fragment reads.  Lane offsets within a stage: A for step q
+            // (tile i adds i*32 rows: the A swizzle repeats every 16 rows);
+            // B for column tile j (step q adds QB bytes, half h adds HB: the
+            // B swizzle depends only on the K row modulo 4 (16-bit) or 8
+            // (8-bit)).
+            constexpr uint32_t QB = (C::ES == 2 ? 16 : F::STEP_BYTES) * C::B_ROW;
+            constexpr uint32_t HB = (C::ES == 2 ? 4 : 8) * C::B_ROW;
+            uint32_t la[2], lb[4];
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                la[q] = a_off<C>(wm * C::WM + lrow, q * (F::STEP_BYTES / 16) + lhalf * (C::FRAG_BYTES / 16));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t col16 = wn * C::WN + j * 32 + 16 * (grp & 1);
+                if constexpr (C::ES == 2)
+                    lb[j] = C::A_BYTES + b_off<C>(8 * (grp >> 1) + (gp >> 2), (col16 >> 3) + ((gp & 3) >> 1)) +
+                            8 * (gp & 1);
+                else
+                    lb[j] = C::A_BYTES + b_off<C>(C::FRAG_BYTES * (grp >> 1) + (gp >> 1), col16 >> 4) +
+                            8 * (gp & 1);
+            }
+            // read group r (0..6) of step q from the stage at stage_off, in
+            // the order the MFMAs consume them: A0+B0, B1, B2, B3, A1, A2, A3
+            auto read_group = [&](Frags& f, int q, int r, uint32_t stage_off) {
+                auto ra = [&](int i) {
+                    f.a[q][i][0] = lds_load16(lds0, stage_off + la[q] + i * 32 * C::KT_BYTES);
+                };
+                auto rb = [&](int j) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const uint32_t o = stage_off + lb[j] + q * QB + h * HB;
+                        if constexpr (C::ES == 2) f.b[q][j][h] = lds_read_tr16(lds0, o);
+                        else f.b[q][j][h] = lds_read_tr8(lds0, o);
+                    }
+                };
+                if (r == 0) { ra(0); rb(0); }
+                else if (r <= 3) rb(r);
+                else ra(r - 3);
+            };
+            auto mma1 = [&](const Frags& f, int q, int idx) {
+                const int i = idx / 4, j = idx % 4;
+                const u32x4 b = {f.b[q][j][0][0], f.b[q][j][0][1], f.b[q][j][1][0], f.b[q][j][1][1]};
+                acc[i][j] = F::mma(f.a[q][i][0], b, acc[i][j]);
+            };
+
+            Frags fr;
+#pragma unroll
+            for (int p = 0; p < NS; ++p) {
+                const i32x4 ra = rsA((int64_t)p * C::KT_BYTES, true);
+                const i32x4 rb = rsB((int64_t)p * stepB, true);
+                static_for<0, DMA_PER_TILE>([&](auto Q) { dma_piece(Q, ra, rb, p * STAGE_BYTES); });
+            }
+            wait_vmem<(NS - 1) * DMA_PER_TILE>();
+            wg_barrier();
+#pragma unroll
+            for (int r = 0; r < 7; ++r) read_group(fr, 0, r, 0);
+            int scur = 0;
+            int64_t kA = (int64_t)NS * C::KT_BYTES, kB = (int64_t)NS * stepB;   // tile t+NS
+            for (int t = 0; t < nt - 1; ++t) {
+                const int snext = scur + 1 == NS ? 0 : scur + 1;
+                const uint32_t cur = (uint32_t)scur * STAGE_BYTES;
+                const uint32_t nxt = (uint32_t)snext * STAGE_BYTES;
+                const bool live = t + NS < nt;
+                i32x4 ra, rb;
+                // phase X
+                static_for<0, 16>([&](auto IDX) {
+                    constexpr int idx = decltype(IDX)::value;
+                    mma1(fr, 0, idx);
+                    if constexpr (idx < 7) read_group(fr, 1, idx, cur);
+                    if constexpr (idx == 8) ra = rsA(kA, live);
+                    if constexpr (idx == 10) rb = rsB(kB, live);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+                wait_vmem<WAIT_AHEAD>();
+                wait_lds();
+                wg_barrier();
+                // phase Y
+                static_for<0, 16>([&](auto IDX) {
+                    constexpr int idx = decltype(IDX)::value;
+                    mma1(fr, 1, idx);
+                    if constexpr ((idx & 1) == 0)
+                        dma_piece(std::integral_constant<int, idx / 2>{}, ra, rb, cur);
+                    else if constexpr (idx / 2 < 7)
+                        read_group(fr, 0, idx / 2, nxt);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+                scur = snext;
+                kA += C::KT_BYTES;
+                kB += stepB;
+            }
+            // last K tile
+            const uint32_t cur = (uint32_t)scur * STAGE_BYTES;
+            static_for<0, 16>([&](auto IDX) {
+                constexpr int idx = decltype(IDX)::value;
+                mma1(fr, 0, idx);
+                if constexpr (idx < 7) read_group(fr, 1, idx, cur);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            wait_lds();
+#pragma unroll
+            for (int idx = 0; idx < 16; ++idx) mma1(fr, 1, idx);
+        }
+    } else if (direct && pingpong) {
         if constexpr (ALIGNED && !IS_FP8 && C::WAVES_M == 2 && NS >= 3) {
             // Interior tile, whole K tiles: two-group ping-pong.  The two
             // wavefronts on each SIMD belong to different groups (group =
@@ -608,8 +792,8 @@ void gemm_kernel(GemmArgs g) {
                 });
             }
         }
-    } else if (direct) {
-        if constexpr (ALIGNED) {
+    } else if (!ONE_WAVE && direct) {
+        if constexpr (ALIGNED && !ONE_WAVE) {
             // Interior tile: full K tiles stream through direct loads issued
             // AHEAD tiles early into NS rotating stages; one barrier per K tile.
             // At the top of iteration kt this wave waits for its own loads of
@@ -769,9 +953,15 @@ static hipError_t launch_cfg(const GemmArgs& a0, bool aligned, hipStream_t strea
     return hipGetLastError();
 }
 
-using CfgF16 = Cfg<Kind::F16, 256, 256, 2, 4, 64, 4>;
-using CfgBF16 = Cfg<Kind::BF16, 256, 256, 2, 4, 64, 4>;
-using CfgI8 = Cfg<Kind::I8, 256, 256, 2, 4, 64, 4>;
+#ifndef MPDT_WAVES_N16
+#define MPDT_WAVES_N16 2
+#endif
+#ifndef MPDT_STAGES16
+#define MPDT_STAGES16 4
+#endif
+using CfgF16 = Cfg<Kind::F16, 256, 256, 2, MPDT_WAVES_N16, 64, MPDT_STAGES16>;
+using CfgBF16 = Cfg<Kind::BF16, 256, 256, 2, MPDT_WAVES_N16, 64, MPDT_STAGES16>;
+using CfgI8 = Cfg<Kind::I8, 256, 256, 2, MPDT_WAVES_N16, 64, MPDT_STAGES16>;
 using CfgFP8 = Cfg<Kind::FP8, 128, 256, 2, 4, 128, 2>;
 
 hipError_t launch_gemm(Kind kind, const GemmArgs& a, bool aligned, hipStream_t stream) {
