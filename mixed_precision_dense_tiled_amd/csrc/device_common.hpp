@@ -55,15 +55,21 @@ __device__ __forceinline__ i32x4 rsrc_words(uint64_t base, uint32_t range) {
 // barriers.  (The compiler's own tracking of direct-to-LDS loads falls back to
 // waiting for every load in flight where control flow merges, which would
 // empty a multi-stage pipeline at each loop entry.)  OFF (0..4095) moves both
-// addresses, so several loads can share one M0 value.  The s_nop gives an M0
-// write just before it its one wait state.
-template <int OFF = 0>
+// addresses, so several loads can share one M0 value.  NOP: the load may
+// follow a write of M0 directly, which needs one wait state (s_nop 0) -- the
+// first load after a new M0 value.
+template <int OFF = 0, bool NOP = true>
 __device__ __forceinline__ void lds_dma16(i32x4 r, MPDT_LDS char* dst, uint32_t voff,
                                           uint32_t soff) {
     static_assert(OFF >= 0 && OFF < 4096, "12-bit instruction offset");
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen offset:%4 lds"
-                 :
-                 : "{m0}"((uint32_t)(uintptr_t)dst), "v"(voff), "s"(r), "s"(soff), "n"(OFF));
+    if constexpr (NOP)
+        asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen offset:%4 lds"
+                     :
+                     : "{m0}"((uint32_t)(uintptr_t)dst), "v"(voff), "s"(r), "s"(soff), "n"(OFF));
+    else
+        asm volatile("buffer_load_dwordx4 %1, %2, %3 offen offset:%4 lds"
+                     :
+                     : "{m0}"((uint32_t)(uintptr_t)dst), "v"(voff), "s"(r), "s"(soff), "n"(OFF));
 }
 
 // Keep the bytes [0, nbytes) of a 16-byte chunk, zero the rest (nbytes 0..16).

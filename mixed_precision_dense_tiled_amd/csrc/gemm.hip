@@ -232,9 +232,10 @@ void gemm_kernel(GemmArgs g) {
     constexpr bool IS_FP8 = (KD == Kind::FP8);
     constexpr int NS = C::STAGES;
     constexpr int AHEAD = NS - 1;                 // K tiles loaded ahead of the one computed
-    // ONE_WAVE: one wavefront per SIMD (4 per workgroup), each holding a large
-    // wave tile; its own instruction stream overlaps operand reads and direct
-    // loads with its MFMAs.  Otherwise two wavefronts per SIMD in ping-pong.
+    // ONE_WAVE: the interior-tile kernel, one wavefront per SIMD (4 per
+    // workgroup) with a 128 x 128 wave tile; its own instruction stream
+    // overlaps operand reads and direct loads with its MFMAs.  Otherwise the
+    // general kernel (edge tiles, unaligned rows, K tails, FP8).
     constexpr bool ONE_WAVE = !IS_FP8 && C::NT == 256;
 
     // LDS stages, each its own object, so that the compiler can tell a
@@ -284,7 +285,22 @@ void gemm_kernel(GemmArgs g) {
     const int wn = wave % C::WAVES_N;
 
     int tm, tn;
-    tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+    if (g.int_tm > 0 && g.int_tn > 0) {
+        // the interior int_tm x int_tn tiles were launched separately: this
+        // grid covers the bottom tile rows, then the right tile columns
+        const int bottom = (g.tiles_m - g.int_tm) * g.tiles_n;
+        const int b = blockIdx.x;
+        if (b < bottom) {
+            tm = g.int_tm + b / g.tiles_n;
+            tn = b % g.tiles_n;
+        } else {
+            const int r = b - bottom, cols = g.tiles_n - g.int_tn;
+            tm = r / cols;
+            tn = g.int_tn + r % cols;
+        }
+    } else {
+        tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+    }
     const int m0 = tm * C::BM;
     const int n0 = tn * C::BN;
     const bool full_mn = (m0 + C::BM <= g.M) && (n0 + C::BN <= g.N);
@@ -544,11 +560,14 @@ void gemm_kernel(GemmArgs g) {
 
     // ---- K loop -------------------------------------------------------------
     const bool whole_k = (k_bytes % C::KT_BYTES) == 0;
-    const bool pingpong = !IS_FP8 && !ONE_WAVE && C::WAVES_M == 2 && NS >= 3 && whole_k;
     const bool direct = ALIGNED && full_mn && g.lda_b < (int64_t(1) << 31) / C::BM &&
                         g.ldb_b < (int64_t(1) << 31) / C::KROWS;
-    if (ONE_WAVE && direct && whole_k && k_bytes >= (int64_t)NS * C::KT_BYTES) {
-        if constexpr (ALIGNED && ONE_WAVE && C::STEPS == 2 && C::TM == 4 && C::TN == 4) {
+    if constexpr (ONE_WAVE) {
+        // Launched over interior tiles only, with aligned rows and whole K
+        // tiles (the host checks all of it; this guard keeps any other tile
+        // from being touched).
+        if (!(direct && whole_k && k_bytes >= (int64_t)NS * C::KT_BYTES)) return;
+        if constexpr (ALIGNED && C::STEPS == 2 && C::TM == 4 && C::TN == 4) {
             // Interior tile, whole K tiles (at least NS), one wavefront per
             // SIMD with a 128 x 128 wave tile.  Per K tile t (two MFMA steps):
             //   phase X: the 16 MFMAs of step 0, interleaved with the LDS
@@ -608,11 +627,14 @@ void gemm_kernel(GemmArgs g) {
             };
             auto dma_piece = [&](auto P, i32x4 ra, i32x4 rb, uint32_t stage_off) {
                 constexpr int p = decltype(P)::value;
+                // (M0 changes before the first piece of each operand only)
                 if constexpr (p < C::UA)
-                    lds_dma16<p * 1024>(ra, lds0 + stage_off + wave * C::UA * 1024, voffA, soffA(p));
+                    lds_dma16<p * 1024, p == 0>(ra, lds0 + stage_off + wave * C::UA * 1024, voffA,
+                                                soffA(p));
                 else
-                    lds_dma16<(p - C::UA) * 1024>(rb, lds0 + stage_off + C::A_BYTES + wave * C::UB * 1024,
-                                                  (p & 1) ? voffB1 : voffB0, soffB(p - C::UA));
+                    lds_dma16<(p - C::UA) * 1024, p == C::UA>(
+                        rb, lds0 + stage_off + C::A_BYTES + wave * C::UB * 1024,
+                        (p & 1) ? voffB1 : voffB0, soffB(p - C::UA));
             };
 
             // Fragment reads.  Lane offsets within a stage: A for step q
@@ -717,83 +739,8 @@ void gemm_kernel(GemmArgs g) {
 #pragma unroll
             for (int idx = 0; idx < 16; ++idx) mma1(fr, 1, idx);
         }
-    } else if (direct && pingpong) {
-        if constexpr (ALIGNED && !IS_FP8 && C::WAVES_M == 2 && NS >= 3) {
-            // Interior tile, whole K tiles: two-group ping-pong.  The two
-            // wavefronts on each SIMD belong to different groups (group =
-            // wave / 4 = wm) and alternate roles between workgroup barriers:
-            // a compute slot issues the MFMAs of a K tile from registers and,
-            // in between, reads step 0 of the next tile's operand fragments;
-            // a memory slot reads the remaining steps of the current tile
-            // (group 0 also issues all direct loads, AHEAD = NS-1 tiles
-            // ahead, into NS stages).  Splitting the LDS reads this way keeps
-            // both waves of a SIMD reading LDS, which sustains a higher LDS
-            // rate than one wave alone.
-            //   slot 2t:   group 0 memory(t), loads tile t+AHEAD | group 1 computes t-1, reads t/0
-            //   slot 2t+1: group 0 computes t, reads t+1/0      | group 1 memory(t)
-            // A stage holding tile t is read in slots 2t-1 .. 2t+1 and refilled
-            // from slot 2t+2 on.  Tile t+1 is first read in slot 2t+1: group 0
-            // waits for its loads of tile t+1 at the end of its memory slot 2t.
-            const int nt = (int)(k_bytes / C::KT_BYTES);
-            const bool g0 = (wm == 0);
-            constexpr int PA = C::A_BYTES / 1024 / 4, PB = C::B_BYTES / 1024 / 4;
-            constexpr int PER_TILE = PA + PB;            // direct loads per group-0 wave per tile
-            static_assert((PA * RPA) % PERIOD_A == 0 && (PB * RPB) % PERIOD_B == 0,
-                          "each wave's pieces start on a swizzle period");
-            Frags fr;
-            auto dma_all = [&](int kt, const Stage& s) {   // one group moves the whole tile
-#pragma unroll
-                for (int u = 0; u < PA; ++u) dma_a(kt, s.A, wn * PA, u);
-#pragma unroll
-                for (int u = 0; u < PB; ++u) dma_b(kt, s.B, wn * PB, u);
-            };
-            // wait until at most `later` tiles of loads (issued after the one
-            // wanted) are still in flight
-            auto wait_tiles = [&](int later) {
-                if (later >= 3) wait_vmem<3 * PER_TILE>();
-                else if (later == 2) wait_vmem<2 * PER_TILE>();
-                else if (later == 1) wait_vmem<PER_TILE>();
-                else wait_vmem<0>();
-            };
-            if (g0) {
-                static_for<0, AHEAD>([&](auto p) {
-                    if (decltype(p)::value < nt) dma_all(decltype(p)::value, stage(p));
-                });
-                wait_tiles(min(AHEAD - 1, nt - 1));
-            }
-            wg_barrier();
-            if (!g0) wg_barrier();   // group 1 runs one slot behind
-            load_step(stage(I0{}), fr, 0);
-            for (int t0 = 0; t0 < nt; t0 += NS) {
-                static_for<0, NS>([&](auto U) {
-                    constexpr int u = decltype(U)::value;
-                    const int t = t0 + u;
-                    if (t < nt) {
-                        // memory slot: remaining steps of tile t
-                        if (g0 && t + AHEAD < nt)
-                            dma_all(t + AHEAD, stage(std::integral_constant<int, (u + AHEAD) % NS>{}));
-#pragma unroll
-                        for (int q = 1; q < C::STEPS; ++q) load_step(stage(U), fr, q);
-                        if (g0 && t + 1 < nt) wait_tiles(min(AHEAD - 1, nt - 2 - t));
-                        wait_lds();
-                        wg_barrier();
-                        // compute slot: MFMAs of tile t; once step 0's are
-                        // issued, its registers take step 0 of tile t+1
-                        mma_step(fr, 0, acc);
-                        if (t + 1 < nt)
-                            load_step(stage(std::integral_constant<int, (u + 1) % NS>{}), fr, 0);
-#pragma unroll
-                        for (int q = 1; q < C::STEPS; ++q) mma_step(fr, q, acc);
-                        if (g0 || t + 1 < nt) {
-                            wait_lds();
-                            wg_barrier();
-                        }
-                    }
-                });
-            }
-        }
-    } else if (!ONE_WAVE && direct) {
-        if constexpr (ALIGNED && !ONE_WAVE) {
+    } else if (direct) {
+        if constexpr (ALIGNED) {
             // Interior tile: full K tiles stream through direct loads issued
             // AHEAD tiles early into NS rotating stages; one barrier per K tile.
             // At the top of iteration kt this wave waits for its own loads of
@@ -938,38 +885,63 @@ void gemm_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------
 // Host-side launchers (called by the C ABI after validation).
 // ---------------------------------------------------------------------------
-template <Kind KD, class C>
-static hipError_t launch_cfg(const GemmArgs& a0, bool aligned, hipStream_t stream) {
-    GemmArgs a = a0;
-    a.tiles_m = (a.M + C::BM - 1) / C::BM;
-    a.tiles_n = (a.N + C::BN - 1) / C::BN;
-    const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
-    if (tiles == 0) return hipSuccess;
-    dim3 grid((unsigned)tiles), block(C::NT);
-    if (aligned)
-        hipLaunchKernelGGL((gemm_kernel<KD, C, true>), grid, block, 0, stream, a);
-    else
-        hipLaunchKernelGGL((gemm_kernel<KD, C, false>), grid, block, 0, stream, a);
+template <Kind KD, class C, bool ALIGNED>
+static hipError_t launch_grid(const GemmArgs& a, int64_t tiles, hipStream_t stream) {
+    if (tiles <= 0) return hipSuccess;
+    hipLaunchKernelGGL((gemm_kernel<KD, C, ALIGNED>), dim3((unsigned)tiles), dim3(C::NT), 0, stream, a);
     return hipGetLastError();
 }
 
-#ifndef MPDT_WAVES_N16
-#define MPDT_WAVES_N16 2
-#endif
-#ifndef MPDT_STAGES16
-#define MPDT_STAGES16 4
-#endif
-using CfgF16 = Cfg<Kind::F16, 256, 256, 2, MPDT_WAVES_N16, 64, MPDT_STAGES16>;
-using CfgBF16 = Cfg<Kind::BF16, 256, 256, 2, MPDT_WAVES_N16, 64, MPDT_STAGES16>;
-using CfgI8 = Cfg<Kind::I8, 256, 256, 2, MPDT_WAVES_N16, 64, MPDT_STAGES16>;
+// General kernel over every tile (or over the edge tiles around an interior
+// block launched separately).
+template <Kind KD, class C>
+static hipError_t launch_general(GemmArgs a, bool aligned, int int_tm, int int_tn,
+                                 hipStream_t stream) {
+    a.tiles_m = (a.M + C::BM - 1) / C::BM;
+    a.tiles_n = (a.N + C::BN - 1) / C::BN;
+    a.int_tm = int_tm;
+    a.int_tn = int_tn;
+    const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n - (int64_t)int_tm * int_tn;
+    return aligned ? launch_grid<KD, C, true>(a, tiles, stream)
+                   : launch_grid<KD, C, false>(a, tiles, stream);
+}
+
+// FP16 / BF16 / INT8: the full 256 x 256 tiles of an aligned problem with
+// whole K tiles (at least STAGES of them) go to the one-wave kernel; the
+// remaining edge tiles, and every other problem, to the general kernel.
+template <Kind KD, class C1, class C8>
+static hipError_t launch_mma(const GemmArgs& a0, bool aligned, hipStream_t stream) {
+    static_assert(C1::BM == C8::BM && C1::BN == C8::BN, "one tile grid for both kernels");
+    const int64_t kb = (int64_t)a0.K * C1::ES;
+    const bool one = aligned && kb % C1::KT_BYTES == 0 && kb >= (int64_t)C1::STAGES * C1::KT_BYTES &&
+                     a0.lda_b < (int64_t(1) << 31) / C1::BM && a0.ldb_b < (int64_t(1) << 31) / C1::KROWS;
+    const int int_tm = one ? a0.M / C1::BM : 0;
+    const int int_tn = one ? a0.N / C1::BN : 0;
+    if (int_tm > 0 && int_tn > 0) {
+        GemmArgs a = a0;
+        a.tiles_m = int_tm;
+        a.tiles_n = int_tn;
+        a.int_tm = a.int_tn = 0;
+        const hipError_t e = launch_grid<KD, C1, true>(a, (int64_t)int_tm * int_tn, stream);
+        if (e != hipSuccess) return e;
+        return launch_general<KD, C8>(a0, aligned, int_tm, int_tn, stream);
+    }
+    return launch_general<KD, C8>(a0, aligned, 0, 0, stream);
+}
+
+// one wavefront per SIMD, interior tiles
+template <Kind KD> using Cfg1W = Cfg<KD, 256, 256, 2, 2, 64, 4>;
+// eight wavefronts, everything else
+template <Kind KD> using Cfg8W = Cfg<KD, 256, 256, 2, 4, 64, 4>;
 using CfgFP8 = Cfg<Kind::FP8, 128, 256, 2, 4, 128, 2>;
 
 hipError_t launch_gemm(Kind kind, const GemmArgs& a, bool aligned, hipStream_t stream) {
     switch (kind) {
-        case Kind::F16: return launch_cfg<Kind::F16, CfgF16>(a, aligned, stream);
-        case Kind::BF16: return launch_cfg<Kind::BF16, CfgBF16>(a, aligned, stream);
-        case Kind::I8: return launch_cfg<Kind::I8, CfgI8>(a, aligned, stream);
-        case Kind::FP8: return launch_cfg<Kind::FP8, CfgFP8>(a, aligned, stream);
+        case Kind::F16: return launch_mma<Kind::F16, Cfg1W<Kind::F16>, Cfg8W<Kind::F16>>(a, aligned, stream);
+        case Kind::BF16:
+            return launch_mma<Kind::BF16, Cfg1W<Kind::BF16>, Cfg8W<Kind::BF16>>(a, aligned, stream);
+        case Kind::I8: return launch_mma<Kind::I8, Cfg1W<Kind::I8>, Cfg8W<Kind::I8>>(a, aligned, stream);
+        case Kind::FP8: return launch_general<Kind::FP8, CfgFP8>(a, aligned, 0, 0, stream);
     }
     return hipErrorInvalidValue;
 }

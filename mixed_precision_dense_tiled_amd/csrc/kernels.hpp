@@ -22,6 +22,7 @@ struct GemmArgs {
     const float* sB;
     int64_t ld_sb;
     int tiles_m, tiles_n;
+    int int_tm, int_tn;   // interior tiles launched separately (0: none)
 };
 
 // aligned: every row start of A and B is 16-byte aligned.

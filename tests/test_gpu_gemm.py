@@ -138,6 +138,33 @@ def test_guard_bands_untouched(gpu_ok):
     assert (h[mask] == -3.25).all()
 
 
+# Aligned rows with whole 32-element K tiles: full 256 x 256 tiles run the
+# one-wave interior kernel, the rest the general kernel in a second launch.
+# K = 96 (three K tiles) is below the interior kernel's minimum and runs
+# the general kernel alone; K = 128 is its minimum.
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("M,N,K", [(600, 776, 512), (512, 512, 128), (768, 264, 96),
+                                   (256, 1024, 1056), (264, 256, 160)])
+def test_interior_and_edge_tiles_integer_bit_exact(gpu_ok, fmt, M, N, K):
+    A, B, C = inputs.gemm16_operands(M, N, K, dist="int4", fmt=fmt, seeds=(M, N, K))
+    D, R, _, _ = run16(fmt, A, B, C)
+    assert np.array_equal(D, R.astype(np.float32)), f"{fmt} {M}x{N}x{K}"
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_interior_and_edge_tiles_uniform_in_place(gpu_ok, fmt):
+    M, N, K = 520, 780, 640
+    A, B, C = inputs.gemm16_operands(M, N, K, dist="uniform", fmt=fmt, seeds=(31, 32, 33))
+    tC = dev(C)
+    fn = mp.gemm_f16 if fmt == "f16" else mp.gemm_bf16
+    D = fn(dev(A), dev(B), tC, out=tC)
+    R, S = FN16[fmt][1](A, B, C)
+    check_fp(host(D), R, S, 1e-5, f"{fmt} interior+edge in place")
+    t0 = fn(dev(A), dev(B), None)
+    tz = fn(dev(A), dev(B), torch.zeros(M, N, device=gpu_ok))
+    assert torch.equal(t0.view(torch.int32), tz.view(torch.int32))
+
+
 EDGE = [1, 15, 16, 17, 31, 33, 127, 128, 129, 255, 257]
 
 
@@ -155,7 +182,8 @@ def test_edge_sweep(gpu_ok):
 
 # ------------------------------------------------------------------ INT8 --
 @pytest.mark.parametrize("M,N,K", [(64, 64, 64), (300, 520, 200), (513, 257, 129), (1, 1, 1),
-                                   (256, 256, 512)])
+                                   (256, 256, 512), (600, 776, 512), (512, 272, 256),
+                                   (256, 512, 192)])
 def test_i8_bit_exact(gpu_ok, M, N, K):
     A, B, C = inputs.i8_operands(M, N, K, seeds=(M, N, K))
     D = host(mp.gemm_i8_i32(dev(A), dev(B), dev(C)))
