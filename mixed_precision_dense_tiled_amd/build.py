@@ -49,6 +49,19 @@ def build_library(extra_flags=()) -> str:
     return LIB
 
 
+CLOCK_LIB = os.path.join(PKG, "libmpdt_clock.so")
+
+
+def build_clock_library(extra_flags=()) -> str:
+    """The same kernels with per-workgroup clock stamps (bench.py reads the
+    shader clock of the timed GEMM from it; never used for results)."""
+    srcs = [os.path.join(CSRC, s) for s in HIP_SOURCES]
+    tmp = CLOCK_LIB + ".tmp"
+    _run([hipcc(), *HIP_FLAGS, "-DMPDT_CLOCK_STAMPS", *extra_flags, *srcs, "-o", tmp], cwd=CSRC)
+    os.replace(tmp, CLOCK_LIB)
+    return CLOCK_LIB
+
+
 def build_probes(extra_flags=()) -> str:
     """Layout-probe kernels used by the GPU tests (not part of the C ABI)."""
     tmp = PROBE_LIB + ".tmp"
@@ -72,6 +85,7 @@ def build_all():
     build_oracle()
     build_library()
     build_probes()
+    build_clock_library()
 
 
 if __name__ == "__main__":

@@ -42,6 +42,21 @@
 
 namespace mpdt {
 
+#ifdef MPDT_CLOCK_STAMPS
+// Instrumented build (a separate measurement library, never the product
+// one): workgroup w < CLOCK_STAMP_WGS records the shader clock (s_memtime)
+// and the 100 MHz real-time counter (s_memrealtime) at kernel entry, after
+// the K loop and after its last store has completed -- enough to read the
+// shader clock the kernel actually ran at and where its time went.
+constexpr int CLOCK_STAMP_WGS = 4096;
+__device__ uint64_t g_clock_stamps[CLOCK_STAMP_WGS * 6];
+#define MPDT_STAMP(i)                                        \
+    const uint64_t stamp_t##i = __builtin_amdgcn_s_memtime(); \
+    const uint64_t stamp_r##i = __builtin_amdgcn_s_memrealtime();
+#else
+#define MPDT_STAMP(i)
+#endif
+
 // ---------------------------------------------------------------------------
 // Per-format MFMA traits.  A "step" is one MFMA along K.
 // ---------------------------------------------------------------------------
@@ -278,6 +293,7 @@ void gemm_kernel(GemmArgs g) {
     };
     using I0 = std::integral_constant<int, 0>;
 
+    MPDT_STAMP(0)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar registers
@@ -809,6 +825,7 @@ void gemm_kernel(GemmArgs g) {
         }
     }
 
+    MPDT_STAMP(1)
     // ---- epilogue -----------------------------------------------------------
     // Lane layout of a 32x32 accumulator: column lrow; register r holds row
     // 8*(r/4) + 4*lhalf + (r%4).
@@ -880,6 +897,15 @@ void gemm_kernel(GemmArgs g) {
                 }
             }
     }
+#ifdef MPDT_CLOCK_STAMPS
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's stores have completed
+    MPDT_STAMP(2)
+    if (threadIdx.x == 0 && blockIdx.x < CLOCK_STAMP_WGS) {
+        uint64_t* q = g_clock_stamps + blockIdx.x * 6;
+        q[0] = stamp_t0; q[1] = stamp_t1; q[2] = stamp_t2;
+        q[3] = stamp_r0; q[4] = stamp_r1; q[5] = stamp_r2;
+    }
+#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -947,3 +973,14 @@ hipError_t launch_gemm(Kind kind, const GemmArgs& a, bool aligned, hipStream_t s
 }
 
 }  // namespace mpdt
+
+#ifdef MPDT_CLOCK_STAMPS
+// Copy the stamps of the first n workgroups of the last instrumented launch
+// (6 per workgroup: shader clock at entry / after the K loop / at the end,
+// then the real-time counter at the same three points) to host memory.
+extern "C" __attribute__((visibility("default"))) int mpdt_clock_stamps(uint64_t* host, int n) {
+    if (n < 0 || n > mpdt::CLOCK_STAMP_WGS) return (int)hipErrorInvalidValue;
+    return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(mpdt::g_clock_stamps), (size_t)n * 6 * 8, 0,
+                                    hipMemcpyDeviceToHost);
+}
+#endif

@@ -17,7 +17,7 @@ def pytest_configure(config):
 def _ensure_built():
     pkg = os.path.join(ROOT, "mixed_precision_dense_tiled_amd")
     need = [os.path.join(ROOT, "oracle", "liboracle.so"), os.path.join(pkg, "libmpdt.so"),
-            os.path.join(pkg, "libmpdt_probes.so")]
+            os.path.join(pkg, "libmpdt_probes.so"), os.path.join(pkg, "libmpdt_clock.so")]
     if not all(os.path.exists(p) for p in need):
         import __graft_entry__
         __graft_entry__.build()
