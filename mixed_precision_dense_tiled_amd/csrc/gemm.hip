@@ -106,6 +106,9 @@ struct Cfg {
     static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int KT_BYTES = KT_BYTES_;             // bytes of K per K tile
     static constexpr int STAGES = STAGES_;                 // LDS stages (loads run STAGES-1 ahead)
+    // register slots of the register-staged path (FP8 keeps one: its wider
+    // B tile and block accumulators leave no room for more)
+    static constexpr int REG_SLOTS = (KD == Kind::FP8) ? 1 : 3;
     static constexpr int NT = 64 * WAVES_M * WAVES_N;
     static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     static constexpr int TM = WM / 32, TN = WN / 32;       // MFMA tiles per wave
@@ -325,25 +328,32 @@ void gemm_kernel(GemmArgs g) {
     const int ntk = (int)((k_bytes + C::KT_BYTES - 1) / C::KT_BYTES);
 
     // ---- register-staged loads (edge tiles, unaligned rows, K tail) --------
-    u32x4 ra[C::UA];
-    u32x4 rb[C::UB];
-    float rsa = 0.0f;   // FP8: this thread's A-row scale of the staged K tile
+    // A ring of NSLOT register slots (tile t in slot t % NSLOT): the loads of
+    // a K tile are issued NSLOT tiles before its data goes to LDS, so their
+    // latency hides behind that many tiles of MFMA work.  Slot indices are
+    // compile-time constants.
+    constexpr int NSLOT = C::REG_SLOTS;
+    u32x4 ra[NSLOT][C::UA];
+    u32x4 rb[NSLOT][C::UB];
+    float rsa[NSLOT];   // FP8: this thread's A-row scale of the staged K tile
+#pragma unroll
+    for (int q = 0; q < NSLOT; ++q) rsa[q] = 0.0f;
 
-    auto load_scale = [&](int kt) {
+    auto load_scale = [&](int kt, int q) {
         if constexpr (IS_FP8) {
             if (tid < C::BM) {
                 const int row = m0 + tid;
-                rsa = (row < g.M) ? g.sA[(int64_t)row * g.ld_sa + kt] : 0.0f;
+                rsa[q] = (row < g.M) ? g.sA[(int64_t)row * g.ld_sa + kt] : 0.0f;
             }
         }
     };
-    auto store_scale = [&](const Stage& s) {
+    auto store_scale = [&](const Stage& s, int q) {
         if constexpr (IS_FP8) {
-            if (tid < C::BM) s.S[tid] = rsa;
+            if (tid < C::BM) s.S[tid] = rsa[q];
         }
     };
 
-    auto reg_load = [&](int kt) {
+    auto reg_load = [&](int kt, int q) {
         const int64_t kb0 = (int64_t)kt * C::KT_BYTES;   // byte offset along K (A)
 #pragma unroll
         for (int u = 0; u < C::UA; ++u) {
@@ -353,7 +363,7 @@ void gemm_kernel(GemmArgs g) {
             const char* rowp = g.A + (int64_t)row * g.lda_b;
             const char* p = rowp + kb0 + c * 16;
             const char* end = (row < g.M) ? rowp + k_bytes : p;
-            ra[u] = load16_row<ALIGNED>(p, end);
+            ra[q][u] = load16_row<ALIGNED>(p, end);
         }
 #pragma unroll
         for (int u = 0; u < C::UB; ++u) {
@@ -363,23 +373,23 @@ void gemm_kernel(GemmArgs g) {
             const char* rowp = g.B + (int64_t)krow * g.ldb_b;
             const char* p = rowp + (int64_t)n0 * C::ES + c * 16;
             const char* end = (krow < g.K) ? rowp + (int64_t)g.N * C::ES : p;
-            rb[u] = load16_row<ALIGNED>(p, end);
+            rb[q][u] = load16_row<ALIGNED>(p, end);
         }
-        load_scale(kt);
+        load_scale(kt, q);
     };
 
-    auto reg_store = [&](const Stage& s) {
+    auto reg_store = [&](const Stage& s, int q) {
 #pragma unroll
         for (int u = 0; u < C::UA; ++u) {
             const int slot = tid + C::NT * u;
-            lds_store16(s.A, a_off<C>(slot / C::CPR_A, slot % C::CPR_A), ra[u]);
+            lds_store16(s.A, a_off<C>(slot / C::CPR_A, slot % C::CPR_A), ra[q][u]);
         }
 #pragma unroll
         for (int u = 0; u < C::UB; ++u) {
             const int slot = tid + C::NT * u;
-            lds_store16(s.B, b_off<C>(slot / C::CPR_B, slot % C::CPR_B), rb[u]);
+            lds_store16(s.B, b_off<C>(slot / C::CPR_B, slot % C::CPR_B), rb[q][u]);
         }
-        store_scale(s);
+        store_scale(s, q);
     };
 
     // ---- direct global -> LDS loads (full interior K tiles, aligned rows) ---
@@ -767,7 +777,7 @@ void gemm_kernel(GemmArgs g) {
 #pragma unroll
             for (int p = 0; p < AHEAD; ++p)
                 if (p < nfull) dma_tile(p, stage_rt(p));
-            load_scale(0);
+            load_scale(0, 0);
             for (int kt0 = 0; kt0 < nfull; kt0 += NS) {
 #pragma unroll
                 for (int u = 0; u < NS; ++u) {
@@ -777,47 +787,50 @@ void gemm_kernel(GemmArgs g) {
                         if (later >= 2) wait_vmem<2 * DMA_PER_TILE>();
                         else if (later == 1) wait_vmem<DMA_PER_TILE>();
                         else wait_vmem<0>();
-                        store_scale(stage_rt(u));
+                        store_scale(stage_rt(u), 0);
                         wait_lds();
                         wg_barrier();
                         if (kt + AHEAD < nfull)
                             dma_tile(kt + AHEAD, stage_rt((u + AHEAD) % NS));
-                        if (kt + 1 < nfull) load_scale(kt + 1);
+                        if (kt + 1 < nfull) load_scale(kt + 1, 0);
                         compute_tile(stage_rt(u), kt);
                         wait_lds();
                     }
                 }
             }
             if (nfull < ntk) {   // K tail: one partial tile through registers
-                reg_load(nfull);
+                reg_load(nfull, 0);
                 wait_vmem<0>();
                 wg_barrier();   // every wave is past the reads of this stage's last tile
                 const Stage sT = stage_rt(nfull % NS);
-                reg_store(sT);
+                reg_store(sT, 0);
                 wait_lds();
                 wg_barrier();
                 compute_tile(sT, nfull);
             }
         }
     } else if (ntk > 0) {
-        // Edge tile or rows not 16-byte aligned: guarded loads through
-        // registers, two stages, the loads of tile t+2 in flight while tile
-        // t+1 is computed.
-        reg_load(0);
-        reg_store(stage(I0{}));
-        if (ntk > 1) reg_load(1);
+        // Edge tile or rows not 16-byte aligned: guarded loads through the
+        // register ring, two LDS stages.  Iteration t computes tile t from
+        // stage t % 2, moves tile t+1 from its register slot to the other
+        // stage, and issues the loads of tile t+1+NSLOT into that same slot.
+        constexpr int UNR = (NSLOT % 2 == 0) ? NSLOT : 2 * NSLOT;   // both indices constant
+        reg_load(0, 0);
+        reg_store(stage(I0{}), 0);
+#pragma unroll
+        for (int q = 1; q <= NSLOT; ++q)
+            if (q < ntk) reg_load(q, q % NSLOT);
         wait_lds();
         wg_barrier();
-        for (int kt0 = 0; kt0 < ntk; kt0 += 2) {
-            static_for<0, 2>([&](auto U) {
+        for (int kt0 = 0; kt0 < ntk; kt0 += UNR) {
+            static_for<0, UNR>([&](auto U) {
                 constexpr int u = decltype(U)::value;
                 const int kt = kt0 + u;
                 if (kt < ntk) {
-                    compute_tile(stage(U), kt);
-                    if (kt + 1 < ntk) {
-                        reg_store(stage(std::integral_constant<int, u ^ 1>{}));
-                        if (kt + 2 < ntk) reg_load(kt + 2);
-                    }
+                    compute_tile(stage(std::integral_constant<int, u % 2>{}), kt);
+                    if (kt + 1 < ntk)
+                        reg_store(stage(std::integral_constant<int, (u + 1) % 2>{}), (u + 1) % NSLOT);
+                    if (kt + 1 + NSLOT < ntk) reg_load(kt + 1 + NSLOT, (u + 1) % NSLOT);
                     wait_lds();
                     wg_barrier();
                 }
