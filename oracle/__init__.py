@@ -73,6 +73,18 @@ def _load():
                                                         + [_vp, _c_i64, _vp, _c_i64]
                                                         + [_vp, _c_i64, _vp, _c_i64]
                                                         + [_c_i64, _vp, _vp, _vp, _vp])
+        _lib.oracle_f32_to_f16_rne.restype = ctypes.c_uint16
+        _lib.oracle_f32_to_f16_rne.argtypes = [ctypes.c_float]
+        _lib.oracle_f32_to_e4m3_rne_sat.restype = ctypes.c_uint8
+        _lib.oracle_f32_to_e4m3_rne_sat.argtypes = [ctypes.c_float]
+        _lib.oracle_gemm_w8a8.restype = ctypes.c_int
+        _lib.oracle_gemm_w8a8.argtypes = ([_c_i64] * 3 + [_vp, _c_i64, _vp, _vp, _c_i64, _vp, _vp]
+                                          + [_vp, _c_i64, _vp, _c_i64])
+        _lib.oracle_quantize_i8_rows.restype = ctypes.c_int
+        _lib.oracle_quantize_i8_rows.argtypes = [_c_i64, _c_i64, _vp, _c_i64, _vp, _c_i64, _vp]
+        _lib.oracle_quantize_fp8_blocks.restype = ctypes.c_int
+        _lib.oracle_quantize_fp8_blocks.argtypes = ([_c_i64, _c_i64, _vp, _c_i64, _c_i64, _c_i64]
+                                                    + [_vp, _c_i64, _vp, _c_i64])
         _lib.oracle_gemv_w8a8.restype = ctypes.c_int
         _lib.oracle_gemv_w8a8.argtypes = [_c_i64, _c_i64, _vp, ctypes.c_float, _vp, _c_i64, _vp,
                                           _vp, _vp]
@@ -140,6 +152,20 @@ def f32_to_bf16_rne(x: np.ndarray) -> np.ndarray:
     out = np.empty(x.shape, np.uint16)
     _load().oracle_round_bf16(x.ctypes.data, out.ctypes.data, x.size)
     return out
+
+
+def f32_to_f16_rne(x: np.ndarray) -> np.ndarray:
+    """oracle_f32_to_f16_rne elementwise (FP16 bit patterns)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    f = _load().oracle_f32_to_f16_rne
+    return np.array([f(float(v)) for v in x.ravel()], dtype=np.uint16).reshape(x.shape)
+
+
+def f32_to_e4m3_rne_sat(x: np.ndarray) -> np.ndarray:
+    """oracle_f32_to_e4m3_rne_sat elementwise (E4M3FN codes)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    f = _load().oracle_f32_to_e4m3_rne_sat
+    return np.array([f(float(v)) for v in x.ravel()], dtype=np.uint8).reshape(x.shape)
 
 
 # ------------------------------------------------------------------ GEMMs --
@@ -291,3 +317,49 @@ def gemv_w8a8(x, s_x, W, s_w):
                                 s_w.ctypes.data, z.ctypes.data, y.ctypes.data),
            "oracle_gemv_w8a8")
     return z, y
+
+
+# ------------------------------------------------------ W8A8, M tokens --
+def gemm_w8a8(X, s_x, W, s_w, bias=None):
+    """oracle_gemm_w8a8: X int8 [M, K], s_x FP32 [M], W int8 [N, K] (one
+    output channel per row), s_w FP32 [N], bias FP32 [N] or None.
+    Returns (Z int32 [M, N], Y BF16 bits [M, N])."""
+    M, K = X.shape
+    N = W.shape[0]
+    px, ldx = _mat(X, np.int8)
+    pw, ldw = _mat(W, np.int8)
+    s_x = np.ascontiguousarray(s_x, dtype=np.float32)
+    s_w = np.ascontiguousarray(s_w, dtype=np.float32)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    Z = np.empty((M, N), np.int32)
+    Y = np.empty((M, N), np.uint16)
+    _check(_load().oracle_gemm_w8a8(M, N, K, px, ldx, s_x.ctypes.data, pw, ldw, s_w.ctypes.data,
+                                    _ptr(b), Z.ctypes.data, max(N, 1), Y.ctypes.data, max(N, 1)),
+           "gemm_w8a8")
+    return Z, Y
+
+
+# ------------------------------------------------------------ quantisers --
+def quantize_i8_rows(X):
+    """oracle_quantize_i8_rows: X BF16 bits [M, K] -> (Q int8 [M, K], S FP32 [M])."""
+    M, K = X.shape
+    px, ldx = _mat(X, np.uint16)
+    Q = np.empty((M, K), np.int8)
+    S = np.empty(M, np.float32)
+    _check(_load().oracle_quantize_i8_rows(M, K, px, ldx, Q.ctypes.data, max(K, 1), S.ctypes.data),
+           "quantize_i8_rows")
+    return Q, S
+
+
+def quantize_fp8_blocks(X, br, bc=128):
+    """oracle_quantize_fp8_blocks: X FP32 [R, C] in br x bc blocks ->
+    (Q E4M3 codes [R, C], S FP32 [ceil(R/br), ceil(C/bc)])."""
+    R, Cc = X.shape
+    px, ldx = _mat(X, np.float32)
+    Q = np.empty((R, Cc), np.uint8)
+    nbr, nbc = -(-R // br), -(-Cc // bc)
+    S = np.empty((nbr, nbc), np.float32)
+    _check(_load().oracle_quantize_fp8_blocks(R, Cc, px, ldx, br, bc, Q.ctypes.data, max(Cc, 1),
+                                              S.ctypes.data, max(nbc, 1)),
+           "quantize_fp8_blocks")
+    return Q, S

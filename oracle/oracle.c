@@ -87,6 +87,64 @@ uint16_t oracle_f32_to_bf16_rne(float x) {
     return (uint16_t)(sign | kept);
 }
 
+/* Exponent E of the binade of a > 0 (2^E <= a < 2^(E+1)). */
+static int binade(double a) {
+    int e;
+    frexp(a, &e);   /* a = m * 2^e, m in [0.5, 1) */
+    return e - 1;
+}
+
+/* FP32 -> FP16, round to nearest, ties to even.  A binade [2^E, 2^(E+1))
+ * with E >= -14 holds 1024 values spaced 2^(E-10); below 2^-14 the spacing
+ * is the subnormal quantum 2^-24.  The value is counted in quanta of its
+ * binade (exact in double) and rounded with rint, which rounds to the
+ * nearest integer, ties to even, in the default rounding mode.  A count of
+ * 2048 is the first value of the next binade; past 65504 the result is
+ * infinity. */
+uint16_t oracle_f32_to_f16_rne(float x) {
+    uint16_t sign = signbit(x) ? 0x8000u : 0u;
+    if (isnan(x)) return (uint16_t)(sign | 0x7e00u);
+    double a = fabs((double)x);
+    if (a == 0.0) return sign;
+    if (isinf(x)) return (uint16_t)(sign | 0x7c00u);
+    int E = binade(a);
+    if (E < -14) {
+        double n = rint(ldexp(a, 24));          /* subnormal quanta, 0..1024 */
+        return (uint16_t)(sign | (uint16_t)n);  /* 1024 encodes 2^-14 */
+    }
+    double n = rint(ldexp(a, 10 - E));          /* 1024..2048 */
+    if (n == 2048.0) {
+        n = 1024.0;
+        E += 1;
+    }
+    if (E > 15) return (uint16_t)(sign | 0x7c00u);
+    return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)(n - 1024.0));
+}
+
+/* FP32 -> E4M3FN, round to nearest, ties to even, saturating.  Normal
+ * binades E = -6..8 hold 8 values spaced 2^(E-3); below 2^-6 the spacing is
+ * 2^-9.  Anything that rounds beyond 448 (1.75 * 2^8, the largest finite
+ * value) saturates to 448. */
+uint8_t oracle_f32_to_e4m3_rne_sat(float x) {
+    uint8_t sign = signbit(x) ? 0x80u : 0u;
+    if (isnan(x)) return (uint8_t)(sign | 0x7fu);
+    double a = fabs((double)x);
+    if (a == 0.0) return sign;
+    if (a >= 448.0) return (uint8_t)(sign | 0x7eu);
+    int E = binade(a);
+    if (E < -6) {
+        double n = rint(ldexp(a, 9));           /* 0..8; 8 encodes 2^-6 */
+        return (uint8_t)(sign | (uint8_t)n);
+    }
+    double n = rint(ldexp(a, 3 - E));           /* 8..16 */
+    if (n == 16.0) {
+        n = 8.0;
+        E += 1;
+    }
+    if (E > 8 || (E == 8 && n > 14.0)) return (uint8_t)(sign | 0x7eu);
+    return (uint8_t)(sign | (uint8_t)((E + 7) << 3) | (uint8_t)(n - 8.0));
+}
+
 void oracle_decode_f16(const uint16_t* in, double* out, int64_t n) {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_f16_to_f64(in[i]);
 }
@@ -392,4 +450,100 @@ int oracle_gemv_w8a8(int64_t N, int64_t K, const int8_t* x, float s_x,
         y[o] = oracle_f32_to_bf16_rne(t);
     }
     return err ? 3 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* M-token W8A8 layer with optional bias (see oracle.h).                      */
+/* ------------------------------------------------------------------------ */
+int oracle_gemm_w8a8(int64_t M, int64_t N, int64_t K, const int8_t* X, int64_t ldx,
+                     const float* s_x, const int8_t* W, int64_t ldw, const float* s_w,
+                     const float* bias, int32_t* Z, int64_t ldz, uint16_t* Y, int64_t ldy) {
+    if (M < 0 || N < 0 || K < 0 || !X || !s_x || !W || !s_w || !Y) return 1;
+    if ((M > 0 && K > 0 && ldx < K) || (N > 0 && K > 0 && ldw < K) || ldy < N ||
+        (Z && ldz < N))
+        return 1;
+    for (int64_t m = 0; m < M; ++m)
+        if (!isfinite(s_x[m])) return 2;
+    for (int64_t o = 0; o < N; ++o)
+        if (!isfinite(s_w[o]) || (bias && !isfinite(bias[o]))) return 2;
+    int rc = 0;
+#pragma omp parallel for schedule(static) reduction(max : rc)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t o = 0; o < N; ++o) {
+            int64_t acc = 0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += (int64_t)X[m * ldx + k] * (int64_t)W[o * ldw + k];
+            if (acc > INT32_MAX || acc < INT32_MIN) {
+                rc = 3;
+                continue;
+            }
+            /* float(z) rounds to nearest (exact for |z| <= 2^24), then two
+             * FP32 products and the bias, each an IEEE operation rounded once */
+            float t = (float)(int32_t)acc;
+            t = t * s_x[m];
+            t = t * s_w[o];
+            if (bias) t = t + bias[o];
+            if (Z) Z[m * ldz + o] = (int32_t)acc;
+            Y[m * ldy + o] = oracle_f32_to_bf16_rne(t);
+        }
+    }
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Per-token INT8 quantisation (see oracle.h).                                */
+/* ------------------------------------------------------------------------ */
+int oracle_quantize_i8_rows(int64_t M, int64_t K, const uint16_t* X, int64_t ldx,
+                            int8_t* Q, int64_t ldq, float* S) {
+    if (M < 0 || K < 0 || !X || !Q || !S || (K > 0 && (ldx < K || ldq < K))) return 1;
+    for (int64_t m = 0; m < M; ++m) {
+        double amax = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double v = oracle_bf16_to_f64(X[m * ldx + k]);
+            if (!isfinite(v)) return 2;
+            if (fabs(v) > amax) amax = fabs(v);
+        }
+        /* amax is a BF16 value, exact in FP32 */
+        float s = (amax > 0.0) ? (float)amax / 127.0f : 1.0f;
+        S[m] = s;
+        for (int64_t k = 0; k < K; ++k) {
+            float t = (float)oracle_bf16_to_f64(X[m * ldx + k]) / s;
+            double r = rint((double)t);
+            if (r > 127.0) r = 127.0;
+            if (r < -127.0) r = -127.0;
+            Q[m * ldq + k] = (int8_t)r;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* FP8 E4M3 block quantisation (see oracle.h).                                */
+/* ------------------------------------------------------------------------ */
+int oracle_quantize_fp8_blocks(int64_t R, int64_t Cc, const float* X, int64_t ldx,
+                               int64_t br, int64_t bc, uint8_t* Q, int64_t ldq,
+                               float* S, int64_t lds) {
+    if (R < 0 || Cc < 0 || br < 1 || bc < 1 || !X || !Q || !S) return 1;
+    const int64_t nbr = (R + br - 1) / br, nbc = (Cc + bc - 1) / bc;
+    if (Cc > 0 && (ldx < Cc || ldq < Cc)) return 1;
+    if (nbc > 0 && lds < nbc) return 1;
+    for (int64_t i = 0; i < R; ++i)
+        for (int64_t j = 0; j < Cc; ++j)
+            if (!isfinite(X[i * ldx + j])) return 2;
+    for (int64_t bi = 0; bi < nbr; ++bi) {
+        for (int64_t bj = 0; bj < nbc; ++bj) {
+            const int64_t i0 = bi * br, i1 = (i0 + br < R) ? i0 + br : R;
+            const int64_t j0 = bj * bc, j1 = (j0 + bc < Cc) ? j0 + bc : Cc;
+            float amax = 0.0f;
+            for (int64_t i = i0; i < i1; ++i)
+                for (int64_t j = j0; j < j1; ++j)
+                    if (fabsf(X[i * ldx + j]) > amax) amax = fabsf(X[i * ldx + j]);
+            const float s = (amax > 0.0f) ? amax / 448.0f : 1.0f;
+            S[bi * lds + bj] = s;
+            for (int64_t i = i0; i < i1; ++i)
+                for (int64_t j = j0; j < j1; ++j)
+                    Q[i * ldq + j] = oracle_f32_to_e4m3_rne_sat(X[i * ldx + j] / s);
+        }
+    }
+    return 0;
 }

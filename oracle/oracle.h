@@ -46,6 +46,13 @@ double   oracle_f16_to_f64(uint16_t h);
 double   oracle_bf16_to_f64(uint16_t b);
 double   oracle_e4m3_to_f64(uint8_t q);
 uint16_t oracle_f32_to_bf16_rne(float x);
+/* FP32 -> IEEE FP16, round to nearest, ties to even, with subnormals;
+ * overflow gives infinity.  (Format table of the "Tensor Core" page,
+ * section "Precision": FP16 1/5/10.) */
+uint16_t oracle_f32_to_f16_rne(float x);
+/* FP32 -> OCP E4M3FN, round to nearest, ties to even, saturating to +-448
+ * (no infinities in the format; NaN gives S.1111.111). */
+uint8_t  oracle_f32_to_e4m3_rne_sat(float x);
 
 void oracle_decode_f16(const uint16_t* in, double* out, int64_t n);
 void oracle_decode_bf16(const uint16_t* in, double* out, int64_t n);
@@ -108,6 +115,36 @@ int oracle_gemm_fp8_blockscaled_at(int64_t M, int64_t N, int64_t K,
 int oracle_gemv_w8a8(int64_t N, int64_t K, const int8_t* x, float s_x,
                      const int8_t* W, int64_t ldw, const float* s_w,
                      int32_t* z, uint16_t* y);
+
+/* ---- M-token W8A8 linear layer (the same layer for M >= 1 tokens, each
+ * with its own per-token activation scale), with an optional bias added in
+ * the dequantised floating-point epilogue ("NVIDIA A100: from chip to SIMT",
+ * section 5.1: a bias is added after dequantisation).
+ * Z[m][o] = sum_k X[m][k] * W[o][k] (exact);
+ * Y[m][o] = bf16_rne( fl32( fl32( fl32(float(Z) * s_x[m]) * s_w[o] ) + bias[o] ) )
+ * (the bias step is skipped when bias is NULL).  X is M x K (ldx), W is N x K
+ * (ldw); Z (may be NULL) and Y are M x N with leading dimensions ldz, ldy. ---- */
+int oracle_gemm_w8a8(int64_t M, int64_t N, int64_t K, const int8_t* X, int64_t ldx,
+                     const float* s_x, const int8_t* W, int64_t ldw, const float* s_w,
+                     const float* bias, int32_t* Z, int64_t ldz, uint16_t* Y, int64_t ldy);
+
+/* ---- Per-token symmetric INT8 quantisation of activations (the step that
+ * produces q_x and s_x upstream of the W8A8 layer, same section: symmetric,
+ * zero point 0, one scale per token).  For each row m of the M x K BF16
+ * matrix X: amax = max_k |X[m][k]|; s = fl32(amax / 127) (s = 1 when
+ * amax = 0); Q[m][k] = clamp(rne(fl32(X[m][k] / s)), -127, 127).  S[m] = s. ---- */
+int oracle_quantize_i8_rows(int64_t M, int64_t K, const uint16_t* X, int64_t ldx,
+                            int8_t* Q, int64_t ldq, float* S);
+
+/* ---- FP8 E4M3 block quantisation (the scale factors FP8 needs, "per tensor,
+ * per row or per block", "Tensor Core" page, section "Precision").  The
+ * R x Cc FP32 matrix X is cut into br x bc blocks (partial blocks at the
+ * edges keep their own scale); for each block amax = max |x|,
+ * s = fl32(amax / 448) (s = 1 when amax = 0), Q = e4m3_rne_sat(fl32(x / s)).
+ * S is ceil(R/br) x ceil(Cc/bc) with leading dimension lds. ---- */
+int oracle_quantize_fp8_blocks(int64_t R, int64_t Cc, const float* X, int64_t ldx,
+                               int64_t br, int64_t bc, uint8_t* Q, int64_t ldq,
+                               float* S, int64_t lds);
 
 #ifdef __cplusplus
 }
