@@ -39,7 +39,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--only", default="all",
-                   choices=["all", "bf16", "gemv", "fp8", "f16_ragged", "f16_64", "i8", "copy"])
+                   choices=["all", "bf16", "bf16out", "gemv", "fp8", "f16_ragged", "f16_64", "i8",
+                            "copy"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the bounded oracle sample")
@@ -169,6 +170,23 @@ def main():
                          "kernel": "gemm_kernel<BF16,256x256,one wave per SIMD>", "launch_us": st,
                          "clock": clock},
         }
+        del tA, tB, tC, tD
+
+    # ---------------- BF16 4096^3 with a BF16 D (16-bit-output variant) -------
+    if args.only in ("all", "bf16out"):
+        M = N = K = 4096
+        A, B, C = inputs.gemm16_operands(M, N, K, dist="normal", fmt="bf16")
+        tA, tB, tC = to_dev(A), to_dev(B), to_dev(C)
+        tD = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        region, per = timed(lambda i: mp.gemm_bf16_bf16out(tA, tB, tC, out=tD), args.steps,
+                            args.warmup, stream)
+        st = stats(per, region, args.steps)
+        tf = 2.0 * M * N * K / (st["mean_us"] * 1e-6) / 1e12
+        extra["gemm_bf16_bf16out"] = {
+            "workload": "gemm_bf16_bf16out D=bf16(A*B+C), M=N=K=4096, FP32 C, BF16 D",
+            "TFLOP_s": tf, "launch_us": st,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16, "unit": "TFLOP/s",
+                         "frac": tf / PEAK_BF16}}
         del tA, tB, tC, tD
 
     # ---------------- W8A8 GEMV, cold cache ------------------------------------

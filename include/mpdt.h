@@ -80,6 +80,19 @@ mpdt_status gemm_bf16(int64_t M, int64_t N, int64_t K,
                       const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                       const float* C, int64_t ldc, float* D, int64_t ldd, void* stream);
 
+/* 16-bit-output variants: the same D = A . B + C formed in FP32, then
+ * rounded once (to nearest, ties to even) to the input format -- IEEE FP16
+ * (subnormals kept, overflow to infinity) for gemm_f16_f16out, bfloat16 for
+ * gemm_bf16_bf16out -- halving the bytes written ("Tensor Core" page, the
+ * improvements listed after its WMMA exercise: write the result back as
+ * BF16).  C stays FP32 (may be NULL); D holds 16-bit patterns. */
+mpdt_status gemm_f16_f16out(int64_t M, int64_t N, int64_t K,
+                            const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                            const float* C, int64_t ldc, uint16_t* D, int64_t ldd, void* stream);
+mpdt_status gemm_bf16_bf16out(int64_t M, int64_t N, int64_t K,
+                              const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                              const float* C, int64_t ldc, uint16_t* D, int64_t ldd, void* stream);
+
 /* D[M x N] (INT32) = A[M x K] (INT8) . B[K x N] (INT8) + C (INT32), exact
  * as long as no partial sum leaves the INT32 range (K * 128^2 + |C| < 2^31
  * guarantees it).  C may be NULL. */

@@ -18,7 +18,8 @@ import os
 
 import torch
 
-__all__ = ["gemm_f16", "gemm_bf16", "gemm_i8_i32", "gemm_fp8_blockscaled", "gemv_w8a8",
+__all__ = ["gemm_f16", "gemm_bf16", "gemm_f16_f16out", "gemm_bf16_bf16out", "gemm_i8_i32",
+           "gemm_fp8_blockscaled", "gemv_w8a8",
            "MpdtError", "lib", "lib_path", "version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -51,7 +52,8 @@ def lib() -> ctypes.CDLL:
                 "(run `python -m mixed_precision_dense_tiled_amd.build`)")
         L = ctypes.CDLL(_LIB_PATH)
         gemm_args = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]
-        for name in ("gemm_f16", "gemm_bf16", "gemm_i8_i32"):
+        for name in ("gemm_f16", "gemm_bf16", "gemm_i8_i32", "gemm_f16_f16out",
+                     "gemm_bf16_bf16out"):
             getattr(L, name).argtypes = gemm_args
             getattr(L, name).restype = ctypes.c_int
         L.gemm_fp8_blockscaled.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
@@ -98,7 +100,7 @@ def _mat(t: torch.Tensor, itemsize: int, name: str):
     return t.data_ptr(), int(ld)
 
 
-def _gemm16(fn, A, B, C, out):
+def _gemm16(fn, A, B, C, out, out_dtype=torch.float32):
     M, K = A.shape
     K2, N = B.shape
     if K2 != K:
@@ -107,8 +109,8 @@ def _gemm16(fn, A, B, C, out):
     pb, ldb = _mat(B, 2, "B")
     pc, ldc = (None, N) if C is None else _mat(C, 4, "C")
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
-    pd, ldd = _mat(out, 4, "out")
+        out = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    pd, ldd = _mat(out, out_dtype.itemsize, "out")
     _check(fn, getattr(lib(), fn)(M, N, K, pa, lda, pb, ldb, pc, ldc, pd, ldd, _stream(A)))
     return out
 
@@ -121,6 +123,18 @@ def gemm_f16(A, B, C=None, out=None):
 def gemm_bf16(A, B, C=None, out=None):
     """D = A . B + C; A [M,K], B [K,N] BF16 bits, C/D [M,N] FP32 (C optional)."""
     return _gemm16("gemm_bf16", A, B, C, out)
+
+
+def gemm_f16_f16out(A, B, C=None, out=None):
+    """D = fp16(A . B + C); A [M,K], B [K,N] FP16 bits, C [M,N] FP32 (optional);
+    returns D as a float16 tensor."""
+    return _gemm16("gemm_f16_f16out", A, B, C, out, torch.float16)
+
+
+def gemm_bf16_bf16out(A, B, C=None, out=None):
+    """D = bf16(A . B + C); A [M,K], B [K,N] BF16 bits, C [M,N] FP32 (optional);
+    returns D as a bfloat16 tensor."""
+    return _gemm16("gemm_bf16_bf16out", A, B, C, out, torch.bfloat16)
 
 
 def gemm_i8_i32(A, B, C=None, out=None):

@@ -115,10 +115,16 @@ mpdt_status check_gemm(const char* fn, int64_t M, int64_t N, int64_t K, const vo
     return MPDT_SUCCESS;
 }
 
+// FP16 / BF16 GEMM; D is FP32 (out16 = 0) or in the input format (out16 = 1).
 mpdt_status run_gemm16(const char* fn, mpdt::Kind kind, int64_t M, int64_t N, int64_t K,
                        const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
-                       const float* C, int64_t ldc, float* D, int64_t ldd, void* stream) {
-    mpdt_status s = check_gemm(fn, M, N, K, A, lda, 2, B, ldb, 2, C, ldc, 4, D, ldd, 4, nullptr, 0);
+                       const float* C, int64_t ldc, void* D, int64_t ldd, int out16,
+                       void* stream) {
+    const int64_t esd = out16 ? 2 : 4;
+    // a 16-bit D cannot be updated in place from an FP32 C
+    if (out16 && C && (const void*)C == (const void*)D)
+        return fail(MPDT_ERROR_ALIASING, fn, "C may not alias a 16-bit D");
+    mpdt_status s = check_gemm(fn, M, N, K, A, lda, 2, B, ldb, 2, C, ldc, 4, D, ldd, esd, nullptr, 0);
     if (s != MPDT_SUCCESS || M == 0 || N == 0) return s;
     if ((s = check_device(fn)) != MPDT_SUCCESS) return s;
     mpdt::GemmArgs a{};
@@ -133,6 +139,8 @@ mpdt_status run_gemm16(const char* fn, mpdt::Kind kind, int64_t M, int64_t N, in
     a.M = (int)M;
     a.N = (int)N;
     a.K = (int)K;
+    a.out16 = out16;
+    a.d16_vec = out16 && aligned_to(D, 16) && (ldd * 2) % 16 == 0;
     const bool al = aligned_to(A, 16) && aligned_to(B, 16) && (a.lda_b % 16 == 0) &&
                     (a.ldb_b % 16 == 0);
     return launched(mpdt::launch_gemm(kind, a, al, (hipStream_t)stream), fn);
@@ -143,13 +151,29 @@ mpdt_status run_gemm16(const char* fn, mpdt::Kind kind, int64_t M, int64_t N, in
 MPDT_EXPORT mpdt_status gemm_f16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
                                  const uint16_t* B, int64_t ldb, const float* C, int64_t ldc,
                                  float* D, int64_t ldd, void* stream) {
-    return run_gemm16("gemm_f16", mpdt::Kind::F16, M, N, K, A, lda, B, ldb, C, ldc, D, ldd, stream);
+    return run_gemm16("gemm_f16", mpdt::Kind::F16, M, N, K, A, lda, B, ldb, C, ldc, D, ldd, 0,
+                      stream);
+}
+
+MPDT_EXPORT mpdt_status gemm_f16_f16out(int64_t M, int64_t N, int64_t K, const uint16_t* A,
+                                        int64_t lda, const uint16_t* B, int64_t ldb, const float* C,
+                                        int64_t ldc, uint16_t* D, int64_t ldd, void* stream) {
+    return run_gemm16("gemm_f16_f16out", mpdt::Kind::F16, M, N, K, A, lda, B, ldb, C, ldc, D, ldd,
+                      1, stream);
+}
+
+MPDT_EXPORT mpdt_status gemm_bf16_bf16out(int64_t M, int64_t N, int64_t K, const uint16_t* A,
+                                          int64_t lda, const uint16_t* B, int64_t ldb,
+                                          const float* C, int64_t ldc, uint16_t* D, int64_t ldd,
+                                          void* stream) {
+    return run_gemm16("gemm_bf16_bf16out", mpdt::Kind::BF16, M, N, K, A, lda, B, ldb, C, ldc, D,
+                      ldd, 1, stream);
 }
 
 MPDT_EXPORT mpdt_status gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
                                   const uint16_t* B, int64_t ldb, const float* C, int64_t ldc,
                                   float* D, int64_t ldd, void* stream) {
-    return run_gemm16("gemm_bf16", mpdt::Kind::BF16, M, N, K, A, lda, B, ldb, C, ldc, D, ldd,
+    return run_gemm16("gemm_bf16", mpdt::Kind::BF16, M, N, K, A, lda, B, ldb, C, ldc, D, ldd, 0,
                       stream);
 }
 

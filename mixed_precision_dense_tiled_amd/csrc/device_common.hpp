@@ -157,6 +157,13 @@ __device__ __forceinline__ u32x2 lds_read_tr8(const MPDT_LDS char* base, uint32_
     return __builtin_bit_cast(u32x2, r);
 }
 
+// Round FP32 to FP16 (nearest, ties to even, subnormals kept, overflow to
+// infinity) with the hardware conversion.
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+    _Float16 h = (_Float16)x;
+    return __builtin_bit_cast(uint16_t, h);
+}
+
 // Round FP32 to BF16 (nearest, ties to even) with the hardware conversion.
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
     __bf16 h = (__bf16)x;

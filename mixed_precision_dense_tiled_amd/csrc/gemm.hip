@@ -764,6 +764,9 @@ void gemm_kernel(GemmArgs g) {
             wait_lds();
 #pragma unroll
             for (int idx = 0; idx < 16; ++idx) mma1(fr, 1, idx);
+            // the empty-range loads of the last tiles still write (zeros) to
+            // LDS: let them land before anything else uses it or the wave ends
+            wait_vmem<0>();
         }
     } else if (direct) {
         if constexpr (ALIGNED) {
@@ -841,74 +844,141 @@ void gemm_kernel(GemmArgs g) {
     MPDT_STAMP(1)
     // ---- epilogue -----------------------------------------------------------
     // Lane layout of a 32x32 accumulator: column lrow; register r holds row
-    // 8*(r/4) + 4*lhalf + (r%4).
-    using OutT = typename std::conditional<KD == Kind::FP8, uint16_t,
-                 typename std::conditional<KD == Kind::I8, int32_t, float>::type>::type;
+    // 8*(r/4) + 4*lhalf + (r%4).  D = acc + C in FP32 (INT32), then written in
+    // the output format: FP32 / INT32, or FP16 / BF16 (one round to nearest
+    // even) for the 16-bit-output entry points; FP8 writes BF16.
     using CT = typename std::conditional<KD == Kind::I8, int32_t, float>::type;
-    OutT* const Dp = (OutT*)g.D;
     const CT* const Cp = (const CT*)g.C;
     const int row_base = m0 + wm * C::WM + 4 * (int)lhalf;
     const int col_base = n0 + wn * C::WN + (int)lrow;
-    auto out_val = [&](float a, CT c) -> OutT {
-        if constexpr (KD == Kind::FP8) return f32_to_bf16_bits(a);
-        else return (OutT)(a + c);
-    };
     constexpr int NTILE = C::TM * C::TN;
-    if (full_mn) {
-        // Interior tile: the wave's 32x32 tiles are written in turn, and C of
-        // the next tile is read before this one is stored, so the reads of C
-        // stream instead of costing one round trip per element.  (C is either
-        // exactly D or disjoint from it -- the C ABI rejects partial overlaps
-        // -- so reading C of other elements ahead of these stores is safe.)
-        // Row offsets (8*(r/4) + r%4) * ld are wave-uniform.
-        auto dtile = [&](int t) {
-            return Dp + (int64_t)(row_base + (t / C::TN) * 32) * g.ldd + col_base + (t % C::TN) * 32;
+    auto epilogue = [&](auto out_tag) {
+        using OutT = typename decltype(out_tag)::type;
+        OutT* const Dp = (OutT*)g.D;
+        auto out_val = [&](float a, CT c) -> OutT {
+            if constexpr (KD == Kind::FP8) return f32_to_bf16_bits(a);
+            else if constexpr (std::is_same<OutT, uint16_t>::value) {
+                if constexpr (KD == Kind::F16) return f32_to_f16_bits(a + c);
+                else return f32_to_bf16_bits(a + c);
+            } else return (OutT)(a + c);
         };
-        auto ctile = [&](int t) {
-            return Cp + (int64_t)(row_base + (t / C::TN) * 32) * g.ldc + col_base + (t % C::TN) * 32;
-        };
-        auto load_c = [&](int t, CT (&cv)[16]) {
-            const CT* cp = ctile(t);
+        if constexpr (ONE_WAVE && std::is_same<OutT, uint16_t>::value) {
+            if (g.d16_vec) {
+                // 16-bit D of a one-wave interior tile, staged through LDS so
+                // that it leaves in 16-byte stores of whole row segments (the
+                // accumulator layout gives each lane one column, so direct
+                // stores would be 2 bytes wide).  After a barrier (every wave
+                // is done with the K-loop stages) each wave owns a 32 KiB
+                // region: its 128 x 128 tile row-major, 256 bytes per row.
+                // C is added in FP32 and rounded once, as in the direct form.
+                wg_barrier();
+                MPDT_LDS char* const reg = lds_cast(sA0) + wave * (C::WM * C::WN * 2);
+                static_assert(C::WM * C::WN * 2 * 4 <= NS * STAGE_BYTES, "epilogue staging fits");
+                auto ctile = [&](int t) {
+                    return Cp + (int64_t)(row_base + (t / C::TN) * 32) * g.ldc + col_base +
+                           (t % C::TN) * 32;
+                };
+                auto load_c = [&](int t, CT (&cv)[16]) {
+                    const CT* cp = ctile(t);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) cv[r] = cp[(int64_t)(8 * (r >> 2) + (r & 3)) * g.ldc];
-        };
-        auto store_t = [&](int t, const CT (&cv)[16]) {
-            OutT* dp = dtile(t);
+                    for (int r = 0; r < 16; ++r)
+                        cv[r] = Cp ? cp[(int64_t)(8 * (r >> 2) + (r & 3)) * g.ldc] : (CT)0;
+                };
+                auto stage_t = [&](int t, const CT (&cv)[16]) {
+                    const int i = t / C::TN, j = t % C::TN;
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                dp[(int64_t)(8 * (r >> 2) + (r & 3)) * g.ldd] =
-                    out_val(acc[t / C::TN][t % C::TN][r], cv[r]);
-        };
-        if (KD != Kind::FP8 && Cp) {
-            CT cbuf[2][16];
-            load_c(0, cbuf[0]);
-            static_for<0, NTILE>([&](auto T) {
-                constexpr int t = decltype(T)::value;
-                if constexpr (t + 1 < NTILE) load_c(t + 1, cbuf[(t + 1) & 1]);
-                store_t(t, cbuf[t & 1]);
-            });
-        } else {
-            CT zero[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) zero[r] = (CT)0;
-            static_for<0, NTILE>([&](auto T) { store_t(decltype(T)::value, zero); });
+                    for (int r = 0; r < 16; ++r) {
+                        const uint32_t row = i * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
+                        const uint32_t col = j * 32 + lrow;
+                        *(MPDT_LDS uint16_t*)(reg + row * (C::WN * 2) + col * 2) =
+                            out_val(acc[i][j][r], cv[r]);
+                    }
+                };
+                CT cbuf[2][16];
+                load_c(0, cbuf[0]);
+                static_for<0, NTILE>([&](auto T) {
+                    constexpr int t = decltype(T)::value;
+                    if constexpr (t + 1 < NTILE) load_c(t + 1, cbuf[(t + 1) & 1]);
+                    stage_t(t, cbuf[t & 1]);
+                });
+                // rows of 256 bytes = 16 chunks of 16 bytes; 64 lanes move 4 rows
+                constexpr int CPR = C::WN * 2 / 16;
+                OutT* const dbase = Dp + (int64_t)(m0 + wm * C::WM) * g.ldd + n0 + wn * C::WN;
+#pragma unroll 4
+                for (int q = 0; q < C::WM * CPR / 64; ++q) {
+                    const int idx = q * 64 + lane;
+                    const int row = idx / CPR, c = idx % CPR;
+                    const u32x4 v = lds_load16(reg, (uint32_t)(row * (C::WN * 2) + c * 16));
+                    *reinterpret_cast<u32x4*>(dbase + (int64_t)row * g.ldd + c * 8) = v;
+                }
+                return;
+            }
         }
-    } else {
-        // Edge tile: every element checked.
+        if (full_mn) {
+            // Interior tile: the wave's 32x32 tiles are written in turn, and C of
+            // the next tile is read before this one is stored, so the reads of C
+            // stream instead of costing one round trip per element.  (C is either
+            // exactly D or disjoint from it -- the C ABI rejects partial overlaps
+            // -- so reading C of other elements ahead of these stores is safe.)
+            // Row offsets (8*(r/4) + r%4) * ld are wave-uniform.
+            auto dtile = [&](int t) {
+                return Dp + (int64_t)(row_base + (t / C::TN) * 32) * g.ldd + col_base + (t % C::TN) * 32;
+            };
+            auto ctile = [&](int t) {
+                return Cp + (int64_t)(row_base + (t / C::TN) * 32) * g.ldc + col_base + (t % C::TN) * 32;
+            };
+            auto load_c = [&](int t, CT (&cv)[16]) {
+                const CT* cp = ctile(t);
 #pragma unroll
-        for (int i = 0; i < C::TM; ++i)
+                for (int r = 0; r < 16; ++r) cv[r] = cp[(int64_t)(8 * (r >> 2) + (r & 3)) * g.ldc];
+            };
+            auto store_t = [&](int t, const CT (&cv)[16]) {
+                OutT* dp = dtile(t);
 #pragma unroll
-            for (int j = 0; j < C::TN; ++j) {
-                const int col = col_base + j * 32;
+                for (int r = 0; r < 16; ++r)
+                    dp[(int64_t)(8 * (r >> 2) + (r & 3)) * g.ldd] =
+                        out_val(acc[t / C::TN][t % C::TN][r], cv[r]);
+            };
+            if (KD != Kind::FP8 && Cp) {
+                CT cbuf[2][16];
+                load_c(0, cbuf[0]);
+                static_for<0, NTILE>([&](auto T) {
+                    constexpr int t = decltype(T)::value;
+                    if constexpr (t + 1 < NTILE) load_c(t + 1, cbuf[(t + 1) & 1]);
+                    store_t(t, cbuf[t & 1]);
+                });
+            } else {
+                CT zero[16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
-                    if (row < g.M && col < g.N) {
-                        const CT c = (KD != Kind::FP8 && Cp) ? Cp[(int64_t)row * g.ldc + col] : (CT)0;
-                        Dp[(int64_t)row * g.ldd + col] = out_val(acc[i][j][r], c);
+                for (int r = 0; r < 16; ++r) zero[r] = (CT)0;
+                static_for<0, NTILE>([&](auto T) { store_t(decltype(T)::value, zero); });
+            }
+        } else {
+            // Edge tile: every element checked.
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j) {
+                    const int col = col_base + j * 32;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
+                        if (row < g.M && col < g.N) {
+                            const CT c = (KD != Kind::FP8 && Cp) ? Cp[(int64_t)row * g.ldc + col] : (CT)0;
+                            Dp[(int64_t)row * g.ldd + col] = out_val(acc[i][j][r], c);
+                        }
                     }
                 }
-            }
+        }
+    };
+    using Out32 = typename std::conditional<KD == Kind::I8, int32_t, float>::type;
+    if constexpr (KD == Kind::FP8) {
+        epilogue(std::common_type<uint16_t>{});
+    } else if constexpr (KD == Kind::I8) {
+        epilogue(std::common_type<Out32>{});
+    } else {
+        if (g.out16) epilogue(std::common_type<uint16_t>{});
+        else epilogue(std::common_type<Out32>{});
     }
 #ifdef MPDT_CLOCK_STAMPS
     __builtin_amdgcn_s_waitcnt(0);   // this wave's stores have completed

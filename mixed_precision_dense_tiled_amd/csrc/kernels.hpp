@@ -23,6 +23,8 @@ struct GemmArgs {
     int64_t ld_sb;
     int tiles_m, tiles_n;
     int int_tm, int_tn;   // interior tiles launched separately (0: none)
+    int out16;            // FP16/BF16 inputs: D is written in the input format (RNE)
+    int d16_vec;          // out16 with D and its rows 16-byte aligned: wide stores allowed
 };
 
 // aligned: every row start of A and B is 16-byte aligned.

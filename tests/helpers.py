@@ -37,17 +37,21 @@ def host(t: torch.Tensor, dtype=None) -> np.ndarray:
     return a.view(dtype) if dtype is not None else a
 
 
-def check_fp(D, R, S, frob_max, what="", bf16_out=False):
+def check_fp(D, R, S, frob_max, what="", bf16_out=False, f16_out=False):
     """Per-element bound and relative Frobenius error; returns (worst margin, frob).
 
-    bf16_out: the output was rounded to BF16 after accumulation; the bound then
-    also admits that one rounding (half a BF16 ulp, at most 2^-8 |value|)."""
+    bf16_out / f16_out: the output was rounded to BF16 / FP16 after
+    accumulation; the bound then also admits that one rounding (half an ulp:
+    at most 2^-8 |value| for BF16, 2^-11 |value| for FP16, plus half the
+    smallest FP16 subnormal)."""
     D = np.asarray(D, np.float64)
     assert np.isfinite(D).all(), f"{what}: non-finite output"
     err = np.abs(D - R)
     bound = 1e-3 * S + 1e-6
     if bf16_out:
         bound = bound + 2.0 ** -8 * np.maximum(np.abs(R), np.abs(D))
+    if f16_out:
+        bound = bound + 2.0 ** -11 * np.maximum(np.abs(R), np.abs(D)) + 2.0 ** -25
     margin = float((err / bound).max()) if err.size else 0.0
     bad = np.argwhere(err > bound)
     assert bad.size == 0, (f"{what}: {len(bad)} elements over the bound, first at {bad[:5].tolist()}, "
