@@ -7,7 +7,9 @@ M = N = K = 4096 (row-major, FP32 C and D), on inputs already resident in
 HBM.  The other workloads of the suite (W8A8 batch-1 GEMV 1 x 4096 . 4096 x
 14336 with a cold cache, FP8 block-scaled 4096 x 7168 x 7168, ragged FP16
 8191 x 8193 x 4099, FP16 64^3, INT8 4096^3) are timed the same way and
-reported under "extra", each with its own roofline figure.
+reported under "extra", each with its own roofline figure, as are the next
+steps around them: BF16 4096^3 with a BF16 D, the W8A8 layer for 4 and 16
+tokens, and the INT8 / FP8 quantisers.
 
 Prints ONE JSON line.  Kernel durations come from HIP events recorded on the
 stream the kernels run on (torch's current stream).
@@ -39,8 +41,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--only", default="all",
-                   choices=["all", "bf16", "bf16out", "gemv", "fp8", "f16_ragged", "f16_64", "i8",
-                            "copy"])
+                   choices=["all", "bf16", "bf16out", "gemv", "w8a8_tokens", "quant", "fp8",
+                            "f16_ragged", "f16_64", "i8", "copy"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the bounded oracle sample")
@@ -217,6 +219,56 @@ def main():
                          "traffic": traffic_for("gemv_w8a8_14336x4096", digest)},
         }
         del tWs
+
+    # ---------------- W8A8 layer for a few tokens, cold cache --------------------
+    if args.only in ("all", "w8a8_tokens"):
+        N, K = 14336, 4096
+        r = np.random.default_rng(12)
+        copies = 8
+        W = r.integers(-127, 128, (N, K)).astype(np.int8)
+        tWs = [to_dev(W) for _ in range(copies)]
+        tsw = to_dev(r.uniform(0.001, 0.01, N).astype(np.float32))
+        tb = to_dev(r.standard_normal(N).astype(np.float32))
+        for M in (4, 16):
+            tX = to_dev(r.integers(-127, 128, (M, K)).astype(np.int8))
+            tsx = to_dev(r.uniform(0.01, 0.1, M).astype(np.float32))
+            ty = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            region, per = timed(lambda i: mp.gemm_w8a8(tX, tsx, tWs[i % copies], tsw, tb, out=ty),
+                                args.steps, args.warmup, stream)
+            st = stats(per, region, args.steps)
+            nbytes = N * K + M * K + 4 * M + 8 * N + 2 * M * N
+            gbs = nbytes / (st["mean_us"] * 1e-6) / 1e9
+            extra[f"gemm_w8a8_m{M}"] = {
+                "workload": f"W8A8 layer, {M} tokens x 4096 . W int8 [14336 x 4096], bias, BF16 out; "
+                            "cold: 8 rotating W copies",
+                "GB_s": gbs, "algorithmic_bytes": nbytes, "launch_us": st,
+                "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s",
+                             "frac": gbs / PEAK_HBM}}
+        del tWs
+
+    # ---------------- quantisers -----------------------------------------------
+    if args.only in ("all", "quant"):
+        r = np.random.default_rng(13)
+        X = r.standard_normal((16, 4096)).astype(np.float32)
+        tX = to_dev((X.view(np.uint32) >> 16).astype(np.uint16))
+        region, per = timed(lambda i: mp.quantize_i8_rows(tX), args.steps, args.warmup, stream)
+        extra["quantize_i8_rows_16x4096"] = {
+            "workload": "per-token INT8 quantisation of 16 BF16 tokens x 4096 (latency bound)",
+            "launch_us": stats(per, region, args.steps)}
+        for name, (R, Cc, br) in (("a", (4096, 7168, 1)), ("b", (7168, 7168, 128))):
+            tA = torch.randn((R, Cc), device=dev)
+            region, per = timed(lambda i: mp.quantize_fp8_blocks(tA, br), max(args.steps // 2, 5),
+                                args.warmup, stream)
+            st = stats(per, region, max(args.steps // 2, 5))
+            nbytes = R * Cc * 5 + 4 * (-(-R // br)) * (-(-Cc // 128))
+            gbs = nbytes / (st["mean_us"] * 1e-6) / 1e9
+            extra[f"quantize_fp8_blocks_{name}"] = {
+                "workload": f"FP8 E4M3 block quantisation of FP32 {R} x {Cc} in {br} x 128 blocks "
+                            "(the FP8 GEMM workload's operand)",
+                "GB_s": gbs, "algorithmic_bytes": nbytes, "launch_us": st,
+                "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s",
+                             "frac": gbs / PEAK_HBM}}
+            del tA
 
     # ---------------- FP8 block-scaled 4096 x 7168 x 7168 ----------------------
     if args.only in ("all", "fp8"):

@@ -1,6 +1,7 @@
 /*
  * mpdt.h -- C ABI of libmpdt.so: tiled mixed-precision matrix
- * multiply-accumulate and the batch-1 W8A8 linear layer on AMD MI355X
+ * multiply-accumulate, the W8A8 linear layer and the quantisation steps
+ * around them on AMD MI355X
  * (gfx950 / CDNA4).  Plain C: integers, device pointers, a stream handle.
  *
  * Operations and where they are defined:
@@ -127,6 +128,44 @@ mpdt_status gemv_w8a8(int64_t M, int64_t N, int64_t K,
                       const int8_t* x, float x_scale,
                       const int8_t* W, int64_t ldw, const float* w_scale,
                       uint16_t* y, int32_t* z_out, void* stream);
+
+/* W8A8 linear layer for M >= 1 tokens (a small batch), each token with its
+ * own activation scale, and an optional bias added after the dequantisation
+ * ("NVIDIA A100: from chip to SIMT", section 5.1: the bias belongs in the
+ * floating-point epilogue).  For every token m and output channel o:
+ *   Z[m][o] = sum_k X[m][k] * W[o][k]                                (INT32, exact)
+ *   Y[m][o] = bf16_rne( ((float(Z) * x_scale[m]) * w_scale[o]) + bias[o] )
+ * each step one IEEE FP32 operation, in this order (the bias step is skipped
+ * when bias is NULL).  X: M x K INT8 (ldx); W: N x K INT8, one output channel
+ * per row (ldw); x_scale: M FP32; w_scale, bias: N FP32; Y: M x N BF16 bits
+ * (ldy); Z (optional, may be NULL): M x N INT32 (ldz).  The weights are read
+ * once per group of up to 16 tokens.  Exact while K * 128^2 < 2^31. */
+mpdt_status gemm_w8a8(int64_t M, int64_t N, int64_t K,
+                      const int8_t* X, int64_t ldx, const float* x_scale,
+                      const int8_t* W, int64_t ldw, const float* w_scale, const float* bias,
+                      uint16_t* Y, int64_t ldy, int32_t* Z, int64_t ldz, void* stream);
+
+/* Per-token symmetric INT8 quantisation of activations (the step that makes
+ * the W8A8 layer's q_x and s_x; same section: symmetric, zero point 0, one
+ * scale per token).  For each row m of the M x K BF16 matrix X (ldx):
+ *   scales[m] = amax_k |X[m][k]| / 127   (FP32 division; 1 when the row is 0)
+ *   Q[m][k]   = clamp(rne(X[m][k] / scales[m]), -127, 127)    (INT8, ldq)
+ * rne = round to nearest, ties to even. */
+mpdt_status quantize_i8_rows(int64_t M, int64_t K, const uint16_t* X, int64_t ldx,
+                             int8_t* Q, int64_t ldq, float* scales, void* stream);
+
+/* FP8 E4M3 block quantisation ("Tensor Core" page, section "Precision": FP8
+ * needs scale factors per tensor, per row or per block).  The R x C FP32
+ * matrix X (ldx) is cut into block_rows x 128 blocks (block_rows = 1 for the
+ * 1 x 128 activation blocks, 128 for the 128 x 128 weight blocks of
+ * gemm_fp8_blockscaled; edge blocks keep their own scale):
+ *   s = amax_block |x| / 448   (FP32 division; 1 for an all-zero block)
+ *   Q = e4m3_rne(x / s)        (OCP E4M3FN codes, ldq)
+ * scales is ceil(R/block_rows) x ceil(C/128) FP32 with leading dimension lds
+ * -- exactly the scale_a / scale_b operand of gemm_fp8_blockscaled. */
+mpdt_status quantize_fp8_blocks(int64_t R, int64_t C, const float* X, int64_t ldx,
+                                int64_t block_rows, uint8_t* Q, int64_t ldq,
+                                float* scales, int64_t lds, void* stream);
 
 /* Static text for a status code. */
 const char* mpdt_status_string(mpdt_status s);

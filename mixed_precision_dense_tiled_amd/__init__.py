@@ -19,7 +19,8 @@ import os
 import torch
 
 __all__ = ["gemm_f16", "gemm_bf16", "gemm_f16_f16out", "gemm_bf16_bf16out", "gemm_i8_i32",
-           "gemm_fp8_blockscaled", "gemv_w8a8",
+           "gemm_fp8_blockscaled", "gemv_w8a8", "gemm_w8a8", "quantize_i8_rows",
+           "quantize_fp8_blocks",
            "MpdtError", "lib", "lib_path", "version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -62,6 +63,13 @@ def lib() -> ctypes.CDLL:
         L.gemv_w8a8.argtypes = [_i64, _i64, _i64, _vp, ctypes.c_float, _vp, _i64, _vp, _vp, _vp,
                                 _vp]
         L.gemv_w8a8.restype = ctypes.c_int
+        L.gemm_w8a8.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _i64,
+                                _vp, _i64, _vp]
+        L.gemm_w8a8.restype = ctypes.c_int
+        L.quantize_i8_rows.argtypes = [_i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]
+        L.quantize_i8_rows.restype = ctypes.c_int
+        L.quantize_fp8_blocks.argtypes = [_i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp]
+        L.quantize_fp8_blocks.restype = ctypes.c_int
         L.mpdt_status_string.argtypes = [ctypes.c_int]
         L.mpdt_status_string.restype = ctypes.c_char_p
         L.mpdt_last_error.argtypes = []
@@ -193,3 +201,68 @@ def gemv_w8a8(x, x_scale, W, w_scale, out=None, z_out=None, return_z=False):
     if return_z or z_out is not None:
         return out, z_out
     return out
+
+
+def _vec(t, n, dtype, name):
+    if t.dtype != dtype or t.numel() != n or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name} must be a contiguous {dtype} GPU tensor of {n} entries")
+    return t.data_ptr()
+
+
+def gemm_w8a8(X, x_scale, W, w_scale, bias=None, out=None, z_out=None, return_z=False):
+    """W8A8 layer for M tokens: X INT8 [M, K], x_scale FP32 [M], W INT8 [N, K]
+    (one output channel per row), w_scale FP32 [N], bias FP32 [N] or None;
+    returns Y BF16 [M, N] (and the INT32 sums when return_z or z_out is given)."""
+    M, K = X.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("W must be [N, K]")
+    px, ldx = _mat(X, 1, "X")
+    pw, ldw = _mat(W, 1, "W")
+    psx = _vec(x_scale, M, torch.float32, "x_scale")
+    psw = _vec(w_scale, N, torch.float32, "w_scale")
+    pb = None if bias is None else _vec(bias, N, torch.float32, "bias")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=W.device)
+    py, ldy = _mat(out, 2, "out")
+    if z_out is None and return_z:
+        z_out = torch.empty((M, N), dtype=torch.int32, device=W.device)
+    pz, ldz = (None, N) if z_out is None else _mat(z_out, 4, "z_out")
+    _check("gemm_w8a8", lib().gemm_w8a8(M, N, K, px, ldx, psx, pw, ldw, psw, pb, py, ldy, pz, ldz,
+                                        _stream(W)))
+    if return_z or z_out is not None:
+        return out, z_out
+    return out
+
+
+def quantize_i8_rows(X, q_out=None, scales_out=None):
+    """Per-token INT8 quantisation of BF16 activations X [M, K] (any 2-byte
+    dtype holding BF16 bits); returns (Q INT8 [M, K], scales FP32 [M])."""
+    M, K = X.shape
+    px, ldx = _mat(X, 2, "X")
+    if q_out is None:
+        q_out = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    if scales_out is None:
+        scales_out = torch.empty(M, dtype=torch.float32, device=X.device)
+    pq, ldq = _mat(q_out, 1, "q_out")
+    ps = _vec(scales_out, M, torch.float32, "scales_out")
+    _check("quantize_i8_rows", lib().quantize_i8_rows(M, K, px, ldx, pq, ldq, ps, _stream(X)))
+    return q_out, scales_out
+
+
+def quantize_fp8_blocks(X, block_rows, q_out=None, scales_out=None):
+    """FP8 E4M3 block quantisation of an FP32 matrix X [R, C] in
+    block_rows x 128 blocks (block_rows 1 or 128); returns (Q uint8 [R, C],
+    scales FP32 [ceil(R/block_rows), ceil(C/128)])."""
+    R, Cc = X.shape
+    px, ldx = _mat(X, 4, "X")
+    nbr, nbc = -(-R // block_rows), -(-Cc // 128)
+    if q_out is None:
+        q_out = torch.empty((R, Cc), dtype=torch.uint8, device=X.device)
+    if scales_out is None:
+        scales_out = torch.empty((nbr, nbc), dtype=torch.float32, device=X.device)
+    pq, ldq = _mat(q_out, 1, "q_out")
+    ps, lds = _mat(scales_out, 4, "scales_out")
+    _check("quantize_fp8_blocks", lib().quantize_fp8_blocks(R, Cc, px, ldx, block_rows, pq, ldq, ps,
+                                                            lds, _stream(X)))
+    return q_out, scales_out

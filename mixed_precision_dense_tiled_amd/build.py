@@ -18,7 +18,7 @@ PROBE_LIB = os.path.join(PKG, "libmpdt_probes.so")
 ORACLE_DIR = os.path.join(ROOT, "oracle")
 ORACLE_LIB = os.path.join(ORACLE_DIR, "liboracle.so")
 
-HIP_SOURCES = ["abi.hip", "gemm.hip", "gemv_w8a8.hip"]
+HIP_SOURCES = ["abi.hip", "gemm.hip", "gemv_w8a8.hip", "quant.hip"]
 
 # Packed FP32 instructions are switched off for all device code (-packed-fp32-ops).
 HIP_FLAGS = [

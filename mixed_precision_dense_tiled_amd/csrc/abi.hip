@@ -280,6 +280,121 @@ MPDT_EXPORT mpdt_status gemv_w8a8(int64_t M, int64_t N, int64_t K, const int8_t*
     return launched(mpdt::launch_gemv_w8a8(a, al, (hipStream_t)stream), fn);
 }
 
+MPDT_EXPORT mpdt_status gemm_w8a8(int64_t M, int64_t N, int64_t K, const int8_t* X, int64_t ldx,
+                                  const float* x_scale, const int8_t* W, int64_t ldw,
+                                  const float* w_scale, const float* bias, uint16_t* Y, int64_t ldy,
+                                  int32_t* Z, int64_t ldz, void* stream) {
+    const char* fn = "gemm_w8a8";
+    if (!dims_ok(M, N, K)) return fail(MPDT_ERROR_INVALID_VALUE, fn, "dimension out of range");
+    if (M == 0 || N == 0) return MPDT_SUCCESS;
+    if (!Y || !x_scale || !w_scale)
+        return fail(MPDT_ERROR_INVALID_VALUE, fn, "Y, x_scale or w_scale is NULL");
+    if (K > 0) {
+        if (!X || !W) return fail(MPDT_ERROR_INVALID_VALUE, fn, "X or W is NULL");
+        if (ldx < K || ldw < K) return fail(MPDT_ERROR_INVALID_VALUE, fn, "ldx or ldw < K");
+    }
+    if (ldy < N || (Z && ldz < N)) return fail(MPDT_ERROR_INVALID_VALUE, fn, "ldy or ldz < N");
+    if (!aligned_to(Y, 2) || !aligned_to(x_scale, 4) || !aligned_to(w_scale, 4) ||
+        (bias && !aligned_to(bias, 4)) || (Z && !aligned_to(Z, 4)))
+        return fail(MPDT_ERROR_MISALIGNED, fn, "pointer not aligned to its element size");
+    Span sx, sw, ssx, ssw, sb, sy, sz;
+    if (!span_of(X, K > 0 ? M : 0, K, ldx, 1, &sx) || !span_of(W, K > 0 ? N : 0, K, ldw, 1, &sw) ||
+        !span_of(x_scale, 1, M, M, 4, &ssx) || !span_of(w_scale, 1, N, N, 4, &ssw) ||
+        !span_of(bias, bias ? 1 : 0, N, N, 4, &sb) || !span_of(Y, M, N, ldy, 2, &sy) ||
+        !span_of(Z, Z ? M : 0, N, ldz, 4, &sz))
+        return fail(MPDT_ERROR_INVALID_VALUE, fn, "operand too large");
+    const Span ins[5] = {sx, sw, ssx, ssw, sb};
+    for (const Span& in : ins)
+        if (sy.overlaps(in) || sz.overlaps(in))
+            return fail(MPDT_ERROR_ALIASING, fn, "an output overlaps an input");
+    if (sy.overlaps(sz)) return fail(MPDT_ERROR_ALIASING, fn, "Y overlaps Z");
+    mpdt_status s = check_device(fn);
+    if (s != MPDT_SUCCESS) return s;
+    mpdt::W8A8Args a{};
+    a.X = X;
+    a.ldx = ldx;
+    a.x_scale = x_scale;
+    a.W = W;
+    a.ldw = ldw;
+    a.w_scale = w_scale;
+    a.bias = bias;
+    a.Y = Y;
+    a.ldy = ldy;
+    a.Z = Z;
+    a.ldz = ldz;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    const bool al = aligned_to(X, 16) && aligned_to(W, 16) && ldx % 16 == 0 && ldw % 16 == 0;
+    return launched(mpdt::launch_gemm_w8a8(a, al, (hipStream_t)stream), fn);
+}
+
+MPDT_EXPORT mpdt_status quantize_i8_rows(int64_t M, int64_t K, const uint16_t* X, int64_t ldx,
+                                         int8_t* Q, int64_t ldq, float* scales, void* stream) {
+    const char* fn = "quantize_i8_rows";
+    if (M < 0 || K < 0 || M > kMaxDim || K > kMaxDim)
+        return fail(MPDT_ERROR_INVALID_VALUE, fn, "dimension out of range");
+    if (M == 0) return MPDT_SUCCESS;
+    if (!scales) return fail(MPDT_ERROR_INVALID_VALUE, fn, "scales is NULL");
+    if (K > 0 && (!X || !Q)) return fail(MPDT_ERROR_INVALID_VALUE, fn, "X or Q is NULL");
+    if (K > 0 && (ldx < K || ldq < K)) return fail(MPDT_ERROR_INVALID_VALUE, fn, "ldx or ldq < K");
+    if ((X && !aligned_to(X, 2)) || !aligned_to(scales, 4))
+        return fail(MPDT_ERROR_MISALIGNED, fn, "pointer not aligned to its element size");
+    Span sx, sq, ss;
+    if (!span_of(X, K > 0 ? M : 0, K, ldx, 2, &sx) || !span_of(Q, K > 0 ? M : 0, K, ldq, 1, &sq) ||
+        !span_of(scales, 1, M, M, 4, &ss))
+        return fail(MPDT_ERROR_INVALID_VALUE, fn, "operand too large");
+    if (sq.overlaps(sx) || ss.overlaps(sx) || sq.overlaps(ss))
+        return fail(MPDT_ERROR_ALIASING, fn, "an output overlaps the input or the other output");
+    mpdt_status s = check_device(fn);
+    if (s != MPDT_SUCCESS) return s;
+    mpdt::QuantI8Args a{};
+    a.X = X;
+    a.ldx = ldx;
+    a.Q = Q;
+    a.ldq = ldq;
+    a.S = scales;
+    a.K = K;
+    a.M = (int)M;
+    return launched(mpdt::launch_quantize_i8_rows(a, (hipStream_t)stream), fn);
+}
+
+MPDT_EXPORT mpdt_status quantize_fp8_blocks(int64_t R, int64_t C, const float* X, int64_t ldx,
+                                            int64_t block_rows, uint8_t* Q, int64_t ldq,
+                                            float* scales, int64_t lds, void* stream) {
+    const char* fn = "quantize_fp8_blocks";
+    if (R < 0 || C < 0 || R > kMaxDim || C > kMaxDim)
+        return fail(MPDT_ERROR_INVALID_VALUE, fn, "dimension out of range");
+    if (block_rows != 1 && block_rows != 128)
+        return fail(MPDT_ERROR_INVALID_VALUE, fn, "block_rows must be 1 or 128");
+    if (R == 0 || C == 0) return MPDT_SUCCESS;
+    const int64_t nbr = (R + block_rows - 1) / block_rows, nbc = (C + 127) / 128;
+    if (!X || !Q || !scales) return fail(MPDT_ERROR_INVALID_VALUE, fn, "X, Q or scales is NULL");
+    if (ldx < C || ldq < C || lds < nbc)
+        return fail(MPDT_ERROR_INVALID_VALUE, fn, "ldx or ldq < C, or lds < ceil(C/128)");
+    if (!aligned_to(X, 4) || !aligned_to(scales, 4))
+        return fail(MPDT_ERROR_MISALIGNED, fn, "pointer not aligned to its element size");
+    Span sx, sq, ss;
+    if (!span_of(X, R, C, ldx, 4, &sx) || !span_of(Q, R, C, ldq, 1, &sq) ||
+        !span_of(scales, nbr, nbc, lds, 4, &ss))
+        return fail(MPDT_ERROR_INVALID_VALUE, fn, "operand too large");
+    if (sq.overlaps(sx) || ss.overlaps(sx) || sq.overlaps(ss))
+        return fail(MPDT_ERROR_ALIASING, fn, "an output overlaps the input or the other output");
+    mpdt_status s = check_device(fn);
+    if (s != MPDT_SUCCESS) return s;
+    mpdt::QuantFp8Args a{};
+    a.X = X;
+    a.ldx = ldx;
+    a.Q = Q;
+    a.ldq = ldq;
+    a.S = scales;
+    a.lds = lds;
+    a.R = R;
+    a.C = C;
+    a.block_rows = (int)block_rows;
+    return launched(mpdt::launch_quantize_fp8_blocks(a, (hipStream_t)stream), fn);
+}
+
 MPDT_EXPORT const char* mpdt_status_string(mpdt_status s) {
     switch (s) {
         case MPDT_SUCCESS: return "success";

@@ -119,4 +119,132 @@ hipError_t launch_gemv_w8a8(const GemvArgs& a, bool aligned, hipStream_t stream)
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// The same layer for M tokens at once (a small batch), each with its own
+// activation scale, and an optional bias added after the dequantisation
+// (section 5.1 of the same page: a bias belongs in the floating-point
+// epilogue).  The weights are still streamed from HBM exactly once for up to
+// 16 tokens: the workgroup stages the tokens' K slice in LDS, each wave owns
+// two output channels and, for every 16-byte chunk of a weight row, takes the
+// v_dot4 products with the same chunk of every token.  Larger batches are cut
+// into groups of 16 tokens on the host (one launch each).
+//   z[m][o] = sum_k X[m][k] * W[o][k]          (INT32, exact)
+//   y[m][o] = bf16_rne( ((float(z) * s_x[m]) * s_w[o]) + bias[o] )
+// ---------------------------------------------------------------------------
+constexpr int TOK_WAVES = 4;       // wavefronts per workgroup
+constexpr int TOK_ROWS = 2;        // output channels per wavefront
+constexpr int TOK_KC = 4096;       // K bytes staged per pass (MG * 4 KiB of LDS)
+
+template <int MG, bool ALIGNED>
+__global__ __launch_bounds__(64 * TOK_WAVES) void gemm_w8a8_kernel(W8A8Args g) {
+    __shared__ __attribute__((aligned(16))) char xs[MG][TOK_KC];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int row0 = (blockIdx.x * TOK_WAVES + wave) * TOK_ROWS;
+    const int64_t K = g.K;
+
+    int acc[TOK_ROWS][MG];
+#pragma unroll
+    for (int r = 0; r < TOK_ROWS; ++r)
+#pragma unroll
+        for (int m = 0; m < MG; ++m) acc[r][m] = 0;
+
+    for (int64_t kc = 0; kc < K; kc += TOK_KC) {
+        const int64_t kn = min((int64_t)TOK_KC, K - kc);   // valid bytes of this pass
+        // stage the tokens' K slice (zero past M and past K)
+        for (int i = tid; i < MG * (TOK_KC / 16); i += 64 * TOK_WAVES) {
+            const int m = i / (TOK_KC / 16), c = i % (TOK_KC / 16);
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (m < g.M) {
+                const char* rowp = (const char*)g.X + (int64_t)m * g.ldx + kc;
+                v = load16_row<ALIGNED>(rowp + c * 16, rowp + kn);
+            }
+            lds_store16(lds_cast(xs[m]), c * 16, v);
+        }
+        __syncthreads();
+        // weights of this wave's rows for the whole pass, then the products
+        u32x4 wv[TOK_ROWS][TOK_KC / 1024];
+#pragma unroll
+        for (int r = 0; r < TOK_ROWS; ++r) {
+            const int row = row0 + r;
+            const char* rowp = (const char*)g.W + (int64_t)row * g.ldw + kc;
+#pragma unroll
+            for (int u = 0; u < TOK_KC / 1024; ++u) {
+                const int64_t off = 16 * (lane + 64 * u);
+                if (row >= g.N)
+                    wv[r][u] = u32x4{0u, 0u, 0u, 0u};
+                else if (ALIGNED && off + 16 <= kn)
+                    wv[r][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rowp + off));
+                else
+                    wv[r][u] = load16_row<ALIGNED>(rowp + off, rowp + kn);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < TOK_KC / 1024; ++u) {
+#pragma unroll
+            for (int m = 0; m < MG; ++m) {
+                const u32x4 xv = lds_load16(lds_cast(xs[m]), (uint32_t)(16 * (lane + 64 * u)));
+#pragma unroll
+                for (int r = 0; r < TOK_ROWS; ++r) acc[r][m] = dot16(wv[r][u], xv, acc[r][m]);
+            }
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int r = 0; r < TOK_ROWS; ++r)
+#pragma unroll
+        for (int m = 0; m < MG; ++m) acc[r][m] = wave_sum(acc[r][m]);
+
+    // lane r * MG + m writes channel row0 + r of token m
+#pragma unroll
+    for (int r = 0; r < TOK_ROWS; ++r)
+#pragma unroll
+        for (int m = 0; m < MG; ++m) {
+            const int row = row0 + r;
+            if (lane == r * MG + m && row < g.N && m < g.M) {
+                const int z = acc[r][m];
+                if (g.Z) g.Z[(int64_t)m * g.ldz + row] = z;
+                float v = (float)z;
+                v = v * g.x_scale[m];
+                v = v * g.w_scale[row];
+                if (g.bias) v = v + g.bias[row];
+                g.Y[(int64_t)m * g.ldy + row] = f32_to_bf16_bits(v);
+            }
+        }
+}
+
+template <int MG>
+static hipError_t launch_tokens(const W8A8Args& a, bool aligned, hipStream_t stream) {
+    const int rows_per_wg = TOK_WAVES * TOK_ROWS;
+    dim3 grid((unsigned)((a.N + rows_per_wg - 1) / rows_per_wg)), block(64 * TOK_WAVES);
+    if (aligned)
+        hipLaunchKernelGGL((gemm_w8a8_kernel<MG, true>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((gemm_w8a8_kernel<MG, false>), grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_w8a8(const W8A8Args& a0, bool aligned, hipStream_t stream) {
+    if (a0.N <= 0 || a0.M <= 0) return hipSuccess;
+    // groups of at most 16 tokens, each group one launch reading W once
+    for (int m0 = 0; m0 < a0.M; m0 += 16) {
+        W8A8Args a = a0;
+        a.M = min(16, a0.M - m0);
+        a.X = a0.X + (int64_t)m0 * a0.ldx;
+        a.x_scale = a0.x_scale + m0;
+        a.Y = a0.Y + (int64_t)m0 * a0.ldy;
+        a.Z = a0.Z ? a0.Z + (int64_t)m0 * a0.ldz : nullptr;
+        hipError_t e;
+        if (a.M == 1) e = launch_tokens<1>(a, aligned, stream);
+        else if (a.M == 2) e = launch_tokens<2>(a, aligned, stream);
+        else if (a.M <= 4) e = launch_tokens<4>(a, aligned, stream);
+        else if (a.M <= 8) e = launch_tokens<8>(a, aligned, stream);
+        else e = launch_tokens<16>(a, aligned, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 }  // namespace mpdt

@@ -44,4 +44,49 @@ struct GemvArgs {
 // aligned: x and every row of W start 16-byte aligned.
 hipError_t launch_gemv_w8a8(const GemvArgs& a, bool aligned, hipStream_t stream);
 
+// M-token W8A8 layer (M >= 1 tokens, per-token activation scales, optional
+// bias).  Leading dimensions in elements.
+struct W8A8Args {
+    const int8_t* X;
+    int64_t ldx;
+    const float* x_scale;   // [M]
+    const int8_t* W;
+    int64_t ldw;
+    const float* w_scale;   // [N]
+    const float* bias;      // [N] or null
+    uint16_t* Y;
+    int64_t ldy;
+    int32_t* Z;             // or null
+    int64_t ldz;
+    int M, N, K;
+};
+
+// aligned: X, W and their rows start 16-byte aligned.
+hipError_t launch_gemm_w8a8(const W8A8Args& a, bool aligned, hipStream_t stream);
+
+// Per-token INT8 quantisation of BF16 activations (M x K, leading dims in elements).
+struct QuantI8Args {
+    const uint16_t* X;
+    int64_t ldx;
+    int8_t* Q;
+    int64_t ldq;
+    float* S;
+    int64_t K;
+    int M;
+};
+hipError_t launch_quantize_i8_rows(const QuantI8Args& a, hipStream_t stream);
+
+// FP8 E4M3 block quantisation of an R x C FP32 matrix in block_rows x 128 blocks.
+struct QuantFp8Args {
+    const float* X;
+    int64_t ldx;
+    uint8_t* Q;
+    int64_t ldq;
+    float* S;
+    int64_t lds;
+    int64_t R, C;
+    int block_rows;   // 1 or 128
+};
+hipError_t launch_quantize_fp8_blocks(const QuantFp8Args& a, hipStream_t stream);
+
 }  // namespace mpdt

@@ -1,0 +1,157 @@
+// quant.hip -- the quantisation steps on either side of the low-precision
+// matrix paths, for gfx950:
+//
+//   * per-token symmetric INT8 quantisation of BF16 activations, the step that
+//     produces q_x and s_x for the W8A8 layer ("NVIDIA A100: from chip to
+//     SIMT", section 5.1: symmetric, zero point 0, one scale per token, made
+//     at run time by the previous operator or a separate quantisation step):
+//       s = amax_k |x[m][k]| / 127   (1 for an all-zero row)
+//       q[m][k] = clamp(rne(x[m][k] / s), -127, 127)
+//   * FP8 E4M3 block quantisation, the scale factors FP8 needs ("Tensor Core"
+//     page, section "Precision": per tensor, per row or per block), in 1 x 128
+//     or 128 x 128 blocks:
+//       s = amax_block |x| / 448     (1 for an all-zero block)
+//       q = e4m3_rne(x / s)          (|x / s| <= 448 up to one rounding)
+//
+// Both are memory-bound elementwise passes with one reduction per row or
+// block; every division is the IEEE-rounded FP32 one and rounding to an
+// integer is v_rndne (ties to even).  The FP32 -> E4M3 step is the gfx950
+// conversion instruction (OCP E4M3, round to nearest even).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace mpdt {
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    return v;
+}
+
+// maximum over the 256 threads of a workgroup (every thread gets it)
+__device__ __forceinline__ float block_max256(float v, float* red) {
+    v = wave_max(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    const float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float((uint32_t)b << 16);
+}
+
+// ---- per-token INT8 quantisation: one workgroup per token ------------------
+__global__ __launch_bounds__(256) void quantize_i8_rows_kernel(QuantI8Args g) {
+    __shared__ float red[4];
+    const int m = blockIdx.x;
+    const uint16_t* xr = g.X + (int64_t)m * g.ldx;
+    int8_t* qr = g.Q + (int64_t)m * g.ldq;
+    float amax = 0.0f;
+    for (int64_t k = threadIdx.x; k < g.K; k += 256) amax = fmaxf(amax, fabsf(bf16_bits_to_f32(xr[k])));
+    amax = block_max256(amax, red);
+    const float s = amax > 0.0f ? amax / 127.0f : 1.0f;
+    if (threadIdx.x == 0) g.S[m] = s;
+    for (int64_t k = threadIdx.x; k < g.K; k += 256) {
+        float r = __builtin_rintf(bf16_bits_to_f32(xr[k]) / s);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        qr[k] = (int8_t)(int)r;
+    }
+}
+
+hipError_t launch_quantize_i8_rows(const QuantI8Args& a, hipStream_t stream) {
+    if (a.M <= 0) return hipSuccess;
+    hipLaunchKernelGGL(quantize_i8_rows_kernel, dim3((unsigned)a.M), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+// ---- FP8 block quantisation ----------------------------------------------
+__device__ __forceinline__ uint8_t to_e4m3(float v) {
+    return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xff);
+}
+
+// 1 x 128 blocks: a wavefront takes FP8_RB consecutive blocks of one row,
+// two elements per lane per block (each load instruction reads 512
+// consecutive bytes); all loads are issued before the first reduction.
+constexpr int FP8_RB = 4;
+
+__global__ __launch_bounds__(256) void quantize_fp8_rowblocks_kernel(QuantFp8Args g) {
+    const int64_t nbc = (g.C + 127) / 128;
+    const int64_t groups = (nbc + FP8_RB - 1) / FP8_RB;              // block groups per row
+    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (w >= (int64_t)g.R * groups) return;         // whole wave: no barrier in this kernel
+    const int lane = threadIdx.x & 63;
+    const int64_t r = w / groups, bj0 = (w % groups) * FP8_RB;
+    const float* xr = g.X + r * g.ldx;
+    uint8_t* qr = g.Q + r * g.ldq;
+    float v[FP8_RB][2];
+#pragma unroll
+    for (int b = 0; b < FP8_RB; ++b) {
+        const int64_t c0 = (bj0 + b) * 128 + 2 * lane;
+        v[b][0] = c0 < g.C ? xr[c0] : 0.0f;
+        v[b][1] = c0 + 1 < g.C ? xr[c0 + 1] : 0.0f;
+    }
+#pragma unroll
+    for (int b = 0; b < FP8_RB; ++b) {
+        if (bj0 + b >= nbc) break;
+        const int64_t c0 = (bj0 + b) * 128 + 2 * lane;
+        const float amax = wave_max(fmaxf(fabsf(v[b][0]), fabsf(v[b][1])));
+        const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+        if (lane == 0) g.S[r * g.lds + bj0 + b] = s;
+        if (c0 < g.C) qr[c0] = to_e4m3(v[b][0] / s);
+        if (c0 + 1 < g.C) qr[c0 + 1] = to_e4m3(v[b][1] / s);
+    }
+}
+
+// 128 x 128 blocks: one workgroup per block; thread t covers column t % 128
+// of the block's rows t / 128, t / 128 + 2, ... (each wave instruction reads
+// 256 consecutive bytes of one row).
+__global__ __launch_bounds__(256) void quantize_fp8_tileblocks_kernel(QuantFp8Args g) {
+    __shared__ float red[4];
+    const int64_t nbc = (g.C + 127) / 128;
+    const int64_t bi = blockIdx.x / nbc, bj = blockIdx.x % nbc;
+    const int64_t c = bj * 128 + (threadIdx.x & 127);
+    const int64_t r0 = bi * 128 + (threadIdx.x >> 7);
+    const bool col_ok = c < g.C;
+    // the thread's 64 values stay in registers between the two passes
+    float v[64];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+        const int64_t r = r0 + 2 * i;
+        v[i] = (col_ok && r < g.R) ? g.X[r * g.ldx + c] : 0.0f;
+        amax = fmaxf(amax, fabsf(v[i]));
+    }
+    amax = block_max256(amax, red);
+    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    if (threadIdx.x == 0) g.S[bi * g.lds + bj] = s;
+    if (col_ok) {
+#pragma unroll
+        for (int i = 0; i < 64; ++i) {
+            const int64_t r = r0 + 2 * i;
+            if (r < g.R) g.Q[r * g.ldq + c] = to_e4m3(v[i] / s);
+        }
+    }
+}
+
+hipError_t launch_quantize_fp8_blocks(const QuantFp8Args& a, hipStream_t stream) {
+    if (a.R <= 0 || a.C <= 0) return hipSuccess;
+    const int64_t nbc = (a.C + 127) / 128;
+    if (a.block_rows == 1) {
+        const int64_t waves = (int64_t)a.R * ((nbc + FP8_RB - 1) / FP8_RB);
+        hipLaunchKernelGGL(quantize_fp8_rowblocks_kernel, dim3((unsigned)((waves + 3) / 4)),
+                           dim3(256), 0, stream, a);
+    } else {
+        const int64_t nbr = (a.R + 127) / 128;
+        hipLaunchKernelGGL(quantize_fp8_tileblocks_kernel, dim3((unsigned)(nbr * nbc)), dim3(256), 0,
+                           stream, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace mpdt

@@ -1,0 +1,142 @@
+"""GPU parity of the W8A8 layer for M tokens (with and without bias) and of
+the two quantisers, against the oracle, bit-exact (every step is an integer
+sum or a fixed sequence of IEEE FP32 operations, then one rounding):
+
+  * gemm_w8a8: M = 1, 2, 3, 5, 8, 16, 17, 40 tokens (groups of 16 per launch),
+    N not a multiple of a workgroup's rows, K not a multiple of the 4 KiB
+    pass, with and without bias, padded and misaligned operands, -128 at the
+    INT32 bound, K = 0, and the full 4096 x 14336 layer for 4 tokens;
+  * quantize_i8_rows: random BF16 rows, exact ties, zero rows, K tails;
+  * quantize_fp8_blocks: 1 x 128 and 128 x 128 blocks, ragged edges, a zero
+    block, the FP8 workload's operand sizes, and the result fed to
+    gemm_fp8_blockscaled."""
+import numpy as np
+import pytest
+import torch
+
+import mixed_precision_dense_tiled_amd as mp
+import oracle
+from helpers import check_fp, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def w8a8_inputs(M, N, K, seed):
+    r = np.random.default_rng(seed)
+    X = r.integers(-127, 128, (M, K)).astype(np.int8)
+    W = r.integers(-127, 128, (N, K)).astype(np.int8)
+    sx = r.uniform(0.01, 0.1, M).astype(np.float32)
+    sw = r.uniform(0.001, 0.01, N).astype(np.float32)
+    bias = r.standard_normal(N).astype(np.float32)
+    return X, sx, W, sw, bias
+
+
+def run_w8a8(X, sx, W, sw, bias, ldx=None, ldw=None, shift=0):
+    tX = dev(X, ldx, pad=55)
+    if shift:
+        M, K = X.shape
+        base = dev(np.concatenate([np.zeros(shift, np.int8), X.ravel()]))
+        tX = base[shift:].view(M, K)
+    y, z = mp.gemm_w8a8(tX, dev(sx), dev(W, ldw, pad=-66), dev(sw),
+                        None if bias is None else dev(bias), return_z=True)
+    torch.cuda.synchronize()
+    zr, yr = oracle.gemm_w8a8(X, sx, W, sw, bias)
+    return host(z), host(y).view(np.uint16), zr, yr
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 16, 17, 40])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_w8a8_tokens_bit_exact(gpu_ok, M, with_bias):
+    X, sx, W, sw, bias = w8a8_inputs(M, 1000, 4500, seed=M)
+    z, y, zr, yr = run_w8a8(X, sx, W, sw, bias if with_bias else None)
+    assert np.array_equal(z, zr) and np.array_equal(y, yr)
+
+
+@pytest.mark.parametrize("M,N,K,ldx,ldw,shift", [(4, 333, 1000, 1003, 1001, 0), (6, 17, 64, None, 80, 3),
+                                                 (16, 9, 8193, None, None, 0), (2, 1, 1, None, None, 1)])
+def test_w8a8_tokens_shapes_padded_unaligned(gpu_ok, M, N, K, ldx, ldw, shift):
+    X, sx, W, sw, bias = w8a8_inputs(M, N, K, seed=N + K)
+    z, y, zr, yr = run_w8a8(X, sx, W, sw, bias, ldx=ldx, ldw=ldw, shift=shift)
+    assert np.array_equal(z, zr) and np.array_equal(y, yr)
+
+
+def test_w8a8_tokens_int32_bound_full_layer_and_k_zero(gpu_ok):
+    K, N = 4096, 64
+    X = np.full((3, K), -128, np.int8)
+    W = np.full((N, K), -128, np.int8)
+    W[1::2] = 127
+    sx = np.full(3, 0.05, np.float32)
+    sw = np.full(N, 0.001, np.float32)
+    z, y, zr, yr = run_w8a8(X, sx, W, sw, None)
+    assert z[0, 0] == K * 128 * 128 and np.array_equal(z, zr) and np.array_equal(y, yr)
+    X, sx, W, sw, bias = w8a8_inputs(4, 14336, 4096, seed=99)
+    z, y, zr, yr = run_w8a8(X, sx, W, sw, bias)
+    assert np.array_equal(z, zr) and np.array_equal(y, yr)
+    bias = np.linspace(-2, 2, 30).astype(np.float32)
+    y, z = mp.gemm_w8a8(torch.zeros((5, 0), dtype=torch.int8, device=gpu_ok), dev(np.ones(5, np.float32)),
+                        torch.zeros((30, 0), dtype=torch.int8, device=gpu_ok), dev(np.ones(30, np.float32)),
+                        dev(bias), return_z=True)
+    assert not host(z).any()
+    assert np.array_equal(host(y).view(np.uint16), np.tile(oracle.f32_to_bf16_rne(bias), (5, 1)))
+
+
+def bf16_matrix(shape, seed, scale=1.0):
+    r = np.random.default_rng(seed)
+    v = (r.standard_normal(shape) * scale).astype(np.float32)
+    return (v.view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("M,K", [(1, 4096), (7, 4096), (3, 1000), (2, 1), (64, 4099)])
+def test_quantize_i8_rows_bit_exact(gpu_ok, M, K):
+    X = bf16_matrix((M, K), seed=M * 7 + K, scale=3.0)
+    q, s = mp.quantize_i8_rows(dev(X))
+    qr, sr = oracle.quantize_i8_rows(X)
+    assert np.array_equal(host(q), qr) and np.array_equal(host(s), sr)
+
+
+def test_quantize_i8_rows_ties_zero_rows_padding(gpu_ok):
+    row = np.array([127, 2.5, 3.5, -0.5, -1.5, 126.5, 0.5, -2.5], np.float32)
+    X = np.zeros((3, 8), np.uint16)
+    X[0] = (row.view(np.uint32) >> 16).astype(np.uint16)
+    X[2] = bf16_matrix((1, 8), 5)[0]
+    tX = dev(X, 13, pad=0x7FC0)                      # NaN padding must not be read
+    q_out = dev(np.full((3, 8), 99, np.int8), 11, pad=77)
+    q, s = mp.quantize_i8_rows(tX, q_out=q_out)
+    qr, sr = oracle.quantize_i8_rows(X)
+    assert np.array_equal(host(q), qr) and np.array_equal(host(s), sr)
+    assert host(q)[0].tolist() == [127, 2, 4, 0, -2, 126, 0, -2] and host(s)[1] == 1.0
+    full = host(q_out.as_strided((3, 11), (11, 1)))
+    assert (full[:, 8:] == 77).all()                 # padding of Q untouched
+
+
+@pytest.mark.parametrize("R,C,br", [(256, 384, 128), (130, 200, 128), (5, 300, 1), (129, 257, 1),
+                                    (1, 1, 1), (1, 1, 128)])
+def test_quantize_fp8_blocks_bit_exact(gpu_ok, R, C, br):
+    r = np.random.default_rng(R * C + br)
+    X = (r.standard_normal((R, C)) * 2.0 ** r.integers(-10, 10, (R, 1))).astype(np.float32)
+    if R > 128 and C > 128:
+        X[:128, 128:256] = 0.0                        # an all-zero block
+    q, s = mp.quantize_fp8_blocks(dev(X), br)
+    qr, sr = oracle.quantize_fp8_blocks(X, br)
+    assert np.array_equal(host(s), sr)
+    assert np.array_equal(host(q), qr)
+
+
+def test_quantize_fp8_workload_sizes_feed_the_fp8_gemm(gpu_ok):
+    M, N, K = 512, 768, 1024
+    r = np.random.default_rng(3)
+    A = r.standard_normal((M, K)).astype(np.float32)
+    B = r.standard_normal((K, N)).astype(np.float32)
+    qa, sa = mp.quantize_fp8_blocks(dev(A), 1)
+    qb, sb = mp.quantize_fp8_blocks(dev(B), 128)
+    qar, sar = oracle.quantize_fp8_blocks(A, 1)
+    qbr, sbr = oracle.quantize_fp8_blocks(B, 128)
+    assert np.array_equal(host(qa), qar) and np.array_equal(host(sa), sar)
+    assert np.array_equal(host(qb), qbr) and np.array_equal(host(sb), sbr)
+    D = mp.gemm_fp8_blockscaled(qa, sa, qb, sb)
+    got = oracle.bf16_to_f64(host(D).view(np.uint16))
+    R_, S_ = oracle.gemm_fp8_blockscaled(qar, sar, qbr, sbr)
+    check_fp(got, R_, S_, 1e-2, "quantised fp8 gemm", bf16_out=True)
+    # and the quantised product approximates the FP32 product of the originals
+    ref = A.astype(np.float64) @ B.astype(np.float64)
+    assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 0.1
