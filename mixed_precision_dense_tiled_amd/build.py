@@ -9,6 +9,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -18,11 +19,16 @@ PROBE_LIB = os.path.join(PKG, "libmpdt_probes.so")
 ORACLE_DIR = os.path.join(ROOT, "oracle")
 ORACLE_LIB = os.path.join(ORACLE_DIR, "liboracle.so")
 
-HIP_SOURCES = ["abi.hip", "gemm.hip", "gemv_w8a8.hip", "quant.hip"]
+HIP_SOURCES = ["abi.hip", "gemm.hip", "gemm_fp8.hip", "gemv_w8a8.hip", "quant.hip"]
+
+# Per-source device-compiler options.  The one-wave FP8 GEMM rescales its MFMA
+# block sums with FP32 FMAs every K tile; VALU instructions cannot read AGPRs,
+# so its MFMAs are built in the form that writes VGPRs.
+SOURCE_FLAGS = {"gemm_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 # Packed FP32 instructions are switched off for all device code (-packed-fp32-ops).
 HIP_FLAGS = [
-    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
+    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fvisibility=hidden", "-Wall",
     "-I", os.path.join(ROOT, "include"),
@@ -41,12 +47,24 @@ def _run(cmd, cwd):
     subprocess.run(cmd, cwd=cwd, check=True)
 
 
+def _link(out: str, sources, extra_flags=()) -> str:
+    """Compile each source to an object (in parallel, with its own options),
+    then link them into the shared library `out`."""
+    objdir = os.path.join(CSRC, "_build", os.path.basename(out))
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, s + ".o") for s in sources]
+    cmds = [[hipcc(), *HIP_FLAGS, *SOURCE_FLAGS.get(s, []), *extra_flags, "-c",
+             os.path.join(CSRC, s), "-o", o] for s, o in zip(sources, objs)]
+    with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1, 8)) as ex:
+        list(ex.map(lambda c: _run(c, CSRC), cmds))
+    tmp = out + ".tmp"
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], cwd=CSRC)
+    os.replace(tmp, out)
+    return out
+
+
 def build_library(extra_flags=()) -> str:
-    srcs = [os.path.join(CSRC, s) for s in HIP_SOURCES]
-    tmp = LIB + ".tmp"
-    _run([hipcc(), *HIP_FLAGS, *extra_flags, *srcs, "-o", tmp], cwd=CSRC)
-    os.replace(tmp, LIB)
-    return LIB
+    return _link(LIB, HIP_SOURCES, extra_flags)
 
 
 CLOCK_LIB = os.path.join(PKG, "libmpdt_clock.so")
@@ -55,20 +73,12 @@ CLOCK_LIB = os.path.join(PKG, "libmpdt_clock.so")
 def build_clock_library(extra_flags=()) -> str:
     """The same kernels with per-workgroup clock stamps (bench.py reads the
     shader clock of the timed GEMM from it; never used for results)."""
-    srcs = [os.path.join(CSRC, s) for s in HIP_SOURCES]
-    tmp = CLOCK_LIB + ".tmp"
-    _run([hipcc(), *HIP_FLAGS, "-DMPDT_CLOCK_STAMPS", *extra_flags, *srcs, "-o", tmp], cwd=CSRC)
-    os.replace(tmp, CLOCK_LIB)
-    return CLOCK_LIB
+    return _link(CLOCK_LIB, HIP_SOURCES, ("-DMPDT_CLOCK_STAMPS", *extra_flags))
 
 
 def build_probes(extra_flags=()) -> str:
     """Layout-probe kernels used by the GPU tests (not part of the C ABI)."""
-    tmp = PROBE_LIB + ".tmp"
-    _run([hipcc(), *HIP_FLAGS, *extra_flags, os.path.join(CSRC, "probes.hip"), "-o", tmp],
-         cwd=CSRC)
-    os.replace(tmp, PROBE_LIB)
-    return PROBE_LIB
+    return _link(PROBE_LIB, ["probes.hip"], extra_flags)
 
 
 def build_oracle() -> str:

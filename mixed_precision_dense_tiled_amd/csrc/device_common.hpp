@@ -72,6 +72,21 @@ __device__ __forceinline__ void lds_dma16(i32x4 r, MPDT_LDS char* dst, uint32_t 
                      : "{m0}"((uint32_t)(uintptr_t)dst), "v"(voff), "s"(r), "s"(soff), "n"(OFF));
 }
 
+// 4-byte variant of lds_dma16: lane l's dword from buffer offset voff + soff +
+// OFF lands at dst + OFF + 4 * l.  Same ordering rules.
+template <int OFF = 0, bool NOP = true>
+__device__ __forceinline__ void lds_dma4(i32x4 r, MPDT_LDS char* dst, uint32_t voff, uint32_t soff) {
+    static_assert(OFF >= 0 && OFF < 4096, "12-bit instruction offset");
+    if constexpr (NOP)
+        asm volatile("s_nop 0\n\tbuffer_load_dword %1, %2, %3 offen offset:%4 lds"
+                     :
+                     : "{m0}"((uint32_t)(uintptr_t)dst), "v"(voff), "s"(r), "s"(soff), "n"(OFF));
+    else
+        asm volatile("buffer_load_dword %1, %2, %3 offen offset:%4 lds"
+                     :
+                     : "{m0}"((uint32_t)(uintptr_t)dst), "v"(voff), "s"(r), "s"(soff), "n"(OFF));
+}
+
 // Keep the bytes [0, nbytes) of a 16-byte chunk, zero the rest (nbytes 0..16).
 __device__ __forceinline__ u32x4 mask_tail(u32x4 v, int nbytes) {
 #pragma unroll

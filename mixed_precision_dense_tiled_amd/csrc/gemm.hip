@@ -37,211 +37,13 @@
 
 #include <type_traits>
 
-#include "device_common.hpp"
-#include "kernels.hpp"
+#include "gemm_common.hpp"
 
 namespace mpdt {
-
-#ifdef MPDT_CLOCK_STAMPS
-// Instrumented build (a separate measurement library, never the product
-// one): workgroup w < CLOCK_STAMP_WGS records the shader clock (s_memtime)
-// and the 100 MHz real-time counter (s_memrealtime) at kernel entry, after
-// the K loop and after its last store has completed -- enough to read the
-// shader clock the kernel actually ran at and where its time went.
-constexpr int CLOCK_STAMP_WGS = 4096;
-__device__ uint64_t g_clock_stamps[CLOCK_STAMP_WGS * 6];
-#define MPDT_STAMP(i)                                        \
-    const uint64_t stamp_t##i = __builtin_amdgcn_s_memtime(); \
-    const uint64_t stamp_r##i = __builtin_amdgcn_s_memrealtime();
-#else
-#define MPDT_STAMP(i)
-#endif
-
-// ---------------------------------------------------------------------------
-// Per-format MFMA traits.  A "step" is one MFMA along K.
-// ---------------------------------------------------------------------------
-template <Kind KD> struct Fmt;
-
-template <> struct Fmt<Kind::F16> {
-    static constexpr int ES = 2;            // bytes per element
-    static constexpr int STEP_BYTES = 32;   // K bytes per MFMA (32x32x16)
-    using Acc = f32x16;
-    __device__ static Acc mma(u32x4 a, u32x4 b, Acc c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-    }
-};
-template <> struct Fmt<Kind::BF16> {
-    static constexpr int ES = 2;
-    static constexpr int STEP_BYTES = 32;   // 32x32x16
-    using Acc = f32x16;
-    __device__ static Acc mma(u32x4 a, u32x4 b, Acc c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-    }
-};
-template <> struct Fmt<Kind::I8> {
-    static constexpr int ES = 1;
-    static constexpr int STEP_BYTES = 32;   // 32x32x32
-    using Acc = i32x16;
-    __device__ static Acc mma(u32x4 a, u32x4 b, Acc c) {
-        return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
-                                                     __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
-    }
-};
-template <> struct Fmt<Kind::FP8> {
-    static constexpr int ES = 1;
-    static constexpr int STEP_BYTES = 64;   // 32x32x64, E4M3 x E4M3, unit (127) E8M0 scales
-    using Acc = f32x16;
-    __device__ static Acc mma(i32x8 a, i32x8 b, Acc c) {
-        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
-    }
-};
-
-// ---------------------------------------------------------------------------
-// Tile geometry and LDS layout.
-// ---------------------------------------------------------------------------
-template <Kind KD, int BM_, int BN_, int WAVES_M_, int WAVES_N_, int KT_BYTES_, int STAGES_>
-struct Cfg {
-    static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
-    static constexpr int KT_BYTES = KT_BYTES_;             // bytes of K per K tile
-    static constexpr int STAGES = STAGES_;                 // LDS stages (loads run STAGES-1 ahead)
-    // register slots of the register-staged path (FP8 keeps one: its wider
-    // B tile and block accumulators leave no room for more)
-    static constexpr int REG_SLOTS = (KD == Kind::FP8) ? 1 : 3;
-    static constexpr int NT = 64 * WAVES_M * WAVES_N;
-    static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-    static constexpr int TM = WM / 32, TN = WN / 32;       // MFMA tiles per wave
-    static constexpr int ES = Fmt<KD>::ES;
-    static constexpr int KROWS = KT_BYTES / ES;            // K elements per K tile
-    static constexpr int STEPS = KT_BYTES / Fmt<KD>::STEP_BYTES;
-    static constexpr int FRAG_BYTES = Fmt<KD>::STEP_BYTES / 2;  // per lane per operand
-    static constexpr int CPR_A = KT_BYTES / 16;            // 16-byte chunks per A row
-    static constexpr int A_BYTES = BM * KT_BYTES;
-    static constexpr int B_ROW = BN * ES;                  // bytes per K row of the B tile
-    static constexpr int B_BYTES = KROWS * B_ROW;
-    static constexpr int CPR_B = B_ROW / 16;               // 16-byte chunks per B row
-    static constexpr int SA_BYTES = (KD == Kind::FP8) ? BM * 4 : 0;   // A-row scales (FP8)
-    static constexpr int LDS_BYTES = STAGES * (A_BYTES + B_BYTES) + 2 * SA_BYTES;
-    static constexpr int UA = A_BYTES / 16 / NT;           // 16-byte loads per thread, A
-    static constexpr int UB = B_BYTES / 16 / NT;           // 16-byte loads per thread, B
-    static_assert(A_BYTES % (16 * NT) == 0 && B_BYTES % (16 * NT) == 0, "staging split");
-    static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "1 KiB load pieces");
-    static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be 32-aligned");
-    static_assert(KT_BYTES == 64 || KT_BYTES == 128, "K tile of 64 or 128 bytes");
-    static_assert(STEPS >= 1, "at least one MFMA step per K tile");
-    static_assert(KD != Kind::FP8 || (KT_BYTES == 128 && STAGES == 2),
-                  "FP8: one K tile per 128-wide scale block, two stages");
-    static_assert(STAGES >= 2 && STAGES <= 5, "2..5 stages");
-    static_assert(LDS_BYTES <= 163840, "LDS budget");
-};
-
-// A tile: row r (0..BM-1) holds the CPR_A 16-byte chunks of its K bytes; chunk
-// c is stored at c ^ swz_a(r).  An MFMA operand read (ds_read_b128) takes one
-// chunk from 32 consecutive rows; the swizzle puts rows r..r+7 in 8 distinct
-// 16-byte bank slots of a 128-byte bank window and rows r..r+15 in 16
-// distinct slots of a 256-byte window.
-//   8 chunks per row (128-byte rows): (r & 7) ^ ((r >> 3) & 1)
-//   4 chunks per row (64-byte rows, two rows per 128 bytes): ((r >> 1) ^ (r >> 2)) & 3
-template <int CPR>
-__device__ __forceinline__ uint32_t swz_a(uint32_t r) {
-    if constexpr (CPR == 8) return (r & 7u) ^ ((r >> 3) & 1u);
-    else return ((r >> 1) ^ (r >> 2)) & 3u;
-}
-
-// B tile: K row k holds CPR_B chunks; chunk c is stored at c ^ swz_b(k).
-//  16-bit: a transposing read touches 4 consecutive K rows x 2 (or 4) chunks;
-//          swz values {0,6,12,10} put them in distinct banks.
-//  8-bit:  it touches 8 consecutive K rows x 1 (or 2) chunks; swz = Gray-like
-//          (r ^ 2r) spreads them over distinct banks.
-template <int ES>
-__device__ __forceinline__ uint32_t swz_b(uint32_t k) {
-    if constexpr (ES == 2) {
-        const uint32_t r = k & 3u;
-        return (r ^ (r << 1)) << 1;
-    } else {
-        const uint32_t r = k & 7u;
-        return (r ^ (r << 1)) & 15u;
-    }
-}
-
-template <class C>
-__device__ __forceinline__ uint32_t a_off(uint32_t r, uint32_t c) {
-    return r * C::KT_BYTES + ((c ^ swz_a<C::CPR_A>(r)) << 4);
-}
-template <class C>
-__device__ __forceinline__ uint32_t b_off(uint32_t k, uint32_t c) {
-    return k * C::B_ROW + ((c ^ swz_b<C::ES>(k)) << 4);
-}
-
-// ---------------------------------------------------------------------------
-// Workgroup -> output tile.  Workgroups are handed to the 8 XCDs round-robin;
-// the first 8*floor(T/8) ids are renumbered so that each XCD receives a
-// contiguous run of tiles, and runs are laid out in groups of GROUP_M tile
-// rows so an XCD's concurrent tiles share A row panels and B column panels in
-// its own L2.
-// ---------------------------------------------------------------------------
-constexpr int NUM_XCD = 8;
-constexpr int GROUP_M = 4;
-
-__device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int& tm, int& tn) {
-    const int total = tiles_m * tiles_n;
-    const int per = total / NUM_XCD;
-    int t = wg;
-    if (wg < per * NUM_XCD) t = (wg % NUM_XCD) * per + wg / NUM_XCD;
-    const int group_size = GROUP_M * tiles_n;
-    const int group = t / group_size;
-    const int first_m = group * GROUP_M;
-    const int gsz = min(tiles_m - first_m, GROUP_M);
-    const int in_group = t - group * group_size;
-    tm = first_m + in_group % gsz;
-    tn = in_group / gsz;
-}
 
 // ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
-struct Stage {
-    MPDT_LDS char* A;
-    MPDT_LDS char* B;
-    MPDT_LDS float* S;   // FP8: per-row A scales of the staged K tile
-};
-
-// s_waitcnt vmcnt(N): at most N vector-memory operations of this wave
-// (direct-to-LDS loads included) are still in flight.  Memory reads retire in
-// issue order, so this waits for all but the N most recent.
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
-// s_waitcnt lgkmcnt(0): this wave's LDS reads and writes have completed.
-__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
-// Workgroup barrier without a memory fence.  (A fence would make the compiler
-// drain every direct-to-LDS load in flight, defeating the multi-stage
-// pipeline.)  LDS visibility is managed explicitly: a wave waits for its own
-// LDS writes (wait_lds) or direct loads (wait_vmem) before the barrier.  The
-// signal fences keep the compiler from moving memory accesses across it and
-// sched_barrier keeps the scheduler from moving anything across it.
-__device__ __forceinline__ void wg_barrier() {
-    __builtin_amdgcn_sched_barrier(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-// Compile-time loop: f(integral_constant<int, I>) for I in [B, E).
-template <int B, int E, class Fn>
-__device__ __forceinline__ void static_for(Fn&& f) {
-    if constexpr (B < E) {
-        f(std::integral_constant<int, B>{});
-        static_for<B + 1, E>(f);
-    }
-}
-
 template <Kind KD, class C, bool ALIGNED>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::NT / 256, C::NT / 256)))
 void gemm_kernel(GemmArgs g) {
@@ -267,12 +69,17 @@ void gemm_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(1024))) char sB0[C::B_BYTES];
     __shared__ __attribute__((aligned(1024))) char sA1[C::A_BYTES + C::SA_BYTES];
     __shared__ __attribute__((aligned(1024))) char sB1[C::B_BYTES];
-    __shared__ __attribute__((aligned(NS > 2 ? 1024 : 16))) char sA2[NS > 2 ? C::A_BYTES : 16];
+    __shared__ __attribute__((aligned(NS > 2 ? 1024 : 16))) char sA2[NS > 2 ? C::A_BYTES + C::SA_BYTES : 16];
     __shared__ __attribute__((aligned(NS > 2 ? 1024 : 16))) char sB2[NS > 2 ? C::B_BYTES : 16];
-    __shared__ __attribute__((aligned(NS > 3 ? 1024 : 16))) char sA3[NS > 3 ? C::A_BYTES : 16];
+    __shared__ __attribute__((aligned(NS > 3 ? 1024 : 16))) char sA3[NS > 3 ? C::A_BYTES + C::SA_BYTES : 16];
     __shared__ __attribute__((aligned(NS > 3 ? 1024 : 16))) char sB3[NS > 3 ? C::B_BYTES : 16];
-    __shared__ __attribute__((aligned(NS > 4 ? 1024 : 16))) char sA4[NS > 4 ? C::A_BYTES : 16];
+    __shared__ __attribute__((aligned(NS > 4 ? 1024 : 16))) char sA4[NS > 4 ? C::A_BYTES + C::SA_BYTES : 16];
     __shared__ __attribute__((aligned(NS > 4 ? 1024 : 16))) char sB4[NS > 4 ? C::B_BYTES : 16];
+    // FP8 keeps the A-row scales of a stage's K tile right after its A tile.
+    auto scales_of = [&](char* a) -> MPDT_LDS float* {
+        if constexpr (C::SA_BYTES > 0) return (MPDT_LDS float*)(lds_cast(a) + C::A_BYTES);
+        else return nullptr;
+    };
     // stage(I): the LDS buffers of stage I (a compile-time index, so that
     // every access names its buffer object directly).
     auto stage = [&](auto I) -> Stage {
@@ -280,11 +87,11 @@ void gemm_kernel(GemmArgs g) {
         if constexpr (ONE_WAVE)
             return {lds_cast(sA0) + i * STAGE_BYTES, lds_cast(sA0) + i * STAGE_BYTES + C::A_BYTES,
                     nullptr};
-        else if constexpr (i == 0) return {lds_cast(sA0), lds_cast(sB0), (MPDT_LDS float*)(sA0 + C::A_BYTES)};
-        else if constexpr (i == 1) return {lds_cast(sA1), lds_cast(sB1), (MPDT_LDS float*)(sA1 + C::A_BYTES)};
-        else if constexpr (i == 2) return {lds_cast(sA2), lds_cast(sB2), nullptr};
-        else if constexpr (i == 3) return {lds_cast(sA3), lds_cast(sB3), nullptr};
-        else return {lds_cast(sA4), lds_cast(sB4), nullptr};
+        else if constexpr (i == 0) return {lds_cast(sA0), lds_cast(sB0), scales_of(sA0)};
+        else if constexpr (i == 1) return {lds_cast(sA1), lds_cast(sB1), scales_of(sA1)};
+        else if constexpr (i == 2) return {lds_cast(sA2), lds_cast(sB2), scales_of(sA2)};
+        else if constexpr (i == 3) return {lds_cast(sA3), lds_cast(sB3), scales_of(sA3)};
+        else return {lds_cast(sA4), lds_cast(sB4), scales_of(sA4)};
     };
     // Same with a run-time index (folds to a constant inside unrolled loops).
     auto stage_rt = [&](int i) -> Stage {
@@ -292,7 +99,8 @@ void gemm_kernel(GemmArgs g) {
                 : i == 3 ? lds_cast(sA3) : lds_cast(sA4),
                 i == 0 ? lds_cast(sB0) : i == 1 ? lds_cast(sB1) : i == 2 ? lds_cast(sB2)
                 : i == 3 ? lds_cast(sB3) : lds_cast(sB4),
-                (i & 1) ? (MPDT_LDS float*)(sA1 + C::A_BYTES) : (MPDT_LDS float*)(sA0 + C::A_BYTES)};
+                i == 0 ? scales_of(sA0) : i == 1 ? scales_of(sA1) : i == 2 ? scales_of(sA2)
+                : i == 3 ? scales_of(sA3) : scales_of(sA4)};
     };
     using I0 = std::integral_constant<int, 0>;
 
@@ -1043,6 +851,21 @@ template <Kind KD> using Cfg1W = Cfg<KD, 256, 256, 2, 2, 64, 4>;
 // eight wavefronts, everything else
 template <Kind KD> using Cfg8W = Cfg<KD, 256, 256, 2, 4, 64, 4>;
 using CfgFP8 = Cfg<Kind::FP8, 128, 256, 2, 4, 128, 2>;
+static_assert(CfgFP8::BM == FP8_TILE_M && CfgFP8::BN == FP8_TILE_N, "one tile grid for both FP8 kernels");
+
+// FP8: the full tiles of a problem the one-wave kernel takes (gemm_fp8.hip)
+// go to it, the edge tiles and every other problem to the general kernel.
+static hipError_t launch_fp8(const GemmArgs& a0, bool aligned, hipStream_t stream) {
+    const bool one = fp8_1w_eligible(a0, aligned);
+    const int int_tm = one ? a0.M / FP8_TILE_M : 0;
+    const int int_tn = one ? a0.N / FP8_TILE_N : 0;
+    if (int_tm > 0 && int_tn > 0) {
+        const hipError_t e = launch_fp8_1w(a0, int_tm, int_tn, stream);
+        if (e != hipSuccess) return e;
+        return launch_general<Kind::FP8, CfgFP8>(a0, aligned, int_tm, int_tn, stream);
+    }
+    return launch_general<Kind::FP8, CfgFP8>(a0, aligned, 0, 0, stream);
+}
 
 hipError_t launch_gemm(Kind kind, const GemmArgs& a, bool aligned, hipStream_t stream) {
     switch (kind) {
@@ -1050,7 +873,7 @@ hipError_t launch_gemm(Kind kind, const GemmArgs& a, bool aligned, hipStream_t s
         case Kind::BF16:
             return launch_mma<Kind::BF16, Cfg1W<Kind::BF16>, Cfg8W<Kind::BF16>>(a, aligned, stream);
         case Kind::I8: return launch_mma<Kind::I8, Cfg1W<Kind::I8>, Cfg8W<Kind::I8>>(a, aligned, stream);
-        case Kind::FP8: return launch_general<Kind::FP8, CfgFP8>(a, aligned, 0, 0, stream);
+        case Kind::FP8: return launch_fp8(a, aligned, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -30,6 +30,12 @@ struct GemmArgs {
 // aligned: every row start of A and B is 16-byte aligned.
 hipError_t launch_gemm(Kind kind, const GemmArgs& a, bool aligned, hipStream_t stream);
 
+// FP8 one-wavefront kernel (gemm_fp8.hip) over the full FP8_TILE_M x
+// FP8_TILE_N tiles of a problem it takes (fp8_1w_eligible).
+constexpr int FP8_TILE_M = 128, FP8_TILE_N = 256;
+bool fp8_1w_eligible(const GemmArgs& a, bool aligned);
+hipError_t launch_fp8_1w(const GemmArgs& a, int tiles_m, int tiles_n, hipStream_t stream);
+
 struct GemvArgs {
     const int8_t* x;
     const int8_t* W;

@@ -211,8 +211,13 @@ def run_fp8(qa, sa, qb, sb, lda=None, ldb=None):
     return got, R, S
 
 
+# Full 128 x 256 tiles with whole 128-wide K blocks (at least three) go to the
+# one-wavefront kernel, the rest (edge tiles, short or ragged K) to the
+# general one: (256, 512, 384) and (384, 768, 512) are all one-wave tiles with
+# the fewest K blocks it takes, (300, 600, 768) mixes both kernels in one call.
 @pytest.mark.parametrize("M,N,K", [(128, 256, 256), (300, 520, 400), (129, 130, 131),
-                                   (1, 1, 1), (256, 512, 1024)])
+                                   (1, 1, 1), (256, 512, 1024), (256, 512, 384),
+                                   (384, 768, 512), (300, 600, 768)])
 def test_fp8_parity(gpu_ok, M, N, K):
     qa, sa, qb, sb = inputs.fp8_operands(M, N, K, seeds=(M, N))
     got, R, S = run_fp8(qa, sa, qb, sb)
@@ -227,6 +232,28 @@ def test_fp8_unaligned_and_unit_scales(gpu_ok):
     ones_a, ones_b = np.ones_like(sa), np.ones_like(sb)
     got, R, S = run_fp8(qa, ones_a, qb, ones_b)
     check_fp(got, R, S, 1e-2, "fp8 unit scales", bf16_out=True)
+
+
+def test_fp8_padded_scales_and_output(gpu_ok):
+    """Scale matrices and D with leading dimensions wider than their rows.  A
+    16-byte aligned D (ldd a multiple of 8) keeps the interior tiles on the
+    one-wavefront kernel; an odd ldd sends the whole problem to the general
+    kernel.  Both must agree with the oracle."""
+    M, N, K = 256, 768, 640
+    qa, sa, qb, sb = inputs.fp8_operands(M, N, K, seeds=(31, 32))
+    R, S = oracle.gemm_fp8_blockscaled(qa, sa, qb, sb)
+    ta, tb = dev(qa), dev(qb)
+    tsa = dev(sa, sa.shape[1] + 3, pad=np.float32(1e30))
+    tsb = dev(sb, sb.shape[1] + 2, pad=np.float32(-1e30))
+    for ldd in (N + 8, N + 3):
+        buf = torch.full((M, ldd), -1, dtype=torch.int16, device=gpu_ok).view(torch.bfloat16)
+        out = buf[:, :N]
+        mp.gemm_fp8_blockscaled(ta, tsa, tb, tsb, out=out)
+        torch.cuda.synchronize()
+        whole = host(buf).view(np.uint16)
+        assert (whole[:, N:] == 0xFFFF).all(), f"ldd {ldd}: padding of D was written"
+        got = oracle.bf16_to_f64(whole[:, :N])
+        check_fp(got, R, S, 1e-2, f"fp8 padded ldd={ldd}", bf16_out=True)
 
 
 def test_fp8_k_zero(gpu_ok):
