@@ -39,17 +39,21 @@ namespace mpdt {
 // s1(i1, j) (i: 32-row tile, j: 32-column tile) with four block accumulators
 // blk[j], reused by both row tiles:
 //   slots 0-3   promote blk[j] of row tile 1 of K tile t-1, then s0(i0, j);
-//   slots 4-7   s1(i0, j); read row tile 1's A fragments and the scales;
+//   slots 4-7   s1(i0, j); read the rest of tile t's fragments and its scales;
 //   wait for this wave's direct loads of tile t+1 and its LDS reads, then a
 //   workgroup barrier: tile t+1 is in LDS and tile t's stage is free;
 //   slots 8-11  promote blk[j] of row tile 0, then s0(i1, j);
-//   slots 12-15 s1(i1, j);
-//   slots 8-15 also issue the direct loads of tile t+NS into tile t's stage
-//   and read tile t+1's fragments for slots 0-7 as their registers free up.
-// Every K tile issues the same 14 direct loads per wave (four 1 KiB A pieces,
-// eight B pieces, the wave's 64 A-row scales and its B scale); past the last
-// tile they read an empty buffer range, so the vmcnt arithmetic never changes
-// and the loop body is one basic block whose order scheduling barriers pin.
+//   slots 12-15 s1(i1, j); the direct loads of tile t+NS into tile t's stage;
+//               tile t+1's fragments for slots 0-7 (their registers are free).
+// One wave issues one instruction per four cycles and a 64-cycle MFMA covers
+// sixteen: the 16 FMAs of a promotion fill the slots they sit in, so the LDS
+// reads, direct loads and scalar work go to the other slots.  The K loop is
+// unrolled by the number of stages so every LDS address and M0 value is a
+// constant.  Every K tile issues the same 13 direct loads per wave (four 1
+// KiB A pieces, eight B pieces and one scale load: waves 0 and 1 fetch the
+// A-row scales of rows 0-63 and 64-127, waves 2 and 3 the two B scales);
+// past the last tile they read an empty buffer range, so the vmcnt
+// arithmetic never changes.
 template <class C>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_fp8_1w_kernel(GemmArgs g) {
@@ -59,9 +63,9 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
                       C::STEPS == 2 && C::UA == 4 && C::UB == 8 && C::B_ROW == 256,
                   "128 x 256 tile, 2 x 2 waves, one 128-byte K tile per scale block");
     constexpr int NS = C::STAGES;
-    constexpr int SC_OFF = C::A_BYTES + C::B_BYTES;   // per wave: 256 B A-row scales, 256 B B scale
-    constexpr int STAGE_BYTES = SC_OFF + 4 * 512;
-    constexpr int DMA_PER_TILE = C::UA + C::UB + 2;
+    constexpr int SC_OFF = C::A_BYTES + C::B_BYTES;   // 4 scale regions of 256 B
+    constexpr int STAGE_BYTES = SC_OFF + 4 * 256;
+    constexpr int DMA_PER_TILE = C::UA + C::UB + 1;
     constexpr int WAIT_AHEAD = (NS - 2) * DMA_PER_TILE;   // loads of tiles t+2..t+NS-1
     static_assert(NS >= 2 && NS * STAGE_BYTES <= 163840, "LDS budget");
     __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE_BYTES];
@@ -86,7 +90,10 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
     // u: K rows (8 wave + u) * 4 .. +3.  The A swizzle repeats every 16 rows and
     // the B swizzle every 8 K rows, so even and odd pieces have one lane offset
     // each.  Pieces sharing an M0 value move through the instruction offset,
-    // which the scalar offset takes back off the global address.
+    // which the scalar offset takes back off the global address.  Each buffer
+    // resource starts at the K tile's first byte and spans exactly the bytes
+    // the tile reads (all inside the operand for a full tile), or nothing
+    // past the last tile.
     constexpr int RPA = 1024 / C::KT_BYTES, RPB = 1024 / C::B_ROW;
     const uint32_t lda = (uint32_t)g.lda_b, ldb = (uint32_t)g.ldb_b;
     const int lra = lane / C::CPR_A, lrb = lane / C::CPR_B;
@@ -98,55 +105,55 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
         voffB[p] = (uint32_t)lrb * ldb +
                    (((uint32_t)(lane % C::CPR_B) ^ swz_b<1>(p * RPB + lrb)) << 4);
     }
-    // scales: lane l fetches the A-row scale of row (l >> 1) + 32 (l & 1) of the
-    // wave's 64 rows, so a lane later finds rows r and r + 32 side by side
-    const uint32_t voffSA = (uint32_t)((lane >> 1) + 32 * (lane & 1)) * (uint32_t)g.ld_sa * 4u;
-    const uint32_t vzero = 0;
-    auto soffA = [&](int u) {
+    auto soffA = [&](int u) __attribute__((always_inline)) {
         return (uint32_t)((wave * C::UA + u) * RPA) * lda - (uint32_t)(u & 3) * 1024u;
     };
-    auto soffB = [&](int u) {
+    auto soffB = [&](int u) __attribute__((always_inline)) {
         return (uint32_t)((wave * C::UB + u) * RPB) * ldb - (uint32_t)(u & 3) * 1024u;
     };
-    const int nkb = nt, ncb = (g.N + 127) / 128;
-    const int nb = (n0 + wn * C::WN) / 128;
-    const uint64_t baseA = (uint64_t)(uintptr_t)g.A + (uint64_t)((int64_t)m0 * g.lda_b);
-    const uint64_t baseB = (uint64_t)(uintptr_t)g.B + (uint64_t)n0;
-    const int64_t restA0 = ((int64_t)(g.M - 1) * g.lda_b + g.K) - (int64_t)m0 * g.lda_b;
-    const int64_t restB0 = ((int64_t)(g.K - 1) * g.ldb_b + g.N) - n0;
-    const int64_t stepB = (int64_t)C::KROWS * g.ldb_b;
-    const int64_t saFirst = (int64_t)(m0 + wm * C::WM) * g.ld_sa * 4;
-    const uint64_t baseSA = (uint64_t)(uintptr_t)g.sA + (uint64_t)saFirst;
-    const int64_t restSA0 = ((int64_t)(g.M - 1) * g.ld_sa + nkb) * 4 - saFirst;
-    const uint64_t baseSB = (uint64_t)(uintptr_t)g.sB + (uint64_t)nb * 4;
-    const int64_t restSB0 = ((int64_t)(nkb - 1) * g.ld_sb + ncb) * 4 - (int64_t)nb * 4;
-    const int64_t stepSB = g.ld_sb * 4;
-    auto clamp31 = [](int64_t r) { return (uint32_t)(r > 0x7fffffff ? 0x7fffffff : r); };
+    const uint32_t rangeA = (uint32_t)(C::BM - 1) * lda + C::KT_BYTES;
+    const uint32_t rangeB = (uint32_t)(C::KROWS - 1) * ldb + C::B_ROW;
+    uint64_t baseA = (uint64_t)(uintptr_t)g.A + (uint64_t)((int64_t)m0 * g.lda_b);
+    uint64_t baseB = (uint64_t)(uintptr_t)g.B + (uint64_t)n0;
+    const uint64_t stepB = (uint64_t)C::KROWS * (uint64_t)g.ldb_b;
+    // Scale loads (one per wave and K tile, 64 lanes into the wave's 256-byte
+    // region of the stage).  Waves 0, 1: A-row scales of rows 64 w .. 64 w + 63,
+    // lane l taking row (l >> 1) + 32 (l & 1), so that rows q and q + 32 sit
+    // side by side.  Waves 2, 3: the B scales of the tile's two 128-column
+    // blocks, lane l taking block l & 1.
+    const bool scaleA = wave < 2;
+    const uint32_t ldsa4 = (uint32_t)g.ld_sa * 4u;
+    const uint32_t voffS = scaleA ? (uint32_t)((lane >> 1) + 32 * (lane & 1)) * ldsa4
+                                  : (uint32_t)(lane & 1) * 4u;
+    const uint32_t rangeS = scaleA ? 63u * ldsa4 + 4u : 8u;
+    uint64_t baseS = scaleA ? (uint64_t)(uintptr_t)g.sA + (uint64_t)((int64_t)(m0 + wave * 64) * ldsa4)
+                            : (uint64_t)(uintptr_t)g.sB + (uint64_t)(n0 / 128) * 4u;
+    const uint64_t stepS = scaleA ? 4u : (uint64_t)g.ld_sb * 4u;
     struct Rs {
-        i32x4 a, b, sa, sb;
+        i32x4 a, b, s;
     };
-    // resources of K tile kt (offsets kt * 128 in A, kt * stepB in B, kt * 4 in
-    // the A scales, kt * stepSB in the B scales); a dead tile gets range 0
-    auto rs_tile = [&](int64_t kA, int64_t kB, int64_t kSA, int64_t kSB, bool live) -> Rs {
-        return {rsrc_words(baseA + (uint64_t)kA, live ? clamp31(restA0 - kA) : 0u),
-                rsrc_words(baseB + (uint64_t)kB, live ? clamp31(restB0 - kB) : 0u),
-                rsrc_words(baseSA + (uint64_t)kSA, live ? clamp31(restSA0 - kSA) : 0u),
-                rsrc_words(baseSB + (uint64_t)kSB, live ? clamp31(restSB0 - kSB) : 0u)};
+    auto rs_next = [&](bool live) __attribute__((always_inline)) -> Rs {   // resources of the next K tile to load
+        const Rs r = {rsrc_words(baseA, live ? rangeA : 0u), rsrc_words(baseB, live ? rangeB : 0u),
+                      rsrc_words(baseS, live ? rangeS : 0u)};
+        baseA += C::KT_BYTES;
+        baseB += stepB;
+        baseS += stepS;
+        return r;
     };
-    auto dma_piece = [&](auto P, const Rs& r, uint32_t stage_off) {
+    const uint32_t vzero = 0;
+    auto dma_piece = [&](auto P, const Rs& r, auto STG) __attribute__((always_inline)) {
         constexpr int p = decltype(P)::value;
-        MPDT_LDS char* const st = lds0 + stage_off;
+        MPDT_LDS char* const st = lds0 + decltype(STG)::value * STAGE_BYTES;
         if constexpr (p < C::UA) {
             lds_dma16<p * 1024, p == 0>(r.a, st + wave * (C::UA * 1024), voffA[p & 1], soffA(p));
         } else if constexpr (p < C::UA + C::UB) {
             constexpr int u = p - C::UA;   // two M0 groups of four pieces
             lds_dma16<(u & 3) * 1024, (u & 3) == 0>(
                 r.b, st + C::A_BYTES + wave * (C::UB * 1024) + (u >> 2) * 4096, voffB[u & 1], soffB(u));
-        } else if constexpr (p == C::UA + C::UB) {
-            lds_dma4<0, true>(r.sa, st + SC_OFF + wave * 512, voffSA, 0u);
         } else {
-            lds_dma4<0, true>(r.sb, st + SC_OFF + wave * 512 + 256, vzero, 0u);
+            lds_dma4<0, true>(r.s, st + SC_OFF + wave * 256, voffS, 0u);
         }
+        (void)vzero;
     };
 
     // ---- fragment reads -----------------------------------------------------
@@ -165,20 +172,20 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
         const uint32_t col16 = wn * C::WN + j * 32 + 16 * (grp & 1);
         lb[j] = C::A_BYTES + b_off<C>(32 * (grp >> 1) + (gp >> 1), col16 >> 4) + 8 * (gp & 1);
     }
-    const uint32_t lsa = SC_OFF + wave * 512 + 8 * lrow;   // rows lrow and lrow + 32
-    const uint32_t lsb = SC_OFF + wave * 512 + 256;
+    const uint32_t lsa = SC_OFF + wm * 256 + 8 * lrow;      // A-row scales of rows lrow, lrow + 32
+    const uint32_t lsb = SC_OFF + 2 * 256 + 4 * wn;         // this wave's B scale
     constexpr uint32_t QB = 64 * C::B_ROW, HB = 8 * C::B_ROW;
 
     struct Fr {
         u32x4 a[2][2][2];   // [row tile][step][16-byte half]
         u32x2 b[2][4][4];   // [step][column tile][8-row read]
     } fr;
-    auto rdA = [&](int i, int s, uint32_t so) {
+    auto rdA = [&](int i, int s, uint32_t so) __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < 2; ++q)
             fr.a[i][s][q] = lds_load16(lds0, so + la[s][q] + (uint32_t)(i * 32 * C::KT_BYTES));
     };
-    auto rdB = [&](int s, int j, uint32_t so) {
+    auto rdB = [&](int s, int j, uint32_t so) __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 0; h < 4; ++h) fr.b[s][j][h] = lds_read_tr8(lds0, so + lb[j] + s * QB + h * HB);
     };
@@ -195,7 +202,7 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
     }
     float f[2] = {0.0f, 0.0f};   // sa * sb of the row tiles being promoted
     // slot n's MFMA: step (n >> 2) & 1, row tile n >> 3, column tile n & 3
-    auto mfma = [&](int n) {
+    auto mfma = [&](int n) __attribute__((always_inline)) {
         const int s = (n >> 2) & 1, i = n >> 3, j = n & 3;
         i32x8 a8, b8;
 #pragma unroll
@@ -210,50 +217,101 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
             blk[j] = F::mma(b8, a8, blk[j]);
         }
     };
-    auto promote = [&](int i, int j) {
+    auto promote = [&](int i, int j) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(blk[j][r], f[i], acc[i][j][r]);
     };
     u32x2 sap;
     float sbv;
-    auto read_scales = [&](uint32_t so) {
+    auto read_scales = [&](uint32_t so) __attribute__((always_inline)) {
         sap = *reinterpret_cast<const MPDT_LDS u32x2*>(lds0 + so + lsa);
         sbv = *reinterpret_cast<const MPDT_LDS float*>(lds0 + so + lsb);
     };
-    auto make_f = [&]() {
+    auto make_f = [&]() __attribute__((always_inline)) {
         const uint32_t s0 = sap[0], s1 = sap[1];
         f[0] = __uint_as_float(s0) * sbv;
         f[1] = __uint_as_float(s1) * sbv;
     };
-    // slots 0..7 of a K tile whose stage is at `cur`
-    auto phase_x = [&](uint32_t cur) {
-        static_for<0, 8>([&](auto N) {
+
+    // Slots 0..7 of K tile t in stage S: promotions of the previous tile's row
+    // tile 1 in slots 0-3; the last five direct loads of tile t-1+NS (into
+    // stage S-1) in slots 0-4; tile t's remaining fragments and its scales in
+    // slots 4-6 (their registers were last used in slots 7 and 11-15 of tile
+    // t-1); the resources of tile t+NS in slot 5.
+    Rs rs;
+    auto phase_x = [&](auto STG, bool live_next) __attribute__((always_inline)) {
+        constexpr uint32_t cur = decltype(STG)::value * STAGE_BYTES;
+        using PREV = std::integral_constant<int, (decltype(STG)::value + NS - 1) % NS>;
+        static_for<0, 8>([&](auto N) __attribute__((always_inline)) {
             constexpr int n = decltype(N)::value;
             if constexpr (n < 4) promote(1, n);
             mfma(n);
-            if constexpr (n == 0) rdB(1, 3, cur);
-            if constexpr (n == 1) rdA(1, 0, cur);
-            if constexpr (n == 2) rdA(1, 1, cur);
-            if constexpr (n == 4) read_scales(cur);
+            if constexpr (n <= 4) dma_piece(std::integral_constant<int, 8 + n>{}, rs, PREV{});
+            if constexpr (n == 4) { rdB(1, 3, cur); read_scales(cur); }
+            if constexpr (n == 5) { rdA(1, 0, cur); rs = rs_next(live_next); }
+            if constexpr (n == 6) rdA(1, 1, cur);
             if constexpr (n == 7) make_f();
             __builtin_amdgcn_sched_barrier(0);
         });
     };
-
-    // ---- prologue: tiles 0..NS-1 into stages 0..NS-1 ------------------------
-    int64_t kA = 0, kB = 0, kSA = 0, kSB = 0;
+    // Slots 8..15 of a K tile in stage S that is followed by another: the
+    // barrier, promotions of row tile 0 in slots 8-11; one direct load of
+    // tile t+NS into stage S per slot (the first eight of its 13: a direct
+    // load occupies the CU's address unit for 16 cycles, so four waves
+    // issuing one per 64-cycle MFMA slot keep it just below saturation); in
+    // slots 12-15 the reads of tile t+1's fragments for its slots 0-7 from
+    // stage S+1.
+    auto phase_y = [&](auto STG) __attribute__((always_inline)) {
+        constexpr int S = decltype(STG)::value;
+        constexpr uint32_t nxt = ((S + 1) % NS) * STAGE_BYTES;
+        wait_vmem<WAIT_AHEAD>();
+        wait_lds();
+        wg_barrier();
+        static_for<8, 16>([&](auto N) __attribute__((always_inline)) {
+            constexpr int n = decltype(N)::value;
+            if constexpr (n < 12) promote(0, n - 8);
+            mfma(n);
+            dma_piece(std::integral_constant<int, n - 8>{}, rs, STG);
+            if constexpr (n == 12) {
+                rdA(0, 0, nxt);
+                rdB(0, 0, nxt);
+                rdB(0, 1, nxt);
+            }
+            if constexpr (n == 13) {
+                rdB(0, 2, nxt);
+                rdB(0, 3, nxt);
+            }
+            if constexpr (n == 14) {
+                rdA(0, 1, nxt);
+                rdB(1, 0, nxt);
+                rdB(1, 1, nxt);
+            }
+            if constexpr (n == 15) rdB(1, 2, nxt);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    auto last_tile = [&](auto STG) __attribute__((always_inline)) {
+        phase_x(STG, false);
+        static_for<8, 16>([&](auto N) __attribute__((always_inline)) {
+            constexpr int n = decltype(N)::value;
+            if constexpr (n < 12) promote(0, n - 8);
+            mfma(n);
+            __builtin_amdgcn_sched_barrier(0);
+        });
 #pragma unroll
-    for (int p = 0; p < NS; ++p) {
-        const Rs r = rs_tile(kA, kB, kSA, kSB, true);
-        static_for<0, DMA_PER_TILE>([&](auto Q) { dma_piece(Q, r, (uint32_t)(p * STAGE_BYTES)); });
-        kA += C::KT_BYTES;
-        kB += stepB;
-        kSA += 4;
-        kSB += stepSB;
-    }
-    wait_vmem<(NS - 1) * DMA_PER_TILE>();
+        for (int j = 0; j < 4; ++j) promote(1, j);
+    };
+
+    // ---- prologue: tiles 0..NS-1 into stages 0..NS-1 (the last five loads of
+    // tile NS-1 are issued by tile 0's slots 0-4, as in the steady state) ---
+    static_for<0, NS>([&](auto P) __attribute__((always_inline)) {
+        rs = rs_next(true);
+        constexpr int np = decltype(P)::value == NS - 1 ? 8 : DMA_PER_TILE;
+        static_for<0, np>([&](auto Q) __attribute__((always_inline)) { dma_piece(Q, rs, P); });
+    });
+    wait_vmem<(NS - 2) * DMA_PER_TILE + 8>();
     wg_barrier();
-    // the reads a previous tile's slots 8..15 would have made
+    // the reads a previous tile's slots 12..15 would have made
     rdA(0, 0, 0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) rdB(0, j, 0);
@@ -261,51 +319,26 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 3; ++j) rdB(1, j, 0);
 
-    int scur = 0;
-    for (int t = 0; t < nt - 1; ++t) {
-        const int snext = scur + 1 == NS ? 0 : scur + 1;
-        const uint32_t cur = (uint32_t)scur * STAGE_BYTES;
-        const uint32_t nxt = (uint32_t)snext * STAGE_BYTES;
-        const Rs rs = rs_tile(kA, kB, kSA, kSB, t + NS < nt);   // tile t+NS
-        phase_x(cur);
-        wait_vmem<WAIT_AHEAD>();
-        wait_lds();
-        wg_barrier();
-        static_for<8, 16>([&](auto N) {
-            constexpr int n = decltype(N)::value;
-            if constexpr (n < 12) promote(0, n - 8);
-            mfma(n);
-            // direct loads of tile t+NS into this tile's stage
-            if constexpr (n < 14) {
-                dma_piece(std::integral_constant<int, 2 * (n - 8)>{}, rs, cur);
-                dma_piece(std::integral_constant<int, 2 * (n - 8) + 1>{}, rs, cur);
-            } else {
-                dma_piece(std::integral_constant<int, 12 + (n - 14)>{}, rs, cur);
-            }
-            // tile t+1's fragments for slots 0..7, as their registers free up
-            if constexpr (n == 8) rdA(0, 0, nxt);
-            if constexpr (n >= 9 && n <= 12) rdB(0, n - 9, nxt);
-            if constexpr (n == 13) { rdA(0, 1, nxt); rdB(1, 0, nxt); }
-            if constexpr (n == 14) rdB(1, 1, nxt);
-            if constexpr (n == 15) rdB(1, 2, nxt);
-            __builtin_amdgcn_sched_barrier(0);
+    // ---- K loop, unrolled by NS (stage of tile t = t % NS) ------------------
+    int t = 0;
+    for (; t + NS <= nt - 1; t += NS) {
+        static_for<0, NS>([&](auto S) __attribute__((always_inline)) {
+            phase_x(S, t + decltype(S)::value + NS < nt);
+            phase_y(S);
         });
-        scur = snext;
-        kA += C::KT_BYTES;
-        kB += stepB;
-        kSA += 4;
-        kSB += stepSB;
     }
-    // last K tile
-    phase_x((uint32_t)scur * STAGE_BYTES);
-    static_for<8, 16>([&](auto N) {
-        constexpr int n = decltype(N)::value;
-        if constexpr (n < 12) promote(0, n - 8);
-        mfma(n);
-        __builtin_amdgcn_sched_barrier(0);
+    static_for<0, NS - 1>([&](auto S) __attribute__((always_inline)) {
+        if (t < nt - 1) {
+            phase_x(S, t + NS < nt);
+            phase_y(S);
+            ++t;
+        }
     });
-#pragma unroll
-    for (int j = 0; j < 4; ++j) promote(1, j);
+    // t == nt - 1: the last tile, in stage t % NS
+    const int sl = t % NS;
+    if (sl == 0) last_tile(std::integral_constant<int, 0>{});
+    else if (sl == 1) last_tile(std::integral_constant<int, 1>{});
+    else last_tile(std::integral_constant<int, (NS > 2 ? 2 : 1)>{});
     // the empty-range loads of the last tiles still write (zeros) to LDS
     wait_vmem<0>();
 
