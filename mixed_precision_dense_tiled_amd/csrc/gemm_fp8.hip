@@ -39,21 +39,26 @@ namespace mpdt {
 // s1(i1, j) (i: 32-row tile, j: 32-column tile) with four block accumulators
 // blk[j], reused by both row tiles:
 //   slots 0-3   promote blk[j] of row tile 1 of K tile t-1, then s0(i0, j);
-//   slots 4-7   s1(i0, j); read the rest of tile t's fragments and its scales;
+//   slots 4-7   s1(i0, j); read the rest of tile t's fragments;
 //   wait for this wave's direct loads of tile t+1 and its LDS reads, then a
 //   workgroup barrier: tile t+1 is in LDS and tile t's stage is free;
 //   slots 8-11  promote blk[j] of row tile 0, then s0(i1, j);
-//   slots 12-15 s1(i1, j); the direct loads of tile t+NS into tile t's stage;
-//               tile t+1's fragments for slots 0-7 (their registers are free).
-// One wave issues one instruction per four cycles and a 64-cycle MFMA covers
-// sixteen: the 16 FMAs of a promotion fill the slots they sit in, so the LDS
-// reads, direct loads and scalar work go to the other slots.  The K loop is
-// unrolled by the number of stages so every LDS address and M0 value is a
-// constant.  Every K tile issues the same 13 direct loads per wave (four 1
-// KiB A pieces, eight B pieces and one scale load: waves 0 and 1 fetch the
-// A-row scales of rows 0-63 and 64-127, waves 2 and 3 the two B scales);
-// past the last tile they read an empty buffer range, so the vmcnt
-// arithmetic never changes.
+//   slots 12-15 s1(i1, j); read tile t+1's scales and its fragments for
+//               slots 0-7 (their registers are free by then).
+// The 13 direct loads of tile t+NS (into tile t's stage) go one per slot over
+// slots 8-15 of tile t and 0-4 of tile t+1: a 1 KiB direct load keeps the
+// CU's address unit busy for 16 cycles, so four waves issuing one per
+// 64-cycle MFMA slot stay just below its rate, where bursts stalled the
+// issuing waves.  A wave issues one instruction per four cycles and a
+// 64-cycle MFMA covers sixteen: the 16 FMAs of a promotion fill the slot they
+// sit in, so the LDS reads and scalar work go to the other slots.  The K loop
+// is unrolled by the number of stages and LDS holds the A tiles of all
+// stages, then the B tiles, then the scales, so every LDS address and M0
+// value is a base register or constant plus an immediate.  Every K tile
+// issues the same 13 direct loads per wave (four 1 KiB A pieces, eight B
+// pieces and one scale load: waves 0 and 1 fetch the A-row scales of rows
+// 0-63 and 64-127, waves 2 and 3 the two B scales); past the last tile they
+// read an empty buffer range, so the vmcnt arithmetic never changes.
 template <class C>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_fp8_1w_kernel(GemmArgs g) {
@@ -63,12 +68,16 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
                       C::STEPS == 2 && C::UA == 4 && C::UB == 8 && C::B_ROW == 256,
                   "128 x 256 tile, 2 x 2 waves, one 128-byte K tile per scale block");
     constexpr int NS = C::STAGES;
-    constexpr int SC_OFF = C::A_BYTES + C::B_BYTES;   // 4 scale regions of 256 B
-    constexpr int STAGE_BYTES = SC_OFF + 4 * 256;
+    // LDS: the A tiles of all stages, then their B tiles, then their scale
+    // regions (4 x 256 B per stage), so that every fragment read is a base
+    // register plus an immediate offset (16 bits).
+    constexpr int B_OFF = NS * C::A_BYTES;
+    constexpr int S_OFF = B_OFF + NS * C::B_BYTES;
+    constexpr int LDS_TOTAL = S_OFF + NS * 1024;
     constexpr int DMA_PER_TILE = C::UA + C::UB + 1;
     constexpr int WAIT_AHEAD = (NS - 2) * DMA_PER_TILE;   // loads of tiles t+2..t+NS-1
-    static_assert(NS >= 2 && NS * STAGE_BYTES <= 163840, "LDS budget");
-    __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE_BYTES];
+    static_assert(NS >= 2 && NS <= 4 && LDS_TOTAL <= 163840, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) char lds[LDS_TOTAL];
     MPDT_LDS char* const lds0 = lds_cast(lds);
 
     MPDT_STAMP(0)
@@ -113,8 +122,8 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
     };
     const uint32_t rangeA = (uint32_t)(C::BM - 1) * lda + C::KT_BYTES;
     const uint32_t rangeB = (uint32_t)(C::KROWS - 1) * ldb + C::B_ROW;
-    uint64_t baseA = (uint64_t)(uintptr_t)g.A + (uint64_t)((int64_t)m0 * g.lda_b);
-    uint64_t baseB = (uint64_t)(uintptr_t)g.B + (uint64_t)n0;
+    const uint64_t baseA = (uint64_t)(uintptr_t)g.A + (uint64_t)((int64_t)m0 * g.lda_b);
+    const uint64_t baseB = (uint64_t)(uintptr_t)g.B + (uint64_t)n0;
     const uint64_t stepB = (uint64_t)C::KROWS * (uint64_t)g.ldb_b;
     // Scale loads (one per wave and K tile, 64 lanes into the wave's 256-byte
     // region of the stage).  Waves 0, 1: A-row scales of rows 64 w .. 64 w + 63,
@@ -126,34 +135,42 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
     const uint32_t voffS = scaleA ? (uint32_t)((lane >> 1) + 32 * (lane & 1)) * ldsa4
                                   : (uint32_t)(lane & 1) * 4u;
     const uint32_t rangeS = scaleA ? 63u * ldsa4 + 4u : 8u;
-    uint64_t baseS = scaleA ? (uint64_t)(uintptr_t)g.sA + (uint64_t)((int64_t)(m0 + wave * 64) * ldsa4)
+    const uint64_t baseS = scaleA ? (uint64_t)(uintptr_t)g.sA + (uint64_t)((int64_t)(m0 + wave * 64) * ldsa4)
                             : (uint64_t)(uintptr_t)g.sB + (uint64_t)(n0 / 128) * 4u;
     const uint64_t stepS = scaleA ? 4u : (uint64_t)g.ld_sb * 4u;
+    // Resources of the next K tile to load, advanced in place (the base
+    // address stays below 2^48, so its high word never reaches the stride
+    // field); a dead tile (past the last) gets range 0.
     struct Rs {
         i32x4 a, b, s;
     };
-    auto rs_next = [&](bool live) __attribute__((always_inline)) -> Rs {   // resources of the next K tile to load
-        const Rs r = {rsrc_words(baseA, live ? rangeA : 0u), rsrc_words(baseB, live ? rangeB : 0u),
-                      rsrc_words(baseS, live ? rangeS : 0u)};
-        baseA += C::KT_BYTES;
-        baseB += stepB;
-        baseS += stepS;
-        return r;
+    Rs rs = {rsrc_words(baseA, rangeA), rsrc_words(baseB, rangeB), rsrc_words(baseS, rangeS)};
+    auto bump = [](i32x4& r, uint64_t step) __attribute__((always_inline)) {
+        const uint64_t b = ((uint64_t)(uint32_t)r[1] << 32 | (uint32_t)r[0]) + step;
+        r[0] = (int32_t)(uint32_t)b;
+        r[1] = (int32_t)(uint32_t)(b >> 32);
     };
-    const uint32_t vzero = 0;
+    auto rs_next = [&](bool live) __attribute__((always_inline)) {
+        bump(rs.a, C::KT_BYTES);
+        bump(rs.b, stepB);
+        bump(rs.s, stepS);
+        rs.a[2] = live ? (int32_t)rangeA : 0;
+        rs.b[2] = live ? (int32_t)rangeB : 0;
+        rs.s[2] = live ? (int32_t)rangeS : 0;
+    };
     auto dma_piece = [&](auto P, const Rs& r, auto STG) __attribute__((always_inline)) {
-        constexpr int p = decltype(P)::value;
-        MPDT_LDS char* const st = lds0 + decltype(STG)::value * STAGE_BYTES;
+        constexpr int p = decltype(P)::value, S = decltype(STG)::value;
         if constexpr (p < C::UA) {
-            lds_dma16<p * 1024, p == 0>(r.a, st + wave * (C::UA * 1024), voffA[p & 1], soffA(p));
+            lds_dma16<p * 1024, p == 0>(r.a, lds0 + S * C::A_BYTES + wave * (C::UA * 1024), voffA[p & 1],
+                                        soffA(p));
         } else if constexpr (p < C::UA + C::UB) {
             constexpr int u = p - C::UA;   // two M0 groups of four pieces
             lds_dma16<(u & 3) * 1024, (u & 3) == 0>(
-                r.b, st + C::A_BYTES + wave * (C::UB * 1024) + (u >> 2) * 4096, voffB[u & 1], soffB(u));
+                r.b, lds0 + B_OFF + S * C::B_BYTES + wave * (C::UB * 1024) + (u >> 2) * 4096,
+                voffB[u & 1], soffB(u));
         } else {
-            lds_dma4<0, true>(r.s, st + SC_OFF + wave * 256, voffS, 0u);
+            lds_dma4<0, true>(r.s, lds0 + S_OFF + S * 1024 + wave * 256, voffS, 0u);
         }
-        (void)vzero;
     };
 
     // ---- fragment reads -----------------------------------------------------
@@ -170,24 +187,36 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const uint32_t col16 = wn * C::WN + j * 32 + 16 * (grp & 1);
-        lb[j] = C::A_BYTES + b_off<C>(32 * (grp >> 1) + (gp >> 1), col16 >> 4) + 8 * (gp & 1);
+        lb[j] = B_OFF + b_off<C>(32 * (grp >> 1) + (gp >> 1), col16 >> 4) + 8 * (gp & 1);
     }
-    const uint32_t lsa = SC_OFF + wm * 256 + 8 * lrow;      // A-row scales of rows lrow, lrow + 32
-    const uint32_t lsb = SC_OFF + 2 * 256 + 4 * wn;         // this wave's B scale
+    const uint32_t lsa = S_OFF + wm * 256 + 8 * lrow;      // A-row scales of rows lrow, lrow + 32
+    const uint32_t lsb = S_OFF + 2 * 256 + 4 * wn;         // this wave's B scale
     constexpr uint32_t QB = 64 * C::B_ROW, HB = 8 * C::B_ROW;
+    static_assert(C::B_BYTES + QB + 3 * HB < 65536, "16-bit read offsets");
 
     struct Fr {
         u32x4 a[2][2][2];   // [row tile][step][16-byte half]
         u32x2 b[2][4][4];   // [step][column tile][8-row read]
     } fr;
-    auto rdA = [&](int i, int s, uint32_t so) __attribute__((always_inline)) {
+    auto rdA = [&](int i, int s, auto STG) __attribute__((always_inline)) {
+        constexpr uint32_t so = decltype(STG)::value * C::A_BYTES;
 #pragma unroll
         for (int q = 0; q < 2; ++q)
-            fr.a[i][s][q] = lds_load16(lds0, so + la[s][q] + (uint32_t)(i * 32 * C::KT_BYTES));
+            fr.a[i][s][q] = lds_load16(lds0, la[s][q] + so + (uint32_t)(i * 32 * C::KT_BYTES));
     };
-    auto rdB = [&](int s, int j, uint32_t so) __attribute__((always_inline)) {
+    auto rdB = [&](int s, int j, auto STG) __attribute__((always_inline)) {
+        // A stage past the 16-bit immediate range moves the base once per
+        // call (kept opaque, so the compiler does not fold it back into four
+        // separate adds).
+        constexpr uint32_t so = decltype(STG)::value * C::B_BYTES;
+        constexpr uint32_t hi = (so + QB + 3 * HB) >= 65536u ? 65536u : 0u;
+        uint32_t base = lb[j];
+        if constexpr (hi != 0) {
+            base += hi;
+            asm volatile("" : "+v"(base));
+        }
 #pragma unroll
-        for (int h = 0; h < 4; ++h) fr.b[s][j][h] = lds_read_tr8(lds0, so + lb[j] + s * QB + h * HB);
+        for (int h = 0; h < 4; ++h) fr.b[s][j][h] = lds_read_tr8(lds0, base + (so - hi) + s * QB + h * HB);
     };
 
     Acc acc[2][4], blk[4];
@@ -223,34 +252,32 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
     };
     u32x2 sap;
     float sbv;
-    auto read_scales = [&](uint32_t so) __attribute__((always_inline)) {
-        sap = *reinterpret_cast<const MPDT_LDS u32x2*>(lds0 + so + lsa);
-        sbv = *reinterpret_cast<const MPDT_LDS float*>(lds0 + so + lsb);
+    auto read_scales = [&](auto STG) __attribute__((always_inline)) {
+        constexpr uint32_t so = decltype(STG)::value * 1024;
+        sap = *reinterpret_cast<const MPDT_LDS u32x2*>(lds0 + lsa + so);
+        sbv = *reinterpret_cast<const MPDT_LDS float*>(lds0 + lsb + so);
     };
-    auto make_f = [&]() __attribute__((always_inline)) {
-        const uint32_t s0 = sap[0], s1 = sap[1];
-        f[0] = __uint_as_float(s0) * sbv;
-        f[1] = __uint_as_float(s1) * sbv;
+    auto make_f = [&](int i) __attribute__((always_inline)) {
+        const uint32_t sa = sap[i];
+        f[i] = __uint_as_float(sa) * sbv;
     };
 
     // Slots 0..7 of K tile t in stage S: promotions of the previous tile's row
     // tile 1 in slots 0-3; the last five direct loads of tile t-1+NS (into
-    // stage S-1) in slots 0-4; tile t's remaining fragments and its scales in
-    // slots 4-6 (their registers were last used in slots 7 and 11-15 of tile
-    // t-1); the resources of tile t+NS in slot 5.
-    Rs rs;
+    // stage S-1) in slots 0-4; tile t's remaining fragments in slots 4-6
+    // (their registers were last used in slots 11-15 of tile t-1), its row
+    // tile 1 multiplier in slot 4 (the previous one was last used in slot 3);
+    // the resources of tile t+NS in slot 5.
     auto phase_x = [&](auto STG, bool live_next) __attribute__((always_inline)) {
-        constexpr uint32_t cur = decltype(STG)::value * STAGE_BYTES;
         using PREV = std::integral_constant<int, (decltype(STG)::value + NS - 1) % NS>;
         static_for<0, 8>([&](auto N) __attribute__((always_inline)) {
             constexpr int n = decltype(N)::value;
             if constexpr (n < 4) promote(1, n);
             mfma(n);
             if constexpr (n <= 4) dma_piece(std::integral_constant<int, 8 + n>{}, rs, PREV{});
-            if constexpr (n == 4) { rdB(1, 3, cur); read_scales(cur); }
-            if constexpr (n == 5) { rdA(1, 0, cur); rs = rs_next(live_next); }
-            if constexpr (n == 6) rdA(1, 1, cur);
-            if constexpr (n == 7) make_f();
+            if constexpr (n == 4) { rdB(1, 3, STG); make_f(1); }
+            if constexpr (n == 5) { rdA(1, 0, STG); rs_next(live_next); }
+            if constexpr (n == 6) rdA(1, 1, STG);
             __builtin_amdgcn_sched_barrier(0);
         });
     };
@@ -263,7 +290,7 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
     // stage S+1.
     auto phase_y = [&](auto STG) __attribute__((always_inline)) {
         constexpr int S = decltype(STG)::value;
-        constexpr uint32_t nxt = ((S + 1) % NS) * STAGE_BYTES;
+        using NXT = std::integral_constant<int, (S + 1) % NS>;
         wait_vmem<WAIT_AHEAD>();
         wait_lds();
         wg_barrier();
@@ -273,20 +300,22 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
             mfma(n);
             dma_piece(std::integral_constant<int, n - 8>{}, rs, STG);
             if constexpr (n == 12) {
-                rdA(0, 0, nxt);
-                rdB(0, 0, nxt);
-                rdB(0, 1, nxt);
+                read_scales(NXT{});
+                rdA(0, 0, NXT{});
+                rdB(0, 0, NXT{});
+                rdB(0, 1, NXT{});
             }
             if constexpr (n == 13) {
-                rdB(0, 2, nxt);
-                rdB(0, 3, nxt);
+                rdB(0, 2, NXT{});
+                rdB(0, 3, NXT{});
             }
             if constexpr (n == 14) {
-                rdA(0, 1, nxt);
-                rdB(1, 0, nxt);
-                rdB(1, 1, nxt);
+                make_f(0);   // tile t+1's row tile 0 multiplier (this one's was last used in slot 11)
+                rdA(0, 1, NXT{});
+                rdB(1, 0, NXT{});
+                rdB(1, 1, NXT{});
             }
-            if constexpr (n == 15) rdB(1, 2, nxt);
+            if constexpr (n == 15) rdB(1, 2, NXT{});
             __builtin_amdgcn_sched_barrier(0);
         });
     };
@@ -305,19 +334,22 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
     // ---- prologue: tiles 0..NS-1 into stages 0..NS-1 (the last five loads of
     // tile NS-1 are issued by tile 0's slots 0-4, as in the steady state) ---
     static_for<0, NS>([&](auto P) __attribute__((always_inline)) {
-        rs = rs_next(true);
+        if constexpr (decltype(P)::value > 0) rs_next(true);
         constexpr int np = decltype(P)::value == NS - 1 ? 8 : DMA_PER_TILE;
         static_for<0, np>([&](auto Q) __attribute__((always_inline)) { dma_piece(Q, rs, P); });
     });
     wait_vmem<(NS - 2) * DMA_PER_TILE + 8>();
     wg_barrier();
-    // the reads a previous tile's slots 12..15 would have made
-    rdA(0, 0, 0);
+    // what a previous tile's slots 12..15 would have read and computed
+    using I0 = std::integral_constant<int, 0>;
+    read_scales(I0{});
+    rdA(0, 0, I0{});
 #pragma unroll
-    for (int j = 0; j < 4; ++j) rdB(0, j, 0);
-    rdA(0, 1, 0);
+    for (int j = 0; j < 4; ++j) rdB(0, j, I0{});
+    rdA(0, 1, I0{});
 #pragma unroll
-    for (int j = 0; j < 3; ++j) rdB(1, j, 0);
+    for (int j = 0; j < 3; ++j) rdB(1, j, I0{});
+    make_f(0);
 
     // ---- K loop, unrolled by NS (stage of tile t = t % NS) ------------------
     int t = 0;
@@ -351,7 +383,7 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
     // 16-byte pieces of whole rows.
     wg_barrier();   // every wave is past its reads of the K-tile stages
     MPDT_LDS char* const reg = lds0 + wave * (C::WM * C::WN * 2);
-    static_assert(4 * C::WM * C::WN * 2 <= NS * STAGE_BYTES, "epilogue staging fits");
+    static_assert(4 * C::WM * C::WN * 2 <= LDS_TOTAL, "epilogue staging fits");
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
