@@ -43,8 +43,9 @@ namespace mpdt {
 //   wait for this wave's direct loads of tile t+1 and its LDS reads, then a
 //   workgroup barrier: tile t+1 is in LDS and tile t's stage is free;
 //   slots 8-11  promote blk[j] of row tile 0, then s0(i1, j);
-//   slots 12-15 s1(i1, j); read tile t+1's scales and its fragments for
-//               slots 0-7 (their registers are free by then).
+//   slots 12-15 s1(i1, j);
+//   slots 8-15  also read tile t+1's scales and its fragments for slots 0-7,
+//               one B column tile per slot as its registers free up.
 // The 13 direct loads of tile t+NS (into tile t's stage) go one per slot over
 // slots 8-15 of tile t and 0-4 of tile t+1: a 1 KiB direct load keeps the
 // CU's address unit busy for 16 cycles, so four waves issuing one per
@@ -264,8 +265,8 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
 
     // Slots 0..7 of K tile t in stage S: promotions of the previous tile's row
     // tile 1 in slots 0-3; the last five direct loads of tile t-1+NS (into
-    // stage S-1) in slots 0-4; tile t's remaining fragments in slots 4-6
-    // (their registers were last used in slots 11-15 of tile t-1), its row
+    // stage S-1) in slots 0-4; tile t's remaining fragments in slots 2, 5 and
+    // 6 (their registers were last used in slots 11-15 of tile t-1), its row
     // tile 1 multiplier in slot 4 (the previous one was last used in slot 3);
     // the resources of tile t+NS in slot 5.
     auto phase_x = [&](auto STG, bool live_next) __attribute__((always_inline)) {
@@ -275,7 +276,8 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
             if constexpr (n < 4) promote(1, n);
             mfma(n);
             if constexpr (n <= 4) dma_piece(std::integral_constant<int, 8 + n>{}, rs, PREV{});
-            if constexpr (n == 4) { rdB(1, 3, STG); make_f(1); }
+            if constexpr (n == 2) rdB(1, 3, STG);
+            if constexpr (n == 4) make_f(1);
             if constexpr (n == 5) { rdA(1, 0, STG); rs_next(live_next); }
             if constexpr (n == 6) rdA(1, 1, STG);
             __builtin_amdgcn_sched_barrier(0);
@@ -285,9 +287,11 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
     // barrier, promotions of row tile 0 in slots 8-11; one direct load of
     // tile t+NS into stage S per slot (the first eight of its 13: a direct
     // load occupies the CU's address unit for 16 cycles, so four waves
-    // issuing one per 64-cycle MFMA slot keep it just below saturation); in
-    // slots 12-15 the reads of tile t+1's fragments for its slots 0-7 from
-    // stage S+1.
+    // issuing one per 64-cycle MFMA slot keep it just below saturation); the
+    // reads of tile t+1's scales and its fragments for slots 0-7 from stage
+    // S+1, each in the slot after the last use of the registers it fills (one
+    // B column tile per slot: a burst of reads backs up the LDS queue and
+    // stalls the MFMAs that wait for it).
     auto phase_y = [&](auto STG) __attribute__((always_inline)) {
         constexpr int S = decltype(STG)::value;
         using NXT = std::integral_constant<int, (S + 1) % NS>;
@@ -299,22 +303,11 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
             if constexpr (n < 12) promote(0, n - 8);
             mfma(n);
             dma_piece(std::integral_constant<int, n - 8>{}, rs, STG);
-            if constexpr (n == 12) {
-                read_scales(NXT{});
-                rdA(0, 0, NXT{});
-                rdB(0, 0, NXT{});
-                rdB(0, 1, NXT{});
-            }
-            if constexpr (n == 13) {
-                rdB(0, 2, NXT{});
-                rdB(0, 3, NXT{});
-            }
-            if constexpr (n == 14) {
-                make_f(0);   // tile t+1's row tile 0 multiplier (this one's was last used in slot 11)
-                rdA(0, 1, NXT{});
-                rdB(1, 0, NXT{});
-                rdB(1, 1, NXT{});
-            }
+            if constexpr (n == 8) { read_scales(NXT{}); rdA(0, 0, NXT{}); }
+            if constexpr (n >= 9 && n <= 12) rdB(0, n - 9, NXT{});
+            if constexpr (n == 12) rdA(0, 1, NXT{});
+            if constexpr (n == 13) rdB(1, 0, NXT{});
+            if constexpr (n == 14) { rdB(1, 1, NXT{}); make_f(0); }
             if constexpr (n == 15) rdB(1, 2, NXT{});
             __builtin_amdgcn_sched_barrier(0);
         });
