@@ -148,7 +148,7 @@ def main():
         flop = 2.0 * M * N * K
         avg_s = st["mean_us"] * 1e-6
         achieved = flop / avg_s / 1e12
-        digest = source_digest("gemm.hip", "device_common.hpp")
+        digest = source_digest("gemm.hip", "gemm_common.hpp", "device_common.hpp")
         traffic = traffic_for("gemm_bf16_4096", digest)
         clock = gemm_clock(tA, tB, tC, tD, stream, M, N, K)
         result = {

@@ -44,7 +44,9 @@ namespace mpdt {
 // ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
-template <Kind KD, class C, bool ALIGNED>
+// OUT16 (FP16 / BF16 inputs): D is written in the input format; a separate
+// instantiation, so the two output forms are distinct kernels.
+template <Kind KD, class C, bool ALIGNED, bool OUT16 = false>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::NT / 256, C::NT / 256)))
 void gemm_kernel(GemmArgs g) {
     using F = Fmt<KD>;
@@ -785,7 +787,7 @@ void gemm_kernel(GemmArgs g) {
     } else if constexpr (KD == Kind::I8) {
         epilogue(std::common_type<Out32>{});
     } else {
-        if (g.out16) epilogue(std::common_type<uint16_t>{});
+        if constexpr (OUT16) epilogue(std::common_type<uint16_t>{});
         else epilogue(std::common_type<Out32>{});
     }
 #ifdef MPDT_CLOCK_STAMPS
@@ -805,6 +807,13 @@ void gemm_kernel(GemmArgs g) {
 template <Kind KD, class C, bool ALIGNED>
 static hipError_t launch_grid(const GemmArgs& a, int64_t tiles, hipStream_t stream) {
     if (tiles <= 0) return hipSuccess;
+    if constexpr (KD == Kind::F16 || KD == Kind::BF16) {
+        if (a.out16) {
+            hipLaunchKernelGGL((gemm_kernel<KD, C, ALIGNED, true>), dim3((unsigned)tiles), dim3(C::NT), 0,
+                               stream, a);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((gemm_kernel<KD, C, ALIGNED>), dim3((unsigned)tiles), dim3(C::NT), 0, stream, a);
     return hipGetLastError();
 }
