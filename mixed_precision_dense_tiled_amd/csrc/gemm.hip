@@ -11,7 +11,13 @@
 // tiles, conflict-free shared-memory layout).  Everything below is designed
 // for CDNA4: 64-lane wavefronts, 32x32 MFMA tiles, a 160 KiB LDS, XCD-local L2.
 //
-// Structure of one workgroup (512 threads = 8 wavefronts, two per SIMD):
+// Two shapes of one kernel template:
+//   * one wavefront per SIMD (256 threads, FP16/BF16/INT8 full 256 x 256
+//     tiles of an aligned problem): a 128 x 128 wave tile, and a K loop whose
+//     program order is written out so the LDS reads of the next MFMA step and
+//     the direct loads of later K tiles issue between the MFMAs;
+//   * eight wavefronts, two per SIMD (everything else).
+// In both:
 //   * WG tile BM x BN of D; wave tile (BM / WAVES_M) x (BN / WAVES_N) held in
 //     MFMA accumulators for the whole K loop (acc starts at zero; C is added
 //     once in the epilogue).
@@ -19,9 +25,7 @@
 //     INT8 elements; 128 FP8 elements, exactly one scale block).
 //   * Interior tiles with 16-byte aligned rows: buffer loads that write LDS
 //     directly (no register round trip) fill NS rotating stages, issued
-//     NS-1 tiles ahead.  For FP16/BF16/INT8 the two wavefronts of each SIMD
-//     alternate between a compute slot (MFMAs) and a memory slot (operand
-//     reads from LDS, direct-load issue) between workgroup barriers.
+//     NS-1 tiles ahead.
 //   * Edge tiles, unaligned rows and the K tail: 16-byte global loads into
 //     registers (bounded: bytes past M, N or K read as zero, with an
 //     in-register re-alignment for rows that are not 16-byte aligned), then
