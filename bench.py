@@ -18,6 +18,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -50,10 +51,16 @@ def parse():
 
 
 def source_digest(*names) -> str:
+    """Digest of the listed kernel sources with comments and blank lines
+    removed (counters describe the code, so comment edits keep them valid)."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "mixed_precision_dense_tiled_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "mixed_precision_dense_tiled_amd", "csrc", n)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+        h.update("\n".join(lines).encode())
     return h.hexdigest()[:16]
 
 
