@@ -87,6 +87,17 @@ __device__ __forceinline__ void lds_dma4(i32x4 r, MPDT_LDS char* dst, uint32_t v
                      : "{m0}"((uint32_t)(uintptr_t)dst), "v"(voff), "s"(r), "s"(soff), "n"(OFF));
 }
 
+// Keep the bytes [0, nbytes) of an 8-byte piece, zero the rest (nbytes 0..8).
+__device__ __forceinline__ u32x2 mask_tail8(u32x2 v, int nbytes) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        const int keep = nbytes - 4 * w;
+        const uint32_t m = keep >= 4 ? 0xffffffffu : (keep <= 0 ? 0u : (0xffffffffu >> (8 * (4 - keep))));
+        v[w] &= m;
+    }
+    return v;
+}
+
 // Keep the bytes [0, nbytes) of a 16-byte chunk, zero the rest (nbytes 0..16).
 __device__ __forceinline__ u32x4 mask_tail(u32x4 v, int nbytes) {
 #pragma unroll

@@ -403,13 +403,23 @@ void gemm_kernel(GemmArgs g) {
     const bool direct = ALIGNED && full_mn && g.lda_b < (int64_t(1) << 31) / C::BM &&
                         g.ldb_b < (int64_t(1) << 31) / C::KROWS;
     if constexpr (ONE_WAVE) {
-        // Launched over interior tiles only, with aligned rows and whole K
-        // tiles (the host checks all of it; this guard keeps any other tile
-        // from being touched).
-        if (!(direct && whole_k && k_bytes >= (int64_t)NS * C::KT_BYTES)) return;
+        // Launched over every tile of a problem with at least NS K tiles whose
+        // operand offsets fit 32 bits (the host checks it; this guard keeps
+        // any other problem from being touched).  Rows need only element
+        // alignment (16-byte loads from any byte address return the bytes
+        // there).  Partial tiles at the M and N edges and a partial last K
+        // tile need no separate path: every buffer resource ends at its
+        // operand's last byte, so A rows past M and B rows past K read as
+        // zero; B columns past N (and A rows' bytes past K, which belong to
+        // the next row) are finite or not but only reach outputs past N (the
+        // masked epilogue drops them) or are masked to zero in the last K
+        // tile's A fragments.
+        if (!(k_bytes >= (int64_t)NS * C::KT_BYTES && g.lda_b < (int64_t(1) << 31) / C::BM &&
+              g.ldb_b < (int64_t(1) << 31) / C::KROWS && g.ldb_b >= C::B_ROW))
+            return;
         if constexpr (ALIGNED && C::STEPS == 2 && C::TM == 4 && C::TN == 4) {
-            // Interior tile, whole K tiles (at least NS), one wavefront per
-            // SIMD with a 128 x 128 wave tile.  Per K tile t (two MFMA steps):
+            // One wavefront per SIMD with a 128 x 128 wave tile, at least NS K
+            // tiles.  Per K tile t (two MFMA steps):
             //   phase X: the 16 MFMAs of step 0, interleaved with the LDS
             //            reads of step 1's fragments and the set-up of the
             //            direct loads of tile t+NS;
@@ -427,7 +437,8 @@ void gemm_kernel(GemmArgs g) {
             // barriers: a single wave per SIMD issues in order, so whatever
             // sits between two MFMAs is issued while the first one runs.
             static_assert(C::UA == 4 && C::UB == 4, "four A and four B pieces per wave and K tile");
-            const int nt = (int)(k_bytes / C::KT_BYTES);
+            const int nt = (int)((k_bytes + C::KT_BYTES - 1) / C::KT_BYTES);
+            const int last_bytes = (int)(k_bytes - (int64_t)(nt - 1) * C::KT_BYTES);   // 1..KT_BYTES
             constexpr int WAIT_AHEAD = (NS - 2) * DMA_PER_TILE;   // loads of tiles t+2..t+NS-1
             MPDT_LDS char* const lds0 = lds_cast(sA0);
 
@@ -454,8 +465,15 @@ void gemm_kernel(GemmArgs g) {
             };
             const uint64_t baseA = (uint64_t)(uintptr_t)g.A + (uint64_t)((int64_t)m0 * g.lda_b);
             const uint64_t baseB = (uint64_t)(uintptr_t)g.B + (uint64_t)((int64_t)n0 * C::ES);
-            const int64_t restA0 = span_a - (int64_t)m0 * g.lda_b;   // bytes of A from baseA
-            const int64_t restB0 = span_b - (int64_t)n0 * C::ES;
+            // bytes of A / B from baseA / baseB, plus the 16 bytes past each
+            // operand's end that the host found to lie in the operand's last
+            // memory page (ext_a / ext_b): a 16-byte load that starts inside
+            // the operand then returns its bytes even where it runs past the
+            // end (a load that straddles the range end loses its bytes); the
+            // bytes past the end only reach outputs that are not stored or
+            // are masked in the last K tile
+            const int64_t restA0 = span_a + g.ext_a - (int64_t)m0 * g.lda_b;
+            const int64_t restB0 = span_b + g.ext_b - (int64_t)n0 * C::ES;
             const int64_t stepB = (int64_t)C::KROWS * g.ldb_b;          // bytes per K tile of B
             auto clamp31 = [](int64_t r) { return (uint32_t)(r > 0x7fffffff ? 0x7fffffff : r); };
             // resources of K tile kt (kA = kt * KT_BYTES, kB = kt * stepB)
@@ -567,7 +585,29 @@ void gemm_kernel(GemmArgs g) {
                 kA += C::KT_BYTES;
                 kB += stepB;
             }
-            // last K tile
+            // last K tile; if it is partial, the fragment bytes at K and past
+            // it (A: the next row's bytes, B: the rows past K, zeros or the
+            // bytes of the page past the end) are cleared, so that every
+            // product past K is exactly zero whatever those bytes hold.  A
+            // lane's A fragment of step q covers K bytes [16 c, 16 c + 16) of
+            // the tile, c = 2 q + lhalf; its B fragment half h covers
+            // [32 q + 16 lhalf + 8 h, +8), in K order.
+            auto mask_a = [&](int q) {
+                const int c = q * (F::STEP_BYTES / 16) + (int)lhalf * (C::FRAG_BYTES / 16);
+                const int keep = min(max(last_bytes - 16 * c, 0), 16);
+                const int keep_b0 = min(max(last_bytes - (32 * q + 16 * (int)lhalf), 0), 8);
+                const int keep_b1 = min(max(last_bytes - (32 * q + 16 * (int)lhalf + 8), 0), 8);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) fr.a[q][i][0] = mask_tail(fr.a[q][i][0], keep);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    fr.b[q][j][0] = mask_tail8(fr.b[q][j][0], keep_b0);
+                    fr.b[q][j][1] = mask_tail8(fr.b[q][j][1], keep_b1);
+                }
+            };
+            static_assert(F::STEP_BYTES == 32 && C::FRAG_BYTES == 16, "fragment K ranges as above");
+            const bool partial = last_bytes < C::KT_BYTES;
+            if (partial) mask_a(0);
             const uint32_t cur = (uint32_t)scur * STAGE_BYTES;
             static_for<0, 16>([&](auto IDX) {
                 constexpr int idx = decltype(IDX)::value;
@@ -576,6 +616,7 @@ void gemm_kernel(GemmArgs g) {
                 __builtin_amdgcn_sched_barrier(0);
             });
             wait_lds();
+            if (partial) mask_a(1);
 #pragma unroll
             for (int idx = 0; idx < 16; ++idx) mma1(fr, 1, idx);
             // the empty-range loads of the last tiles still write (zeros) to
@@ -677,7 +718,7 @@ void gemm_kernel(GemmArgs g) {
             } else return (OutT)(a + c);
         };
         if constexpr (ONE_WAVE && std::is_same<OutT, uint16_t>::value) {
-            if (g.d16_vec) {
+            if (g.d16_vec && full_mn) {
                 // 16-bit D of a one-wave interior tile, staged through LDS so
                 // that it leaves in 16-byte stores of whole row segments (the
                 // accumulator layout gives each lane one column, so direct
@@ -836,25 +877,43 @@ static hipError_t launch_general(GemmArgs a, bool aligned, int int_tm, int int_t
                    : launch_grid<KD, C, false>(a, tiles, stream);
 }
 
-// FP16 / BF16 / INT8: the full 256 x 256 tiles of an aligned problem with
-// whole K tiles (at least STAGES of them) go to the one-wave kernel; the
-// remaining edge tiles, and every other problem, to the general kernel.
+// 16 when the 16 bytes after an operand's last byte lie in the same 4 KiB
+// page as that byte (so they are mapped whatever the allocation), else 0.
+static int page_slack(const char* base, int64_t span) {
+    const uint64_t end = (uint64_t)(uintptr_t)base + (uint64_t)span;   // one past the last byte
+    return ((end - 1) >> 12) == ((end + 15) >> 12) ? 16 : 0;
+}
+
+// FP16 / BF16 / INT8: a problem with at least STAGES K tiles (the last may be
+// partial) and 32-bit operand offsets goes to the one-wave kernel, edge tiles
+// and unaligned rows included, except the tile row holding A's last row when
+// a 16-byte load there would run past A's end into an unmapped page (rows of
+// K bytes not a multiple of 16), and likewise the tile column holding B's
+// last column; those, and every other problem, go to the general kernel.
 template <Kind KD, class C1, class C8>
 static hipError_t launch_mma(const GemmArgs& a0, bool aligned, hipStream_t stream) {
     static_assert(C1::BM == C8::BM && C1::BN == C8::BN, "one tile grid for both kernels");
     const int64_t kb = (int64_t)a0.K * C1::ES;
-    const bool one = aligned && kb % C1::KT_BYTES == 0 && kb >= (int64_t)C1::STAGES * C1::KT_BYTES &&
-                     a0.lda_b < (int64_t(1) << 31) / C1::BM && a0.ldb_b < (int64_t(1) << 31) / C1::KROWS;
-    const int int_tm = one ? a0.M / C1::BM : 0;
-    const int int_tn = one ? a0.N / C1::BN : 0;
-    if (int_tm > 0 && int_tn > 0) {
+    // (the direct loads' scalar offsets take a piece's instruction offset back
+    // off its row offset, which needs rows of at least one B tile row: ldb >=
+    // BN elements; lda >= K >= STAGES K tiles covers A)
+    const bool one = kb >= (int64_t)C1::STAGES * C1::KT_BYTES && a0.lda_b < (int64_t(1) << 31) / C1::BM &&
+                     a0.ldb_b < (int64_t(1) << 31) / C1::KROWS && a0.ldb_b >= C1::B_ROW;
+    if (one) {
         GemmArgs a = a0;
-        a.tiles_m = int_tm;
-        a.tiles_n = int_tn;
-        a.int_tm = a.int_tn = 0;
-        const hipError_t e = launch_grid<KD, C1, true>(a, (int64_t)int_tm * int_tn, stream);
-        if (e != hipSuccess) return e;
-        return launch_general<KD, C8>(a0, aligned, int_tm, int_tn, stream);
+        a.ext_a = page_slack(a0.A, (int64_t)(a0.M - 1) * a0.lda_b + kb);
+        a.ext_b = page_slack(a0.B, (int64_t)(a0.K - 1) * a0.ldb_b + (int64_t)a0.N * C1::ES);
+        const int tiles_m = (a0.M + C1::BM - 1) / C1::BM, tiles_n = (a0.N + C1::BN - 1) / C1::BN;
+        const int int_tm = tiles_m - ((kb % 16 != 0 && a.ext_a == 0) ? 1 : 0);
+        const int int_tn = tiles_n - ((((int64_t)a0.N * C1::ES) % 16 != 0 && a.ext_b == 0) ? 1 : 0);
+        if (int_tm > 0 && int_tn > 0) {
+            a.tiles_m = int_tm;
+            a.tiles_n = int_tn;
+            a.int_tm = a.int_tn = 0;
+            const hipError_t e = launch_grid<KD, C1, true>(a, (int64_t)int_tm * int_tn, stream);
+            if (e != hipSuccess) return e;
+            return launch_general<KD, C8>(a0, aligned, int_tm, int_tn, stream);
+        }
     }
     return launch_general<KD, C8>(a0, aligned, 0, 0, stream);
 }

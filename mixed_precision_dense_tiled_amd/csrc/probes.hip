@@ -13,6 +13,12 @@
 //     [KS/2 * (l/32), KS/2 * (l/32 + 1)) in order), D (32 x 32, row-major,
 //     FP32 or INT32) stored with the accumulator mapping the GEMM epilogue
 //     uses (register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32).
+//   mpdt_probe_unaligned(src, off, soff, range, out_dma, out_ld): lane l moves
+//     bytes [soff + off + 16 l, +16) of src once with a direct-to-LDS buffer
+//     load (lane offset off + 16 l, scalar offset soff; then LDS ->
+//     out_dma[l]) and once with a plain 16-byte load (-> out_ld[l]); neither
+//     offset need be a multiple of 16.  With range < soff + off + 1024 it also
+//     shows which offsets the buffer range check covers.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -32,6 +38,19 @@ __global__ __launch_bounds__(64) void probe_tr_kernel(int bits, const u32x4* ima
     __syncthreads();
     const uint32_t off = offsets[lane] & (4096u - 8u);
     out[lane] = (bits == 16) ? lds_read_tr16(lds, off) : lds_read_tr8(lds, off);
+}
+
+__global__ __launch_bounds__(64) void probe_unaligned_kernel(const char* src, uint32_t off, uint32_t soff,
+                                                             uint32_t range, u32x4* out_dma, u32x4* out_ld) {
+    __shared__ __attribute__((aligned(1024))) char smem[1024];
+    MPDT_LDS char* lds = lds_cast(smem);
+    const int lane = threadIdx.x;
+    const i32x4 r = rsrc_words((uint64_t)(uintptr_t)src, range);
+    lds_dma16<0, true>(r, lds, off + 16u * (uint32_t)lane, soff);
+    __builtin_amdgcn_s_waitcnt(0);   // every counter at zero: the direct load has landed
+    __syncthreads();
+    out_dma[lane] = lds_load16(lds, 16u * (uint32_t)lane);
+    out_ld[lane] = *reinterpret_cast<const u32x4*>(src + soff + off + 16u * (uint32_t)lane);
 }
 
 template <int KIND>
@@ -121,5 +140,14 @@ MPDT_EXPORT int mpdt_probe_mfma(int kind, const void* A, const void* B, void* D,
         case 3: hipLaunchKernelGGL(mpdt::probe_mfma_kernel<3>, dim3(1), dim3(64), 0, s, a, b, D); break;
         default: return (int)hipErrorInvalidValue;
     }
+    return (int)hipGetLastError();
+}
+
+// size: bytes of src; every byte either load may touch lies inside it.
+MPDT_EXPORT int mpdt_probe_unaligned(const void* src, uint32_t size, uint32_t off, uint32_t soff,
+                                     uint32_t range, void* out_dma, void* out_ld, void* stream) {
+    if ((uint64_t)soff + off + 1024u > size || range > size) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(mpdt::probe_unaligned_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                       (const char*)src, off, soff, range, (mpdt::u32x4*)out_dma, (mpdt::u32x4*)out_ld);
     return (int)hipGetLastError();
 }

@@ -70,4 +70,7 @@ def probes():
     L.mpdt_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                   ctypes.c_void_p]
     L.mpdt_probe_mfma.restype = ctypes.c_int
+    L.mpdt_probe_unaligned.argtypes = [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                                       ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    L.mpdt_probe_unaligned.restype = ctypes.c_int
     return L

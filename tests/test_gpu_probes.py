@@ -99,3 +99,51 @@ def test_mfma_fp8_layout_and_every_code(gpu_ok):
     rel = np.abs(D - ref) / S
     print("fp8 MFMA worst |err| / S:", rel.max())
     assert (rel <= 1e-3).all()
+
+
+@pytest.mark.parametrize("off,soff", [(0, 0), (2, 0), (6, 0), (14, 0), (1, 0), (7, 0),
+                                      (0, 4), (2, 4), (6, 36), (0, 32772), (3, 5)])
+def test_unaligned_16_byte_loads(gpu_ok, off, soff):
+    """A 16-byte direct-to-LDS buffer load and a plain 16-byte load from an
+    address that is only 2-byte (or 1-byte) aligned, through the lane offset
+    or the scalar offset, return the bytes at that address: rows of FP16 /
+    8-bit operands whose leading dimension is not a multiple of 16 bytes can
+    use the same loads."""
+    L = probes()
+    size = 65536
+    src = np.random.default_rng(off + 17 * soff).integers(0, 256, size, dtype=np.uint8)
+    t = dev(src)
+    out_dma = torch.zeros(1024, dtype=torch.uint8, device=gpu_ok)
+    out_ld = torch.zeros(1024, dtype=torch.uint8, device=gpu_ok)
+    assert L.mpdt_probe_unaligned(t.data_ptr(), size, off, soff, size, out_dma.data_ptr(),
+                                  out_ld.data_ptr(), _stream()) == 0
+    torch.cuda.synchronize()
+    want = src[soff + off:soff + off + 1024]
+    assert np.array_equal(host(out_ld), want), "plain load"
+    assert np.array_equal(host(out_dma), want), "direct-to-LDS load"
+
+
+def test_buffer_range_check_covers(gpu_ok):
+    """Which offsets the raw-buffer range check covers: with the range ending
+    512 bytes in, lanes whose lane offset passes it read zero; a scalar offset
+    is reported as covered or not (printed; the kernels do not rely on it)."""
+    L = probes()
+    size = 65536
+    src = np.random.default_rng(5).integers(1, 256, size, dtype=np.uint8)
+    t = dev(src)
+    out_dma = torch.zeros(1024, dtype=torch.uint8, device=gpu_ok)
+    out_ld = torch.zeros(1024, dtype=torch.uint8, device=gpu_ok)
+    # lane offset only: lanes 32.. start at byte 512 = the range
+    assert L.mpdt_probe_unaligned(t.data_ptr(), size, 0, 0, 512, out_dma.data_ptr(), out_ld.data_ptr(),
+                                  _stream()) == 0
+    torch.cuda.synchronize()
+    got = host(out_dma).reshape(64, 16)
+    assert np.array_equal(got[:32].ravel(), src[:512]) and not got[32:].any()
+    # scalar offset 256 with the same range: covered iff lanes 16..31 read zero
+    assert L.mpdt_probe_unaligned(t.data_ptr(), size, 0, 256, 512, out_dma.data_ptr(), out_ld.data_ptr(),
+                                  _stream()) == 0
+    torch.cuda.synchronize()
+    got = host(out_dma).reshape(64, 16)
+    print("scalar offset inside the range check:", not got[16:32].any())
+    assert np.array_equal(got[:16].ravel(), src[256:512])
+    assert not got[32:].any()
