@@ -98,6 +98,26 @@ __device__ __forceinline__ u32x2 mask_tail8(u32x2 v, int nbytes) {
     return v;
 }
 
+// Zero the bytes [0, nbytes) of a 16-byte chunk / an 8-byte piece, keep the rest.
+__device__ __forceinline__ u32x4 mask_head(u32x4 v, int nbytes) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const int drop = nbytes - 4 * w;   // bytes of dword w to clear
+        const uint32_t m = drop >= 4 ? 0u : (drop <= 0 ? 0xffffffffu : (0xffffffffu << (8 * drop)));
+        v[w] &= m;
+    }
+    return v;
+}
+__device__ __forceinline__ u32x2 mask_head8(u32x2 v, int nbytes) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        const int drop = nbytes - 4 * w;
+        const uint32_t m = drop >= 4 ? 0u : (drop <= 0 ? 0xffffffffu : (0xffffffffu << (8 * drop)));
+        v[w] &= m;
+    }
+    return v;
+}
+
 // Keep the bytes [0, nbytes) of a 16-byte chunk, zero the rest (nbytes 0..16).
 __device__ __forceinline__ u32x4 mask_tail(u32x4 v, int nbytes) {
 #pragma unroll

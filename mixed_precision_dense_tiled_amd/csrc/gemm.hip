@@ -136,6 +136,13 @@ void gemm_kernel(GemmArgs g) {
     }
     const int m0 = tm * C::BM;
     const int n0 = tn * C::BN;
+    // One-wave kernel: the last tile column of a problem whose B rows end
+    // inside a 16-byte chunk is loaded from column N - BN, so that no 16-byte
+    // load runs past B's end, and stores only its own columns [n0, N).
+    int n0_load = n0;
+    if constexpr (ONE_WAVE) {
+        if (n0 + C::BN > g.N && ((int64_t)g.N * C::ES) % 16 != 0 && g.N >= C::BN) n0_load = g.N - C::BN;
+    }
     const bool full_mn = (m0 + C::BM <= g.M) && (n0 + C::BN <= g.N);
 
     const int64_t k_bytes = (int64_t)g.K * C::ES;
@@ -410,12 +417,16 @@ void gemm_kernel(GemmArgs g) {
         // there).  Partial tiles at the M and N edges and a partial last K
         // tile need no separate path: every buffer resource ends at its
         // operand's last byte, so A rows past M and B rows past K read as
-        // zero; B columns past N (and A rows' bytes past K, which belong to
-        // the next row) are finite or not but only reach outputs past N (the
-        // masked epilogue drops them) or are masked to zero in the last K
-        // tile's A fragments.
+        // zero; B columns past N only reach outputs the masked epilogue
+        // drops.  A 16-byte load that straddles a resource's end loses all
+        // its bytes, so no load may: the last tile column of B is shifted
+        // left (n0_load), and the last K tile is read as the KT-byte window
+        // that ends on the 16-byte boundary at or after K (each row's end then
+        // falls on a chunk boundary); its bytes before the previous tile's end
+        // and from K on are cleared in the fragments.
         if (!(k_bytes >= (int64_t)NS * C::KT_BYTES && g.lda_b < (int64_t(1) << 31) / C::BM &&
-              g.ldb_b < (int64_t(1) << 31) / C::KROWS && g.ldb_b >= C::B_ROW))
+              g.ldb_b < (int64_t(1) << 31) / C::KROWS && g.ldb_b >= C::B_ROW &&
+              (((int64_t)g.N * C::ES) % 16 == 0 || g.N >= C::BN)))
             return;
         if constexpr (ALIGNED && C::STEPS == 2 && C::TM == 4 && C::TN == 4) {
             // One wavefront per SIMD with a 128 x 128 wave tile, at least NS K
@@ -439,6 +450,8 @@ void gemm_kernel(GemmArgs g) {
             static_assert(C::UA == 4 && C::UB == 4, "four A and four B pieces per wave and K tile");
             const int nt = (int)((k_bytes + C::KT_BYTES - 1) / C::KT_BYTES);
             const int last_bytes = (int)(k_bytes - (int64_t)(nt - 1) * C::KT_BYTES);   // 1..KT_BYTES
+            const int shift = (16 - last_bytes % 16) % 16;   // the last window starts this far back
+            const int64_t kA_last = (int64_t)(nt - 1) * C::KT_BYTES - shift;
             constexpr int WAIT_AHEAD = (NS - 2) * DMA_PER_TILE;   // loads of tiles t+2..t+NS-1
             MPDT_LDS char* const lds0 = lds_cast(sA0);
 
@@ -464,17 +477,11 @@ void gemm_kernel(GemmArgs g) {
                 return (uint32_t)((wave * C::UB + u) * RPB) * (uint32_t)g.ldb_b - (uint32_t)u * 1024u;
             };
             const uint64_t baseA = (uint64_t)(uintptr_t)g.A + (uint64_t)((int64_t)m0 * g.lda_b);
-            const uint64_t baseB = (uint64_t)(uintptr_t)g.B + (uint64_t)((int64_t)n0 * C::ES);
-            // bytes of A / B from baseA / baseB, plus the 16 bytes past each
-            // operand's end that the host found to lie in the operand's last
-            // memory page (ext_a / ext_b): a 16-byte load that starts inside
-            // the operand then returns its bytes even where it runs past the
-            // end (a load that straddles the range end loses its bytes); the
-            // bytes past the end only reach outputs that are not stored or
-            // are masked in the last K tile
-            const int64_t restA0 = span_a + g.ext_a - (int64_t)m0 * g.lda_b;
-            const int64_t restB0 = span_b + g.ext_b - (int64_t)n0 * C::ES;
+            const uint64_t baseB = (uint64_t)(uintptr_t)g.B + (uint64_t)((int64_t)n0_load * C::ES);
+            const int64_t restA0 = span_a - (int64_t)m0 * g.lda_b;   // bytes of A from baseA
+            const int64_t restB0 = span_b - (int64_t)n0_load * C::ES;
             const int64_t stepB = (int64_t)C::KROWS * g.ldb_b;          // bytes per K tile of B
+            const int64_t kB_last = ((int64_t)(nt - 1) * C::KROWS - shift / C::ES) * g.ldb_b;
             auto clamp31 = [](int64_t r) { return (uint32_t)(r > 0x7fffffff ? 0x7fffffff : r); };
             // resources of K tile kt (kA = kt * KT_BYTES, kB = kt * stepB)
             auto rsA = [&](int64_t kA, bool live) {
@@ -543,8 +550,9 @@ void gemm_kernel(GemmArgs g) {
             Frags fr;
 #pragma unroll
             for (int p = 0; p < NS; ++p) {
-                const i32x4 ra = rsA((int64_t)p * C::KT_BYTES, true);
-                const i32x4 rb = rsB((int64_t)p * stepB, true);
+                const bool lastp = p == nt - 1;
+                const i32x4 ra = rsA(lastp ? kA_last : (int64_t)p * C::KT_BYTES, true);
+                const i32x4 rb = rsB(lastp ? kB_last : (int64_t)p * stepB, true);
                 static_for<0, DMA_PER_TILE>([&](auto Q) { dma_piece(Q, ra, rb, p * STAGE_BYTES); });
             }
             wait_vmem<(NS - 1) * DMA_PER_TILE>();
@@ -558,14 +566,15 @@ void gemm_kernel(GemmArgs g) {
                 const uint32_t cur = (uint32_t)scur * STAGE_BYTES;
                 const uint32_t nxt = (uint32_t)snext * STAGE_BYTES;
                 const bool live = t + NS < nt;
+                const bool lastl = t + NS == nt - 1;   // the tile loaded now is the last
                 i32x4 ra, rb;
                 // phase X
                 static_for<0, 16>([&](auto IDX) {
                     constexpr int idx = decltype(IDX)::value;
                     mma1(fr, 0, idx);
                     if constexpr (idx < 7) read_group(fr, 1, idx, cur);
-                    if constexpr (idx == 8) ra = rsA(kA, live);
-                    if constexpr (idx == 10) rb = rsB(kB, live);
+                    if constexpr (idx == 8) ra = rsA(lastl ? kA_last : kA, live);
+                    if constexpr (idx == 10) rb = rsB(lastl ? kB_last : kB, live);
                     __builtin_amdgcn_sched_barrier(0);
                 });
                 wait_vmem<WAIT_AHEAD>();
@@ -585,25 +594,28 @@ void gemm_kernel(GemmArgs g) {
                 kA += C::KT_BYTES;
                 kB += stepB;
             }
-            // last K tile; if it is partial, the fragment bytes at K and past
-            // it (A: the next row's bytes, B: the rows past K, zeros or the
-            // bytes of the page past the end) are cleared, so that every
-            // product past K is exactly zero whatever those bytes hold.  A
-            // lane's A fragment of step q covers K bytes [16 c, 16 c + 16) of
-            // the tile, c = 2 q + lhalf; its B fragment half h covers
-            // [32 q + 16 lhalf + 8 h, +8), in K order.
+            // last K tile; if it is partial, only the window bytes [shift,
+            // shift + last_bytes) are new K: the fragment bytes outside (the
+            // previous tile's last bytes, and from K on the next row's bytes,
+            // B rows past K or zeros) are cleared in A and in B, so every
+            // product outside is exactly zero whatever those bytes hold.  A
+            // lane's A fragment of step q covers window bytes [16 c, 16 c + 16),
+            // c = 2 q + lhalf; its B fragment half h covers [32 q + 16 lhalf +
+            // 8 h, +8), in K order.
+            auto keep_n = [](int from, int len, int x) { return min(max(x - from, 0), len); };
             auto mask_a = [&](int q) {
-                const int c = q * (F::STEP_BYTES / 16) + (int)lhalf * (C::FRAG_BYTES / 16);
-                const int keep = min(max(last_bytes - 16 * c, 0), 16);
-                const int keep_b0 = min(max(last_bytes - (32 * q + 16 * (int)lhalf), 0), 8);
-                const int keep_b1 = min(max(last_bytes - (32 * q + 16 * (int)lhalf + 8), 0), 8);
+                const int lo = shift, hi = shift + last_bytes;
+                const int a0 = 16 * (q * (F::STEP_BYTES / 16) + (int)lhalf * (C::FRAG_BYTES / 16));
+                const int b0 = 32 * q + 16 * (int)lhalf;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) fr.a[q][i][0] = mask_tail(fr.a[q][i][0], keep);
+                for (int i = 0; i < 4; ++i)
+                    fr.a[q][i][0] = mask_head(mask_tail(fr.a[q][i][0], keep_n(a0, 16, hi)), keep_n(a0, 16, lo));
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    fr.b[q][j][0] = mask_tail8(fr.b[q][j][0], keep_b0);
-                    fr.b[q][j][1] = mask_tail8(fr.b[q][j][1], keep_b1);
-                }
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        fr.b[q][j][h] = mask_head8(mask_tail8(fr.b[q][j][h], keep_n(b0 + 8 * h, 8, hi)),
+                                                   keep_n(b0 + 8 * h, 8, lo));
             };
             static_assert(F::STEP_BYTES == 32 && C::FRAG_BYTES == 16, "fragment K ranges as above");
             const bool partial = last_bytes < C::KT_BYTES;
@@ -705,7 +717,7 @@ void gemm_kernel(GemmArgs g) {
     using CT = typename std::conditional<KD == Kind::I8, int32_t, float>::type;
     const CT* const Cp = (const CT*)g.C;
     const int row_base = m0 + wm * C::WM + 4 * (int)lhalf;
-    const int col_base = n0 + wn * C::WN + (int)lrow;
+    const int col_base = n0_load + wn * C::WN + (int)lrow;
     constexpr int NTILE = C::TM * C::TN;
     auto epilogue = [&](auto out_tag) {
         using OutT = typename decltype(out_tag)::type;
@@ -809,21 +821,32 @@ void gemm_kernel(GemmArgs g) {
                 static_for<0, NTILE>([&](auto T) { store_t(decltype(T)::value, zero); });
             }
         } else {
-            // Edge tile: every element checked.
+            // Edge tile: every element checked; as above, C of the next 32x32
+            // tile is read (masked) before this one is stored, so the reads
+            // are not one round trip per element.
+            auto ok = [&](int t, int r) {
+                const int row = row_base + (t / C::TN) * 32 + 8 * (r >> 2) + (r & 3);
+                const int col = col_base + (t % C::TN) * 32;
+                return row < g.M && col < g.N && col >= n0;
+            };
+            auto at = [&](int t, int r, int64_t ld) {
+                return (int64_t)(row_base + (t / C::TN) * 32 + 8 * (r >> 2) + (r & 3)) * ld + col_base +
+                       (t % C::TN) * 32;
+            };
+            auto load_c = [&](int t, CT (&cv)[16]) {
 #pragma unroll
-            for (int i = 0; i < C::TM; ++i)
+                for (int r = 0; r < 16; ++r)
+                    cv[r] = (KD != Kind::FP8 && Cp && ok(t, r)) ? Cp[at(t, r, g.ldc)] : (CT)0;
+            };
+            CT cbuf[2][16];
+            load_c(0, cbuf[0]);
+            static_for<0, NTILE>([&](auto T) {
+                constexpr int t = decltype(T)::value;
+                if constexpr (t + 1 < NTILE) load_c(t + 1, cbuf[(t + 1) & 1]);
 #pragma unroll
-                for (int j = 0; j < C::TN; ++j) {
-                    const int col = col_base + j * 32;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
-                        if (row < g.M && col < g.N) {
-                            const CT c = (KD != Kind::FP8 && Cp) ? Cp[(int64_t)row * g.ldc + col] : (CT)0;
-                            Dp[(int64_t)row * g.ldd + col] = out_val(acc[i][j][r], c);
-                        }
-                    }
-                }
+                for (int r = 0; r < 16; ++r)
+                    if (ok(t, r)) Dp[at(t, r, g.ldd)] = out_val(acc[t / C::TN][t % C::TN][r], cbuf[t & 1][r]);
+            });
         }
     };
     using Out32 = typename std::conditional<KD == Kind::I8, int32_t, float>::type;
@@ -877,19 +900,11 @@ static hipError_t launch_general(GemmArgs a, bool aligned, int int_tm, int int_t
                    : launch_grid<KD, C, false>(a, tiles, stream);
 }
 
-// 16 when the 16 bytes after an operand's last byte lie in the same 4 KiB
-// page as that byte (so they are mapped whatever the allocation), else 0.
-static int page_slack(const char* base, int64_t span) {
-    const uint64_t end = (uint64_t)(uintptr_t)base + (uint64_t)span;   // one past the last byte
-    return ((end - 1) >> 12) == ((end + 15) >> 12) ? 16 : 0;
-}
-
 // FP16 / BF16 / INT8: a problem with at least STAGES K tiles (the last may be
 // partial) and 32-bit operand offsets goes to the one-wave kernel, edge tiles
-// and unaligned rows included, except the tile row holding A's last row when
-// a 16-byte load there would run past A's end into an unmapped page (rows of
-// K bytes not a multiple of 16), and likewise the tile column holding B's
-// last column; those, and every other problem, go to the general kernel.
+// and unaligned rows included (B rows of at least one tile row, and at least
+// one full tile column when B's rows end inside a 16-byte chunk); any other
+// problem to the general kernel.
 template <Kind KD, class C1, class C8>
 static hipError_t launch_mma(const GemmArgs& a0, bool aligned, hipStream_t stream) {
     static_assert(C1::BM == C8::BM && C1::BN == C8::BN, "one tile grid for both kernels");
@@ -898,22 +913,14 @@ static hipError_t launch_mma(const GemmArgs& a0, bool aligned, hipStream_t strea
     // off its row offset, which needs rows of at least one B tile row: ldb >=
     // BN elements; lda >= K >= STAGES K tiles covers A)
     const bool one = kb >= (int64_t)C1::STAGES * C1::KT_BYTES && a0.lda_b < (int64_t(1) << 31) / C1::BM &&
-                     a0.ldb_b < (int64_t(1) << 31) / C1::KROWS && a0.ldb_b >= C1::B_ROW;
+                     a0.ldb_b < (int64_t(1) << 31) / C1::KROWS && a0.ldb_b >= C1::B_ROW &&
+                     (((int64_t)a0.N * C1::ES) % 16 == 0 || a0.N >= C1::BN);
     if (one) {
         GemmArgs a = a0;
-        a.ext_a = page_slack(a0.A, (int64_t)(a0.M - 1) * a0.lda_b + kb);
-        a.ext_b = page_slack(a0.B, (int64_t)(a0.K - 1) * a0.ldb_b + (int64_t)a0.N * C1::ES);
-        const int tiles_m = (a0.M + C1::BM - 1) / C1::BM, tiles_n = (a0.N + C1::BN - 1) / C1::BN;
-        const int int_tm = tiles_m - ((kb % 16 != 0 && a.ext_a == 0) ? 1 : 0);
-        const int int_tn = tiles_n - ((((int64_t)a0.N * C1::ES) % 16 != 0 && a.ext_b == 0) ? 1 : 0);
-        if (int_tm > 0 && int_tn > 0) {
-            a.tiles_m = int_tm;
-            a.tiles_n = int_tn;
-            a.int_tm = a.int_tn = 0;
-            const hipError_t e = launch_grid<KD, C1, true>(a, (int64_t)int_tm * int_tn, stream);
-            if (e != hipSuccess) return e;
-            return launch_general<KD, C8>(a0, aligned, int_tm, int_tn, stream);
-        }
+        a.tiles_m = (a0.M + C1::BM - 1) / C1::BM;
+        a.tiles_n = (a0.N + C1::BN - 1) / C1::BN;
+        a.int_tm = a.int_tn = 0;
+        return launch_grid<KD, C1, true>(a, (int64_t)a.tiles_m * a.tiles_n, stream);
     }
     return launch_general<KD, C8>(a0, aligned, 0, 0, stream);
 }

@@ -25,7 +25,6 @@ struct GemmArgs {
     int int_tm, int_tn;   // interior tiles launched separately (0: none)
     int out16;            // FP16/BF16 inputs: D is written in the input format (RNE)
     int d16_vec;          // out16 with D and its rows 16-byte aligned: wide stores allowed
-    int ext_a, ext_b;     // one-wave kernel: bytes past A's / B's end inside their last page (0 or 16)
 };
 
 // aligned: every row start of A and B is 16-byte aligned.
