@@ -165,6 +165,35 @@ def test_interior_and_edge_tiles_uniform_in_place(gpu_ok, fmt):
     assert torch.equal(t0.view(torch.int32), tz.view(torch.int32))
 
 
+# The one-wave kernel takes every tile of a problem with at least four K
+# tiles: its last K tile is read as a 64-byte window ending on the 16-byte
+# boundary at or after K (the bytes before the previous tile's end and from K
+# on cleared in the fragments), and the last tile column of B is loaded from
+# column N - 256 when B's rows end inside a 16-byte chunk.  Every residue of
+# K modulo 32 elements that exercises a different window offset, rows padded
+# with NaN, integer inputs: bit-exact.
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("K", [129, 131, 135, 136, 137, 143, 144, 145, 159, 160])
+def test_one_wave_k_window_bit_exact(gpu_ok, fmt, K):
+    M, N = 300, 272
+    A, B, C = inputs.gemm16_operands(M, N, K, dist="int4", fmt=fmt, seeds=(K, M, N))
+    D, R, _, _ = run16(fmt, A, B, C, lda=K + 5, ldb=N + 3)
+    assert np.array_equal(D, R.astype(np.float32)), f"{fmt} K={K}"
+
+
+# B rows that end inside a 16-byte chunk (N * 2 bytes not a multiple of 16)
+# with N >= 256: the shifted last tile column must store only its own columns,
+# also in place (D == C, where a second write of a column would add A.B twice).
+@pytest.mark.parametrize("N", [257, 263, 511, 777])
+def test_one_wave_shifted_last_column_in_place(gpu_ok, N):
+    M, K = 264, 200
+    A, B, C = inputs.gemm16_operands(M, N, K, dist="int4", fmt="f16", seeds=(N, 1, 2))
+    tC = dev(C)
+    D = mp.gemm_f16(dev(A), dev(B, N + 1, pad=NAN16["f16"]), tC, out=tC)
+    R, _ = oracle.gemm_f16(A, B, C)
+    assert np.array_equal(host(D), R.astype(np.float32)), f"N={N}"
+
+
 EDGE = [1, 15, 16, 17, 31, 33, 127, 128, 129, 255, 257]
 
 
@@ -187,6 +216,16 @@ def test_edge_sweep(gpu_ok):
 def test_i8_bit_exact(gpu_ok, M, N, K):
     A, B, C = inputs.i8_operands(M, N, K, seeds=(M, N, K))
     D = host(mp.gemm_i8_i32(dev(A), dev(B), dev(C)))
+    assert np.array_equal(D, oracle.gemm_i8_i32(A, B, C))
+
+
+# INT8 through the one-wave kernel: K tails of every 16-byte residue class,
+# rows of B ending inside a 16-byte chunk (N % 16 != 0), unaligned rows.
+@pytest.mark.parametrize("M,N,K", [(260, 263, 257), (300, 300, 263), (256, 511, 300),
+                                   (257, 270, 321), (129, 777, 399)])
+def test_i8_one_wave_edges_bit_exact(gpu_ok, M, N, K):
+    A, B, C = inputs.i8_operands(M, N, K, seeds=(M, N, K))
+    D = host(mp.gemm_i8_i32(dev(A, K + 3, pad=-128), dev(B, N + 7, pad=127), dev(C)))
     assert np.array_equal(D, oracle.gemm_i8_i32(A, B, C))
 
 
