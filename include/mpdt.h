@@ -139,7 +139,7 @@ mpdt_status gemv_w8a8(int64_t M, int64_t N, int64_t K,
  * when bias is NULL).  X: M x K INT8 (ldx); W: N x K INT8, one output channel
  * per row (ldw); x_scale: M FP32; w_scale, bias: N FP32; Y: M x N BF16 bits
  * (ldy); Z (optional, may be NULL): M x N INT32 (ldz).  The weights are read
- * once per group of up to 16 tokens.  Exact while K * 128^2 < 2^31. */
+ * once per group of up to 32 tokens.  Exact while K * 128^2 < 2^31. */
 mpdt_status gemm_w8a8(int64_t M, int64_t N, int64_t K,
                       const int8_t* X, int64_t ldx, const float* x_scale,
                       const int8_t* W, int64_t ldw, const float* w_scale, const float* bias,

@@ -203,6 +203,17 @@ __device__ __forceinline__ u32x2 lds_read_tr8(const MPDT_LDS char* base, uint32_
     return __builtin_bit_cast(u32x2, r);
 }
 
+// FP32 multiply and add, each rounded on its own: never contracted into a
+// fused multiply-add with a neighbouring operation.
+__device__ __forceinline__ float mul_rn(float a, float b) {
+#pragma clang fp contract(off)
+    return a * b;
+}
+__device__ __forceinline__ float add_rn(float a, float b) {
+#pragma clang fp contract(off)
+    return a + b;
+}
+
 // Round FP32 to FP16 (nearest, ties to even, subnormals kept, overflow to
 // infinity) with the hardware conversion.
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {

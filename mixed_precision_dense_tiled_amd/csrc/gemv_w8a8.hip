@@ -123,125 +123,122 @@ hipError_t launch_gemv_w8a8(const GemvArgs& a, bool aligned, hipStream_t stream)
 // The same layer for M tokens at once (a small batch), each with its own
 // activation scale, and an optional bias added after the dequantisation
 // (section 5.1 of the same page: a bias belongs in the floating-point
-// epilogue).  The weights are still streamed from HBM exactly once for up to
-// 16 tokens: the workgroup stages the tokens' K slice in LDS, each wave owns
-// two output channels and, for every 16-byte chunk of a weight row, takes the
-// v_dot4 products with the same chunk of every token.  Larger batches are cut
-// into groups of 16 tokens on the host (one launch each).
+// epilogue).
 //   z[m][o] = sum_k X[m][k] * W[o][k]          (INT32, exact)
 //   y[m][o] = bf16_rne( ((float(z) * s_x[m]) * s_w[o]) + bias[o] )
+// With more than one token the products are a small GEMM, Z = X . W^T, whose
+// operands are both K-contiguous: a 32x32x32 INT8 MFMA takes 32 tokens
+// (rows of X, zero past M) as its A operand and 32 output channels (rows of
+// W) as its B operand, each lane reading 16 consecutive K bytes of one row
+// straight from memory -- no LDS, no transposes.  The weights are streamed
+// exactly once per 32 tokens: a workgroup owns 32 channels, its four waves
+// take interleaved 128-byte slices of K (4 MFMA steps each, so every wave
+// load covers 128 contiguous bytes of each of its 32 rows), then add their
+// partial sums through LDS.  The work stays HBM-bound: the MFMA rate is far
+// above what 32 tokens need, so the rows of the A operand past M cost nothing
+// that matters.
 // ---------------------------------------------------------------------------
-constexpr int TOK_WAVES = 4;       // wavefronts per workgroup
-constexpr int TOK_ROWS = 2;        // output channels per wavefront
-constexpr int TOK_KC = 4096;       // K bytes staged per pass (MG * 4 KiB of LDS)
+constexpr int TOK_WAVES = 4;                   // wavefronts per workgroup
+constexpr int TOK_GROUP = 8;                   // MFMA steps (32 K bytes each) per wave slice
 
-template <int MG, bool ALIGNED>
 __global__ __launch_bounds__(64 * TOK_WAVES) void gemm_w8a8_kernel(W8A8Args g) {
-    __shared__ __attribute__((aligned(16))) char xs[MG][TOK_KC];
+    __shared__ int partial[TOK_WAVES - 1][16][64];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int row0 = (blockIdx.x * TOK_WAVES + wave) * TOK_ROWS;
+    const int o0 = blockIdx.x * 32;
+    const int r32 = lane & 31;                 // token row (A) / channel (B) of this lane
+    const int half = lane >> 5;                // which 16 bytes of a 32-byte K step
     const int64_t K = g.K;
+    const int64_t kslice = 32 * TOK_GROUP;     // K bytes per wave slice
 
-    int acc[TOK_ROWS][MG];
-#pragma unroll
-    for (int r = 0; r < TOK_ROWS; ++r)
-#pragma unroll
-        for (int m = 0; m < MG; ++m) acc[r][m] = 0;
+    // this lane's rows: token r32 of X, channel o0 + r32 of W; a lane past M
+    // or N reads row 0 instead and zeroes what it read, so the loads of a full
+    // slice carry no branches (and stay in flight together)
+    const bool xrow = r32 < g.M;
+    const bool wrow = o0 + r32 < g.N;
+    const char* xp = (const char*)g.X + (int64_t)(xrow ? r32 : 0) * g.ldx;
+    const char* wp = (const char*)g.W + (int64_t)(wrow ? o0 + r32 : 0) * g.ldw;
+    const uint32_t xkeep = xrow ? ~0u : 0u, wkeep = wrow ? ~0u : 0u;
 
-    for (int64_t kc = 0; kc < K; kc += TOK_KC) {
-        const int64_t kn = min((int64_t)TOK_KC, K - kc);   // valid bytes of this pass
-        // stage the tokens' K slice (zero past M and past K)
-        for (int i = tid; i < MG * (TOK_KC / 16); i += 64 * TOK_WAVES) {
-            const int m = i / (TOK_KC / 16), c = i % (TOK_KC / 16);
-            u32x4 v = u32x4{0u, 0u, 0u, 0u};
-            if (m < g.M) {
-                const char* rowp = (const char*)g.X + (int64_t)m * g.ldx + kc;
-                v = load16_row<ALIGNED>(rowp + c * 16, rowp + kn);
-            }
-            lds_store16(lds_cast(xs[m]), c * 16, v);
+    i32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0;
+    auto mma = [&](const u32x4 (&xv)[TOK_GROUP], const u32x4 (&wv)[TOK_GROUP]) {
+#pragma unroll
+        for (int s = 0; s < TOK_GROUP; ++s)
+            acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, xv[s]),
+                                                        __builtin_bit_cast(i32x4, wv[s]), acc, 0, 0, 0);
+    };
+    int64_t k0 = (int64_t)wave * kslice;
+    // full slices: plain 16-byte loads (any byte alignment is fine for them)
+    for (; k0 + kslice <= K; k0 += (int64_t)TOK_WAVES * kslice) {
+        u32x4 wv[TOK_GROUP], xv[TOK_GROUP];
+#pragma unroll
+        for (int s = 0; s < TOK_GROUP; ++s) {
+            const int64_t off = k0 + 32 * s + 16 * half;
+            wv[s] = *reinterpret_cast<const u32x4*>(wp + off) & wkeep;
+            xv[s] = *reinterpret_cast<const u32x4*>(xp + off) & xkeep;
         }
-        __syncthreads();
-        // weights of this wave's rows for the whole pass, then the products
-        u32x4 wv[TOK_ROWS][TOK_KC / 1024];
+        mma(xv, wv);
+    }
+    // the one partial slice (K past it reads as zero; bounded loads)
+    if (k0 < K) {
+        u32x4 wv[TOK_GROUP], xv[TOK_GROUP];
 #pragma unroll
-        for (int r = 0; r < TOK_ROWS; ++r) {
-            const int row = row0 + r;
-            const char* rowp = (const char*)g.W + (int64_t)row * g.ldw + kc;
-#pragma unroll
-            for (int u = 0; u < TOK_KC / 1024; ++u) {
-                const int64_t off = 16 * (lane + 64 * u);
-                if (row >= g.N)
-                    wv[r][u] = u32x4{0u, 0u, 0u, 0u};
-                else if (ALIGNED && off + 16 <= kn)
-                    wv[r][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rowp + off));
-                else
-                    wv[r][u] = load16_row<ALIGNED>(rowp + off, rowp + kn);
-            }
+        for (int s = 0; s < TOK_GROUP; ++s) {
+            const int64_t off = k0 + 32 * s + 16 * half;
+            wv[s] = load16_row<false>(wp + off, wp + K) & wkeep;
+            xv[s] = load16_row<false>(xp + off, xp + K) & xkeep;
         }
-#pragma unroll
-        for (int u = 0; u < TOK_KC / 1024; ++u) {
-#pragma unroll
-            for (int m = 0; m < MG; ++m) {
-                const u32x4 xv = lds_load16(lds_cast(xs[m]), (uint32_t)(16 * (lane + 64 * u)));
-#pragma unroll
-                for (int r = 0; r < TOK_ROWS; ++r) acc[r][m] = dot16(wv[r][u], xv, acc[r][m]);
-            }
-        }
-        __syncthreads();
+        mma(xv, wv);
     }
 
+    // sum the four waves' partial products (exact INT32)
+    if (wave > 0) {
 #pragma unroll
-    for (int r = 0; r < TOK_ROWS; ++r)
+        for (int r = 0; r < 16; ++r) partial[wave - 1][r][lane] = acc[r];
+    }
+    __syncthreads();
+    if (wave != 0) return;
 #pragma unroll
-        for (int m = 0; m < MG; ++m) acc[r][m] = wave_sum(acc[r][m]);
+    for (int w = 0; w < TOK_WAVES - 1; ++w)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] += partial[w][r][lane];
 
-    // lane r * MG + m writes channel row0 + r of token m
+    // accumulator r of lane l: token 8 (r / 4) + 4 (l / 32) + r % 4, channel o0 + l % 32
+    const int o = o0 + r32;
+    if (o >= g.N) return;
+    const float sw = g.w_scale[o];
+    const float b = g.bias ? g.bias[o] : 0.0f;
 #pragma unroll
-    for (int r = 0; r < TOK_ROWS; ++r)
-#pragma unroll
-        for (int m = 0; m < MG; ++m) {
-            const int row = row0 + r;
-            if (lane == r * MG + m && row < g.N && m < g.M) {
-                const int z = acc[r][m];
-                if (g.Z) g.Z[(int64_t)m * g.ldz + row] = z;
-                float v = (float)z;
-                v = v * g.x_scale[m];
-                v = v * g.w_scale[row];
-                if (g.bias) v = v + g.bias[row];
-                g.Y[(int64_t)m * g.ldy + row] = f32_to_bf16_bits(v);
-            }
+    for (int r = 0; r < 16; ++r) {
+        const int m = 8 * (r >> 2) + 4 * half + (r & 3);
+        if (m < g.M) {
+            const int z = acc[r];
+            if (g.Z) g.Z[(int64_t)m * g.ldz + o] = z;
+            // three separately rounded FP32 operations (no fused multiply-add)
+            float v = mul_rn((float)z, g.x_scale[m]);
+            v = mul_rn(v, sw);
+            if (g.bias) v = add_rn(v, b);
+            g.Y[(int64_t)m * g.ldy + o] = f32_to_bf16_bits(v);
         }
+    }
 }
 
-template <int MG>
-static hipError_t launch_tokens(const W8A8Args& a, bool aligned, hipStream_t stream) {
-    const int rows_per_wg = TOK_WAVES * TOK_ROWS;
-    dim3 grid((unsigned)((a.N + rows_per_wg - 1) / rows_per_wg)), block(64 * TOK_WAVES);
-    if (aligned)
-        hipLaunchKernelGGL((gemm_w8a8_kernel<MG, true>), grid, block, 0, stream, a);
-    else
-        hipLaunchKernelGGL((gemm_w8a8_kernel<MG, false>), grid, block, 0, stream, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_gemm_w8a8(const W8A8Args& a0, bool aligned, hipStream_t stream) {
+hipError_t launch_gemm_w8a8(const W8A8Args& a0, bool /*aligned*/, hipStream_t stream) {
     if (a0.N <= 0 || a0.M <= 0) return hipSuccess;
-    // groups of at most 16 tokens, each group one launch reading W once
-    for (int m0 = 0; m0 < a0.M; m0 += 16) {
+    // groups of at most 32 tokens, each group one launch reading W once
+    for (int m0 = 0; m0 < a0.M; m0 += 32) {
         W8A8Args a = a0;
-        a.M = min(16, a0.M - m0);
+        a.M = min(32, a0.M - m0);
         a.X = a0.X + (int64_t)m0 * a0.ldx;
         a.x_scale = a0.x_scale + m0;
         a.Y = a0.Y + (int64_t)m0 * a0.ldy;
         a.Z = a0.Z ? a0.Z + (int64_t)m0 * a0.ldz : nullptr;
-        hipError_t e;
-        if (a.M == 1) e = launch_tokens<1>(a, aligned, stream);
-        else if (a.M == 2) e = launch_tokens<2>(a, aligned, stream);
-        else if (a.M <= 4) e = launch_tokens<4>(a, aligned, stream);
-        else if (a.M <= 8) e = launch_tokens<8>(a, aligned, stream);
-        else e = launch_tokens<16>(a, aligned, stream);
+        dim3 grid((unsigned)((a.N + 31) / 32)), block(64 * TOK_WAVES);
+        hipLaunchKernelGGL(gemm_w8a8_kernel, grid, block, 0, stream, a);
+        const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

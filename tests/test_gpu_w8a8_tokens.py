@@ -2,9 +2,10 @@
 the two quantisers, against the oracle, bit-exact (every step is an integer
 sum or a fixed sequence of IEEE FP32 operations, then one rounding):
 
-  * gemm_w8a8: M = 1, 2, 3, 5, 8, 16, 17, 40 tokens (groups of 16 per launch),
-    N not a multiple of a workgroup's rows, K not a multiple of the 4 KiB
-    pass, with and without bias, padded and misaligned operands, -128 at the
+  * gemm_w8a8: M = 1, 2, 3, 5, 8, 16, 17, 31, 32, 33, 40, 65 tokens (groups of
+    32 per launch),
+    N not a multiple of a workgroup's 32 channels, K not a multiple of the
+    wave slices, with and without bias, padded and misaligned operands, -128 at the
     INT32 bound, K = 0, and the full 4096 x 14336 layer for 4 tokens;
   * quantize_i8_rows: random BF16 rows, exact ties, zero rows, K tails;
   * quantize_fp8_blocks: 1 x 128 and 128 x 128 blocks, ragged edges, a zero
@@ -44,7 +45,7 @@ def run_w8a8(X, sx, W, sw, bias, ldx=None, ldw=None, shift=0):
     return host(z), host(y).view(np.uint16), zr, yr
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 16, 17, 40])
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 16, 17, 31, 32, 33, 40, 65])
 @pytest.mark.parametrize("with_bias", [False, True])
 def test_w8a8_tokens_bit_exact(gpu_ok, M, with_bias):
     X, sx, W, sw, bias = w8a8_inputs(M, 1000, 4500, seed=M)
