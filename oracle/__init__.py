@@ -85,6 +85,8 @@ def _load():
         _lib.oracle_quantize_fp8_blocks.restype = ctypes.c_int
         _lib.oracle_quantize_fp8_blocks.argtypes = ([_c_i64, _c_i64, _vp, _c_i64, _c_i64, _c_i64]
                                                     + [_vp, _c_i64, _vp, _c_i64])
+        _lib.oracle_bias_act.restype = ctypes.c_int
+        _lib.oracle_bias_act.argtypes = [_c_i64, _c_i64, _vp, _c_i64, _vp, ctypes.c_int]
         _lib.oracle_gemv_w8a8.restype = ctypes.c_int
         _lib.oracle_gemv_w8a8.argtypes = [_c_i64, _c_i64, _vp, ctypes.c_float, _vp, _c_i64, _vp,
                                           _vp, _vp]
@@ -337,6 +339,39 @@ def gemm_w8a8(X, s_x, W, s_w, bias=None):
                                     _ptr(b), Z.ctypes.data, max(N, 1), Y.ctypes.data, max(N, 1)),
            "gemm_w8a8")
     return Z, Y
+
+
+# ------------------------------------------------- bias + activation --
+ACT_NONE, ACT_RELU, ACT_GELU, ACT_SILU = 0, 1, 2, 3
+
+
+def bias_act(R, bias, act):
+    """oracle_bias_act on a copy of the FP64 matrix R: act(R + bias[j])."""
+    R = np.array(R, dtype=np.float64, order="C", copy=True)
+    M, N = R.shape
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    _check(_load().oracle_bias_act(M, N, R.ctypes.data, max(N, 1), _ptr(b), int(act)),
+           "oracle_bias_act")
+    return R
+
+
+def gemm16_bias_act(fmt, A, B, C, bias, act):
+    """FP16 ("f16") / BF16 ("bf16") GEMM followed by the bias and activation
+    epilogue.  Returns (R, S, P): R = act(A.B + C + bias) in FP64, S the
+    GEMM's sum |a.b| and P = A.B + C + bias (the value the activation sees)."""
+    R0, S = (gemm_f16 if fmt == "f16" else gemm_bf16)(A, B, C)
+    return bias_act(R0, bias, act), S, bias_act(R0, bias, ACT_NONE)
+
+
+def gemm16_bias_act_at(fmt, A, B, C, bias, act, ii, jj):
+    """gemm16_bias_act at output positions (ii[p], jj[p]) only."""
+    R0, S = (gemm_f16_at if fmt == "f16" else gemm_bf16_at)(A, B, C, ii, jj)
+    bj = None if bias is None else np.asarray(bias, np.float32)[np.asarray(jj)]
+    # one row of P sampled points, each with its own column's bias
+    row = R0.reshape(1, -1)
+    bb = None if bj is None else bj.reshape(-1)
+    return (bias_act(row, bb, act).reshape(R0.shape), S,
+            bias_act(row, bb, ACT_NONE).reshape(R0.shape))
 
 
 # ------------------------------------------------------------ quantisers --

@@ -547,3 +547,31 @@ int oracle_quantize_fp8_blocks(int64_t R, int64_t Cc, const float* X, int64_t ld
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Bias and activation epilogue (see oracle.h).                               */
+/* ------------------------------------------------------------------------ */
+static double act_of(double v, int act) {
+    switch (act) {
+        case 1: return v > 0.0 ? v : 0.0;
+        /* Phi(v) = erfc(-v / sqrt 2) / 2: the same function as (1 + erf) / 2
+         * without its cancellation for negative v */
+        case 2: return 0.5 * v * erfc(-v / sqrt(2.0));
+        case 3: return v / (1.0 + exp(-v));
+        default: return v;
+    }
+}
+
+int oracle_bias_act(int64_t M, int64_t N, double* R, int64_t ldr, const float* bias, int act) {
+    if (M < 0 || N < 0 || !R || act < 0 || act > 3 || (M > 0 && ldr < N)) return 1;
+    if (bias)
+        for (int64_t j = 0; j < N; ++j)
+            if (!isfinite(bias[j])) return 2;
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j) {
+            double v = R[i * ldr + j];
+            if (bias) v += (double)bias[j];
+            R[i * ldr + j] = act_of(v, act);
+        }
+    return 0;
+}

@@ -146,6 +146,17 @@ int oracle_quantize_fp8_blocks(int64_t R, int64_t Cc, const float* X, int64_t ld
                                int64_t br, int64_t bc, uint8_t* Q, int64_t ldq,
                                float* S, int64_t lds);
 
+/* ---- Bias and activation after a FP16 / BF16 GEMM (the fused epilogue of
+ * the 16-bit GEMM entry points).  In place on an M x N FP64 result R
+ * (leading dimension ldr): R[i][j] = act(R[i][j] + bias[j]), the bias being
+ * one FP32 value per output column ("NVIDIA A100: from chip to SIMT",
+ * section 5.1: a linear layer's bias is added in the floating-point
+ * epilogue; bias may be NULL: no add).  act: 0 identity, 1 ReLU
+ * (v if v > 0, else 0), 2 GELU (v * Phi(v), Phi the standard normal CDF,
+ * Phi(v) = erfc(-v / sqrt 2) / 2 = (1 + erf(v / sqrt 2)) / 2), 3 SiLU (v / (1 + exp(-v))).
+ * Returns 1 for an unknown act or bad arguments, 2 for a non-finite bias. ---- */
+int oracle_bias_act(int64_t M, int64_t N, double* R, int64_t ldr, const float* bias, int act);
+
 #ifdef __cplusplus
 }
 #endif
