@@ -94,6 +94,38 @@ mpdt_status gemm_bf16_bf16out(int64_t M, int64_t N, int64_t K,
                               const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                               const float* C, int64_t ldc, uint16_t* D, int64_t ldd, void* stream);
 
+/* Activations of the fused GEMM epilogue. */
+typedef enum {
+    MPDT_ACT_NONE = 0,   /* identity */
+    MPDT_ACT_RELU = 1,   /* v if v > 0, else +0 (NaN gives +0) */
+    MPDT_ACT_GELU = 2,   /* v * Phi(v), Phi the standard normal CDF (erf form, not the
+                            tanh approximation) */
+    MPDT_ACT_SILU = 3    /* v / (1 + exp(-v)) */
+} mpdt_act;
+
+/* FP16 / BF16 GEMM with a fused bias + activation epilogue, the linear
+ * layer's floating-point epilogue ("NVIDIA A100: from chip to SIMT",
+ * section 5.1, adds the bias there) written together with D:
+ *   v = acc + C[i][j]        (acc: A . B in FP32, as in gemm_f16 / gemm_bf16)
+ *   v = v + bias[j]          (skipped when bias is NULL)
+ *   D[i][j] = act(v)         (act: an mpdt_act; FP32 arithmetic)
+ * then D is FP32 (d16 = 0) or rounded once, to nearest even, to the input
+ * format (d16 = 1: FP16 for gemm_f16_bias_act, BF16 for gemm_bf16_bias_act).
+ * Each step is an FP32 operation in this order (the additions are exact when
+ * every value is a small integer).  GELU and SiLU use the device's erfcf /
+ * expf and an IEEE division: within a few FP32 ulps of the exact function of
+ * v.  bias: N FP32 values (device pointer, 4-byte aligned, may be NULL; D
+ * may not overlap it).  C may be NULL; C == D in place only with d16 = 0.
+ * An act outside mpdt_act or d16 outside {0, 1} is MPDT_ERROR_INVALID_VALUE. */
+mpdt_status gemm_f16_bias_act(int64_t M, int64_t N, int64_t K,
+                              const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                              const float* C, int64_t ldc, const float* bias, int act,
+                              void* D, int64_t ldd, int d16, void* stream);
+mpdt_status gemm_bf16_bias_act(int64_t M, int64_t N, int64_t K,
+                               const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                               const float* C, int64_t ldc, const float* bias, int act,
+                               void* D, int64_t ldd, int d16, void* stream);
+
 /* D[M x N] (INT32) = A[M x K] (INT8) . B[K x N] (INT8) + C (INT32), exact
  * as long as no partial sum leaves the INT32 range (K * 128^2 + |C| < 2^31
  * guarantees it).  C may be NULL. */

@@ -18,7 +18,8 @@ import os
 
 import torch
 
-__all__ = ["gemm_f16", "gemm_bf16", "gemm_f16_f16out", "gemm_bf16_bf16out", "gemm_i8_i32",
+__all__ = ["gemm_f16", "gemm_bf16", "gemm_f16_f16out", "gemm_bf16_bf16out", "gemm_f16_bias_act",
+           "gemm_bf16_bias_act", "ACT_NONE", "ACT_RELU", "ACT_GELU", "ACT_SILU", "gemm_i8_i32",
            "gemm_fp8_blockscaled", "gemv_w8a8", "gemm_w8a8", "quantize_i8_rows",
            "quantize_fp8_blocks",
            "MpdtError", "lib", "lib_path", "version"]
@@ -56,6 +57,10 @@ def lib() -> ctypes.CDLL:
         for name in ("gemm_f16", "gemm_bf16", "gemm_i8_i32", "gemm_f16_f16out",
                      "gemm_bf16_bf16out"):
             getattr(L, name).argtypes = gemm_args
+            getattr(L, name).restype = ctypes.c_int
+        for name in ("gemm_f16_bias_act", "gemm_bf16_bias_act"):
+            getattr(L, name).argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+                                         ctypes.c_int, _vp, _i64, ctypes.c_int, _vp]
             getattr(L, name).restype = ctypes.c_int
         L.gemm_fp8_blockscaled.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
                                            _i64, _vp, _i64, _vp]
@@ -143,6 +148,47 @@ def gemm_bf16_bf16out(A, B, C=None, out=None):
     """D = bf16(A . B + C); A [M,K], B [K,N] BF16 bits, C [M,N] FP32 (optional);
     returns D as a bfloat16 tensor."""
     return _gemm16("gemm_bf16_bf16out", A, B, C, out, torch.bfloat16)
+
+
+# activations of the fused epilogue (mpdt_act)
+ACT_NONE, ACT_RELU, ACT_GELU, ACT_SILU = 0, 1, 2, 3
+
+
+def _gemm16_bias_act(fn, A, B, C, bias, act, out, out_dtype):
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    pa, lda = _mat(A, 2, "A")
+    pb, ldb = _mat(B, 2, "B")
+    pc, ldc = (None, N) if C is None else _mat(C, 4, "C")
+    if bias is not None:
+        if bias.dim() != 1 or bias.numel() != N or bias.element_size() != 4 or not bias.is_cuda:
+            raise ValueError("bias must be a GPU tensor of N 4-byte values")
+        if N > 1 and bias.stride(0) != 1:
+            raise ValueError("bias must be contiguous")
+    pbias = None if bias is None else bias.data_ptr()
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    d16 = out.element_size() == 2
+    pd, ldd = _mat(out, 2 if d16 else 4, "out")
+    _check(fn, getattr(lib(), fn)(M, N, K, pa, lda, pb, ldb, pc, ldc, pbias, int(act), pd, ldd,
+                                  int(d16), _stream(A)))
+    return out
+
+
+def gemm_f16_bias_act(A, B, C=None, bias=None, act=ACT_NONE, out=None, d16=False):
+    """D = act(A . B + C + bias); A [M,K], B [K,N] FP16 bits, C [M,N] FP32 and
+    bias [N] FP32 (both optional); D FP32, or FP16 with d16 (or a 2-byte out)."""
+    return _gemm16_bias_act("gemm_f16_bias_act", A, B, C, bias, act, out,
+                            torch.float16 if d16 else torch.float32)
+
+
+def gemm_bf16_bias_act(A, B, C=None, bias=None, act=ACT_NONE, out=None, d16=False):
+    """D = act(A . B + C + bias); A [M,K], B [K,N] BF16 bits, C [M,N] FP32 and
+    bias [N] FP32 (both optional); D FP32, or BF16 with d16 (or a 2-byte out)."""
+    return _gemm16_bias_act("gemm_bf16_bias_act", A, B, C, bias, act, out,
+                            torch.bfloat16 if d16 else torch.float32)
 
 
 def gemm_i8_i32(A, B, C=None, out=None):

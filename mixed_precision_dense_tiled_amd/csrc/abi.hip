@@ -13,6 +13,10 @@
 #include "kernels.hpp"
 #include "mpdt.h"
 
+static_assert(MPDT_ACT_NONE == mpdt::ACT_NONE && MPDT_ACT_RELU == mpdt::ACT_RELU &&
+                  MPDT_ACT_GELU == mpdt::ACT_GELU && MPDT_ACT_SILU == mpdt::ACT_SILU,
+              "activation codes of the C ABI and the kernels agree");
+
 #define MPDT_EXPORT extern "C" __attribute__((visibility("default")))
 
 namespace {
@@ -109,7 +113,7 @@ mpdt_status check_gemm(const char* fn, int64_t M, int64_t N, int64_t K, const vo
     if (sd.overlaps(sa) || sd.overlaps(sb))
         return fail(MPDT_ERROR_ALIASING, fn, "D overlaps A or B");
     for (int i = 0; i < n_extra; ++i)
-        if (sd.overlaps(extra_inputs[i])) return fail(MPDT_ERROR_ALIASING, fn, "D overlaps a scale array");
+        if (sd.overlaps(extra_inputs[i])) return fail(MPDT_ERROR_ALIASING, fn, "D overlaps a scale or bias array");
     if (C && sd.overlaps(sc) && !(C == D && ldc == ldd))
         return fail(MPDT_ERROR_ALIASING, fn, "C overlaps D without being exactly D");
     return MPDT_SUCCESS;
@@ -119,13 +123,22 @@ mpdt_status check_gemm(const char* fn, int64_t M, int64_t N, int64_t K, const vo
 mpdt_status run_gemm16(const char* fn, mpdt::Kind kind, int64_t M, int64_t N, int64_t K,
                        const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                        const float* C, int64_t ldc, void* D, int64_t ldd, int out16,
-                       void* stream) {
+                       void* stream, bool fused = false, const float* bias = nullptr, int act = 0) {
+    if (out16 != 0 && out16 != 1) return fail(MPDT_ERROR_INVALID_VALUE, fn, "d16 must be 0 or 1");
+    if (fused && (act < MPDT_ACT_NONE || act > MPDT_ACT_SILU))
+        return fail(MPDT_ERROR_INVALID_VALUE, fn, "unknown activation");
     const int64_t esd = out16 ? 2 : 4;
     // a 16-bit D cannot be updated in place from an FP32 C
     if (out16 && C && (const void*)C == (const void*)D)
         return fail(MPDT_ERROR_ALIASING, fn, "C may not alias a 16-bit D");
-    mpdt_status s = check_gemm(fn, M, N, K, A, lda, 2, B, ldb, 2, C, ldc, 4, D, ldd, esd, nullptr, 0);
+    Span sbias;   // the bias: N FP32 values, an input D may not overlap
+    if (!span_of(bias, bias && M > 0 ? 1 : 0, N, N, 4, &sbias))
+        return fail(MPDT_ERROR_INVALID_VALUE, fn, "operand too large");
+    mpdt_status s = check_gemm(fn, M, N, K, A, lda, 2, B, ldb, 2, C, ldc, 4, D, ldd, esd, &sbias,
+                               bias ? 1 : 0);
     if (s != MPDT_SUCCESS || M == 0 || N == 0) return s;
+    if (bias && !aligned_to(bias, 4))
+        return fail(MPDT_ERROR_MISALIGNED, fn, "bias not aligned to 4 bytes");
     if ((s = check_device(fn)) != MPDT_SUCCESS) return s;
     mpdt::GemmArgs a{};
     a.A = (const char*)A;
@@ -141,8 +154,11 @@ mpdt_status run_gemm16(const char* fn, mpdt::Kind kind, int64_t M, int64_t N, in
     a.K = (int)K;
     a.out16 = out16;
     a.d16_vec = out16 && aligned_to(D, 16) && (ldd * 2) % 16 == 0;
+    a.bias = bias;
+    a.act = act;
     const bool al = aligned_to(A, 16) && aligned_to(B, 16) && (a.lda_b % 16 == 0) &&
                     (a.ldb_b % 16 == 0);
+    if (fused) return launched(mpdt::launch_gemm_epi(kind, a, al, (hipStream_t)stream), fn);
     return launched(mpdt::launch_gemm(kind, a, al, (hipStream_t)stream), fn);
 }
 
@@ -175,6 +191,22 @@ MPDT_EXPORT mpdt_status gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_
                                   float* D, int64_t ldd, void* stream) {
     return run_gemm16("gemm_bf16", mpdt::Kind::BF16, M, N, K, A, lda, B, ldb, C, ldc, D, ldd, 0,
                       stream);
+}
+
+MPDT_EXPORT mpdt_status gemm_f16_bias_act(int64_t M, int64_t N, int64_t K, const uint16_t* A,
+                                          int64_t lda, const uint16_t* B, int64_t ldb,
+                                          const float* C, int64_t ldc, const float* bias, int act,
+                                          void* D, int64_t ldd, int d16, void* stream) {
+    return run_gemm16("gemm_f16_bias_act", mpdt::Kind::F16, M, N, K, A, lda, B, ldb, C, ldc, D, ldd,
+                      d16, stream, true, bias, act);
+}
+
+MPDT_EXPORT mpdt_status gemm_bf16_bias_act(int64_t M, int64_t N, int64_t K, const uint16_t* A,
+                                           int64_t lda, const uint16_t* B, int64_t ldb,
+                                           const float* C, int64_t ldc, const float* bias, int act,
+                                           void* D, int64_t ldd, int d16, void* stream) {
+    return run_gemm16("gemm_bf16_bias_act", mpdt::Kind::BF16, M, N, K, A, lda, B, ldb, C, ldc, D,
+                      ldd, d16, stream, true, bias, act);
 }
 
 MPDT_EXPORT mpdt_status gemm_i8_i32(int64_t M, int64_t N, int64_t K, const int8_t* A, int64_t lda,

@@ -14,6 +14,7 @@ typedef __attribute__((ext_vector_type(4))) int32_t i32x4;
 typedef __attribute__((ext_vector_type(8))) int32_t i32x8;
 typedef __attribute__((ext_vector_type(2))) int32_t i32x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(16))) int32_t i32x16;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;

@@ -25,10 +25,17 @@ struct GemmArgs {
     int int_tm, int_tn;   // interior tiles launched separately (0: none)
     int out16;            // FP16/BF16 inputs: D is written in the input format (RNE)
     int d16_vec;          // out16 with D and its rows 16-byte aligned: wide stores allowed
+    const float* bias;    // fused epilogue: FP32 bias per output column (may be null)
+    int act;              // fused epilogue: one of the ACT_* activations
 };
+
+// Activations of the fused epilogue (the values of the C ABI's mpdt_act).
+enum : int { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2, ACT_SILU = 3 };
 
 // aligned: every row start of A and B is 16-byte aligned.
 hipError_t launch_gemm(Kind kind, const GemmArgs& a, bool aligned, hipStream_t stream);
+// FP16 / BF16 with the fused bias / activation epilogue (gemm_epi.hip).
+hipError_t launch_gemm_epi(Kind kind, const GemmArgs& a, bool aligned, hipStream_t stream);
 
 // FP8 one-wavefront kernel (gemm_fp8.hip) over the full FP8_TILE_M x
 // FP8_TILE_N tiles of a problem it takes (fp8_1w_eligible).

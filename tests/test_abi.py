@@ -95,6 +95,32 @@ def test_valid_calls_report_no_device():
     assert b"no HIP device" in L.mpdt_last_error()
 
 
+@pytest.mark.parametrize("fn", ["gemm_f16_bias_act", "gemm_bf16_bias_act"])
+def test_bias_act_validation(fn):
+    L = mp.lib()
+    S = R + (1 << 30)    # a bias array far from everything else
+
+    def call(M=8, N=8, K=8, A=P, lda=8, B=Q, ldb=8, C=None, ldc=8, bias=S, act=2, D=R, ldd=8, d16=0):
+        return getattr(L, fn)(M, N, K, A, lda, B, ldb, C, ldc, bias, act, D, ldd, d16, None)
+
+    assert call(act=4) == INVALID
+    assert call(act=-1) == INVALID
+    assert call(d16=2) == INVALID
+    assert call(lda=7) == INVALID
+    assert call(bias=S + 2) == MISALIGNED
+    assert call(D=R + 2) == MISALIGNED
+    assert call(D=R + 2, d16=1) != MISALIGNED
+    assert call(D=S) == ALIASING             # D over the bias
+    assert call(D=S - 8 * 4 + 4) == ALIASING  # the last row of D over the bias's first value
+    assert call(C=R, d16=1) == ALIASING       # a 16-bit D cannot be C
+    assert call(M=0) == SUCCESS
+    assert call(N=0, act=1) == SUCCESS
+    if not gpu_present:
+        assert call() == NO_DEVICE
+        assert call(bias=None, act=0, C=R) == NO_DEVICE     # in place, no bias
+        assert call(d16=1) == NO_DEVICE
+
+
 def test_i8_validation():
     L = mp.lib()
     assert L.gemm_i8_i32(4, 4, 4, P, 4, Q, 4, None, 4, R + 1, 4, None) == MISALIGNED

@@ -229,6 +229,22 @@ def test_i8_one_wave_edges_bit_exact(gpu_ok, M, N, K):
     assert np.array_equal(D, oracle.gemm_i8_i32(A, B, C))
 
 
+@pytest.mark.parametrize("pad", [0, 3])
+def test_i8_sums_beyond_2_24_exact(gpu_ok, pad):
+    # A, B in [100, 127] and K = 4096 give sums near 5e7, past 2^24: most
+    # are not FP32 values, so the INT32 path must never pass through FP32
+    # (pad 0: one-wave kernel; pad 3: rows not 16-byte aligned, general kernel)
+    M, N, K = 300, 260, 4096
+    r = np.random.default_rng(17 + pad)
+    A = r.integers(100, 128, (M, K)).astype(np.int8)
+    B = r.integers(100, 128, (K, N)).astype(np.int8)
+    C = r.integers(-1000, 1000, (M, N)).astype(np.int32)
+    D = host(mp.gemm_i8_i32(dev(A, K + pad), dev(B), dev(C)))
+    want = oracle.gemm_i8_i32(A, B, C)
+    assert (np.abs(want) > 2 ** 25).mean() > 0.9 and (want % 4 != 0).mean() > 0.5
+    assert np.array_equal(D, want)
+
+
 def test_i8_extremes_unaligned_and_null_c(gpu_ok):
     M, N, K = 130, 270, 1031
     A = np.full((M, K), -128, np.int8)
