@@ -45,7 +45,7 @@ def parse():
     # slower than the rest.  The default warm-up covers that.
     p.add_argument("--warmup", type=int, default=300)
     p.add_argument("--only", default="all",
-                   choices=["all", "bf16", "bf16out", "gemv", "w8a8_tokens", "quant", "fp8",
+                   choices=["all", "bf16", "bf16out", "epi", "gemv", "w8a8_tokens", "quant", "fp8",
                             "f16_ragged", "f16_64", "i8", "copy"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -158,7 +158,7 @@ def main():
         flop = 2.0 * M * N * K
         avg_s = st["mean_us"] * 1e-6
         achieved = flop / avg_s / 1e12
-        digest = source_digest("gemm.hip", "gemm_common.hpp", "device_common.hpp")
+        digest = source_digest("gemm.hip", "gemm_kernel.hpp", "gemm_common.hpp", "device_common.hpp")
         traffic = traffic_for("gemm_bf16_4096", digest)
         clock = gemm_clock(tA, tB, tC, tD, stream, M, N, K)
         result = {
@@ -200,6 +200,25 @@ def main():
             "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16, "unit": "TFLOP/s",
                          "frac": tf / PEAK_BF16}}
         del tA, tB, tC, tD
+
+    # ---------------- BF16 4096^3 + bias + GELU into BF16 (fused epilogue) ------
+    if args.only in ("all", "epi"):
+        M = N = K = 4096
+        A, B, C = inputs.gemm16_operands(M, N, K, dist="normal", fmt="bf16")
+        bias = inputs.normal_f32((N,), inputs.SEED_BIAS)
+        tA, tB, tC, tb = to_dev(A), to_dev(B), to_dev(C), to_dev(bias)
+        tD = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        region, per = timed(lambda i: mp.gemm_bf16_bias_act(tA, tB, tC, tb, mp.ACT_GELU, out=tD),
+                            args.steps, args.warmup, stream)
+        st = stats(per, region, args.steps)
+        tf = 2.0 * M * N * K / (st["mean_us"] * 1e-6) / 1e12
+        extra["gemm_bf16_bias_gelu_bf16out"] = {
+            "workload": "gemm_bf16_bias_act D=bf16(GELU(A*B+C+bias)), M=N=K=4096, FP32 C and "
+                        "bias, BF16 D",
+            "TFLOP_s": tf, "launch_us": st,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16, "unit": "TFLOP/s",
+                         "frac": tf / PEAK_BF16}}
+        del tA, tB, tC, tb, tD
 
     # ---------------- W8A8 GEMV, cold cache ------------------------------------
     if args.only in ("all", "gemv"):

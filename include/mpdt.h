@@ -112,9 +112,11 @@ typedef enum {
  * then D is FP32 (d16 = 0) or rounded once, to nearest even, to the input
  * format (d16 = 1: FP16 for gemm_f16_bias_act, BF16 for gemm_bf16_bias_act).
  * Each step is an FP32 operation in this order (the additions are exact when
- * every value is a small integer).  GELU and SiLU use the device's erfcf /
- * expf and an IEEE division: within a few FP32 ulps of the exact function of
- * v.  bias: N FP32 values (device pointer, 4-byte aligned, may be NULL; D
+ * every value is a small integer; ReLU is exact).  GELU and SiLU are
+ * evaluated in FP32 with the hardware base-2 exponential and reciprocal, GELU's
+ * erfc by the Chebyshev fit of Numerical Recipes (section 6.2, fractional
+ * error below 1.2e-7): the result is within 2^-20 (|v| + |act(v)|) of the
+ * exact function of the computed v.  bias: N FP32 values (device pointer, 4-byte aligned, may be NULL; D
  * may not overlap it).  C may be NULL; C == D in place only with d16 = 0.
  * An act outside mpdt_act or d16 outside {0, 1} is MPDT_ERROR_INVALID_VALUE. */
 mpdt_status gemm_f16_bias_act(int64_t M, int64_t N, int64_t K,

@@ -1,4 +1,4 @@
-// gemm_common.hpp -- pieces shared by the GEMM kernels (gemm.hip,
+// gemm_common.hpp -- pieces shared by the GEMM kernels (gemm_kernel.hpp,
 // gemm_fp8.hip): MFMA traits, tile geometry, LDS swizzles, the workgroup
 // to tile mapping and the wait / barrier primitives.
 #pragma once

@@ -1,5 +1,5 @@
 // gemm_fp8.hip -- the FP8 E4M3 block-scaled GEMM on full 128 x 256 tiles
-// with one wavefront per SIMD (the general kernel in gemm.hip covers edge
+// with one wavefront per SIMD (the general kernel in gemm_kernel.hpp covers edge
 // tiles, unaligned rows and K that is not a whole number of scale blocks).
 //
 // D = sum over 128-wide K blocks of (scale_a[row][kb] * scale_b[kb][col/128])

@@ -55,13 +55,48 @@ namespace mpdt {
 // instantiation, so the two output forms are distinct kernels.
 // BA (FP16 / BF16 inputs): the fused epilogue -- a bias per output column and
 // an activation (GemmArgs::bias, ::act) after C is added.
+// exp(y) through the hardware base-2 exponential (about 1 ulp, plus the
+// rounding of y log2 e: a relative error near |y| 2^-24).
+__device__ __forceinline__ float exp_hw(float y) {
+    return __builtin_amdgcn_exp2f(y * 1.4426950408889634f);
+}
+
+// erfc(x) for x >= 0: the Chebyshev fit of Press, Teukolsky, Vetterling and
+// Flannery ("Numerical Recipes in C", 2nd edition, section 6.2, erfcc), whose
+// fractional error is below 1.2e-7 for every x >= 0:
+//   t = 1 / (1 + x/2),  erfc(x) = t exp(-x^2 + P(t)),  P a degree-9 polynomial.
+// No cancellation anywhere, so the relative accuracy holds deep in the tail.
+__device__ __forceinline__ float erfc_nonneg(float x) {
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, x, 1.0f));
+    float p = 0.17087277f;
+    p = fmaf(p, t, -0.82215223f);
+    p = fmaf(p, t, 1.48851587f);
+    p = fmaf(p, t, -1.13520398f);
+    p = fmaf(p, t, 0.27886807f);
+    p = fmaf(p, t, -0.18628806f);
+    p = fmaf(p, t, 0.09678418f);
+    p = fmaf(p, t, 0.37409196f);
+    p = fmaf(p, t, 1.00002368f);
+    p = fmaf(p, t, -1.26551223f);
+    return t * exp_hw(fmaf(-x, x, p));
+}
+
+// The fused epilogue's activations in FP32.  GELU: v Phi(v) with
+// Phi(v) = erfc(-v / sqrt 2) / 2, taken as v - v erfc(|v| / sqrt 2) / 2 for
+// v >= 0 and v erfc(|v| / sqrt 2) / 2 below.  SiLU: v / (1 + exp(-v)) with
+// the hardware reciprocal (about 1 ulp).
 template <int ACT>
 __device__ __forceinline__ float act_apply(float v) {
-    if constexpr (ACT == ACT_RELU) return v > 0.0f ? v : 0.0f;
-    // x Phi(x), Phi(x) = erfc(-x / sqrt 2) / 2 (no cancellation for x < 0)
-    else if constexpr (ACT == ACT_GELU) return 0.5f * v * erfcf(-v * 0.70710678118654752f);
-    else if constexpr (ACT == ACT_SILU) return v / (1.0f + expf(-v));
-    else return v;
+    if constexpr (ACT == ACT_RELU) {
+        return v > 0.0f ? v : 0.0f;
+    } else if constexpr (ACT == ACT_GELU) {
+        const float h = 0.5f * v * erfc_nonneg(fabsf(v) * 0.70710678118654752f);
+        return v >= 0.0f ? v - h : h;
+    } else if constexpr (ACT == ACT_SILU) {
+        return v * __builtin_amdgcn_rcpf(1.0f + exp_hw(-v));
+    } else {
+        return v;
+    }
 }
 
 template <Kind KD, class C, bool ALIGNED, bool OUT16 = false, bool BA = false>

@@ -18,7 +18,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-SEED_A, SEED_B, SEED_C, SEED_X, SEED_W, SEED_SX, SEED_SW, SEED_QA, SEED_QB = range(1, 10)
+SEED_A, SEED_B, SEED_C, SEED_X, SEED_W, SEED_SX, SEED_SW, SEED_QA, SEED_QB, SEED_BIAS = range(1, 11)
 FP8_BLOCK = 128
 E4M3_MAX = 448.0
 
