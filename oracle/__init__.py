@@ -80,6 +80,10 @@ def _load():
         _lib.oracle_gemm_w8a8.restype = ctypes.c_int
         _lib.oracle_gemm_w8a8.argtypes = ([_c_i64] * 3 + [_vp, _c_i64, _vp, _vp, _c_i64, _vp, _vp]
                                           + [_vp, _c_i64, _vp, _c_i64])
+        _lib.oracle_gemm_w8a8_requant.restype = ctypes.c_int
+        _lib.oracle_gemm_w8a8_requant.argtypes = ([_c_i64] * 3
+                                                  + [_vp, _c_i64, _vp, _vp, _c_i64, _vp, _vp]
+                                                  + [ctypes.c_float, _vp, _c_i64, _vp, _c_i64])
         _lib.oracle_quantize_i8_rows.restype = ctypes.c_int
         _lib.oracle_quantize_i8_rows.argtypes = [_c_i64, _c_i64, _vp, _c_i64, _vp, _c_i64, _vp]
         _lib.oracle_quantize_fp8_blocks.restype = ctypes.c_int
@@ -372,6 +376,25 @@ def gemm16_bias_act_at(fmt, A, B, C, bias, act, ii, jj):
     bb = None if bj is None else bj.reshape(-1)
     return (bias_act(row, bb, act).reshape(R0.shape), S,
             bias_act(row, bb, ACT_NONE).reshape(R0.shape))
+
+
+def gemm_w8a8_requant(X, s_x, W, s_w, bias, s_out):
+    """oracle_gemm_w8a8_requant: as gemm_w8a8, with the FP32 value requantised
+    to INT8 by one output scale.  Returns (Z int32 [M, N], Q int8 [M, N])."""
+    M, K = X.shape
+    N = W.shape[0]
+    px, ldx = _mat(X, np.int8)
+    pw, ldw = _mat(W, np.int8)
+    s_x = np.ascontiguousarray(s_x, dtype=np.float32)
+    s_w = np.ascontiguousarray(s_w, dtype=np.float32)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    Z = np.empty((M, N), np.int32)
+    Q = np.empty((M, N), np.int8)
+    _check(_load().oracle_gemm_w8a8_requant(M, N, K, px, ldx, s_x.ctypes.data, pw, ldw,
+                                            s_w.ctypes.data, _ptr(b), float(np.float32(s_out)),
+                                            Z.ctypes.data, max(N, 1), Q.ctypes.data, max(N, 1)),
+           "gemm_w8a8_requant")
+    return Z, Q
 
 
 # ------------------------------------------------------------ quantisers --

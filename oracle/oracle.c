@@ -491,6 +491,50 @@ int oracle_gemm_w8a8(int64_t M, int64_t N, int64_t K, const int8_t* X, int64_t l
 }
 
 /* ------------------------------------------------------------------------ */
+/* M-token W8A8 layer, requantised to INT8 (see oracle.h).                    */
+/* ------------------------------------------------------------------------ */
+int oracle_gemm_w8a8_requant(int64_t M, int64_t N, int64_t K, const int8_t* X, int64_t ldx,
+                             const float* s_x, const int8_t* W, int64_t ldw, const float* s_w,
+                             const float* bias, float s_out, int32_t* Z, int64_t ldz,
+                             int8_t* Q, int64_t ldq) {
+    if (M < 0 || N < 0 || K < 0 || !X || !s_x || !W || !s_w || !Q) return 1;
+    if ((M > 0 && K > 0 && ldx < K) || (N > 0 && K > 0 && ldw < K) || ldq < N ||
+        (Z && ldz < N))
+        return 1;
+    if (!isfinite(s_out) || !(s_out > 0.0f)) return 1;
+    for (int64_t m = 0; m < M; ++m)
+        if (!isfinite(s_x[m])) return 2;
+    for (int64_t o = 0; o < N; ++o)
+        if (!isfinite(s_w[o]) || (bias && !isfinite(bias[o]))) return 2;
+    int rc = 0;
+#pragma omp parallel for schedule(static) reduction(max : rc)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t o = 0; o < N; ++o) {
+            int64_t acc = 0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += (int64_t)X[m * ldx + k] * (int64_t)W[o * ldw + k];
+            if (acc > INT32_MAX || acc < INT32_MIN) {
+                rc = 3;
+                continue;
+            }
+            float t = (float)(int32_t)acc;
+            t = t * s_x[m];
+            t = t * s_w[o];
+            if (bias) t = t + bias[o];
+            /* one FP32 division, then round half to even (rint in the default
+             * rounding mode) and saturate to the symmetric INT8 range */
+            const float u = t / s_out;
+            double r = rint((double)u);
+            if (r > 127.0) r = 127.0;
+            if (r < -127.0) r = -127.0;
+            if (Z) Z[m * ldz + o] = (int32_t)acc;
+            Q[m * ldq + o] = (int8_t)r;
+        }
+    }
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Per-token INT8 quantisation (see oracle.h).                                */
 /* ------------------------------------------------------------------------ */
 int oracle_quantize_i8_rows(int64_t M, int64_t K, const uint16_t* X, int64_t ldx,

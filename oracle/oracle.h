@@ -128,6 +128,20 @@ int oracle_gemm_w8a8(int64_t M, int64_t N, int64_t K, const int8_t* X, int64_t l
                      const float* s_x, const int8_t* W, int64_t ldw, const float* s_w,
                      const float* bias, int32_t* Z, int64_t ldz, uint16_t* Y, int64_t ldy);
 
+/* ---- The same M-token W8A8 layer with a requantising epilogue: the output
+ * is INT8 for a next layer that takes INT8 (same section: instead of
+ * writing FP16 the epilogue may requantise).  t is the FP32 value whose
+ * BF16 rounding oracle_gemm_w8a8 writes, t = fl32(fl32(fl32(float(Z) *
+ * s_x[m]) * s_w[o]) + bias[o]) (bias step skipped when bias is NULL); then
+ * Q[m][o] = clamp(rne(fl32(t / s_out)), -127, 127) with one output scale
+ * s_out (finite, > 0), symmetric with zero point 0 like the activation
+ * quantiser below.  Z may be NULL.  Returns 1 for bad arguments (s_out not
+ * finite and positive included). ---- */
+int oracle_gemm_w8a8_requant(int64_t M, int64_t N, int64_t K, const int8_t* X, int64_t ldx,
+                             const float* s_x, const int8_t* W, int64_t ldw, const float* s_w,
+                             const float* bias, float s_out, int32_t* Z, int64_t ldz,
+                             int8_t* Q, int64_t ldq);
+
 /* ---- Per-token symmetric INT8 quantisation of activations (the step that
  * produces q_x and s_x upstream of the W8A8 layer, same section: symmetric,
  * zero point 0, one scale per token).  For each row m of the M x K BF16

@@ -14,7 +14,11 @@ what the formats and the mathematics fix (not against a retyped formula):
     448 * 2^e (scale 2^e exactly, codes recovered), every block's largest
     element on the largest code, partial edge blocks with their own scale;
   * M-token W8A8: M = 1 is the pinned batch-1 layer, Z is the exact integer
-    product, the bias with unit scales is an exact integer sum rounded once.
+    product, the bias with unit scales is an exact integer sum rounded once;
+  * the requantising W8A8 epilogue: a worked example in exact binary
+    arithmetic (saturation and a tie), unit scales against numpy's integer
+    product clipped, and agreement with the BF16 layer within half an output
+    step.
 """
 import numpy as np
 import pytest
@@ -162,3 +166,50 @@ def test_w8a8_m_tokens_pins():
     assert np.array_equal(Zb, Z)
     want = oracle.f32_to_bf16_rne((Z.astype(np.int64) + bias.astype(np.int64)).astype(np.float32))
     assert np.array_equal(Yb, want)
+
+
+def test_w8a8_requant_pins():
+    # (1) a worked example in exact binary arithmetic: X = [[1, 2]],
+    # W = [[3, 4], [-5, 6], [40, 40], [-40, -40], [1, 0]]: z = [11, 7, 120, -120, 1];
+    # s_x = 0.5, s_w = [0.25, 1, 1, 1, 0.3125], bias = [0.125, -0.25, 0, 0, 0],
+    # s_out = 1/16: t = [1.5, 3.25, 60, -60, 0.15625] -> t / s_out =
+    # [24, 52, 960, -960, 2.5] -> q = [24, 52, 127, -127, 2] (saturation, a tie to even)
+    X = np.array([[1, 2]], np.int8)
+    W = np.array([[3, 4], [-5, 6], [40, 40], [-40, -40], [1, 0]], np.int8)
+    sx = np.array([0.5], np.float32)
+    sw = np.array([0.25, 1, 1, 1, 0.3125], np.float32)
+    bias = np.array([0.125, -0.25, 0, 0, 0], np.float32)
+    Z, Q = oracle.gemm_w8a8_requant(X, sx, W, sw, bias, 0.0625)
+    assert Z.tolist() == [[11, 7, 120, -120, 1]]
+    assert Q.tolist() == [[24, 52, 127, -127, 2]]
+    # (2) unit scales, s_out = 1: Q = clip(X . W^T, -127, 127) from numpy's
+    # integer product
+    r = np.random.default_rng(13)
+    M, N, K = 4, 200, 400
+    X = r.integers(-3, 4, (M, K)).astype(np.int8)
+    W = r.integers(-3, 4, (N, K)).astype(np.int8)
+    Z, Q = oracle.gemm_w8a8_requant(X, np.ones(M, np.float32), W, np.ones(N, np.float32), None, 1.0)
+    ref = X.astype(np.int64) @ W.astype(np.int64).T
+    assert np.array_equal(Z, ref) and np.array_equal(Q, np.clip(ref, -127, 127))
+    assert (np.abs(ref) > 127).any() and (np.abs(ref) < 127).any()
+    # (3) against the pinned BF16 layer: |Q s_out - t| <= s_out / 2 unless
+    # saturated, with t within half a BF16 ulp of Y
+    X = r.integers(-128, 128, (M, 1000)).astype(np.int8)
+    W = r.integers(-128, 128, (N, 1000)).astype(np.int8)
+    sx = r.uniform(0.01, 0.1, M).astype(np.float32)
+    sw = r.uniform(0.001, 0.01, N).astype(np.float32)
+    bias = r.standard_normal(N).astype(np.float32)
+    s_out = np.float32(0.05)
+    Z, Q = oracle.gemm_w8a8_requant(X, sx, W, sw, bias, s_out)
+    _, Y = oracle.gemm_w8a8(X, sx, W, sw, bias)
+    y = oracle.bf16_to_f64(Y)
+    inside = np.abs(Q) < 127
+    assert inside.mean() > 0.5 and (~inside).any()
+    err = np.abs(Q.astype(np.float64) * s_out - y)
+    assert (err[inside] <= s_out / 2 * (1 + 1e-6) + 2.0 ** -8 * np.abs(y[inside])).all()
+    assert (np.sign(Q[~inside]) == np.sign(y[~inside])).all()
+    assert (np.abs(y[~inside]) >= 126.5 * s_out * (1 - 2.0 ** -8)).all()
+    # (4) s_out must be finite and positive
+    for bad in (0.0, -1.0, np.inf, np.nan):
+        with pytest.raises(oracle.OracleError):
+            oracle.gemm_w8a8_requant(X, sx, W, sw, None, bad)
