@@ -199,7 +199,7 @@ def test_w8a8_requant_pins():
     sx = r.uniform(0.01, 0.1, M).astype(np.float32)
     sw = r.uniform(0.001, 0.01, N).astype(np.float32)
     bias = r.standard_normal(N).astype(np.float32)
-    s_out = np.float32(0.05)
+    s_out = np.float32(0.5)
     Z, Q = oracle.gemm_w8a8_requant(X, sx, W, sw, bias, s_out)
     _, Y = oracle.gemm_w8a8(X, sx, W, sw, bias)
     y = oracle.bf16_to_f64(Y)
