@@ -273,6 +273,21 @@ def main():
                 "GB_s": gbs, "algorithmic_bytes": nbytes, "launch_us": st,
                 "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s",
                              "frac": gbs / PEAK_HBM}}
+            if M == 16:
+                # the same layer requantised to INT8 for a next INT8 layer
+                tq = torch.empty((M, N), dtype=torch.int8, device=dev)
+                region, per = timed(lambda i: mp.gemm_w8a8_requant(tX, tsx, tWs[i % copies], tsw, tb,
+                                                                   0.05, out=tq),
+                                    args.steps, args.warmup, stream)
+                st = stats(per, region, args.steps)
+                nbytes = N * K + M * K + 4 * M + 8 * N + M * N
+                gbs = nbytes / (st["mean_us"] * 1e-6) / 1e9
+                extra["gemm_w8a8_requant_m16"] = {
+                    "workload": "W8A8 layer, 16 tokens x 4096 . W int8 [14336 x 4096], bias, "
+                                "requantised INT8 out; cold: 8 rotating W copies",
+                    "GB_s": gbs, "algorithmic_bytes": nbytes, "launch_us": st,
+                    "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s",
+                                 "frac": gbs / PEAK_HBM}}
         del tWs
 
     # ---------------- quantisers -----------------------------------------------

@@ -179,6 +179,21 @@ mpdt_status gemm_w8a8(int64_t M, int64_t N, int64_t K,
                       const int8_t* W, int64_t ldw, const float* w_scale, const float* bias,
                       uint16_t* Y, int64_t ldy, int32_t* Z, int64_t ldz, void* stream);
 
+/* The same layer with a requantising epilogue, for a next layer that takes
+ * INT8 (same section: the epilogue may requantise instead of writing a
+ * 16-bit result).  With v the FP32 value whose BF16 rounding gemm_w8a8
+ * writes (the same three or four FP32 steps, in the same order):
+ *   Q[m][o] = clamp(rne(v / out_scale), -127, 127)     (INT8, ldq)
+ * one IEEE FP32 division by the single output scale (symmetric, zero point
+ * 0, as quantize_i8_rows; -128 is never produced), rne = round half to
+ * even.  out_scale must be finite and > 0 (else MPDT_ERROR_INVALID_VALUE).
+ * Z (optional) as in gemm_w8a8. */
+mpdt_status gemm_w8a8_requant(int64_t M, int64_t N, int64_t K,
+                              const int8_t* X, int64_t ldx, const float* x_scale,
+                              const int8_t* W, int64_t ldw, const float* w_scale,
+                              const float* bias, float out_scale,
+                              int8_t* Q, int64_t ldq, int32_t* Z, int64_t ldz, void* stream);
+
 /* Per-token symmetric INT8 quantisation of activations (the step that makes
  * the W8A8 layer's q_x and s_x; same section: symmetric, zero point 0, one
  * scale per token).  For each row m of the M x K BF16 matrix X (ldx):

@@ -20,7 +20,7 @@ import torch
 
 __all__ = ["gemm_f16", "gemm_bf16", "gemm_f16_f16out", "gemm_bf16_bf16out", "gemm_f16_bias_act",
            "gemm_bf16_bias_act", "ACT_NONE", "ACT_RELU", "ACT_GELU", "ACT_SILU", "gemm_i8_i32",
-           "gemm_fp8_blockscaled", "gemv_w8a8", "gemm_w8a8", "quantize_i8_rows",
+           "gemm_fp8_blockscaled", "gemv_w8a8", "gemm_w8a8", "gemm_w8a8_requant", "quantize_i8_rows",
            "quantize_fp8_blocks",
            "MpdtError", "lib", "lib_path", "version"]
 
@@ -71,6 +71,9 @@ def lib() -> ctypes.CDLL:
         L.gemm_w8a8.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _i64,
                                 _vp, _i64, _vp]
         L.gemm_w8a8.restype = ctypes.c_int
+        L.gemm_w8a8_requant.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp,
+                                         ctypes.c_float, _vp, _i64, _vp, _i64, _vp]
+        L.gemm_w8a8_requant.restype = ctypes.c_int
         L.quantize_i8_rows.argtypes = [_i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp]
         L.quantize_i8_rows.restype = ctypes.c_int
         L.quantize_fp8_blocks.argtypes = [_i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp]
@@ -276,6 +279,34 @@ def gemm_w8a8(X, x_scale, W, w_scale, bias=None, out=None, z_out=None, return_z=
     pz, ldz = (None, N) if z_out is None else _mat(z_out, 4, "z_out")
     _check("gemm_w8a8", lib().gemm_w8a8(M, N, K, px, ldx, psx, pw, ldw, psw, pb, py, ldy, pz, ldz,
                                         _stream(W)))
+    if return_z or z_out is not None:
+        return out, z_out
+    return out
+
+
+def gemm_w8a8_requant(X, x_scale, W, w_scale, bias, out_scale, out=None, z_out=None,
+                      return_z=False):
+    """The W8A8 layer requantised for a next INT8 layer: as gemm_w8a8, then
+    Q = clamp(rne(value / out_scale), -127, 127); returns Q INT8 [M, N] (and
+    the INT32 sums when return_z or z_out is given)."""
+    M, K = X.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("W must be [N, K]")
+    px, ldx = _mat(X, 1, "X")
+    pw, ldw = _mat(W, 1, "W")
+    psx = _vec(x_scale, M, torch.float32, "x_scale")
+    psw = _vec(w_scale, N, torch.float32, "w_scale")
+    pb = None if bias is None else _vec(bias, N, torch.float32, "bias")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.int8, device=W.device)
+    pq, ldq = _mat(out, 1, "out")
+    if z_out is None and return_z:
+        z_out = torch.empty((M, N), dtype=torch.int32, device=W.device)
+    pz, ldz = (None, N) if z_out is None else _mat(z_out, 4, "z_out")
+    _check("gemm_w8a8_requant",
+           lib().gemm_w8a8_requant(M, N, K, px, ldx, psx, pw, ldw, psw, pb, float(out_scale), pq, ldq,
+                                   pz, ldz, _stream(W)))
     if return_z or z_out is not None:
         return out, z_out
     return out

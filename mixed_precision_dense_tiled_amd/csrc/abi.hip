@@ -6,6 +6,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <cmath>
 #include <cstdio>
 #include <mutex>
 #include <string>
@@ -312,34 +313,39 @@ MPDT_EXPORT mpdt_status gemv_w8a8(int64_t M, int64_t N, int64_t K, const int8_t*
     return launched(mpdt::launch_gemv_w8a8(a, al, (hipStream_t)stream), fn);
 }
 
-MPDT_EXPORT mpdt_status gemm_w8a8(int64_t M, int64_t N, int64_t K, const int8_t* X, int64_t ldx,
-                                  const float* x_scale, const int8_t* W, int64_t ldw,
-                                  const float* w_scale, const float* bias, uint16_t* Y, int64_t ldy,
-                                  int32_t* Z, int64_t ldz, void* stream) {
-    const char* fn = "gemm_w8a8";
+namespace {
+// The M-token W8A8 layer; the output is BF16 Y, or INT8 Q requantised by
+// out_scale (requant).
+mpdt_status run_w8a8(const char* fn, int64_t M, int64_t N, int64_t K, const int8_t* X, int64_t ldx,
+                     const float* x_scale, const int8_t* W, int64_t ldw, const float* w_scale,
+                     const float* bias, void* Y, int64_t ldy, bool requant, float out_scale,
+                     int32_t* Z, int64_t ldz, void* stream) {
+    const int64_t esy = requant ? 1 : 2;
     if (!dims_ok(M, N, K)) return fail(MPDT_ERROR_INVALID_VALUE, fn, "dimension out of range");
+    if (requant && !(std::isfinite(out_scale) && out_scale > 0.0f))
+        return fail(MPDT_ERROR_INVALID_VALUE, fn, "out_scale must be finite and positive");
     if (M == 0 || N == 0) return MPDT_SUCCESS;
     if (!Y || !x_scale || !w_scale)
-        return fail(MPDT_ERROR_INVALID_VALUE, fn, "Y, x_scale or w_scale is NULL");
+        return fail(MPDT_ERROR_INVALID_VALUE, fn, "output, x_scale or w_scale is NULL");
     if (K > 0) {
         if (!X || !W) return fail(MPDT_ERROR_INVALID_VALUE, fn, "X or W is NULL");
         if (ldx < K || ldw < K) return fail(MPDT_ERROR_INVALID_VALUE, fn, "ldx or ldw < K");
     }
-    if (ldy < N || (Z && ldz < N)) return fail(MPDT_ERROR_INVALID_VALUE, fn, "ldy or ldz < N");
-    if (!aligned_to(Y, 2) || !aligned_to(x_scale, 4) || !aligned_to(w_scale, 4) ||
+    if (ldy < N || (Z && ldz < N)) return fail(MPDT_ERROR_INVALID_VALUE, fn, "output ld or ldz < N");
+    if (!aligned_to(Y, esy) || !aligned_to(x_scale, 4) || !aligned_to(w_scale, 4) ||
         (bias && !aligned_to(bias, 4)) || (Z && !aligned_to(Z, 4)))
         return fail(MPDT_ERROR_MISALIGNED, fn, "pointer not aligned to its element size");
     Span sx, sw, ssx, ssw, sb, sy, sz;
     if (!span_of(X, K > 0 ? M : 0, K, ldx, 1, &sx) || !span_of(W, K > 0 ? N : 0, K, ldw, 1, &sw) ||
         !span_of(x_scale, 1, M, M, 4, &ssx) || !span_of(w_scale, 1, N, N, 4, &ssw) ||
-        !span_of(bias, bias ? 1 : 0, N, N, 4, &sb) || !span_of(Y, M, N, ldy, 2, &sy) ||
+        !span_of(bias, bias ? 1 : 0, N, N, 4, &sb) || !span_of(Y, M, N, ldy, esy, &sy) ||
         !span_of(Z, Z ? M : 0, N, ldz, 4, &sz))
         return fail(MPDT_ERROR_INVALID_VALUE, fn, "operand too large");
     const Span ins[5] = {sx, sw, ssx, ssw, sb};
     for (const Span& in : ins)
         if (sy.overlaps(in) || sz.overlaps(in))
             return fail(MPDT_ERROR_ALIASING, fn, "an output overlaps an input");
-    if (sy.overlaps(sz)) return fail(MPDT_ERROR_ALIASING, fn, "Y overlaps Z");
+    if (sy.overlaps(sz)) return fail(MPDT_ERROR_ALIASING, fn, "the output overlaps Z");
     mpdt_status s = check_device(fn);
     if (s != MPDT_SUCCESS) return s;
     mpdt::W8A8Args a{};
@@ -350,8 +356,14 @@ MPDT_EXPORT mpdt_status gemm_w8a8(int64_t M, int64_t N, int64_t K, const int8_t*
     a.ldw = ldw;
     a.w_scale = w_scale;
     a.bias = bias;
-    a.Y = Y;
-    a.ldy = ldy;
+    if (requant) {
+        a.Q = (int8_t*)Y;
+        a.ldq = ldy;
+        a.q_scale = out_scale;
+    } else {
+        a.Y = (uint16_t*)Y;
+        a.ldy = ldy;
+    }
     a.Z = Z;
     a.ldz = ldz;
     a.M = (int)M;
@@ -359,6 +371,24 @@ MPDT_EXPORT mpdt_status gemm_w8a8(int64_t M, int64_t N, int64_t K, const int8_t*
     a.K = (int)K;
     const bool al = aligned_to(X, 16) && aligned_to(W, 16) && ldx % 16 == 0 && ldw % 16 == 0;
     return launched(mpdt::launch_gemm_w8a8(a, al, (hipStream_t)stream), fn);
+}
+}  // namespace
+
+MPDT_EXPORT mpdt_status gemm_w8a8(int64_t M, int64_t N, int64_t K, const int8_t* X, int64_t ldx,
+                                  const float* x_scale, const int8_t* W, int64_t ldw,
+                                  const float* w_scale, const float* bias, uint16_t* Y, int64_t ldy,
+                                  int32_t* Z, int64_t ldz, void* stream) {
+    return run_w8a8("gemm_w8a8", M, N, K, X, ldx, x_scale, W, ldw, w_scale, bias, Y, ldy, false,
+                    1.0f, Z, ldz, stream);
+}
+
+MPDT_EXPORT mpdt_status gemm_w8a8_requant(int64_t M, int64_t N, int64_t K, const int8_t* X,
+                                          int64_t ldx, const float* x_scale, const int8_t* W,
+                                          int64_t ldw, const float* w_scale, const float* bias,
+                                          float out_scale, int8_t* Q, int64_t ldq, int32_t* Z,
+                                          int64_t ldz, void* stream) {
+    return run_w8a8("gemm_w8a8_requant", M, N, K, X, ldx, x_scale, W, ldw, w_scale, bias, Q, ldq,
+                    true, out_scale, Z, ldz, stream);
 }
 
 MPDT_EXPORT mpdt_status quantize_i8_rows(int64_t M, int64_t K, const uint16_t* X, int64_t ldx,

@@ -126,6 +126,8 @@ hipError_t launch_gemv_w8a8(const GemvArgs& a, bool aligned, hipStream_t stream)
 // epilogue).
 //   z[m][o] = sum_k X[m][k] * W[o][k]          (INT32, exact)
 //   y[m][o] = bf16_rne( ((float(z) * s_x[m]) * s_w[o]) + bias[o] )
+// or, requantised for a next layer that takes INT8 (same section),
+//   q[m][o] = clamp(rne(( ... + bias[o]) / s_out), -127, 127)
 // With more than one token the products are a small GEMM, Z = X . W^T, whose
 // operands are both K-contiguous: a 32x32x32 INT8 MFMA takes 32 tokens
 // (rows of X, zero past M) as its A operand and 32 output channels (rows of
@@ -221,7 +223,14 @@ __global__ __launch_bounds__(64 * TOK_WAVES) void gemm_w8a8_kernel(W8A8Args g) {
             float v = mul_rn((float)z, g.x_scale[m]);
             v = mul_rn(v, sw);
             if (g.bias) v = add_rn(v, b);
-            g.Y[(int64_t)m * g.ldy + o] = f32_to_bf16_bits(v);
+            if (g.Q) {
+                // requantised for a next layer that takes INT8: one IEEE
+                // division, round half to even, saturate to +-127
+                const float q = __builtin_rintf(v / g.q_scale);
+                g.Q[(int64_t)m * g.ldq + o] = (int8_t)fminf(fmaxf(q, -127.0f), 127.0f);
+            } else {
+                g.Y[(int64_t)m * g.ldy + o] = f32_to_bf16_bits(v);
+            }
         }
     }
 }
@@ -234,7 +243,8 @@ hipError_t launch_gemm_w8a8(const W8A8Args& a0, bool /*aligned*/, hipStream_t st
         a.M = min(32, a0.M - m0);
         a.X = a0.X + (int64_t)m0 * a0.ldx;
         a.x_scale = a0.x_scale + m0;
-        a.Y = a0.Y + (int64_t)m0 * a0.ldy;
+        a.Y = a0.Y ? a0.Y + (int64_t)m0 * a0.ldy : nullptr;
+        a.Q = a0.Q ? a0.Q + (int64_t)m0 * a0.ldq : nullptr;
         a.Z = a0.Z ? a0.Z + (int64_t)m0 * a0.ldz : nullptr;
         dim3 grid((unsigned)((a.N + 31) / 32)), block(64 * TOK_WAVES);
         hipLaunchKernelGGL(gemm_w8a8_kernel, grid, block, 0, stream, a);

@@ -67,8 +67,11 @@ struct W8A8Args {
     int64_t ldw;
     const float* w_scale;   // [N]
     const float* bias;      // [N] or null
-    uint16_t* Y;
+    uint16_t* Y;            // BF16 output, or null when Q is written
     int64_t ldy;
+    int8_t* Q;              // INT8 requantised output (or null)
+    int64_t ldq;
+    float q_scale;          // Q = clamp(rne(value / q_scale), -127, 127)
     int32_t* Z;             // or null
     int64_t ldz;
     int M, N, K;

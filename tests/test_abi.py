@@ -162,6 +162,27 @@ def test_gemv_validation():
     assert L.gemv_w8a8(1, 0, 64, P, f, Q, 64, R, R + 4096, None, None) == SUCCESS
 
 
+def test_w8a8_requant_validation():
+    L = mp.lib()
+    f = ctypes.c_float
+
+    def call(M=4, N=16, K=64, X=P, ldx=64, sx=P + 4096, W=Q, ldw=64, sw=Q + 65536, bias=None,
+             s=f(0.5), Qo=R, ldq=16, Z=None, ldz=16):
+        return L.gemm_w8a8_requant(M, N, K, X, ldx, sx, W, ldw, sw, bias, s, Qo, ldq, Z, ldz, None)
+
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert call(s=f(bad)) == INVALID
+    assert call(ldq=15) == INVALID
+    assert call(Qo=None) == INVALID
+    assert call(sw=Q + 65538) == MISALIGNED
+    assert call(Qo=R + 1) != MISALIGNED               # INT8 output: any byte address
+    assert call(Qo=Q + 64) == ALIASING                # Q over W
+    assert call(Z=R + 8, ldz=16) == ALIASING          # Z over Q
+    assert call(M=0) == SUCCESS
+    if not gpu_present:
+        assert call() == NO_DEVICE
+
+
 def test_binding_raises_on_status():
     with pytest.raises((mp.MpdtError, ValueError, RuntimeError)):
         mp.gemm_f16(torch.zeros(4, 4, dtype=torch.float16), torch.zeros(4, 4, dtype=torch.float16))

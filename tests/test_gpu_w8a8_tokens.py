@@ -2,6 +2,8 @@
 the two quantisers, against the oracle, bit-exact (every step is an integer
 sum or a fixed sequence of IEEE FP32 operations, then one rounding):
 
+  * gemm_w8a8_requant: the same layer requantised to INT8 (saturation,
+    exact ties to even, a padded output, K = 0);
   * gemm_w8a8: M = 1, 2, 3, 5, 8, 16, 17, 31, 32, 33, 40, 65 tokens (groups of
     32 per launch),
     N not a multiple of a workgroup's 32 channels, K not a multiple of the
@@ -79,6 +81,43 @@ def test_w8a8_tokens_int32_bound_full_layer_and_k_zero(gpu_ok):
                         dev(bias), return_z=True)
     assert not host(z).any()
     assert np.array_equal(host(y).view(np.uint16), np.tile(oracle.f32_to_bf16_rne(bias), (5, 1)))
+
+
+@pytest.mark.parametrize("M", [1, 3, 17, 33, 40])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_w8a8_requant_bit_exact(gpu_ok, M, with_bias):
+    X, sx, W, sw, bias = w8a8_inputs(M, 1000, 4500, seed=M + 100)
+    b = bias if with_bias else None
+    s_out = np.float32(0.6)                        # most codes inside +-127, some saturated
+    Q, Z = mp.gemm_w8a8_requant(dev(X), dev(sx), dev(W, 4501, pad=-7), dev(sw),
+                                None if b is None else dev(b), float(s_out), return_z=True)
+    torch.cuda.synchronize()
+    Zr, Qr = oracle.gemm_w8a8_requant(X, sx, W, sw, b, s_out)
+    q = host(Q)
+    assert np.array_equal(host(Z), Zr) and np.array_equal(q, Qr)
+    assert (np.abs(q) == 127).any() and (np.abs(q) < 127).mean() > 0.5
+
+
+def test_w8a8_requant_padded_output_ties_and_k_zero(gpu_ok):
+    M, N, K = 6, 333, 1000
+    X, sx, W, sw, bias = w8a8_inputs(M, N, K, seed=7)
+    buf = torch.full((M, N + 5), 99, dtype=torch.int8, device=gpu_ok)
+    mp.gemm_w8a8_requant(dev(X, K + 3), dev(sx), dev(W), dev(sw), dev(bias), 0.25, out=buf[:, :N])
+    _, Qr = oracle.gemm_w8a8_requant(X, sx, W, sw, bias, np.float32(0.25))
+    h = host(buf)
+    assert np.array_equal(h[:, :N], Qr) and (h[:, N:] == 99).all()
+    # exact ties: unit scales, s_out = 2, odd integer sums -> t / 2 = k + 1/2 -> even
+    X = np.array([[1, 0], [3, 0], [5, 0], [-1, 0], [-3, 0]], np.int8)
+    W = np.array([[1, 0]], np.int8)
+    Q = mp.gemm_w8a8_requant(dev(X), dev(np.ones(5, np.float32)), dev(W), dev(np.ones(1, np.float32)),
+                             None, 2.0)
+    assert host(Q).ravel().tolist() == [0, 2, 2, 0, -2]
+    # K = 0: Q = rne(bias / s_out)
+    bias = np.array([0.3, -0.7, 100.0, 1e3], np.float32)
+    Q = mp.gemm_w8a8_requant(torch.zeros((2, 0), dtype=torch.int8, device=gpu_ok), dev(np.ones(2, np.float32)),
+                             torch.zeros((4, 0), dtype=torch.int8, device=gpu_ok), dev(np.ones(4, np.float32)),
+                             dev(bias), 0.5)
+    assert host(Q).tolist() == [[1, -1, 127, 127]] * 2
 
 
 def bf16_matrix(shape, seed, scale=1.0):
