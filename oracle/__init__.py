@@ -40,7 +40,7 @@ def _load():
         _lib.oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
         _lib.oracle_f32_to_bf16_rne.restype = ctypes.c_uint16
         _lib.oracle_f32_to_bf16_rne.argtypes = [ctypes.c_float]
-        for name in ("oracle_decode_f16", "oracle_decode_bf16", "oracle_decode_e4m3",
+        for name in ("oracle_decode_f16", "oracle_decode_bf16", "oracle_decode_e4m3", "oracle_decode_e5m2",
                      "oracle_round_bf16"):
             fn = getattr(_lib, name)
             fn.restype = None
@@ -75,6 +75,31 @@ def _load():
                                                         + [_c_i64, _vp, _vp, _vp, _vp])
         _lib.oracle_f32_to_f16_rne.restype = ctypes.c_uint16
         _lib.oracle_f32_to_f16_rne.argtypes = [ctypes.c_float]
+        _lib.oracle_f32_to_e5m2_rne_sat.restype = ctypes.c_uint8
+        _lib.oracle_f32_to_e5m2_rne_sat.argtypes = [ctypes.c_float]
+        _lib.oracle_e5m2_to_f64.restype = ctypes.c_double
+        _lib.oracle_e5m2_to_f64.argtypes = [ctypes.c_uint8]
+        _lib.oracle_gemm_fp8_blockscaled_fmt.restype = ctypes.c_int
+        _lib.oracle_gemm_fp8_blockscaled_fmt.argtypes = ([_c_i64] * 3
+                                                         + [_vp, _c_i64, ctypes.c_int, _vp, _c_i64]
+                                                         + [_vp, _c_i64, ctypes.c_int, _vp, _c_i64]
+                                                         + [_vp, _vp])
+        _lib.oracle_gemm_fp8_blockscaled_fmt_at.restype = ctypes.c_int
+        _lib.oracle_gemm_fp8_blockscaled_fmt_at.argtypes = (
+            [_c_i64] * 3 + [_vp, _c_i64, ctypes.c_int, _vp, _c_i64]
+            + [_vp, _c_i64, ctypes.c_int, _vp, _c_i64] + [_c_i64, _vp, _vp, _vp, _vp])
+        _lib.oracle_gemm_fp8_rowscaled.restype = ctypes.c_int
+        _lib.oracle_gemm_fp8_rowscaled.argtypes = ([_c_i64] * 3
+                                                   + [_vp, _c_i64, ctypes.c_int, _vp, _c_i64]
+                                                   + [_vp, _c_i64, ctypes.c_int, _vp, _c_i64]
+                                                   + [_vp, _vp])
+        _lib.oracle_gemm_fp8_rowscaled_at.restype = ctypes.c_int
+        _lib.oracle_gemm_fp8_rowscaled_at.argtypes = (
+            [_c_i64] * 3 + [_vp, _c_i64, ctypes.c_int, _vp, _c_i64]
+            + [_vp, _c_i64, ctypes.c_int, _vp, _c_i64] + [_c_i64, _vp, _vp, _vp, _vp])
+        _lib.oracle_quantize_fp8_blocks_fmt.restype = ctypes.c_int
+        _lib.oracle_quantize_fp8_blocks_fmt.argtypes = ([_c_i64, _c_i64, _vp, _c_i64, ctypes.c_int]
+                                                        + [_c_i64, _c_i64, _vp, _c_i64, _vp, _c_i64])
         _lib.oracle_f32_to_e4m3_rne_sat.restype = ctypes.c_uint8
         _lib.oracle_f32_to_e4m3_rne_sat.argtypes = [ctypes.c_float]
         _lib.oracle_gemm_w8a8.restype = ctypes.c_int
@@ -151,6 +176,27 @@ def e4m3_to_f64(bits: np.ndarray) -> np.ndarray:
     out = np.empty(bits.shape, np.float64)
     _load().oracle_decode_e4m3(bits.ctypes.data, out.ctypes.data, bits.size)
     return out
+
+
+def e5m2_to_f64(bits: np.ndarray) -> np.ndarray:
+    bits = np.ascontiguousarray(bits, dtype=np.uint8)
+    out = np.empty(bits.shape, np.float64)
+    _load().oracle_decode_e5m2(bits.ctypes.data, out.ctypes.data, bits.size)
+    return out
+
+
+E4M3, E5M2 = 0, 1
+
+
+def fp8_to_f64(bits, fmt):
+    return e4m3_to_f64(bits) if fmt == E4M3 else e5m2_to_f64(bits)
+
+
+def f32_to_e5m2_rne_sat(x: np.ndarray) -> np.ndarray:
+    """oracle_f32_to_e5m2_rne_sat elementwise (E5M2 codes)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    f = _load().oracle_f32_to_e5m2_rne_sat
+    return np.array([f(float(v)) for v in x.ravel()], dtype=np.uint8).reshape(x.shape)
 
 
 def f32_to_bf16_rne(x: np.ndarray) -> np.ndarray:
@@ -289,6 +335,84 @@ def gemm_fp8_blockscaled(A, sA, B, sB):
     return R, S
 
 
+def gemm_fp8_blockscaled_fmt(A, fmt_a, sA, B, fmt_b, sB):
+    """``oracle_gemm_fp8_blockscaled_fmt``: as gemm_fp8_blockscaled with each
+    operand's format given (E4M3 or E5M2)."""
+    M, K = A.shape
+    N = B.shape[1]
+    pa, lda = _mat(A, np.uint8)
+    pb, ldb = _mat(B, np.uint8)
+    psa, ldsa = _mat(sA, np.float32)
+    psb, ldsb = _mat(sB, np.float32)
+    R = np.empty((M, N), np.float64)
+    S = np.empty((M, N), np.float64)
+    _check(_load().oracle_gemm_fp8_blockscaled_fmt(M, N, K, pa, lda, int(fmt_a), psa, ldsa, pb, ldb,
+                                                   int(fmt_b), psb, ldsb, R.ctypes.data, S.ctypes.data),
+           "oracle_gemm_fp8_blockscaled_fmt")
+    return R, S
+
+
+def gemm_fp8_blockscaled_fmt_at(A, fmt_a, sA, B, fmt_b, sB, ii, jj):
+    """``oracle_gemm_fp8_blockscaled_fmt_at``: R, S at (ii[p], jj[p])."""
+    M, K = A.shape
+    N = B.shape[1]
+    pa, lda = _mat(A, np.uint8)
+    pb, ldb = _mat(B, np.uint8)
+    psa, ldsa = _mat(sA, np.float32)
+    psb, ldsb = _mat(sB, np.float32)
+    ii = np.ascontiguousarray(ii, np.int64)
+    jj = np.ascontiguousarray(jj, np.int64)
+    R = np.empty(ii.shape, np.float64)
+    S = np.empty(ii.shape, np.float64)
+    _check(_load().oracle_gemm_fp8_blockscaled_fmt_at(M, N, K, pa, lda, int(fmt_a), psa, ldsa, pb, ldb,
+                                                      int(fmt_b), psb, ldsb, ii.size, ii.ctypes.data,
+                                                      jj.ctypes.data, R.ctypes.data, S.ctypes.data),
+           "oracle_gemm_fp8_blockscaled_fmt_at")
+    return R, S
+
+
+def gemm_fp8_rowscaled(A, fmt_a, sA, B, fmt_b, sB):
+    """``oracle_gemm_fp8_rowscaled``: (R, S) with R = sA[i] sB[j] sum_k a b in
+    FP64; sA holds M values (or 1: per tensor), sB N values (or 1)."""
+    M, K = A.shape
+    N = B.shape[1]
+    pa, lda = _mat(A, np.uint8)
+    pb, ldb = _mat(B, np.uint8)
+    sA = np.ascontiguousarray(sA, np.float32).ravel()
+    sB = np.ascontiguousarray(sB, np.float32).ravel()
+    inc_a = 0 if sA.size == 1 and M != 1 else 1
+    inc_b = 0 if sB.size == 1 and N != 1 else 1
+    R = np.empty((M, N), np.float64)
+    S = np.empty((M, N), np.float64)
+    _check(_load().oracle_gemm_fp8_rowscaled(M, N, K, pa, lda, int(fmt_a), sA.ctypes.data, inc_a, pb,
+                                             ldb, int(fmt_b), sB.ctypes.data, inc_b, R.ctypes.data,
+                                             S.ctypes.data),
+           "oracle_gemm_fp8_rowscaled")
+    return R, S
+
+
+def gemm_fp8_rowscaled_at(A, fmt_a, sA, B, fmt_b, sB, ii, jj):
+    """``oracle_gemm_fp8_rowscaled_at``: R, S at (ii[p], jj[p])."""
+    M, K = A.shape
+    N = B.shape[1]
+    pa, lda = _mat(A, np.uint8)
+    pb, ldb = _mat(B, np.uint8)
+    sA = np.ascontiguousarray(sA, np.float32).ravel()
+    sB = np.ascontiguousarray(sB, np.float32).ravel()
+    inc_a = 0 if sA.size == 1 and M != 1 else 1
+    inc_b = 0 if sB.size == 1 and N != 1 else 1
+    ii = np.ascontiguousarray(ii, np.int64)
+    jj = np.ascontiguousarray(jj, np.int64)
+    R = np.empty(ii.shape, np.float64)
+    S = np.empty(ii.shape, np.float64)
+    _check(_load().oracle_gemm_fp8_rowscaled_at(M, N, K, pa, lda, int(fmt_a), sA.ctypes.data, inc_a,
+                                                pb, ldb, int(fmt_b), sB.ctypes.data, inc_b, ii.size,
+                                                ii.ctypes.data, jj.ctypes.data, R.ctypes.data,
+                                                S.ctypes.data),
+           "oracle_gemm_fp8_rowscaled_at")
+    return R, S
+
+
 def gemm_fp8_blockscaled_at(A, sA, B, sB, ii, jj):
     """``oracle_gemm_fp8_blockscaled_at``: R, S at output positions (ii[p], jj[p])."""
     lib = _load()
@@ -406,6 +530,20 @@ def quantize_i8_rows(X):
     S = np.empty(M, np.float32)
     _check(_load().oracle_quantize_i8_rows(M, K, px, ldx, Q.ctypes.data, max(K, 1), S.ctypes.data),
            "quantize_i8_rows")
+    return Q, S
+
+
+def quantize_fp8_blocks_fmt(X, fmt, br, bc):
+    """oracle_quantize_fp8_blocks_fmt: X FP32 [R, C] in br x bc blocks, into
+    E4M3 (fmt 0) or E5M2 (fmt 1) -> (Q codes [R, C], S FP32 [ceil(R/br), ceil(C/bc)])."""
+    R, Cc = X.shape
+    px, ldx = _mat(X, np.float32)
+    Q = np.empty((R, Cc), np.uint8)
+    nbr, nbc = -(-R // br), -(-Cc // bc)
+    S = np.empty((nbr, nbc), np.float32)
+    _check(_load().oracle_quantize_fp8_blocks_fmt(R, Cc, px, ldx, int(fmt), br, bc, Q.ctypes.data,
+                                                  max(Cc, 1), S.ctypes.data, max(nbc, 1)),
+           "quantize_fp8_blocks_fmt")
     return Q, S
 
 

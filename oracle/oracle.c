@@ -145,6 +145,51 @@ uint8_t oracle_f32_to_e4m3_rne_sat(float x) {
     return (uint8_t)(sign | (uint8_t)((E + 7) << 3) | (uint8_t)(n - 8.0));
 }
 
+/* FP8 E5M2 (OCP): 1 sign, 5 exponent (bias 15), 2 fraction bits; exponent
+ * 31 holds the infinities (fraction 0) and NaNs; largest finite 57344. */
+double oracle_e5m2_to_f64(uint8_t q) {
+    int sign = (q >> 7) & 1;
+    int e = (q >> 2) & 0x1f;
+    int f = q & 0x3;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)f, -16);             /* f/2^2 * 2^-14 */
+    } else if (e == 31) {
+        v = f ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(4 + f), e - 17);    /* (1 + f/2^2) * 2^(e-15) */
+    }
+    return sign ? -v : v;
+}
+
+/* FP32 -> E5M2, round to nearest, ties to even, saturating to +-57344
+ * (1.75 * 2^15) instead of overflowing to infinity.  Normal binades
+ * E = -14..15 hold 4 values spaced 2^(E-2); below 2^-14 the spacing is
+ * 2^-16.  NaN gives S.11111.11. */
+uint8_t oracle_f32_to_e5m2_rne_sat(float x) {
+    uint8_t sign = signbit(x) ? 0x80u : 0u;
+    if (isnan(x)) return (uint8_t)(sign | 0x7fu);
+    double a = fabs((double)x);
+    if (a == 0.0) return sign;
+    if (a >= 57344.0) return (uint8_t)(sign | 0x7bu);
+    int E = binade(a);
+    if (E < -14) {
+        double n = rint(ldexp(a, 16));          /* 0..4; 4 encodes 2^-14 */
+        return (uint8_t)(sign | (uint8_t)n);
+    }
+    double n = rint(ldexp(a, 2 - E));           /* 4..8 */
+    if (n == 8.0) {
+        n = 4.0;
+        E += 1;
+    }
+    if (E > 15) return (uint8_t)(sign | 0x7bu);
+    return (uint8_t)(sign | (uint8_t)((E + 15) << 2) | (uint8_t)(n - 4.0));
+}
+
+void oracle_decode_e5m2(const uint8_t* in, double* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e5m2_to_f64(in[i]);
+}
+
 void oracle_decode_f16(const uint16_t* in, double* out, int64_t n) {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_f16_to_f64(in[i]);
 }
@@ -368,11 +413,19 @@ static int fp8_args_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb
     return 1;
 }
 
-/* One element: for each K block, the block's raw E4M3 product sum times the
+typedef double (*decode8_fn)(uint8_t);
+
+/* 0: E4M3, 1: E5M2 */
+static decode8_fn fp8_decoder(int fmt) {
+    return fmt == 0 ? oracle_e4m3_to_f64 : fmt == 1 ? oracle_e5m2_to_f64 : NULL;
+}
+
+/* One element: for each K block, the block's raw FP8 product sum times the
  * product of the two block scales, summed over blocks in ascending order. */
-static int fp8_element(int64_t K, const uint8_t* A, int64_t lda, const float* sA, int64_t ld_sa,
-                       const uint8_t* B, int64_t ldb, const float* sB, int64_t ld_sb,
-                       int64_t i, int64_t j, double* r_out, double* s_out) {
+static int fp8_element(int64_t K, const uint8_t* A, int64_t lda, decode8_fn da, const float* sA,
+                       int64_t ld_sa, const uint8_t* B, int64_t ldb, decode8_fn db,
+                       const float* sB, int64_t ld_sb, int64_t i, int64_t j, double* r_out,
+                       double* s_out) {
     double r = 0.0, s = 0.0;
     int bad = 0;
     for (int64_t k0 = 0; k0 < K; k0 += FP8_BLOCK) {
@@ -383,9 +436,9 @@ static int fp8_element(int64_t K, const uint8_t* A, int64_t lda, const float* sA
         const int64_t k1 = (k0 + FP8_BLOCK < K) ? k0 + FP8_BLOCK : K;
         double blk = 0.0;
         for (int64_t k = k0; k < k1; ++k) {
-            const double a = oracle_e4m3_to_f64(A[i * lda + k]);
-            const double b = oracle_e4m3_to_f64(B[k * ldb + j]);
-            if (isnan(a) || isnan(b)) bad = 1;
+            const double a = da(A[i * lda + k]);
+            const double b = db(B[k * ldb + j]);
+            if (!isfinite(a) || !isfinite(b)) bad = 1;
             blk += a * b;                                  /* exact products */
             s += fabs(a * sa) * fabs(b * sb);
         }
@@ -396,18 +449,50 @@ static int fp8_element(int64_t K, const uint8_t* A, int64_t lda, const float* sA
     return bad ? 2 : 0;
 }
 
-int oracle_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K,
-                                const uint8_t* A, int64_t lda, const float* sA, int64_t ld_sa,
-                                const uint8_t* B, int64_t ldb, const float* sB, int64_t ld_sb,
-                                double* R, double* S) {
+int oracle_gemm_fp8_blockscaled_fmt(int64_t M, int64_t N, int64_t K,
+                                    const uint8_t* A, int64_t lda, int fmt_a,
+                                    const float* sA, int64_t ld_sa,
+                                    const uint8_t* B, int64_t ldb, int fmt_b,
+                                    const float* sB, int64_t ld_sb, double* R, double* S) {
+    const decode8_fn da = fp8_decoder(fmt_a), db = fp8_decoder(fmt_b);
+    if (!da || !db) return 1;
     if (!fp8_args_ok(M, N, K, lda, ldb, sA, ld_sa, sB, ld_sb) || !R || !S) return 1;
     int err = 0;
     #pragma omp parallel for schedule(dynamic, 4) reduction(|:err)
     for (int64_t i = 0; i < M; ++i)
         for (int64_t j = 0; j < N; ++j)
-            err |= fp8_element(K, A, lda, sA, ld_sa, B, ldb, sB, ld_sb, i, j,
+            err |= fp8_element(K, A, lda, da, sA, ld_sa, B, ldb, db, sB, ld_sb, i, j,
                                &R[i * N + j], &S[i * N + j]);
     return err ? 2 : 0;
+}
+
+int oracle_gemm_fp8_blockscaled_fmt_at(int64_t M, int64_t N, int64_t K,
+                                       const uint8_t* A, int64_t lda, int fmt_a,
+                                       const float* sA, int64_t ld_sa,
+                                       const uint8_t* B, int64_t ldb, int fmt_b,
+                                       const float* sB, int64_t ld_sb,
+                                       int64_t P, const int64_t* ii, const int64_t* jj,
+                                       double* R, double* S) {
+    const decode8_fn da = fp8_decoder(fmt_a), db = fp8_decoder(fmt_b);
+    if (!da || !db) return 1;
+    if (!fp8_args_ok(M, N, K, lda, ldb, sA, ld_sa, sB, ld_sb) || P < 0) return 1;
+    if (P > 0 && (!ii || !jj || !R || !S)) return 1;
+    int err = 0;
+    #pragma omp parallel for schedule(dynamic, 16) reduction(|:err)
+    for (int64_t p = 0; p < P; ++p) {
+        if (ii[p] < 0 || ii[p] >= M || jj[p] < 0 || jj[p] >= N) { err |= 8; continue; }
+        err |= fp8_element(K, A, lda, da, sA, ld_sa, B, ldb, db, sB, ld_sb, ii[p], jj[p], &R[p],
+                           &S[p]);
+    }
+    if (err & 8) return 1;
+    return err ? 2 : 0;
+}
+
+int oracle_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K,
+                                const uint8_t* A, int64_t lda, const float* sA, int64_t ld_sa,
+                                const uint8_t* B, int64_t ldb, const float* sB, int64_t ld_sb,
+                                double* R, double* S) {
+    return oracle_gemm_fp8_blockscaled_fmt(M, N, K, A, lda, 0, sA, ld_sa, B, ldb, 0, sB, ld_sb, R, S);
 }
 
 int oracle_gemm_fp8_blockscaled_at(int64_t M, int64_t N, int64_t K,
@@ -415,15 +500,68 @@ int oracle_gemm_fp8_blockscaled_at(int64_t M, int64_t N, int64_t K,
                                    const uint8_t* B, int64_t ldb, const float* sB, int64_t ld_sb,
                                    int64_t P, const int64_t* ii, const int64_t* jj,
                                    double* R, double* S) {
-    if (!fp8_args_ok(M, N, K, lda, ldb, sA, ld_sa, sB, ld_sb) || P < 0) return 1;
+    return oracle_gemm_fp8_blockscaled_fmt_at(M, N, K, A, lda, 0, sA, ld_sa, B, ldb, 0, sB, ld_sb,
+                                              P, ii, jj, R, S);
+}
+
+/* ------------------------------------------------------------------------ */
+/* FP8 GEMM with per-row A and per-column B scales (see oracle.h).           */
+/* ------------------------------------------------------------------------ */
+static int fp8_row_element(int64_t K, const uint8_t* A, int64_t lda, decode8_fn da, double sa,
+                           const uint8_t* B, int64_t ldb, decode8_fn db, double sb, int64_t i,
+                           int64_t j, double* r_out, double* s_out) {
+    double r = 0.0, s = 0.0;
+    int bad = !isfinite(sa) || !isfinite(sb);
+    for (int64_t k = 0; k < K; ++k) {
+        const double a = da(A[i * lda + k]);
+        const double b = db(B[k * ldb + j]);
+        if (!isfinite(a) || !isfinite(b)) bad = 1;
+        r += a * b;
+        s += fabs(a * b);
+    }
+    *r_out = (sa * sb) * r;
+    *s_out = fabs(sa * sb) * s;
+    return bad ? 2 : 0;
+}
+
+int oracle_gemm_fp8_rowscaled_at(int64_t M, int64_t N, int64_t K,
+                                 const uint8_t* A, int64_t lda, int fmt_a,
+                                 const float* sA, int64_t inc_a,
+                                 const uint8_t* B, int64_t ldb, int fmt_b,
+                                 const float* sB, int64_t inc_b,
+                                 int64_t P, const int64_t* ii, const int64_t* jj,
+                                 double* R, double* S) {
+    const decode8_fn da = fp8_decoder(fmt_a), db = fp8_decoder(fmt_b);
+    if (!da || !db || !dims_ok(M, N, K, lda, ldb) || P < 0) return 1;
+    if ((inc_a != 0 && inc_a != 1) || (inc_b != 0 && inc_b != 1)) return 1;
+    if ((M > 0 && !sA) || (N > 0 && !sB)) return 1;
     if (P > 0 && (!ii || !jj || !R || !S)) return 1;
     int err = 0;
     #pragma omp parallel for schedule(dynamic, 16) reduction(|:err)
     for (int64_t p = 0; p < P; ++p) {
         if (ii[p] < 0 || ii[p] >= M || jj[p] < 0 || jj[p] >= N) { err |= 8; continue; }
-        err |= fp8_element(K, A, lda, sA, ld_sa, B, ldb, sB, ld_sb, ii[p], jj[p], &R[p], &S[p]);
+        err |= fp8_row_element(K, A, lda, da, (double)sA[ii[p] * inc_a], B, ldb, db,
+                               (double)sB[jj[p] * inc_b], ii[p], jj[p], &R[p], &S[p]);
     }
     if (err & 8) return 1;
+    return err ? 2 : 0;
+}
+
+int oracle_gemm_fp8_rowscaled(int64_t M, int64_t N, int64_t K,
+                              const uint8_t* A, int64_t lda, int fmt_a,
+                              const float* sA, int64_t inc_a,
+                              const uint8_t* B, int64_t ldb, int fmt_b,
+                              const float* sB, int64_t inc_b, double* R, double* S) {
+    const decode8_fn da = fp8_decoder(fmt_a), db = fp8_decoder(fmt_b);
+    if (!da || !db || !dims_ok(M, N, K, lda, ldb) || !R || !S) return 1;
+    if ((inc_a != 0 && inc_a != 1) || (inc_b != 0 && inc_b != 1)) return 1;
+    if ((M > 0 && !sA) || (N > 0 && !sB)) return 1;
+    int err = 0;
+    #pragma omp parallel for schedule(dynamic, 4) reduction(|:err)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j)
+            err |= fp8_row_element(K, A, lda, da, (double)sA[i * inc_a], B, ldb, db,
+                                   (double)sB[j * inc_b], i, j, &R[i * N + j], &S[i * N + j]);
     return err ? 2 : 0;
 }
 
@@ -564,10 +702,12 @@ int oracle_quantize_i8_rows(int64_t M, int64_t K, const uint16_t* X, int64_t ldx
 /* ------------------------------------------------------------------------ */
 /* FP8 E4M3 block quantisation (see oracle.h).                                */
 /* ------------------------------------------------------------------------ */
-int oracle_quantize_fp8_blocks(int64_t R, int64_t Cc, const float* X, int64_t ldx,
-                               int64_t br, int64_t bc, uint8_t* Q, int64_t ldq,
-                               float* S, int64_t lds) {
-    if (R < 0 || Cc < 0 || br < 1 || bc < 1 || !X || !Q || !S) return 1;
+int oracle_quantize_fp8_blocks_fmt(int64_t R, int64_t Cc, const float* X, int64_t ldx, int fmt,
+                                   int64_t br, int64_t bc, uint8_t* Q, int64_t ldq,
+                                   float* S, int64_t lds) {
+    if (R < 0 || Cc < 0 || br < 1 || bc < 1 || !X || !Q || !S || (fmt != 0 && fmt != 1)) return 1;
+    /* the largest finite value of the format */
+    const float qmax = fmt == 0 ? 448.0f : 57344.0f;
     const int64_t nbr = (R + br - 1) / br, nbc = (Cc + bc - 1) / bc;
     if (Cc > 0 && (ldx < Cc || ldq < Cc)) return 1;
     if (nbc > 0 && lds < nbc) return 1;
@@ -582,14 +722,22 @@ int oracle_quantize_fp8_blocks(int64_t R, int64_t Cc, const float* X, int64_t ld
             for (int64_t i = i0; i < i1; ++i)
                 for (int64_t j = j0; j < j1; ++j)
                     if (fabsf(X[i * ldx + j]) > amax) amax = fabsf(X[i * ldx + j]);
-            const float s = (amax > 0.0f) ? amax / 448.0f : 1.0f;
+            const float s = (amax > 0.0f) ? amax / qmax : 1.0f;
             S[bi * lds + bj] = s;
             for (int64_t i = i0; i < i1; ++i)
-                for (int64_t j = j0; j < j1; ++j)
-                    Q[i * ldq + j] = oracle_f32_to_e4m3_rne_sat(X[i * ldx + j] / s);
+                for (int64_t j = j0; j < j1; ++j) {
+                    const float u = X[i * ldx + j] / s;
+                    Q[i * ldq + j] = fmt == 0 ? oracle_f32_to_e4m3_rne_sat(u) : oracle_f32_to_e5m2_rne_sat(u);
+                }
         }
     }
     return 0;
+}
+
+int oracle_quantize_fp8_blocks(int64_t R, int64_t Cc, const float* X, int64_t ldx,
+                               int64_t br, int64_t bc, uint8_t* Q, int64_t ldq,
+                               float* S, int64_t lds) {
+    return oracle_quantize_fp8_blocks_fmt(R, Cc, X, ldx, 0, br, bc, Q, ldq, S, lds);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -53,6 +53,12 @@ uint16_t oracle_f32_to_f16_rne(float x);
 /* FP32 -> OCP E4M3FN, round to nearest, ties to even, saturating to +-448
  * (no infinities in the format; NaN gives S.1111.111). */
 uint8_t  oracle_f32_to_e4m3_rne_sat(float x);
+/* OCP E5M2 (the "Precision" section's other FP8 format: 1/5/2 bits, wider
+ * range, for gradients): exact decode (infinities and NaNs at exponent 31),
+ * and FP32 -> E5M2 round to nearest, ties to even, saturating to +-57344. */
+double   oracle_e5m2_to_f64(uint8_t q);
+uint8_t  oracle_f32_to_e5m2_rne_sat(float x);
+void     oracle_decode_e5m2(const uint8_t* in, double* out, int64_t n);
 
 void oracle_decode_f16(const uint16_t* in, double* out, int64_t n);
 void oracle_decode_bf16(const uint16_t* in, double* out, int64_t n);
@@ -98,6 +104,39 @@ int oracle_gemm_i8_i32_at(int64_t M, int64_t N, int64_t K,
  * S[i][j] = sum_k |a[i][k]*sA[i][k/128]| * |b[k][j]*sB[k/128][j/128]|
  * sA is M x ceil(K/128) (leading dimension ld_sa), sB is ceil(K/128) x
  * ceil(N/128) (leading dimension ld_sb). ---- */
+/* The same with each operand's FP8 format given (fmt 0: E4M3, 1: E5M2). */
+int oracle_gemm_fp8_blockscaled_fmt(int64_t M, int64_t N, int64_t K,
+                                    const uint8_t* A, int64_t lda, int fmt_a,
+                                    const float* sA, int64_t ld_sa,
+                                    const uint8_t* B, int64_t ldb, int fmt_b,
+                                    const float* sB, int64_t ld_sb, double* R, double* S);
+int oracle_gemm_fp8_blockscaled_fmt_at(int64_t M, int64_t N, int64_t K,
+                                       const uint8_t* A, int64_t lda, int fmt_a,
+                                       const float* sA, int64_t ld_sa,
+                                       const uint8_t* B, int64_t ldb, int fmt_b,
+                                       const float* sB, int64_t ld_sb,
+                                       int64_t P, const int64_t* ii, const int64_t* jj,
+                                       double* R, double* S);
+
+/* ---- FP8 GEMM with per-row / per-tensor scales (the "Precision" section:
+ * FP8 scale factors per tensor, per row or per block): one scale per row of
+ * A (sA[i * inc_a]) and one per column of B (sB[j * inc_b]); inc 0 makes
+ * the scale per tensor.
+ * R[i][j] = (sA[i*inc_a] * sB[j*inc_b]) * sum_k a[i][k] * b[k][j]
+ * S[i][j] = |sA * sB| * sum_k |a[i][k] * b[k][j]|.  inc_a, inc_b in {0, 1}. ---- */
+int oracle_gemm_fp8_rowscaled(int64_t M, int64_t N, int64_t K,
+                              const uint8_t* A, int64_t lda, int fmt_a,
+                              const float* sA, int64_t inc_a,
+                              const uint8_t* B, int64_t ldb, int fmt_b,
+                              const float* sB, int64_t inc_b, double* R, double* S);
+int oracle_gemm_fp8_rowscaled_at(int64_t M, int64_t N, int64_t K,
+                                 const uint8_t* A, int64_t lda, int fmt_a,
+                                 const float* sA, int64_t inc_a,
+                                 const uint8_t* B, int64_t ldb, int fmt_b,
+                                 const float* sB, int64_t inc_b,
+                                 int64_t P, const int64_t* ii, const int64_t* jj,
+                                 double* R, double* S);
+
 int oracle_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K,
                                 const uint8_t* A, int64_t lda, const float* sA, int64_t ld_sa,
                                 const uint8_t* B, int64_t ldb, const float* sB, int64_t ld_sb,
@@ -156,6 +195,12 @@ int oracle_quantize_i8_rows(int64_t M, int64_t K, const uint16_t* X, int64_t ldx
  * edges keep their own scale); for each block amax = max |x|,
  * s = fl32(amax / 448) (s = 1 when amax = 0), Q = e4m3_rne_sat(fl32(x / s)).
  * S is ceil(R/br) x ceil(Cc/bc) with leading dimension lds. ---- */
+/* The same into E4M3 (fmt 0, s = amax / 448) or E5M2 (fmt 1, s = amax /
+ * 57344); br x bc blocks of any size: 1 x Cc is one scale per row, R x Cc one
+ * per tensor. */
+int oracle_quantize_fp8_blocks_fmt(int64_t R, int64_t Cc, const float* X, int64_t ldx, int fmt,
+                                   int64_t br, int64_t bc, uint8_t* Q, int64_t ldq,
+                                   float* S, int64_t lds);
 int oracle_quantize_fp8_blocks(int64_t R, int64_t Cc, const float* X, int64_t ldx,
                                int64_t br, int64_t bc, uint8_t* Q, int64_t ldq,
                                float* S, int64_t lds);
