@@ -151,6 +151,39 @@ mpdt_status gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K,
                                  const float* scale_b, int64_t ld_sb,
                                  uint16_t* D, int64_t ldd, void* stream);
 
+/* FP8 formats ("Tensor Core" page, section "Precision": E4M3 for weights
+ * and activations, E5M2 -- 5 exponent bits, 2 fraction bits, the range of
+ * FP16 -- for gradients).  Both are the OCP encodings: E4M3 "FN" (bias 7, no
+ * infinities, max 448), E5M2 (bias 15, infinities and NaNs at exponent 31,
+ * max 57344). */
+typedef enum { MPDT_FP8_E4M3 = 0, MPDT_FP8_E5M2 = 1 } mpdt_fp8_format;
+
+/* gemm_fp8_blockscaled with each operand's format given (fmt_a, fmt_b: an
+ * mpdt_fp8_format; any mix).  Same scales, accumulation and output.  Codes
+ * that decode to infinity or NaN give undefined results. */
+mpdt_status gemm_fp8_blockscaled_fmt(int64_t M, int64_t N, int64_t K,
+                                     const uint8_t* A, int64_t lda, int fmt_a,
+                                     const float* scale_a, int64_t ld_sa,
+                                     const uint8_t* B, int64_t ldb, int fmt_b,
+                                     const float* scale_b, int64_t ld_sb,
+                                     uint16_t* D, int64_t ldd, void* stream);
+
+/* FP8 GEMM with per-row / per-tensor scales (same section: FP8 scale factors
+ * per tensor, per row or per block):
+ *   D[i][j] = bf16_rne( (acc[i][j] * scale_a[i * inc_a]) * scale_b[j * inc_b] )
+ * acc = sum_k A[i][k] * B[k][j] of the decoded FP8 values, in FP32 (the
+ * exact products added in FP32 in an order of the kernel's choosing), then
+ * two FP32 products in this order.  scale_a holds one value per row of A
+ * (inc_a = 1) or one for the tensor (inc_a = 0); scale_b one per column of B
+ * (inc_b = 1) or one (inc_b = 0).  Scales are read (must be non-NULL) even
+ * when K = 0, which gives D = bf16(0 * ...).  Formats as above. */
+mpdt_status gemm_fp8_rowscaled(int64_t M, int64_t N, int64_t K,
+                               const uint8_t* A, int64_t lda, int fmt_a,
+                               const float* scale_a, int64_t inc_a,
+                               const uint8_t* B, int64_t ldb, int fmt_b,
+                               const float* scale_b, int64_t inc_b,
+                               uint16_t* D, int64_t ldd, void* stream);
+
 /* Batch-1 W8A8 linear layer.  M must be 1.
  *   z[o] = sum_k x[k] * W[o][k]                      (INT32, exact)
  *   y[o] = bf16_rne( (float(z[o]) * x_scale) * w_scale[o] )   (two FP32 products,

@@ -20,7 +20,8 @@ import torch
 
 __all__ = ["gemm_f16", "gemm_bf16", "gemm_f16_f16out", "gemm_bf16_bf16out", "gemm_f16_bias_act",
            "gemm_bf16_bias_act", "ACT_NONE", "ACT_RELU", "ACT_GELU", "ACT_SILU", "gemm_i8_i32",
-           "gemm_fp8_blockscaled", "gemv_w8a8", "gemm_w8a8", "gemm_w8a8_requant", "quantize_i8_rows",
+           "gemm_fp8_blockscaled", "gemm_fp8_blockscaled_fmt", "gemm_fp8_rowscaled", "FP8_E4M3",
+           "FP8_E5M2", "gemv_w8a8", "gemm_w8a8", "gemm_w8a8_requant", "quantize_i8_rows",
            "quantize_fp8_blocks",
            "MpdtError", "lib", "lib_path", "version"]
 
@@ -65,6 +66,12 @@ def lib() -> ctypes.CDLL:
         L.gemm_fp8_blockscaled.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
                                            _i64, _vp, _i64, _vp]
         L.gemm_fp8_blockscaled.restype = ctypes.c_int
+        L.gemm_fp8_blockscaled_fmt.argtypes = [_i64, _i64, _i64, _vp, _i64, ctypes.c_int, _vp, _i64,
+                                               _vp, _i64, ctypes.c_int, _vp, _i64, _vp, _i64, _vp]
+        L.gemm_fp8_blockscaled_fmt.restype = ctypes.c_int
+        L.gemm_fp8_rowscaled.argtypes = [_i64, _i64, _i64, _vp, _i64, ctypes.c_int, _vp, _i64,
+                                         _vp, _i64, ctypes.c_int, _vp, _i64, _vp, _i64, _vp]
+        L.gemm_fp8_rowscaled.restype = ctypes.c_int
         L.gemv_w8a8.argtypes = [_i64, _i64, _i64, _vp, ctypes.c_float, _vp, _i64, _vp, _vp, _vp,
                                 _vp]
         L.gemv_w8a8.restype = ctypes.c_int
@@ -224,6 +231,49 @@ def gemm_fp8_blockscaled(A, scale_a, B, scale_b, out=None):
     _check("gemm_fp8_blockscaled",
            lib().gemm_fp8_blockscaled(M, N, K, pa, lda, psa, ldsa, pb, ldb, psb, ldsb, pd, ldd,
                                       _stream(A)))
+    return out
+
+
+# FP8 operand formats (mpdt_fp8_format)
+FP8_E4M3, FP8_E5M2 = 0, 1
+
+
+def gemm_fp8_blockscaled_fmt(A, fmt_a, scale_a, B, fmt_b, scale_b, out=None):
+    """gemm_fp8_blockscaled with each operand's format (FP8_E4M3 / FP8_E5M2)."""
+    M, K = A.shape
+    N = B.shape[1]
+    pa, lda = _mat(A, 1, "A")
+    pb, ldb = _mat(B, 1, "B")
+    psa, ldsa = _mat(scale_a, 4, "scale_a")
+    psb, ldsb = _mat(scale_b, 4, "scale_b")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    pd, ldd = _mat(out, 2, "out")
+    _check("gemm_fp8_blockscaled_fmt",
+           lib().gemm_fp8_blockscaled_fmt(M, N, K, pa, lda, int(fmt_a), psa, ldsa, pb, ldb, int(fmt_b),
+                                          psb, ldsb, pd, ldd, _stream(A)))
+    return out
+
+
+def gemm_fp8_rowscaled(A, fmt_a, scale_a, B, fmt_b, scale_b, out=None):
+    """BF16 D = (A . B) * scale_a[i] * scale_b[j]: FP8 A [M,K], B [K,N];
+    scale_a FP32 with M values (per row) or 1 (per tensor), scale_b with N
+    values (per column) or 1."""
+    M, K = A.shape
+    N = B.shape[1]
+    pa, lda = _mat(A, 1, "A")
+    pb, ldb = _mat(B, 1, "B")
+    inc = []
+    for t, n, name in ((scale_a, M, "scale_a"), (scale_b, N, "scale_b")):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.numel() not in (1, n):
+            raise ValueError(f"{name} must be a contiguous FP32 GPU tensor of 1 or {n} values")
+        inc.append(0 if t.numel() == 1 and n != 1 else 1)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    pd, ldd = _mat(out, 2, "out")
+    _check("gemm_fp8_rowscaled",
+           lib().gemm_fp8_rowscaled(M, N, K, pa, lda, int(fmt_a), scale_a.data_ptr(), inc[0], pb, ldb,
+                                    int(fmt_b), scale_b.data_ptr(), inc[1], pd, ldd, _stream(A)))
     return out
 
 

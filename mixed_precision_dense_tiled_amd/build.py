@@ -19,7 +19,7 @@ PROBE_LIB = os.path.join(PKG, "libmpdt_probes.so")
 ORACLE_DIR = os.path.join(ROOT, "oracle")
 ORACLE_LIB = os.path.join(ORACLE_DIR, "liboracle.so")
 
-HIP_SOURCES = ["abi.hip", "gemm.hip", "gemm_epi.hip", "gemm_fp8.hip", "gemv_w8a8.hip", "quant.hip"]
+HIP_SOURCES = ["abi.hip", "gemm.hip", "gemm_epi.hip", "gemm_fp8.hip", "gemm_fp8_general.hip", "gemv_w8a8.hip", "quant.hip"]
 
 # Per-source device-compiler options.  The one-wave FP8 GEMM rescales its MFMA
 # block sums with FP32 FMAs every K tile; VALU instructions cannot read AGPRs,

@@ -233,23 +233,37 @@ MPDT_EXPORT mpdt_status gemm_i8_i32(int64_t M, int64_t N, int64_t K, const int8_
     return launched(mpdt::launch_gemm(mpdt::Kind::I8, a, al, (hipStream_t)stream), fn);
 }
 
-MPDT_EXPORT mpdt_status gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_t* A,
-                                             int64_t lda, const float* scale_a, int64_t ld_sa,
-                                             const uint8_t* B, int64_t ldb, const float* scale_b,
-                                             int64_t ld_sb, uint16_t* D, int64_t ldd,
-                                             void* stream) {
-    const char* fn = "gemm_fp8_blockscaled";
+namespace {
+// The FP8 GEMMs.  Block-scaled: scale_a M x ceil(K/128) (ld_sa), scale_b
+// ceil(K/128) x ceil(N/128) (ld_sb).  Row-scaled (rows): scale_a holds M
+// values read with increment ld_sa (0 or 1), scale_b N values with
+// increment ld_sb.
+mpdt_status run_fp8(const char* fn, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                    int fmt_a, const float* scale_a, int64_t ld_sa, const uint8_t* B, int64_t ldb,
+                    int fmt_b, const float* scale_b, int64_t ld_sb, bool rows, uint16_t* D,
+                    int64_t ldd, void* stream) {
     if (!dims_ok(M, N, K)) return fail(MPDT_ERROR_INVALID_VALUE, fn, "dimension out of range");
+    if ((fmt_a != MPDT_FP8_E4M3 && fmt_a != MPDT_FP8_E5M2) ||
+        (fmt_b != MPDT_FP8_E4M3 && fmt_b != MPDT_FP8_E5M2))
+        return fail(MPDT_ERROR_INVALID_VALUE, fn, "unknown FP8 format");
+    if (rows && ((ld_sa != 0 && ld_sa != 1) || (ld_sb != 0 && ld_sb != 1)))
+        return fail(MPDT_ERROR_INVALID_VALUE, fn, "scale increments must be 0 or 1");
     const int64_t kb = (K + 127) / 128, nb = (N + 127) / 128;
     Span ssa, ssb;
-    if (M > 0 && N > 0 && K > 0) {
+    if (M > 0 && N > 0 && (K > 0 || rows)) {
         if (!scale_a || !scale_b) return fail(MPDT_ERROR_INVALID_VALUE, fn, "scale array is NULL");
-        if (ld_sa < kb) return fail(MPDT_ERROR_INVALID_VALUE, fn, "ld_sa < ceil(K/128)");
-        if (ld_sb < nb) return fail(MPDT_ERROR_INVALID_VALUE, fn, "ld_sb < ceil(N/128)");
         if (!aligned_to(scale_a, 4) || !aligned_to(scale_b, 4))
             return fail(MPDT_ERROR_MISALIGNED, fn, "scale array not 4-byte aligned");
-        if (!span_of(scale_a, M, kb, ld_sa, 4, &ssa) || !span_of(scale_b, kb, nb, ld_sb, 4, &ssb))
-            return fail(MPDT_ERROR_INVALID_VALUE, fn, "scale array too large");
+        if (rows) {
+            if (!span_of(scale_a, 1, ld_sa ? M : 1, M, 4, &ssa) ||
+                !span_of(scale_b, 1, ld_sb ? N : 1, N, 4, &ssb))
+                return fail(MPDT_ERROR_INVALID_VALUE, fn, "scale array too large");
+        } else {
+            if (ld_sa < kb) return fail(MPDT_ERROR_INVALID_VALUE, fn, "ld_sa < ceil(K/128)");
+            if (ld_sb < nb) return fail(MPDT_ERROR_INVALID_VALUE, fn, "ld_sb < ceil(N/128)");
+            if (!span_of(scale_a, M, kb, ld_sa, 4, &ssa) || !span_of(scale_b, kb, nb, ld_sb, 4, &ssb))
+                return fail(MPDT_ERROR_INVALID_VALUE, fn, "scale array too large");
+        }
     }
     Span extra[2] = {ssa, ssb};
     mpdt_status s = check_gemm(fn, M, N, K, A, lda, 1, B, ldb, 1, nullptr, 0, 4, D, ldd, 2, extra, 2);
@@ -271,8 +285,38 @@ MPDT_EXPORT mpdt_status gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K, co
     a.ld_sa = ld_sa;
     a.sB = scale_b;
     a.ld_sb = ld_sb;
+    a.fp8_fmt = (fmt_a == MPDT_FP8_E5M2 ? 1 : 0) | (fmt_b == MPDT_FP8_E5M2 ? 2 : 0);
+    a.row_scaled = rows ? 1 : 0;
     const bool al = aligned_to(A, 16) && aligned_to(B, 16) && lda % 16 == 0 && ldb % 16 == 0;
-    return launched(mpdt::launch_gemm(mpdt::Kind::FP8, a, al, (hipStream_t)stream), fn);
+    return launched(mpdt::launch_fp8(a, al, (hipStream_t)stream), fn);
+}
+}  // namespace
+
+MPDT_EXPORT mpdt_status gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_t* A,
+                                             int64_t lda, const float* scale_a, int64_t ld_sa,
+                                             const uint8_t* B, int64_t ldb, const float* scale_b,
+                                             int64_t ld_sb, uint16_t* D, int64_t ldd,
+                                             void* stream) {
+    return run_fp8("gemm_fp8_blockscaled", M, N, K, A, lda, MPDT_FP8_E4M3, scale_a, ld_sa, B, ldb,
+                   MPDT_FP8_E4M3, scale_b, ld_sb, false, D, ldd, stream);
+}
+
+MPDT_EXPORT mpdt_status gemm_fp8_blockscaled_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* A,
+                                                 int64_t lda, int fmt_a, const float* scale_a,
+                                                 int64_t ld_sa, const uint8_t* B, int64_t ldb,
+                                                 int fmt_b, const float* scale_b, int64_t ld_sb,
+                                                 uint16_t* D, int64_t ldd, void* stream) {
+    return run_fp8("gemm_fp8_blockscaled_fmt", M, N, K, A, lda, fmt_a, scale_a, ld_sa, B, ldb, fmt_b,
+                   scale_b, ld_sb, false, D, ldd, stream);
+}
+
+MPDT_EXPORT mpdt_status gemm_fp8_rowscaled(int64_t M, int64_t N, int64_t K, const uint8_t* A,
+                                           int64_t lda, int fmt_a, const float* scale_a,
+                                           int64_t inc_a, const uint8_t* B, int64_t ldb, int fmt_b,
+                                           const float* scale_b, int64_t inc_b, uint16_t* D,
+                                           int64_t ldd, void* stream) {
+    return run_fp8("gemm_fp8_rowscaled", M, N, K, A, lda, fmt_a, scale_a, inc_a, B, ldb, fmt_b,
+                   scale_b, inc_b, true, D, ldd, stream);
 }
 
 MPDT_EXPORT mpdt_status gemv_w8a8(int64_t M, int64_t N, int64_t K, const int8_t* x, float x_scale,

@@ -1,24 +1,10 @@
 // gemm.hip -- host entry of the tiled MFMA GEMMs with the plain epilogue
 // (D = A x B + C in the output format): FP16 / BF16 -> FP32 or 16-bit, INT8
-// -> INT32, and FP8 E4M3 with block scales -> BF16.  The kernel template
-// and its launchers are in gemm_kernel.hpp.
+// -> INT32; FP8 goes to gemm_fp8_general.hip.  The kernel template and its
+// launchers are in gemm_kernel.hpp.
 #include "gemm_kernel.hpp"
 
 namespace mpdt {
-
-// FP8: the full tiles of a problem the one-wave kernel takes (gemm_fp8.hip)
-// go to it, the edge tiles and every other problem to the general kernel.
-static hipError_t launch_fp8(const GemmArgs& a0, bool aligned, hipStream_t stream) {
-    const bool one = fp8_1w_eligible(a0, aligned);
-    const int int_tm = one ? a0.M / FP8_TILE_M : 0;
-    const int int_tn = one ? a0.N / FP8_TILE_N : 0;
-    if (int_tm > 0 && int_tn > 0) {
-        const hipError_t e = launch_fp8_1w(a0, int_tm, int_tn, stream);
-        if (e != hipSuccess) return e;
-        return launch_general<Kind::FP8, CfgFP8>(a0, aligned, int_tm, int_tn, stream);
-    }
-    return launch_general<Kind::FP8, CfgFP8>(a0, aligned, 0, 0, stream);
-}
 
 hipError_t launch_gemm(Kind kind, const GemmArgs& a, bool aligned, hipStream_t stream) {
     switch (kind) {

@@ -61,12 +61,20 @@ template <> struct Fmt<Kind::I8> {
 };
 template <> struct Fmt<Kind::FP8> {
     static constexpr int ES = 1;
-    static constexpr int STEP_BYTES = 64;   // 32x32x64, E4M3 x E4M3, unit (127) E8M0 scales
+    static constexpr int STEP_BYTES = 64;   // 32x32x64, unit (127) E8M0 scales
     using Acc = f32x16;
+    // FA, FB: the formats of the first and second operand (the instruction's
+    // format fields: 0 E4M3, 1 E5M2)
+    template <int FA = 0, int FB = 0>
     __device__ static Acc mma(i32x8 a, i32x8 b, Acc c) {
-        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 127, 0, 127);
     }
 };
+
+// FP8 variants of the kernels: bit 0 A is E5M2, bit 1 B is E5M2, bit 2 one
+// scale per row of A and per column of B applied once at the end (otherwise
+// the 1 x 128 / 128 x 128 block scales, applied per K block).
+constexpr int F8_A_E5M2 = 1, F8_B_E5M2 = 2, F8_ROWS = 4;
 
 // ---------------------------------------------------------------------------
 // Tile geometry and LDS layout.

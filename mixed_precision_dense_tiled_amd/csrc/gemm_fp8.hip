@@ -60,11 +60,18 @@ namespace mpdt {
 // pieces and one scale load: waves 0 and 1 fetch the A-row scales of rows
 // 0-63 and 64-127, waves 2 and 3 the two B scales); past the last tile they
 // read an empty buffer range, so the vmcnt arithmetic never changes.
-template <class C>
+//
+// F8 (F8_* bits): E5M2 operands (the MFMA's format fields), or one scale per
+// row of A and per column of B instead of the block scales: then every
+// promotion multiplier is 1 (the scale loads read an empty range) and the
+// scales are applied once, D = bf16((acc * sA[row]) * sB[col]).
+template <class C, int F8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_fp8_1w_kernel(GemmArgs g) {
     using F = Fmt<Kind::FP8>;
     using Acc = F::Acc;
+    constexpr int FA = (F8 & F8_A_E5M2) ? 1 : 0, FB = (F8 & F8_B_E5M2) ? 1 : 0;
+    constexpr bool ROWS = (F8 & F8_ROWS) != 0;
     static_assert(C::NT == 256 && C::WM == 64 && C::WN == 128 && C::KT_BYTES == 128 &&
                       C::STEPS == 2 && C::UA == 4 && C::UB == 8 && C::B_ROW == 256,
                   "128 x 256 tile, 2 x 2 waves, one 128-byte K tile per scale block");
@@ -135,7 +142,7 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
     const uint32_t ldsa4 = (uint32_t)g.ld_sa * 4u;
     const uint32_t voffS = scaleA ? (uint32_t)((lane >> 1) + 32 * (lane & 1)) * ldsa4
                                   : (uint32_t)(lane & 1) * 4u;
-    const uint32_t rangeS = scaleA ? 63u * ldsa4 + 4u : 8u;
+    const uint32_t rangeS = ROWS ? 0u : scaleA ? 63u * ldsa4 + 4u : 8u;
     const uint64_t baseS = scaleA ? (uint64_t)(uintptr_t)g.sA + (uint64_t)((int64_t)(m0 + wave * 64) * ldsa4)
                             : (uint64_t)(uintptr_t)g.sB + (uint64_t)(n0 / 128) * 4u;
     const uint64_t stepS = scaleA ? 4u : (uint64_t)g.ld_sb * 4u;
@@ -240,11 +247,12 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
             a8[e] = (int32_t)fr.a[i][s][e >> 2][e & 3];
             b8[e] = (int32_t)fr.b[s][j][e >> 1][e & 1];
         }
+        // (operands swapped: B's format goes in the first field)
         if (s == 0) {
             const Acc zero = {};
-            blk[j] = F::mma(b8, a8, zero);
+            blk[j] = F::template mma<FB, FA>(b8, a8, zero);
         } else {
-            blk[j] = F::mma(b8, a8, blk[j]);
+            blk[j] = F::template mma<FB, FA>(b8, a8, blk[j]);
         }
     };
     auto promote = [&](int i, int j) __attribute__((always_inline)) {
@@ -259,8 +267,12 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
         sbv = *reinterpret_cast<const MPDT_LDS float*>(lds0 + lsb + so);
     };
     auto make_f = [&](int i) __attribute__((always_inline)) {
-        const uint32_t sa = sap[i];
-        f[i] = __uint_as_float(sa) * sbv;
+        if constexpr (ROWS) {
+            f[i] = 1.0f;
+        } else {
+            const uint32_t sa = sap[i];
+            f[i] = __uint_as_float(sa) * sbv;
+        }
     };
 
     // Slots 0..7 of K tile t in stage S: promotions of the previous tile's row
@@ -374,6 +386,22 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
     // 8-byte LDS write.  Each wave stages its 64 x 128 tile row-major (256
     // bytes per row, 16-byte chunks XOR-swizzled by row) and writes it out in
     // 16-byte pieces of whole rows.
+    if constexpr (ROWS) {
+        // one scale per row of A and per column of B (increments ld_sa,
+        // ld_sb: 1, or 0 for one scale per tensor); full tiles only here
+        float sa[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) sa[i] = g.sA[(int64_t)(m0 + wm * C::WM + i * 32 + (int)lrow) * g.ld_sa];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int col = n0 + wn * C::WN + j * 32 + 8 * (r >> 2) + 4 * (int)lhalf + (r & 3);
+                const float sb = g.sB[(int64_t)col * g.ld_sb];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) acc[i][j][r] = (acc[i][j][r] * sa[i]) * sb;
+            }
+    }
     wg_barrier();   // every wave is past its reads of the K-tile stages
     MPDT_LDS char* const reg = lds0 + wave * (C::WM * C::WN * 2);
     static_assert(4 * C::WM * C::WN * 2 <= LDS_TOTAL, "epilogue staging fits");
@@ -422,15 +450,30 @@ bool fp8_1w_eligible(const GemmArgs& a, bool aligned) {
            a.ld_sa < (int64_t(1) << 31) / (4 * C::WM) && ((uintptr_t)a.D % 16) == 0 && a.ldd % 8 == 0;
 }
 
-hipError_t launch_fp8_1w(const GemmArgs& a0, int tiles_m, int tiles_n, hipStream_t stream) {
+template <int F8>
+static hipError_t launch_fp8_1w_t(const GemmArgs& a, hipStream_t stream) {
     using C = CfgFP8W;
+    hipLaunchKernelGGL((gemm_fp8_1w_kernel<C, F8>), dim3((unsigned)(a.tiles_m * a.tiles_n)), dim3(C::NT),
+                       0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fp8_1w(const GemmArgs& a0, int tiles_m, int tiles_n, hipStream_t stream) {
     GemmArgs a = a0;
     a.tiles_m = tiles_m;
     a.tiles_n = tiles_n;
     a.int_tm = a.int_tn = 0;
-    hipLaunchKernelGGL((gemm_fp8_1w_kernel<C>), dim3((unsigned)(tiles_m * tiles_n)), dim3(C::NT), 0,
-                       stream, a);
-    return hipGetLastError();
+    switch (fp8_variant(a)) {
+        case 0: return launch_fp8_1w_t<0>(a, stream);
+        case 1: return launch_fp8_1w_t<1>(a, stream);
+        case 2: return launch_fp8_1w_t<2>(a, stream);
+        case 3: return launch_fp8_1w_t<3>(a, stream);
+        case 4: return launch_fp8_1w_t<4>(a, stream);
+        case 5: return launch_fp8_1w_t<5>(a, stream);
+        case 6: return launch_fp8_1w_t<6>(a, stream);
+        case 7: return launch_fp8_1w_t<7>(a, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace mpdt

@@ -99,12 +99,16 @@ __device__ __forceinline__ float act_apply(float v) {
     }
 }
 
-template <Kind KD, class C, bool ALIGNED, bool OUT16 = false, bool BA = false>
+// F8 (FP8 only): operand formats and the scaling variant (F8_* bits).
+template <Kind KD, class C, bool ALIGNED, bool OUT16 = false, bool BA = false, int F8 = 0>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::NT / 256, C::NT / 256)))
 void gemm_kernel(GemmArgs g) {
     using F = Fmt<KD>;
     using Acc = typename F::Acc;
     constexpr bool IS_FP8 = (KD == Kind::FP8);
+    constexpr int FA = (F8 & F8_A_E5M2) ? 1 : 0, FB = (F8 & F8_B_E5M2) ? 1 : 0;
+    constexpr bool ROWS = (F8 & F8_ROWS) != 0;   // no block scales in the K loop
+    static_assert(F8 == 0 || IS_FP8, "FP8 variants");
     constexpr int NS = C::STAGES;
     constexpr int AHEAD = NS - 1;                 // K tiles loaded ahead of the one computed
     // ONE_WAVE: the interior-tile kernel, one wavefront per SIMD (4 per
@@ -210,7 +214,7 @@ void gemm_kernel(GemmArgs g) {
     for (int q = 0; q < NSLOT; ++q) rsa[q] = 0.0f;
 
     auto load_scale = [&](int kt, int q) {
-        if constexpr (IS_FP8) {
+        if constexpr (IS_FP8 && !ROWS) {
             if (tid < C::BM) {
                 const int row = m0 + tid;
                 rsa[q] = (row < g.M) ? g.sA[(int64_t)row * g.ld_sa + kt] : 0.0f;
@@ -218,7 +222,7 @@ void gemm_kernel(GemmArgs g) {
         }
     };
     auto store_scale = [&](const Stage& s, int q) {
-        if constexpr (IS_FP8) {
+        if constexpr (IS_FP8 && !ROWS) {
             if (tid < C::BM) s.S[tid] = rsa[q];
         }
     };
@@ -382,7 +386,7 @@ void gemm_kernel(GemmArgs g) {
 #pragma unroll
             for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-                for (int j = 0; j < C::TN; ++j) out[i][j] = F::mma(a8[i], b8[j], out[i][j]);
+                for (int j = 0; j < C::TN; ++j) out[i][j] = F::template mma<FA, FB>(a8[i], b8[j], out[i][j]);
         } else {
 #pragma unroll
             for (int i = 0; i < C::TM; ++i)
@@ -404,7 +408,8 @@ void gemm_kernel(GemmArgs g) {
 #pragma unroll
             for (int s = 0; s < C::STEPS; ++s) load_step(st, f, s);
             const int nb = (n0 + wn * C::WN) / 128;
-            const float sb = (nb < (g.N + 127) / 128) ? g.sB[(int64_t)kt * g.ld_sb + nb] : 0.0f;
+            float sb = 1.0f;
+            if constexpr (!ROWS) sb = (nb < (g.N + 127) / 128) ? g.sB[(int64_t)kt * g.ld_sb + nb] : 0.0f;
 #pragma unroll
             for (int i = 0; i < C::TM; ++i) {
                 Acc blk[C::TN];
@@ -422,13 +427,16 @@ void gemm_kernel(GemmArgs g) {
                         i32x8 b8;
 #pragma unroll
                         for (int e = 0; e < 8; ++e) b8[e] = (int32_t)f.b[s][j][e >> 1][e & 1];
-                        blk[j] = F::mma(a8, b8, blk[j]);
+                        blk[j] = F::template mma<FA, FB>(a8, b8, blk[j]);
                     }
                 }
                 // promote: acc += blk * (sA[row][kb] * sB[kb][n-block])
+                // (row-scaled: acc += blk, the scales come at the end)
                 float fs[16];
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
+                for (int r = 0; r < 16; ++r) fs[r] = 1.0f;
+#pragma unroll
+                for (int r4 = 0; r4 < 4 && !ROWS; ++r4) {
                     const uint32_t r = wm * C::WM + i * 32 + 8 * r4 + 4 * lhalf;
                     const u32x4 v = lds_load16((const MPDT_LDS char*)st.S, r * 4);
 #pragma unroll
@@ -1008,6 +1016,21 @@ void gemm_kernel(GemmArgs g) {
     using Out32 = typename std::conditional<KD == Kind::I8, int32_t, float>::type;
     using OutTag = typename std::conditional<KD == Kind::FP8 || OUT16, std::common_type<uint16_t>,
                                              std::common_type<Out32>>::type;
+    if constexpr (IS_FP8 && ROWS) {
+        // D = bf16((acc * sA[row]) * sB[col]): ld_sa / ld_sb are the scale
+        // vectors' increments (1, or 0 for one scale per tensor)
+        static_for<0, NTILE>([&](auto T) {
+            constexpr int t = decltype(T)::value;
+            const int col = col_base + (t % C::TN) * 32;
+            const float sb = col < g.N ? g.sB[(int64_t)col * g.ld_sb] : 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = row_base + (t / C::TN) * 32 + 8 * (r >> 2) + (r & 3);
+                const float sa = row < g.M ? g.sA[(int64_t)row * g.ld_sa] : 0.0f;
+                acc[t / C::TN][t % C::TN][r] = (acc[t / C::TN][t % C::TN][r] * sa) * sb;
+            }
+        });
+    }
     if constexpr (!BA) epilogue(OutTag{});   // (the fused epilogue stored D above)
 #ifdef MPDT_CLOCK_STAMPS
     __builtin_amdgcn_s_waitcnt(0);   // this wave's stores have completed
@@ -1023,7 +1046,7 @@ void gemm_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------
 // Host-side launchers (called by the C ABI after validation).
 // ---------------------------------------------------------------------------
-template <Kind KD, class C, bool ALIGNED, bool BA>
+template <Kind KD, class C, bool ALIGNED, bool BA, int F8 = 0>
 static hipError_t launch_grid(const GemmArgs& a, int64_t tiles, hipStream_t stream) {
     if (tiles <= 0) return hipSuccess;
     if constexpr (KD == Kind::F16 || KD == Kind::BF16) {
@@ -1033,14 +1056,14 @@ static hipError_t launch_grid(const GemmArgs& a, int64_t tiles, hipStream_t stre
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((gemm_kernel<KD, C, ALIGNED, false, BA>), dim3((unsigned)tiles), dim3(C::NT), 0,
+    hipLaunchKernelGGL((gemm_kernel<KD, C, ALIGNED, false, BA, F8>), dim3((unsigned)tiles), dim3(C::NT), 0,
                        stream, a);
     return hipGetLastError();
 }
 
 // General kernel over every tile (or over the edge tiles around an interior
 // block launched separately).
-template <Kind KD, class C, bool BA = false>
+template <Kind KD, class C, bool BA = false, int F8 = 0>
 static hipError_t launch_general(GemmArgs a, bool aligned, int int_tm, int int_tn,
                                  hipStream_t stream) {
     a.tiles_m = (a.M + C::BM - 1) / C::BM;
@@ -1048,8 +1071,8 @@ static hipError_t launch_general(GemmArgs a, bool aligned, int int_tm, int int_t
     a.int_tm = int_tm;
     a.int_tn = int_tn;
     const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n - (int64_t)int_tm * int_tn;
-    return aligned ? launch_grid<KD, C, true, BA>(a, tiles, stream)
-                   : launch_grid<KD, C, false, BA>(a, tiles, stream);
+    return aligned ? launch_grid<KD, C, true, BA, F8>(a, tiles, stream)
+                   : launch_grid<KD, C, false, BA, F8>(a, tiles, stream);
 }
 
 // FP16 / BF16 / INT8: a problem with at least STAGES K tiles (the last may be

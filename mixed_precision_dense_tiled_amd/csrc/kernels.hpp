@@ -27,13 +27,22 @@ struct GemmArgs {
     int d16_vec;          // out16 with D and its rows 16-byte aligned: wide stores allowed
     const float* bias;    // fused epilogue: FP32 bias per output column (may be null)
     int act;              // fused epilogue: one of the ACT_* activations
+    int fp8_fmt;          // FP8: bit 0 A is E5M2, bit 1 B is E5M2 (else E4M3)
+    int row_scaled;       // FP8: sA / sB are per-row / per-column vectors, ld_sa /
+                          // ld_sb their increments (0: one scale per tensor)
 };
+
+// The F8_* bits of an FP8 call (format of each operand, scaling variant).
+inline int fp8_variant(const GemmArgs& a) { return (a.fp8_fmt & 3) | (a.row_scaled ? 4 : 0); }
 
 // Activations of the fused epilogue (the values of the C ABI's mpdt_act).
 enum : int { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2, ACT_SILU = 3 };
 
 // aligned: every row start of A and B is 16-byte aligned.
 hipError_t launch_gemm(Kind kind, const GemmArgs& a, bool aligned, hipStream_t stream);
+// The FP8 GEMMs (gemm_fp8_general.hip): full tiles of an eligible problem
+// on the one-wave kernel, the rest on the general kernel.
+hipError_t launch_fp8(const GemmArgs& a, bool aligned, hipStream_t stream);
 // FP16 / BF16 with the fused bias / activation epilogue (gemm_epi.hip).
 hipError_t launch_gemm_epi(Kind kind, const GemmArgs& a, bool aligned, hipStream_t stream);
 

@@ -149,6 +149,27 @@ def test_fp8_validation():
     assert ok
 
 
+def test_fp8_format_and_rowscaled_validation():
+    L = mp.lib()
+    S1, S2 = P + 65536, Q + 65536
+
+    def blk(fa=0, fb=1, D=R):
+        return L.gemm_fp8_blockscaled_fmt(256, 300, 260, P, 260, fa, S1, 3, Q, 300, fb, S2, 3, D, 300, None)
+
+    def row(fa=1, fb=1, sa=S1, ia=1, sb=S2, ib=0, K=260, D=R):
+        return L.gemm_fp8_rowscaled(256, 300, K, P, 260, fa, sa, ia, Q, 300, fb, sb, ib, D, 300, None)
+
+    assert blk(fa=2) == INVALID and blk(fb=-1) == INVALID
+    assert row(fa=3) == INVALID
+    assert row(ia=2) == INVALID and row(ib=-1) == INVALID
+    assert row(sa=None) == INVALID and row(sb=None, K=0) == INVALID   # read even for K = 0
+    assert row(sb=S2 + 2) == MISALIGNED
+    assert row(D=S1 - 2 * 300 * 255) == ALIASING                    # D's last row over scale_a
+    assert row(D=S1 + 4 * 255 - 2 * 300 * 255 - 2) == ALIASING
+    if not gpu_present:
+        assert blk() == NO_DEVICE and row() == NO_DEVICE and row(ia=0, ib=1, K=0) == NO_DEVICE
+
+
 def test_gemv_validation():
     L = mp.lib()
     f = ctypes.c_float(0.25)

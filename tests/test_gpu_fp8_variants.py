@@ -1,0 +1,98 @@
+"""GPU parity of the FP8 variants against the oracle: the block-scaled GEMM
+with E5M2 operands (either or both), and the per-row / per-tensor scaled GEMM
+with either format.  The bar is the FP8 GEMM's: per element
+|D - R| <= 1e-3 S + 1e-6 plus half a BF16 ulp, S = sum_k |a b| with the
+scales folded in, and relative Frobenius error <= 1e-2.
+
+Operands are quantised from N(0, 1) FP32 data by the oracle's quantiser (the
+E5M2 codes therefore cover about three binades below the block maximum, as
+scaled gradients do); shapes cover full one-wave tiles, edge tiles and a K
+tail on the general kernel, unaligned rows, per-tensor and per-row scales,
+and a 2048^3 problem checked at sampled outputs."""
+import numpy as np
+import pytest
+import torch
+
+import mixed_precision_dense_tiled_amd as mp
+import oracle
+from helpers import check_fp, dev, host
+
+pytestmark = pytest.mark.gpu
+
+E4, E5 = oracle.E4M3, oracle.E5M2
+FORMATS = [(E4, E5), (E5, E4), (E5, E5)]
+
+
+def quantised(M, N, K, fa, fb, seed, block=True):
+    r = np.random.default_rng(seed)
+    A = r.standard_normal((M, K)).astype(np.float32)
+    B = r.standard_normal((K, N)).astype(np.float32)
+    if block:
+        qa, sa = oracle.quantize_fp8_blocks_fmt(A, fa, 1, 128)
+        qb, sb = oracle.quantize_fp8_blocks_fmt(B, fb, 128, 128)
+    else:
+        # per-row A scales; B quantised per column through its transpose
+        qa, sa = oracle.quantize_fp8_blocks_fmt(A, fa, 1, K)
+        qbt, sbt = oracle.quantize_fp8_blocks_fmt(np.ascontiguousarray(B.T), fb, 1, K)
+        qb, sb = np.ascontiguousarray(qbt.T), sbt
+    return qa, sa, qb, sb
+
+
+def bf16_values(D):
+    return oracle.bf16_to_f64(host(D.view(torch.int16)).view(np.uint16))
+
+
+@pytest.mark.parametrize("fa,fb", FORMATS)
+@pytest.mark.parametrize("M,N,K,pad", [(256, 512, 512, 0), (300, 520, 260, 0), (200, 300, 333, 3)])
+def test_blockscaled_formats(gpu_ok, fa, fb, M, N, K, pad):
+    qa, sa, qb, sb = quantised(M, N, K, fa, fb, seed=M + N + K + 10 * fa + 20 * fb)
+    ta = dev(qa, K + pad) if pad else dev(qa)
+    D = mp.gemm_fp8_blockscaled_fmt(ta, fa, dev(sa), dev(qb), fb, dev(sb))
+    R, S = oracle.gemm_fp8_blockscaled_fmt(qa, fa, sa, qb, fb, sb)
+    check_fp(bf16_values(D), R, S, 1e-2, f"fp8 fmt {fa}{fb} {M}x{N}x{K}", bf16_out=True)
+
+
+@pytest.mark.parametrize("fa,fb", [(E4, E4)] + FORMATS)
+@pytest.mark.parametrize("M,N,K,pad", [(256, 512, 512, 0), (300, 520, 260, 0), (130, 300, 333, 5)])
+def test_rowscaled_per_row(gpu_ok, fa, fb, M, N, K, pad):
+    qa, sa, qb, sb = quantised(M, N, K, fa, fb, seed=M * N + K + fa + 2 * fb, block=False)
+    ta = dev(qa, K + pad) if pad else dev(qa)
+    D = mp.gemm_fp8_rowscaled(ta, fa, dev(sa.ravel()), dev(qb), fb, dev(sb.ravel()))
+    R, S = oracle.gemm_fp8_rowscaled(qa, fa, sa.ravel(), qb, fb, sb.ravel())
+    check_fp(bf16_values(D), R, S, 1e-2, f"rowscaled {fa}{fb} {M}x{N}x{K}", bf16_out=True)
+
+
+@pytest.mark.parametrize("fa,fb", [(E4, E4), (E5, E5)])
+def test_rowscaled_per_tensor_and_mixed(gpu_ok, fa, fb):
+    M, N, K = 384, 768, 640
+    qa, sa, qb, sb = quantised(M, N, K, fa, fb, seed=77 + fa, block=False)
+    s_a = np.float32([0.037])
+    s_b = np.float32([1.75])
+    for xa, xb in ((s_a, s_b), (sa.ravel(), s_b), (s_a, sb.ravel())):
+        D = mp.gemm_fp8_rowscaled(dev(qa), fa, dev(xa), dev(qb), fb, dev(xb))
+        R, S = oracle.gemm_fp8_rowscaled(qa, fa, xa, qb, fb, xb)
+        check_fp(bf16_values(D), R, S, 1e-2, f"per-tensor {xa.size} {xb.size}", bf16_out=True)
+    # unit scales: the row-scaled and block-scaled GEMMs compute the same sum
+    one_r = mp.gemm_fp8_rowscaled(dev(qa), fa, dev(np.float32([1])), dev(qb), fb, dev(np.float32([1])))
+    one_b = mp.gemm_fp8_blockscaled_fmt(dev(qa), fa, dev(np.ones((M, 5), np.float32)), dev(qb), fb,
+                                        dev(np.ones((5, 6), np.float32)))
+    R, S = oracle.gemm_fp8_rowscaled(qa, fa, np.float32([1]), qb, fb, np.float32([1]))
+    check_fp(bf16_values(one_r), R, S, 1e-2, "unit row", bf16_out=True)
+    check_fp(bf16_values(one_b), R, S, 1e-2, "unit block", bf16_out=True)
+
+
+def test_rowscaled_k_zero_and_sampled_2048(gpu_ok):
+    D = mp.gemm_fp8_rowscaled(torch.zeros((40, 0), dtype=torch.uint8, device=gpu_ok), E4,
+                              dev(np.float32([2.0])), torch.zeros((0, 50), dtype=torch.uint8, device=gpu_ok),
+                              E4, dev(np.float32([3.0])))
+    assert not host(D.view(torch.int16)).any()
+    M = N = K = 2048
+    qa, sa, qb, sb = quantised(M, N, K, E4, E4, seed=5, block=False)
+    D = mp.gemm_fp8_rowscaled(dev(qa), E4, dev(sa.ravel()), dev(qb), E4, dev(sb.ravel()))
+    d = bf16_values(D)
+    assert np.isfinite(d).all()
+    r = np.random.default_rng(6)
+    ii = np.concatenate([r.integers(0, M, 3000), [0, M - 1]])
+    jj = np.concatenate([r.integers(0, N, 3000), [N - 1, 0]])
+    R, S = oracle.gemm_fp8_rowscaled_at(qa, E4, sa.ravel(), qb, E4, sb.ravel(), ii, jj)
+    check_fp(d[ii, jj], R, S, 1e-2, "rowscaled 2048^3 sampled", bf16_out=True)
