@@ -249,6 +249,22 @@ mpdt_status quantize_fp8_blocks(int64_t R, int64_t C, const float* X, int64_t ld
                                 int64_t block_rows, uint8_t* Q, int64_t ldq,
                                 float* scales, int64_t lds, void* stream);
 
+/* FP8 quantisation with a choice of format and scale granularity (same
+ * section: per tensor, per row or per block; E4M3 or E5M2):
+ *   s = amax_block |x| / qmax   (qmax 448 for E4M3, 57344 for E5M2; FP32
+ *                                division; 1 for an all-zero block)
+ *   Q = fp8_rne(x / s)          (codes of fmt, ldq)
+ * block_rows x block_cols may be 1 x 128 or 128 x 128 (as above), or cover
+ * whole rows (1 x bc with bc >= C: one scale per row), whole columns
+ * (br x 1 with br >= R: one per column) or the whole matrix (br >= R and
+ * bc >= C: one per tensor); anything else is MPDT_ERROR_INVALID_VALUE.
+ * scales is ceil(R/block_rows) x ceil(C/block_cols) (lds).  The per-tensor
+ * form runs as several kernels on the stream and uses scales[0] as its
+ * accumulator in between. */
+mpdt_status quantize_fp8(int64_t R, int64_t C, const float* X, int64_t ldx, int fmt,
+                         int64_t block_rows, int64_t block_cols, uint8_t* Q, int64_t ldq,
+                         float* scales, int64_t lds, void* stream);
+
 /* Static text for a status code. */
 const char* mpdt_status_string(mpdt_status s);
 /* Thread-local description of the last non-success status on this thread. */

@@ -22,7 +22,7 @@ __all__ = ["gemm_f16", "gemm_bf16", "gemm_f16_f16out", "gemm_bf16_bf16out", "gem
            "gemm_bf16_bias_act", "ACT_NONE", "ACT_RELU", "ACT_GELU", "ACT_SILU", "gemm_i8_i32",
            "gemm_fp8_blockscaled", "gemm_fp8_blockscaled_fmt", "gemm_fp8_rowscaled", "FP8_E4M3",
            "FP8_E5M2", "gemv_w8a8", "gemm_w8a8", "gemm_w8a8_requant", "quantize_i8_rows",
-           "quantize_fp8_blocks",
+           "quantize_fp8_blocks", "quantize_fp8",
            "MpdtError", "lib", "lib_path", "version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -85,6 +85,9 @@ def lib() -> ctypes.CDLL:
         L.quantize_i8_rows.restype = ctypes.c_int
         L.quantize_fp8_blocks.argtypes = [_i64, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp]
         L.quantize_fp8_blocks.restype = ctypes.c_int
+        L.quantize_fp8.argtypes = [_i64, _i64, _vp, _i64, ctypes.c_int, _i64, _i64, _vp, _i64, _vp,
+                                   _i64, _vp]
+        L.quantize_fp8.restype = ctypes.c_int
         L.mpdt_status_string.argtypes = [ctypes.c_int]
         L.mpdt_status_string.restype = ctypes.c_char_p
         L.mpdt_last_error.argtypes = []
@@ -392,4 +395,23 @@ def quantize_fp8_blocks(X, block_rows, q_out=None, scales_out=None):
     ps, lds = _mat(scales_out, 4, "scales_out")
     _check("quantize_fp8_blocks", lib().quantize_fp8_blocks(R, Cc, px, ldx, block_rows, pq, ldq, ps,
                                                             lds, _stream(X)))
+    return q_out, scales_out
+
+
+def quantize_fp8(X, fmt, block_rows, block_cols, q_out=None, scales_out=None):
+    """FP8 quantisation of an FP32 matrix X [R, C] into fmt (FP8_E4M3 or
+    FP8_E5M2) with block_rows x block_cols blocks: 1 x 128, 128 x 128, whole
+    rows (1 x C), whole columns (R x 1) or the whole tensor (R x C); returns
+    (Q uint8 [R, C], scales FP32 [ceil(R/block_rows), ceil(C/block_cols)])."""
+    R, Cc = X.shape
+    px, ldx = _mat(X, 4, "X")
+    nbr, nbc = -(-R // block_rows), -(-Cc // block_cols)
+    if q_out is None:
+        q_out = torch.empty((R, Cc), dtype=torch.uint8, device=X.device)
+    if scales_out is None:
+        scales_out = torch.empty((max(nbr, 1), max(nbc, 1)), dtype=torch.float32, device=X.device)
+    pq, ldq = _mat(q_out, 1, "q_out")
+    ps, lds = _mat(scales_out, 4, "scales_out")
+    _check("quantize_fp8", lib().quantize_fp8(R, Cc, px, ldx, int(fmt), int(block_rows), int(block_cols),
+                                              pq, ldq, ps, lds, _stream(X)))
     return q_out, scales_out

@@ -6,6 +6,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <mutex>
@@ -465,14 +466,62 @@ MPDT_EXPORT mpdt_status quantize_i8_rows(int64_t M, int64_t K, const uint16_t* X
     return launched(mpdt::launch_quantize_i8_rows(a, (hipStream_t)stream), fn);
 }
 
+namespace {
+mpdt_status run_quantize_fp8(const char* fn, int64_t R, int64_t C, const float* X, int64_t ldx,
+                             int fmt, int64_t br, int64_t bc, uint8_t* Q, int64_t ldq,
+                             float* scales, int64_t lds, void* stream) {
+    if (R < 0 || C < 0 || R > kMaxDim || C > kMaxDim)
+        return fail(MPDT_ERROR_INVALID_VALUE, fn, "dimension out of range");
+    if (fmt != MPDT_FP8_E4M3 && fmt != MPDT_FP8_E5M2)
+        return fail(MPDT_ERROR_INVALID_VALUE, fn, "unknown FP8 format");
+    if (br < 1 || bc < 1) return fail(MPDT_ERROR_INVALID_VALUE, fn, "block sizes must be positive");
+    int shape;
+    if (br >= R && bc >= C) shape = mpdt::FP8Q_TENSOR;
+    else if (br == 1 && bc >= C) shape = mpdt::FP8Q_ROW;
+    else if (bc == 1 && br >= R) shape = mpdt::FP8Q_COL;
+    else if (br == 1 && bc == 128) shape = mpdt::FP8Q_ROW128;
+    else if (br == 128 && bc == 128) shape = mpdt::FP8Q_TILE128;
+    else return fail(MPDT_ERROR_INVALID_VALUE, fn, "unsupported block shape");
+    if (R == 0 || C == 0) return MPDT_SUCCESS;
+    const int64_t nbr = (R + br - 1) / br, nbc = (C + bc - 1) / bc;
+    if (!X || !Q || !scales) return fail(MPDT_ERROR_INVALID_VALUE, fn, "X, Q or scales is NULL");
+    if (ldx < C || ldq < C || lds < nbc)
+        return fail(MPDT_ERROR_INVALID_VALUE, fn, "ldx or ldq < C, or lds < scale columns");
+    if (!aligned_to(X, 4) || !aligned_to(scales, 4))
+        return fail(MPDT_ERROR_MISALIGNED, fn, "pointer not aligned to its element size");
+    Span sx, sq, ss;
+    if (!span_of(X, R, C, ldx, 4, &sx) || !span_of(Q, R, C, ldq, 1, &sq) ||
+        !span_of(scales, nbr, nbc, lds, 4, &ss))
+        return fail(MPDT_ERROR_INVALID_VALUE, fn, "operand too large");
+    if (sq.overlaps(sx) || ss.overlaps(sx) || sq.overlaps(ss))
+        return fail(MPDT_ERROR_ALIASING, fn, "an output overlaps the input or the other output");
+    mpdt_status s = check_device(fn);
+    if (s != MPDT_SUCCESS) return s;
+    mpdt::QuantFp8Args a{};
+    a.X = X;
+    a.ldx = ldx;
+    a.Q = Q;
+    a.ldq = ldq;
+    a.S = scales;
+    a.lds = lds;
+    a.R = R;
+    a.C = C;
+    a.block_rows = (int)std::min<int64_t>(br, 128);
+    a.fmt = fmt;
+    a.shape = shape;
+    return launched(mpdt::launch_quantize_fp8_blocks(a, (hipStream_t)stream), fn);
+}
+}  // namespace
+
 MPDT_EXPORT mpdt_status quantize_fp8_blocks(int64_t R, int64_t C, const float* X, int64_t ldx,
                                             int64_t block_rows, uint8_t* Q, int64_t ldq,
                                             float* scales, int64_t lds, void* stream) {
     const char* fn = "quantize_fp8_blocks";
-    if (R < 0 || C < 0 || R > kMaxDim || C > kMaxDim)
-        return fail(MPDT_ERROR_INVALID_VALUE, fn, "dimension out of range");
     if (block_rows != 1 && block_rows != 128)
         return fail(MPDT_ERROR_INVALID_VALUE, fn, "block_rows must be 1 or 128");
+    // (always the 1 x 128 / 128 x 128 kernels, whatever the matrix size)
+    if (R < 0 || C < 0 || R > kMaxDim || C > kMaxDim)
+        return fail(MPDT_ERROR_INVALID_VALUE, fn, "dimension out of range");
     if (R == 0 || C == 0) return MPDT_SUCCESS;
     const int64_t nbr = (R + block_rows - 1) / block_rows, nbc = (C + 127) / 128;
     if (!X || !Q || !scales) return fail(MPDT_ERROR_INVALID_VALUE, fn, "X, Q or scales is NULL");
@@ -498,7 +547,16 @@ MPDT_EXPORT mpdt_status quantize_fp8_blocks(int64_t R, int64_t C, const float* X
     a.R = R;
     a.C = C;
     a.block_rows = (int)block_rows;
+    a.fmt = 0;
+    a.shape = block_rows == 1 ? mpdt::FP8Q_ROW128 : mpdt::FP8Q_TILE128;
     return launched(mpdt::launch_quantize_fp8_blocks(a, (hipStream_t)stream), fn);
+}
+
+MPDT_EXPORT mpdt_status quantize_fp8(int64_t R, int64_t C, const float* X, int64_t ldx, int fmt,
+                                     int64_t block_rows, int64_t block_cols, uint8_t* Q, int64_t ldq,
+                                     float* scales, int64_t lds, void* stream) {
+    return run_quantize_fp8("quantize_fp8", R, C, X, ldx, fmt, block_rows, block_cols, Q, ldq, scales,
+                            lds, stream);
 }
 
 MPDT_EXPORT const char* mpdt_status_string(mpdt_status s) {

@@ -110,8 +110,13 @@ struct QuantFp8Args {
     float* S;
     int64_t lds;
     int64_t R, C;
-    int block_rows;   // 1 or 128
+    int block_rows;   // 1 or 128 (with 128 columns); or the shapes below
+    int fmt;          // 0 E4M3, 1 E5M2
+    int shape;        // FP8Q_* block shape
 };
+// Block shapes of the FP8 quantiser: 1 x 128, 128 x 128, one scale per row
+// (1 x C), per column (R x 1) or per tensor (R x C).
+enum : int { FP8Q_ROW128 = 0, FP8Q_TILE128 = 1, FP8Q_ROW = 2, FP8Q_COL = 3, FP8Q_TENSOR = 4 };
 hipError_t launch_quantize_fp8_blocks(const QuantFp8Args& a, hipStream_t stream);
 
 }  // namespace mpdt

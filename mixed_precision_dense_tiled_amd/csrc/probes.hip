@@ -113,7 +113,9 @@ __global__ __launch_bounds__(64) void probe_mfma_kernel(const char* A, const cha
             b[w] = (int32_t)bv;
         }
         f32x16 c = {};
-        c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+        // kind 3: E4M3 x E4M3; kind 4: E5M2 x E5M2 (the instruction's format fields)
+        if constexpr (KIND == 3) c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+        else c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 1, 1, 0, 127, 0, 127);
         for (int r = 0; r < 16; ++r)
             ((float*)D)[(8 * (r >> 2) + 4 * half + (r & 3)) * 32 + row] = c[r];
     }
@@ -138,6 +140,7 @@ MPDT_EXPORT int mpdt_probe_mfma(int kind, const void* A, const void* B, void* D,
         case 1: hipLaunchKernelGGL(mpdt::probe_mfma_kernel<1>, dim3(1), dim3(64), 0, s, a, b, D); break;
         case 2: hipLaunchKernelGGL(mpdt::probe_mfma_kernel<2>, dim3(1), dim3(64), 0, s, a, b, D); break;
         case 3: hipLaunchKernelGGL(mpdt::probe_mfma_kernel<3>, dim3(1), dim3(64), 0, s, a, b, D); break;
+        case 4: hipLaunchKernelGGL(mpdt::probe_mfma_kernel<4>, dim3(1), dim3(64), 0, s, a, b, D); break;
         default: return (int)hipErrorInvalidValue;
     }
     return (int)hipGetLastError();

@@ -7,18 +7,21 @@
 //     at run time by the previous operator or a separate quantisation step):
 //       s = amax_k |x[m][k]| / 127   (1 for an all-zero row)
 //       q[m][k] = clamp(rne(x[m][k] / s), -127, 127)
-//   * FP8 E4M3 block quantisation, the scale factors FP8 needs ("Tensor Core"
-//     page, section "Precision": per tensor, per row or per block), in 1 x 128
-//     or 128 x 128 blocks:
-//       s = amax_block |x| / 448     (1 for an all-zero block)
-//       q = e4m3_rne(x / s)          (|x / s| <= 448 up to one rounding)
+//   * FP8 quantisation, the scale factors FP8 needs ("Tensor Core" page,
+//     section "Precision": per tensor, per row or per block), in 1 x 128 or
+//     128 x 128 blocks, or one scale per row, per column or per tensor, into
+//     E4M3 (largest value 448) or E5M2 (57344):
+//       s = amax_block |x| / qmax    (1 for an all-zero block)
+//       q = fp8_rne(x / s)           (|x / s| <= qmax up to one rounding)
 //
 // Both are memory-bound elementwise passes with one reduction per row or
 // block; every division is the IEEE-rounded FP32 one and rounding to an
-// integer is v_rndne (ties to even).  The FP32 -> E4M3 step is the gfx950
-// conversion instruction (OCP E4M3, round to nearest even).
+// integer is v_rndne (ties to even).  The FP32 -> FP8 step is the gfx950
+// conversion instruction (OCP E4M3 / E5M2, round to nearest even).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -71,15 +74,19 @@ hipError_t launch_quantize_i8_rows(const QuantI8Args& a, hipStream_t stream) {
 }
 
 // ---- FP8 block quantisation ----------------------------------------------
-__device__ __forceinline__ uint8_t to_e4m3(float v) {
-    return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xff);
+template <int FMT>
+__device__ __forceinline__ uint8_t to_fp8(float v) {
+    if constexpr (FMT == 0) return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xff);
+    else return (uint8_t)(__builtin_amdgcn_cvt_pk_bf8_f32(v, 0.0f, 0, false) & 0xff);
 }
+template <int FMT> constexpr float QMAX = FMT == 0 ? 448.0f : 57344.0f;
 
 // 1 x 128 blocks: a wavefront takes FP8_RB consecutive blocks of one row,
 // two elements per lane per block (each load instruction reads 512
 // consecutive bytes); all loads are issued before the first reduction.
 constexpr int FP8_RB = 4;
 
+template <int FMT>
 __global__ __launch_bounds__(256) void quantize_fp8_rowblocks_kernel(QuantFp8Args g) {
     const int64_t nbc = (g.C + 127) / 128;
     const int64_t groups = (nbc + FP8_RB - 1) / FP8_RB;              // block groups per row
@@ -101,16 +108,17 @@ __global__ __launch_bounds__(256) void quantize_fp8_rowblocks_kernel(QuantFp8Arg
         if (bj0 + b >= nbc) break;
         const int64_t c0 = (bj0 + b) * 128 + 2 * lane;
         const float amax = wave_max(fmaxf(fabsf(v[b][0]), fabsf(v[b][1])));
-        const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+        const float s = amax > 0.0f ? amax / QMAX<FMT> : 1.0f;
         if (lane == 0) g.S[r * g.lds + bj0 + b] = s;
-        if (c0 < g.C) qr[c0] = to_e4m3(v[b][0] / s);
-        if (c0 + 1 < g.C) qr[c0 + 1] = to_e4m3(v[b][1] / s);
+        if (c0 < g.C) qr[c0] = to_fp8<FMT>(v[b][0] / s);
+        if (c0 + 1 < g.C) qr[c0 + 1] = to_fp8<FMT>(v[b][1] / s);
     }
 }
 
 // 128 x 128 blocks: one workgroup per block; thread t covers column t % 128
 // of the block's rows t / 128, t / 128 + 2, ... (each wave instruction reads
 // 256 consecutive bytes of one row).
+template <int FMT>
 __global__ __launch_bounds__(256) void quantize_fp8_tileblocks_kernel(QuantFp8Args g) {
     __shared__ float red[4];
     const int64_t nbc = (g.C + 127) / 128;
@@ -128,30 +136,138 @@ __global__ __launch_bounds__(256) void quantize_fp8_tileblocks_kernel(QuantFp8Ar
         amax = fmaxf(amax, fabsf(v[i]));
     }
     amax = block_max256(amax, red);
-    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    const float s = amax > 0.0f ? amax / QMAX<FMT> : 1.0f;
     if (threadIdx.x == 0) g.S[bi * g.lds + bj] = s;
     if (col_ok) {
 #pragma unroll
         for (int i = 0; i < 64; ++i) {
             const int64_t r = r0 + 2 * i;
-            if (r < g.R) g.Q[r * g.ldq + c] = to_e4m3(v[i] / s);
+            if (r < g.R) g.Q[r * g.ldq + c] = to_fp8<FMT>(v[i] / s);
         }
     }
 }
 
-hipError_t launch_quantize_fp8_blocks(const QuantFp8Args& a, hipStream_t stream) {
-    if (a.R <= 0 || a.C <= 0) return hipSuccess;
+// One scale per row: a workgroup per row, the row read twice (maximum, then
+// quantisation; the second pass mostly from cache).
+template <int FMT>
+__global__ __launch_bounds__(256) void quantize_fp8_perrow_kernel(QuantFp8Args g) {
+    __shared__ float red[4];
+    const int64_t r = blockIdx.x;
+    const float* xr = g.X + r * g.ldx;
+    uint8_t* qr = g.Q + r * g.ldq;
+    float amax = 0.0f;
+    for (int64_t c = threadIdx.x; c < g.C; c += 256) amax = fmaxf(amax, fabsf(xr[c]));
+    amax = block_max256(amax, red);
+    const float s = amax > 0.0f ? amax / QMAX<FMT> : 1.0f;
+    if (threadIdx.x == 0) g.S[r * g.lds] = s;
+    for (int64_t c = threadIdx.x; c < g.C; c += 256) qr[c] = to_fp8<FMT>(xr[c] / s);
+}
+
+// One scale per column: a workgroup per 64 columns, its four wavefronts on
+// interleaved rows (each load instruction reads 256 consecutive bytes of a
+// row), the four partial maxima of a column combined through LDS.
+template <int FMT>
+__global__ __launch_bounds__(256) void quantize_fp8_percol_kernel(QuantFp8Args g) {
+    __shared__ float red[4][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t c = (int64_t)blockIdx.x * 64 + lane;
+    const bool ok = c < g.C;
+    float amax = 0.0f;
+    if (ok)
+        for (int64_t r = wave; r < g.R; r += 4) amax = fmaxf(amax, fabsf(g.X[r * g.ldx + c]));
+    red[wave][lane] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0][lane], red[1][lane]), fmaxf(red[2][lane], red[3][lane]));
+    const float s = amax > 0.0f ? amax / QMAX<FMT> : 1.0f;
+    if (!ok) return;
+    if (wave == 0) g.S[c] = s;
+    for (int64_t r = wave; r < g.R; r += 4) g.Q[r * g.ldq + c] = to_fp8<FMT>(g.X[r * g.ldx + c] / s);
+}
+
+// One scale per tensor, in three launches on the stream: the maximum of every
+// workgroup's part is folded into S[0] with an atomic maximum on its bit
+// pattern (non-negative FP32 values order as unsigned integers), after S[0]
+// was cleared; then every element is quantised with s = S[0] / qmax; then
+// S[0] becomes s.
+__global__ void fp8_tensor_clear_kernel(float* S) { S[0] = 0.0f; }
+
+constexpr int TENSOR_WGS = 1024;   // workgroups of the two grid-stride passes
+constexpr int TENSOR_CH = 4096;    // columns of one work item (a row piece)
+
+__global__ __launch_bounds__(256) void fp8_tensor_amax_kernel(QuantFp8Args g) {
+    __shared__ float red[4];
+    float amax = 0.0f;
+    const int64_t pieces = (g.C + TENSOR_CH - 1) / TENSOR_CH;
+    for (int64_t it = blockIdx.x; it < g.R * pieces; it += gridDim.x) {
+        const int64_t r = it / pieces, c0 = (it % pieces) * TENSOR_CH;
+        const int64_t c1 = std::min<int64_t>(c0 + TENSOR_CH, g.C);
+        for (int64_t c = c0 + threadIdx.x; c < c1; c += 256) amax = fmaxf(amax, fabsf(g.X[r * g.ldx + c]));
+    }
+    amax = block_max256(amax, red);
+    if (threadIdx.x == 0) atomicMax((unsigned int*)g.S, __float_as_uint(amax));
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void fp8_tensor_quant_kernel(QuantFp8Args g) {
+    const float amax = g.S[0];
+    const float s = amax > 0.0f ? amax / QMAX<FMT> : 1.0f;
+    const int64_t pieces = (g.C + TENSOR_CH - 1) / TENSOR_CH;
+    for (int64_t it = blockIdx.x; it < g.R * pieces; it += gridDim.x) {
+        const int64_t r = it / pieces, c0 = (it % pieces) * TENSOR_CH;
+        const int64_t c1 = std::min<int64_t>(c0 + TENSOR_CH, g.C);
+        for (int64_t c = c0 + threadIdx.x; c < c1; c += 256)
+            g.Q[r * g.ldq + c] = to_fp8<FMT>(g.X[r * g.ldx + c] / s);
+    }
+}
+
+__global__ void fp8_tensor_scale_kernel(float* S, int fmt) {
+    const float amax = S[0];
+    S[0] = amax > 0.0f ? amax / (fmt == 0 ? QMAX<0> : QMAX<1>) : 1.0f;
+}
+
+template <int FMT>
+static hipError_t launch_fp8q(const QuantFp8Args& a, hipStream_t stream) {
     const int64_t nbc = (a.C + 127) / 128;
-    if (a.block_rows == 1) {
-        const int64_t waves = (int64_t)a.R * ((nbc + FP8_RB - 1) / FP8_RB);
-        hipLaunchKernelGGL(quantize_fp8_rowblocks_kernel, dim3((unsigned)((waves + 3) / 4)),
-                           dim3(256), 0, stream, a);
-    } else {
-        const int64_t nbr = (a.R + 127) / 128;
-        hipLaunchKernelGGL(quantize_fp8_tileblocks_kernel, dim3((unsigned)(nbr * nbc)), dim3(256), 0,
-                           stream, a);
+    switch (a.shape) {
+        case FP8Q_ROW128: {
+            const int64_t waves = (int64_t)a.R * ((nbc + FP8_RB - 1) / FP8_RB);
+            hipLaunchKernelGGL(quantize_fp8_rowblocks_kernel<FMT>, dim3((unsigned)((waves + 3) / 4)),
+                               dim3(256), 0, stream, a);
+            break;
+        }
+        case FP8Q_TILE128: {
+            const int64_t nbr = (a.R + 127) / 128;
+            hipLaunchKernelGGL(quantize_fp8_tileblocks_kernel<FMT>, dim3((unsigned)(nbr * nbc)), dim3(256),
+                               0, stream, a);
+            break;
+        }
+        case FP8Q_ROW:
+            hipLaunchKernelGGL(quantize_fp8_perrow_kernel<FMT>, dim3((unsigned)a.R), dim3(256), 0, stream, a);
+            break;
+        case FP8Q_COL:
+            hipLaunchKernelGGL(quantize_fp8_percol_kernel<FMT>, dim3((unsigned)((a.C + 63) / 64)), dim3(256),
+                               0, stream, a);
+            break;
+        case FP8Q_TENSOR: {
+            hipLaunchKernelGGL(fp8_tensor_clear_kernel, dim3(1), dim3(1), 0, stream, a.S);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            const int64_t wgs = std::min<int64_t>(TENSOR_WGS, a.R * ((a.C + TENSOR_CH - 1) / TENSOR_CH));
+            hipLaunchKernelGGL(fp8_tensor_amax_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, a);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            hipLaunchKernelGGL(fp8_tensor_quant_kernel<FMT>, dim3((unsigned)wgs), dim3(256), 0, stream, a);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            hipLaunchKernelGGL(fp8_tensor_scale_kernel, dim3(1), dim3(1), 0, stream, a.S, FMT);
+            break;
+        }
+        default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp8_blocks(const QuantFp8Args& a, hipStream_t stream) {
+    if (a.R <= 0 || a.C <= 0) return hipSuccess;
+    return a.fmt == 0 ? launch_fp8q<0>(a, stream) : launch_fp8q<1>(a, stream);
 }
 
 }  // namespace mpdt

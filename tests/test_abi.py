@@ -45,6 +45,7 @@ def test_library_exports_every_declared_symbol():
 P = 1 << 40          # 16-byte aligned base
 Q = P + (1 << 32)    # far away from P
 R = P + (2 << 32)
+R_ = P + (3 << 32)
 
 
 def g16(M, N, K, A=P, lda=None, B=Q, ldb=None, C=None, ldc=None, D=R, ldd=None, fn="gemm_f16"):
@@ -168,6 +169,24 @@ def test_fp8_format_and_rowscaled_validation():
     assert row(D=S1 + 4 * 255 - 2 * 300 * 255 - 2) == ALIASING
     if not gpu_present:
         assert blk() == NO_DEVICE and row() == NO_DEVICE and row(ia=0, ib=1, K=0) == NO_DEVICE
+
+
+def test_quantize_fp8_validation():
+    L = mp.lib()
+
+    def call(R=300, C=500, fmt=1, br=1, bc=500, S=Q, lds=1, Qo=R_):
+        return L.quantize_fp8(R, C, P, 500, fmt, br, bc, Qo, 500, S, lds, None)
+
+    assert call(fmt=2) == INVALID
+    assert call(br=2, bc=64) == INVALID         # unsupported block shape
+    assert call(br=0) == INVALID
+    assert call(br=1, bc=128, lds=3) == INVALID  # lds < ceil(500/128)
+    assert call(S=Q + 2) == MISALIGNED
+    assert call(Qo=P + 100) == ALIASING
+    assert call(R=0) == SUCCESS
+    if not gpu_present:
+        for br, bc, lds in ((1, 500, 1), (300, 1, 500), (300, 500, 1), (1, 128, 4), (128, 128, 4)):
+            assert call(br=br, bc=bc, lds=lds) == NO_DEVICE
 
 
 def test_gemv_validation():

@@ -96,3 +96,42 @@ def test_rowscaled_k_zero_and_sampled_2048(gpu_ok):
     jj = np.concatenate([r.integers(0, N, 3000), [N - 1, 0]])
     R, S = oracle.gemm_fp8_rowscaled_at(qa, E4, sa.ravel(), qb, E4, sb.ravel(), ii, jj)
     check_fp(d[ii, jj], R, S, 1e-2, "rowscaled 2048^3 sampled", bf16_out=True)
+
+
+SHAPES = {"row128": (1, 128), "tile128": (128, 128), "per_row": (1, None), "per_col": (None, 1),
+          "tensor": (None, None)}
+
+
+@pytest.mark.parametrize("fmt", [E4, E5])
+@pytest.mark.parametrize("shape", list(SHAPES))
+@pytest.mark.parametrize("R,C", [(257, 300), (5, 4100), (300, 7)])
+def test_quantize_fp8_bit_exact(gpu_ok, fmt, shape, R, C):
+    r = np.random.default_rng(R * C + fmt)
+    X = (r.standard_normal((R, C)) * 2.0 ** r.integers(-12, 12, (R, 1))).astype(np.float32)
+    X[min(3, R - 1)] = 0.0                                   # an all-zero row
+    br, bc = SHAPES[shape]
+    br = R if br is None else br
+    bc = C if bc is None else bc
+    q, s = mp.quantize_fp8(dev(X, C + 3, pad=np.float32(1e30)), fmt, br, bc)
+    qr, sr = oracle.quantize_fp8_blocks_fmt(X, fmt, br, bc)
+    assert np.array_equal(host(s), sr), shape
+    assert np.array_equal(host(q), qr), shape
+
+
+def test_quantize_fp8_zero_tensor_and_rowscaled_pipeline(gpu_ok):
+    q, s = mp.quantize_fp8(torch.zeros((40, 70), device=gpu_ok), E5, 40, 70)
+    assert host(s).tolist() == [[1.0]] and not host(q).any()
+    # per-token A (E4M3) and per-channel B (E5M2, one scale per column), then
+    # the row-scaled GEMM: close to the FP32 product of the originals
+    M, N, K = 256, 512, 1024
+    r = np.random.default_rng(8)
+    A = r.standard_normal((M, K)).astype(np.float32)
+    B = (r.standard_normal((K, N)) * 1e-3).astype(np.float32)
+    qa, sa = mp.quantize_fp8(dev(A), E4, 1, K)
+    qb, sb = mp.quantize_fp8(dev(B), E5, K, 1)
+    D = mp.gemm_fp8_rowscaled(qa, E4, sa.reshape(-1).contiguous(), qb, E5, sb.reshape(-1).contiguous())
+    got = bf16_values(D)
+    R_, S_ = oracle.gemm_fp8_rowscaled(host(qa), E4, host(sa).ravel(), host(qb), E5, host(sb).ravel())
+    check_fp(got, R_, S_, 1e-2, "quantised rowscaled", bf16_out=True)
+    ref = A.astype(np.float64) @ B.astype(np.float64)
+    assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 0.15

@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from helpers import dev, host, probes
 
 pytestmark = pytest.mark.gpu
@@ -98,6 +99,30 @@ def test_mfma_fp8_layout_and_every_code(gpu_ok):
     # 1e-3 * S per element; one instruction must stay inside it.
     rel = np.abs(D - ref) / S
     print("fp8 MFMA worst |err| / S:", rel.max())
+    assert (rel <= 1e-3).all()
+
+
+def test_mfma_e5m2_every_code(gpu_ok):
+    """Every finite E5M2 code through the FP8 instruction with both format
+    fields set to E5M2 (identity selector in B), and a general product."""
+    codes = np.array([c for c in range(256) if (c & 0x7C) != 0x7C], np.uint8)   # 248 finite codes
+    A = np.resize(codes, 32 * 64).reshape(32, 64).copy()
+    a = oracle.e5m2_to_f64(A)
+    one = np.uint8(0x3C)   # 1.0
+    for t in range(2):
+        B = np.zeros((64, 32), np.uint8)
+        B[np.arange(32) + 32 * t, np.arange(32)] = one
+        D = _run_mfma(4, A, B, torch.float32)
+        assert np.array_equal(D.astype(np.float64), a[:, 32 * t:32 * t + 32])
+    assert set(A.ravel().tolist()) == set(codes.tolist())
+    r = np.random.default_rng(12)
+    small = codes[(codes & 0x7F) >= 0x30]          # |x| >= 2^-3: products inside FP32's normal range
+    A = r.choice(small, (32, 64)).astype(np.uint8)
+    B = r.choice(small, (64, 32)).astype(np.uint8)
+    a, b = oracle.e5m2_to_f64(A), oracle.e5m2_to_f64(B)
+    D = _run_mfma(4, A, B, torch.float32)
+    rel = np.abs(D - a @ b) / (np.abs(a) @ np.abs(b))
+    print("e5m2 MFMA worst |err| / S:", rel.max())
     assert (rel <= 1e-3).all()
 
 
