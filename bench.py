@@ -313,6 +313,23 @@ def main():
                 "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s",
                              "frac": gbs / PEAK_HBM}}
             del tA
+        # per-tensor E5M2 (three launches: maximum, quantisation, scale)
+        R, Cc = 7168, 7168
+        tA = torch.randn((R, Cc), device=dev)
+        tq = torch.empty((R, Cc), dtype=torch.uint8, device=dev)
+        ts = torch.empty((1, 1), dtype=torch.float32, device=dev)
+        region, per = timed(lambda i: mp.quantize_fp8(tA, mp.FP8_E5M2, R, Cc, q_out=tq, scales_out=ts),
+                            max(args.steps // 2, 5), args.warmup, stream)
+        st = stats(per, region, max(args.steps // 2, 5))
+        nbytes = R * Cc * 9 + 4                          # X read twice, Q written
+        gbs = nbytes / (st["mean_us"] * 1e-6) / 1e9
+        extra["quantize_fp8_tensor_e5m2"] = {
+            "workload": "FP8 E5M2 per-tensor quantisation of FP32 7168 x 7168 (maximum pass, then "
+                        "quantisation pass)",
+            "GB_s": gbs, "algorithmic_bytes": nbytes, "launch_us": st,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM}}
+        del tA, tq
 
     # ---------------- FP8 block-scaled 4096 x 7168 x 7168 ----------------------
     if args.only in ("all", "fp8"):
@@ -330,7 +347,35 @@ def main():
             "TFLOP_s": tf, "launch_us": st,
             "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP8, "unit": "TFLOP/s",
                          "frac": tf / PEAK_FP8}}
-        del ta, tb, td
+        # the same operands with B read as E5M2 codes (the format of gradients)
+        qb5 = qb.copy()
+        qb5[(qb5 & 0x7C) == 0x7C] = 0x3C                   # no infinity / NaN codes
+        tb5 = to_dev(qb5)
+        region, per = timed(lambda i: mp.gemm_fp8_blockscaled_fmt(ta, mp.FP8_E4M3, tsa, tb5, mp.FP8_E5M2,
+                                                                  tsb, out=td),
+                            steps, args.warmup, stream)
+        st = stats(per, region, steps)
+        tf = 2.0 * M * N * K / (st["mean_us"] * 1e-6) / 1e12
+        extra["gemm_fp8_blockscaled_e4m3_e5m2"] = {
+            "workload": "FP8 E4M3 A x E5M2 B 4096x7168x7168, 1x128 A / 128x128 B FP32 scales, BF16 out",
+            "TFLOP_s": tf, "launch_us": st,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP8, "unit": "TFLOP/s",
+                         "frac": tf / PEAK_FP8}}
+        # one scale per row of A and per column of B
+        r = np.random.default_rng(14)
+        tra = to_dev(r.uniform(0.5, 2, M).astype(np.float32))
+        trb = to_dev(r.uniform(0.5, 2, N).astype(np.float32))
+        region, per = timed(lambda i: mp.gemm_fp8_rowscaled(ta, mp.FP8_E4M3, tra, tb, mp.FP8_E4M3, trb,
+                                                            out=td),
+                            steps, args.warmup, stream)
+        st = stats(per, region, steps)
+        tf = 2.0 * M * N * K / (st["mean_us"] * 1e-6) / 1e12
+        extra["gemm_fp8_rowscaled"] = {
+            "workload": "FP8 E4M3 4096x7168x7168, per-row A and per-column B FP32 scales, BF16 out",
+            "TFLOP_s": tf, "launch_us": st,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP8, "unit": "TFLOP/s",
+                         "frac": tf / PEAK_FP8}}
+        del ta, tb, td, tb5
 
     # ---------------- FP16 ragged 8191 x 8193 x 4099 ---------------------------
     if args.only in ("all", "f16_ragged"):
