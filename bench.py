@@ -274,6 +274,19 @@ def main():
                 "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s",
                              "frac": gbs / PEAK_HBM}}
             if M == 16:
+                # the same layer with the weights stored K x N
+                tWkn = [tW.t().contiguous() for tW in tWs[:4]]
+                region, per = timed(lambda i: mp.gemm_w8a8_kn(tX, tsx, tWkn[i % 4], tsw, tb, out=ty),
+                                    args.steps, args.warmup, stream)
+                st = stats(per, region, args.steps)
+                gbs = nbytes / (st["mean_us"] * 1e-6) / 1e9
+                extra["gemm_w8a8_kn_m16"] = {
+                    "workload": "W8A8 layer, 16 tokens x 4096 . W int8 stored K x N [4096 x 14336], bias, "
+                                "BF16 out; cold: 4 rotating W copies",
+                    "GB_s": gbs, "algorithmic_bytes": nbytes, "launch_us": st,
+                    "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s",
+                                 "frac": gbs / PEAK_HBM}}
+                del tWkn
                 # the same layer requantised to INT8 for a next INT8 layer
                 tq = torch.empty((M, N), dtype=torch.int8, device=dev)
                 region, per = timed(lambda i: mp.gemm_w8a8_requant(tX, tsx, tWs[i % copies], tsw, tb,

@@ -212,6 +212,15 @@ mpdt_status gemm_w8a8(int64_t M, int64_t N, int64_t K,
                       const int8_t* W, int64_t ldw, const float* w_scale, const float* bias,
                       uint16_t* Y, int64_t ldy, int32_t* Z, int64_t ldz, void* stream);
 
+/* gemm_w8a8 with the weights stored K x N: W[k][o] at W + k * ldw + o,
+ * ldw >= N (the logical [K][N] operand of x . W).  Same Z and Y, same
+ * arithmetic; a K x N chunk of W is staged through LDS so that the matrix
+ * instruction still gets K-consecutive bytes per channel. */
+mpdt_status gemm_w8a8_kn(int64_t M, int64_t N, int64_t K,
+                         const int8_t* X, int64_t ldx, const float* x_scale,
+                         const int8_t* W, int64_t ldw, const float* w_scale, const float* bias,
+                         uint16_t* Y, int64_t ldy, int32_t* Z, int64_t ldz, void* stream);
+
 /* The same layer with a requantising epilogue, for a next layer that takes
  * INT8 (same section: the epilogue may requantise instead of writing a
  * 16-bit result).  With v the FP32 value whose BF16 rounding gemm_w8a8

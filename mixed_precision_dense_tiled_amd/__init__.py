@@ -21,7 +21,7 @@ import torch
 __all__ = ["gemm_f16", "gemm_bf16", "gemm_f16_f16out", "gemm_bf16_bf16out", "gemm_f16_bias_act",
            "gemm_bf16_bias_act", "ACT_NONE", "ACT_RELU", "ACT_GELU", "ACT_SILU", "gemm_i8_i32",
            "gemm_fp8_blockscaled", "gemm_fp8_blockscaled_fmt", "gemm_fp8_rowscaled", "FP8_E4M3",
-           "FP8_E5M2", "gemv_w8a8", "gemm_w8a8", "gemm_w8a8_requant", "quantize_i8_rows",
+           "FP8_E5M2", "gemv_w8a8", "gemm_w8a8", "gemm_w8a8_kn", "gemm_w8a8_requant", "quantize_i8_rows",
            "quantize_fp8_blocks", "quantize_fp8",
            "MpdtError", "lib", "lib_path", "version"]
 
@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.gemm_w8a8.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _i64,
                                 _vp, _i64, _vp]
         L.gemm_w8a8.restype = ctypes.c_int
+        L.gemm_w8a8_kn.argtypes = L.gemm_w8a8.argtypes
+        L.gemm_w8a8_kn.restype = ctypes.c_int
         L.gemm_w8a8_requant.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp,
                                          ctypes.c_float, _vp, _i64, _vp, _i64, _vp]
         L.gemm_w8a8_requant.restype = ctypes.c_int
@@ -332,6 +334,31 @@ def gemm_w8a8(X, x_scale, W, w_scale, bias=None, out=None, z_out=None, return_z=
     pz, ldz = (None, N) if z_out is None else _mat(z_out, 4, "z_out")
     _check("gemm_w8a8", lib().gemm_w8a8(M, N, K, px, ldx, psx, pw, ldw, psw, pb, py, ldy, pz, ldz,
                                         _stream(W)))
+    if return_z or z_out is not None:
+        return out, z_out
+    return out
+
+
+def gemm_w8a8_kn(X, x_scale, W, w_scale, bias=None, out=None, z_out=None, return_z=False):
+    """gemm_w8a8 with W INT8 stored [K, N] (row k holds input k of every
+    output channel); returns Y BF16 [M, N] (and the INT32 sums on request)."""
+    M, K = X.shape
+    N = W.shape[1]
+    if W.shape[0] != K:
+        raise ValueError("W must be [K, N]")
+    px, ldx = _mat(X, 1, "X")
+    pw, ldw = _mat(W, 1, "W")
+    psx = _vec(x_scale, M, torch.float32, "x_scale")
+    psw = _vec(w_scale, N, torch.float32, "w_scale")
+    pb = None if bias is None else _vec(bias, N, torch.float32, "bias")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=W.device)
+    py, ldy = _mat(out, 2, "out")
+    if z_out is None and return_z:
+        z_out = torch.empty((M, N), dtype=torch.int32, device=W.device)
+    pz, ldz = (None, N) if z_out is None else _mat(z_out, 4, "z_out")
+    _check("gemm_w8a8_kn", lib().gemm_w8a8_kn(M, N, K, px, ldx, psx, pw, ldw, psw, pb, py, ldy, pz, ldz,
+                                              _stream(W)))
     if return_z or z_out is not None:
         return out, z_out
     return out

@@ -364,7 +364,7 @@ namespace {
 mpdt_status run_w8a8(const char* fn, int64_t M, int64_t N, int64_t K, const int8_t* X, int64_t ldx,
                      const float* x_scale, const int8_t* W, int64_t ldw, const float* w_scale,
                      const float* bias, void* Y, int64_t ldy, bool requant, float out_scale,
-                     int32_t* Z, int64_t ldz, void* stream) {
+                     int32_t* Z, int64_t ldz, void* stream, bool w_kn = false) {
     const int64_t esy = requant ? 1 : 2;
     if (!dims_ok(M, N, K)) return fail(MPDT_ERROR_INVALID_VALUE, fn, "dimension out of range");
     if (requant && !(std::isfinite(out_scale) && out_scale > 0.0f))
@@ -374,14 +374,16 @@ mpdt_status run_w8a8(const char* fn, int64_t M, int64_t N, int64_t K, const int8
         return fail(MPDT_ERROR_INVALID_VALUE, fn, "output, x_scale or w_scale is NULL");
     if (K > 0) {
         if (!X || !W) return fail(MPDT_ERROR_INVALID_VALUE, fn, "X or W is NULL");
-        if (ldx < K || ldw < K) return fail(MPDT_ERROR_INVALID_VALUE, fn, "ldx or ldw < K");
+        if (ldx < K) return fail(MPDT_ERROR_INVALID_VALUE, fn, "ldx < K");
+        if (ldw < (w_kn ? N : K)) return fail(MPDT_ERROR_INVALID_VALUE, fn, w_kn ? "ldw < N" : "ldw < K");
     }
     if (ldy < N || (Z && ldz < N)) return fail(MPDT_ERROR_INVALID_VALUE, fn, "output ld or ldz < N");
     if (!aligned_to(Y, esy) || !aligned_to(x_scale, 4) || !aligned_to(w_scale, 4) ||
         (bias && !aligned_to(bias, 4)) || (Z && !aligned_to(Z, 4)))
         return fail(MPDT_ERROR_MISALIGNED, fn, "pointer not aligned to its element size");
     Span sx, sw, ssx, ssw, sb, sy, sz;
-    if (!span_of(X, K > 0 ? M : 0, K, ldx, 1, &sx) || !span_of(W, K > 0 ? N : 0, K, ldw, 1, &sw) ||
+    if (!span_of(X, K > 0 ? M : 0, K, ldx, 1, &sx) ||
+        !(w_kn ? span_of(W, K, N, ldw, 1, &sw) : span_of(W, K > 0 ? N : 0, K, ldw, 1, &sw)) ||
         !span_of(x_scale, 1, M, M, 4, &ssx) || !span_of(w_scale, 1, N, N, 4, &ssw) ||
         !span_of(bias, bias ? 1 : 0, N, N, 4, &sb) || !span_of(Y, M, N, ldy, esy, &sy) ||
         !span_of(Z, Z ? M : 0, N, ldz, 4, &sz))
@@ -414,6 +416,7 @@ mpdt_status run_w8a8(const char* fn, int64_t M, int64_t N, int64_t K, const int8
     a.M = (int)M;
     a.N = (int)N;
     a.K = (int)K;
+    a.w_kn = w_kn ? 1 : 0;
     const bool al = aligned_to(X, 16) && aligned_to(W, 16) && ldx % 16 == 0 && ldw % 16 == 0;
     return launched(mpdt::launch_gemm_w8a8(a, al, (hipStream_t)stream), fn);
 }
@@ -425,6 +428,14 @@ MPDT_EXPORT mpdt_status gemm_w8a8(int64_t M, int64_t N, int64_t K, const int8_t*
                                   int32_t* Z, int64_t ldz, void* stream) {
     return run_w8a8("gemm_w8a8", M, N, K, X, ldx, x_scale, W, ldw, w_scale, bias, Y, ldy, false,
                     1.0f, Z, ldz, stream);
+}
+
+MPDT_EXPORT mpdt_status gemm_w8a8_kn(int64_t M, int64_t N, int64_t K, const int8_t* X, int64_t ldx,
+                                     const float* x_scale, const int8_t* W, int64_t ldw,
+                                     const float* w_scale, const float* bias, uint16_t* Y,
+                                     int64_t ldy, int32_t* Z, int64_t ldz, void* stream) {
+    return run_w8a8("gemm_w8a8_kn", M, N, K, X, ldx, x_scale, W, ldw, w_scale, bias, Y, ldy, false,
+                    1.0f, Z, ldz, stream, true);
 }
 
 MPDT_EXPORT mpdt_status gemm_w8a8_requant(int64_t M, int64_t N, int64_t K, const int8_t* X,

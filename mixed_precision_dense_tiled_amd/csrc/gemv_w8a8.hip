@@ -141,6 +141,34 @@ hipError_t launch_gemv_w8a8(const GemvArgs& a, bool aligned, hipStream_t stream)
 // that matters.
 // ---------------------------------------------------------------------------
 constexpr int TOK_WAVES = 4;                   // wavefronts per workgroup
+
+// The epilogue of one 32-token x 32-channel block: accumulator r of lane l
+// holds token 8 (r / 4) + 4 (l / 32) + r % 4 and channel o (= o0 + l % 32).
+__device__ __forceinline__ void w8a8_epilogue(const W8A8Args& g, const i32x16& acc, int o, int half) {
+    if (o >= g.N) return;
+    const float sw = g.w_scale[o];
+    const float b = g.bias ? g.bias[o] : 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int m = 8 * (r >> 2) + 4 * half + (r & 3);
+        if (m < g.M) {
+            const int z = acc[r];
+            if (g.Z) g.Z[(int64_t)m * g.ldz + o] = z;
+            // three separately rounded FP32 operations (no fused multiply-add)
+            float v = mul_rn((float)z, g.x_scale[m]);
+            v = mul_rn(v, sw);
+            if (g.bias) v = add_rn(v, b);
+            if (g.Q) {
+                // requantised for a next layer that takes INT8: one IEEE
+                // division, round half to even, saturate to +-127
+                const float q = __builtin_rintf(v / g.q_scale);
+                g.Q[(int64_t)m * g.ldq + o] = (int8_t)fminf(fmaxf(q, -127.0f), 127.0f);
+            } else {
+                g.Y[(int64_t)m * g.ldy + o] = f32_to_bf16_bits(v);
+            }
+        }
+    }
+}
 constexpr int TOK_GROUP = 8;                   // MFMA steps (32 K bytes each) per wave slice
 
 __global__ __launch_bounds__(64 * TOK_WAVES) void gemm_w8a8_kernel(W8A8Args g) {
@@ -208,30 +236,168 @@ __global__ __launch_bounds__(64 * TOK_WAVES) void gemm_w8a8_kernel(W8A8Args g) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] += partial[w][r][lane];
 
-    // accumulator r of lane l: token 8 (r / 4) + 4 (l / 32) + r % 4, channel o0 + l % 32
-    const int o = o0 + r32;
-    if (o >= g.N) return;
-    const float sw = g.w_scale[o];
-    const float b = g.bias ? g.bias[o] : 0.0f;
+    w8a8_epilogue(g, acc, o0 + r32, half);
+}
+
+// ---------------------------------------------------------------------------
+// The same layer with the weights stored K x N (row k holds input k of every
+// output channel, leading dimension ldw >= N): the logical [K][N] operand of
+// x . W, for callers that keep weights that way.  The MFMA still needs 16
+// consecutive K bytes of one channel per lane, so W is transposed through
+// LDS.  A workgroup of four waves owns 64 channels and walks K in chunks of
+// 1024 rows (64 KiB: each thread loads the 16-byte pieces of four
+// consecutive rows in each of four 256-row blocks, with plain loads and no
+// branches except in the last chunk and the last channel block, so all of
+// them are in flight together).  Two register sets keep the loads of the
+// next two chunks in flight while one is computed.  A chunk is written to
+// LDS channel-major, four K bytes of one channel per 32-bit store (a byte
+// transpose by v_perm; rows padded and swizzled so neither the stores nor
+// the 16-byte operand reads have bank conflicts).  Wave w takes rows
+// 256 w .. 256 w + 255 of every chunk (eight 32-K steps for each of the two
+// 32-channel groups); the four partial sums meet in LDS as above.  The
+// weights arrive as 64-byte pieces of many rows rather than long runs, and
+// stream at about two thirds of the N x K layout's rate.
+// ---------------------------------------------------------------------------
+constexpr int KN_CH = 64;                       // channels per workgroup
+constexpr int KN_PPR = KN_CH / 16;              // 16-byte pieces per row
+constexpr int KN_RB = 4 * (256 / KN_PPR);       // rows per block (every thread: 4 rows x 1 piece)
+constexpr int KN_NB = 4;                        // blocks per chunk
+constexpr int KN_KC = KN_NB * KN_RB;            // K rows per chunk
+constexpr int KN_KW = KN_KC / TOK_WAVES;        // rows of a chunk per wave
+constexpr int KN_G = KN_CH / 32;                // 32-channel MFMA groups
+// LDS: channel c's K bytes at c * KN_PITCH, K offset k stored at k ^ kn_swz(c).
+constexpr int KN_PITCH = KN_KC + 16;
+__device__ __forceinline__ int kn_swz(int c) { return (256 / KN_PPR) * ((c >> 4) & (KN_PPR - 1)); }
+
+__global__ __launch_bounds__(256) void gemm_w8a8_kn_kernel(W8A8Args g) {
+    __shared__ __attribute__((aligned(16))) uint8_t wt[2][KN_CH * KN_PITCH];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // Workgroups are dealt to the eight XCDs in turn; the channel blocks are
+    // dealt so that each XCD gets one contiguous run of them.
+    const int nblk = (g.N + KN_CH - 1) / KN_CH;
+    const int per_xcd = (nblk + 7) / 8;
+    const int blk = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (blk >= nblk) return;                     // whole workgroup: before any barrier
+    const int o0 = blk * KN_CH;
+    const int r32 = lane & 31, half = lane >> 5;
+    const int64_t K = g.K;
+    const int nch = (int)((K + KN_KC - 1) / KN_KC);
+    // this thread's loads: rows KN_RB b + 4 (tid / KN_PPR) + i (b < KN_NB,
+    // i < 4) of a chunk, bytes 16 (tid % KN_PPR) .. +15 of the workgroup's
+    // channel piece (bounded by N: bytes past it read as zero)
+    const int lg = tid / KN_PPR, lc = (tid % KN_PPR) * 16;
+    const char* const wbase = (const char*)g.W + o0 + lc;
+    const int64_t wlen = (int64_t)g.N - o0 - lc;          // valid bytes of the piece
+    const int64_t wend = wlen < 16 ? (wlen > 0 ? wlen : 0) : 16;
+    // Whole chunks of whole pieces take plain 16-byte loads (any byte address
+    // is fine for them) with no branches, so all 16 stay in flight together;
+    // the last chunk and the last channel block take the bounded loads.
+    const bool full_n = o0 + KN_CH <= g.N;
+    auto load_chunk = [&](int c, u32x4 (&v)[KN_NB][4]) {
+        const int64_t k0 = (int64_t)c * KN_KC + 4 * lg;
+        if (full_n && (int64_t)(c + 1) * KN_KC <= K) {
+            const char* p = wbase + k0 * g.ldw;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int m = 8 * (r >> 2) + 4 * half + (r & 3);
-        if (m < g.M) {
-            const int z = acc[r];
-            if (g.Z) g.Z[(int64_t)m * g.ldz + o] = z;
-            // three separately rounded FP32 operations (no fused multiply-add)
-            float v = mul_rn((float)z, g.x_scale[m]);
-            v = mul_rn(v, sw);
-            if (g.bias) v = add_rn(v, b);
-            if (g.Q) {
-                // requantised for a next layer that takes INT8: one IEEE
-                // division, round half to even, saturate to +-127
-                const float q = __builtin_rintf(v / g.q_scale);
-                g.Q[(int64_t)m * g.ldq + o] = (int8_t)fminf(fmaxf(q, -127.0f), 127.0f);
-            } else {
-                g.Y[(int64_t)m * g.ldy + o] = f32_to_bf16_bits(v);
+            for (int b = 0; b < KN_NB; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    v[b][i] = *reinterpret_cast<const u32x4*>(p + (int64_t)(KN_RB * b + i) * g.ldw);
+        } else {
+#pragma unroll
+            for (int b = 0; b < KN_NB; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t k = k0 + KN_RB * b + i;
+                    const char* p = wbase + k * g.ldw;
+                    v[b][i] = (k < K) ? load16_row<false>(p, p + wend) : u32x4{0u, 0u, 0u, 0u};
+                }
+        }
+    };
+    // channel lc + q, K bytes KN_RB b + 4 lg .. +3 of the chunk: byte q of
+    // the four rows' pieces, as one 32-bit LDS store
+    auto store_chunk = [&](int buf, const u32x4 (&v)[KN_NB][4]) {
+#pragma unroll
+        for (int b = 0; b < KN_NB; ++b)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                // byte q of the four rows' pieces: two byte pairs, then the word
+                // (v_perm: selector bytes 0-3 pick the second operand, 4-7 the first)
+                const int w = q >> 2;
+                const uint32_t sel = 0x0c0c0400u | (uint32_t)(q & 3) | ((uint32_t)(q & 3) << 8);
+                const uint32_t lo = __builtin_amdgcn_perm(v[b][1][w], v[b][0][w], sel);
+                const uint32_t hi = __builtin_amdgcn_perm(v[b][3][w], v[b][2][w], sel);
+                const uint32_t word = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+                const int ch = lc + q;
+                *reinterpret_cast<uint32_t*>(&wt[buf][ch * KN_PITCH + ((KN_RB * b + 4 * lg) ^ kn_swz(ch))]) = word;
+            }
+    };
+    const bool xrow = r32 < g.M;
+    const char* xp = (const char*)g.X + (int64_t)(xrow ? r32 : 0) * g.ldx;
+    const uint32_t xkeep = xrow ? ~0u : 0u;
+
+    i32x16 acc[KN_G];
+#pragma unroll
+    for (int j = 0; j < KN_G; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][r] = 0;
+    // Two register sets: the loads of chunks c + 1 and c + 2 are in flight
+    // while chunk c is computed.
+    u32x4 va[KN_NB][4], vb[KN_NB][4];
+    load_chunk(0, va);
+    if (nch > 1) load_chunk(1, vb);
+    auto step = [&](int c, u32x4 (&v)[KN_NB][4]) {
+        const int buf = c & 1;
+        store_chunk(buf, v);
+        __syncthreads();
+        if (c + 2 < nch) load_chunk(c + 2, v);          // in flight during the MFMAs
+        const int64_t kw = (int64_t)c * KN_KC + KN_KW * wave;
+        constexpr int NS = KN_KW / 32;                  // 32-K steps per wave and chunk
+        u32x4 xv[NS];
+        if ((int64_t)(c + 1) * KN_KC <= K) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                xv[s] = *reinterpret_cast<const u32x4*>(xp + kw + 32 * s + 16 * half) & xkeep;
+        } else {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) xv[s] = load16_row<false>(xp + kw + 32 * s + 16 * half, xp + K) & xkeep;
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+#pragma unroll
+            for (int j = 0; j < KN_G; ++j) {
+                // channel 32 j + r32, K bytes KN_KW wave + 32 s + 16 half .. +15 of the chunk
+                const int ch = 32 * j + r32;
+                const u32x4 wv = *reinterpret_cast<const u32x4*>(
+                    &wt[buf][ch * KN_PITCH + ((KN_KW * wave + 32 * s + 16 * half) ^ kn_swz(ch))]);
+                acc[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, xv[s]),
+                                                               __builtin_bit_cast(i32x4, wv), acc[j], 0, 0, 0);
             }
         }
+    };
+    for (int c = 0; c < nch; c += 2) {
+        step(c, va);
+        if (c + 1 < nch) step(c + 1, vb);
+    }
+    // partial sums of waves 1..3 through the first chunk buffer, once every
+    // wave is done reading it
+    __syncthreads();
+    int* const partial = reinterpret_cast<int*>(&wt[0][0]);   // [3][KN_G][16][64]
+    static_assert((TOK_WAVES - 1) * KN_G * 16 * 64 * 4 <= KN_CH * KN_PITCH, "partial sums fit");
+    if (wave > 0) {
+#pragma unroll
+        for (int j = 0; j < KN_G; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) partial[(((wave - 1) * KN_G + j) * 16 + r) * 64 + lane] = acc[j][r];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int j = 0; j < KN_G; ++j) {
+#pragma unroll
+        for (int w = 0; w < TOK_WAVES - 1; ++w)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[j][r] += partial[((w * KN_G + j) * 16 + r) * 64 + lane];
+        w8a8_epilogue(g, acc[j], o0 + 32 * j + r32, half);
     }
 }
 
@@ -246,8 +412,14 @@ hipError_t launch_gemm_w8a8(const W8A8Args& a0, bool /*aligned*/, hipStream_t st
         a.Y = a0.Y ? a0.Y + (int64_t)m0 * a0.ldy : nullptr;
         a.Q = a0.Q ? a0.Q + (int64_t)m0 * a0.ldq : nullptr;
         a.Z = a0.Z ? a0.Z + (int64_t)m0 * a0.ldz : nullptr;
-        dim3 grid((unsigned)((a.N + 31) / 32)), block(64 * TOK_WAVES);
-        hipLaunchKernelGGL(gemm_w8a8_kernel, grid, block, 0, stream, a);
+        if (a.w_kn) {
+            const int nblk = (a.N + KN_CH - 1) / KN_CH;
+            hipLaunchKernelGGL(gemm_w8a8_kn_kernel, dim3((unsigned)(8 * ((nblk + 7) / 8))), dim3(256), 0,
+                               stream, a);
+        } else {
+            dim3 grid((unsigned)((a.N + 31) / 32)), block(64 * TOK_WAVES);
+            hipLaunchKernelGGL(gemm_w8a8_kernel, grid, block, 0, stream, a);
+        }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

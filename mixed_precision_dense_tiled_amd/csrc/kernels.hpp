@@ -84,6 +84,7 @@ struct W8A8Args {
     int32_t* Z;             // or null
     int64_t ldz;
     int M, N, K;
+    int w_kn;               // W stored K x N (ldw >= N) instead of N x K
 };
 
 // aligned: X, W and their rows start 16-byte aligned.

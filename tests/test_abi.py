@@ -202,6 +202,19 @@ def test_gemv_validation():
     assert L.gemv_w8a8(1, 0, 64, P, f, Q, 64, R, R + 4096, None, None) == SUCCESS
 
 
+def test_w8a8_kn_validation():
+    L = mp.lib()
+
+    def call(M=4, N=16, K=64, ldw=16, Y=R, W=Q):
+        return L.gemm_w8a8_kn(M, N, K, P, 64, P + 4096, W, ldw, Q + 65536, None, Y, 16, None, 16, None)
+
+    assert call(ldw=15) == INVALID                     # K x N: ldw >= N
+    assert call(Y=Q + 16 * 63) == ALIASING             # Y over the last row of W (K x N)
+    assert call(Y=Q + 16 * 64) != ALIASING
+    if not gpu_present:
+        assert call() == NO_DEVICE and call(ldw=20) == NO_DEVICE
+
+
 def test_w8a8_requant_validation():
     L = mp.lib()
     f = ctypes.c_float

@@ -2,6 +2,8 @@
 the two quantisers, against the oracle, bit-exact (every step is an integer
 sum or a fixed sequence of IEEE FP32 operations, then one rounding):
 
+  * gemm_w8a8_kn: the same layer with the weights stored K x N (ragged N,
+    padded ldw, K = 1, 4 tokens x the 4096 x 14336 layer);
   * gemm_w8a8_requant: the same layer requantised to INT8 (saturation,
     exact ties to even, a padded output, K = 0);
   * gemm_w8a8: M = 1, 2, 3, 5, 8, 16, 17, 31, 32, 33, 40, 65 tokens (groups of
@@ -118,6 +120,20 @@ def test_w8a8_requant_padded_output_ties_and_k_zero(gpu_ok):
                              torch.zeros((4, 0), dtype=torch.int8, device=gpu_ok), dev(np.ones(4, np.float32)),
                              dev(bias), 0.5)
     assert host(Q).tolist() == [[1, -1, 127, 127]] * 2
+
+
+@pytest.mark.parametrize("M,N,K,ldw,with_bias", [(1, 1000, 4500, None, True), (4, 14336, 4096, None, True),
+                                                 (17, 333, 1000, 347, False), (33, 70, 300, None, True),
+                                                 (16, 5, 1, 9, True), (2, 64, 513, 100, False)])
+def test_w8a8_kn_weights_bit_exact(gpu_ok, M, N, K, ldw, with_bias):
+    X, sx, W, sw, bias = w8a8_inputs(M, N, K, seed=M * 7 + N + K)
+    b = bias if with_bias else None
+    Wkn = np.ascontiguousarray(W.T)                # the same weights stored K x N
+    y, z = mp.gemm_w8a8_kn(dev(X, K + 1, pad=3) if M > 1 else dev(X), dev(sx), dev(Wkn, ldw, pad=-9),
+                           dev(sw), None if b is None else dev(b), return_z=True)
+    torch.cuda.synchronize()
+    zr, yr = oracle.gemm_w8a8(X, sx, W, sw, b)
+    assert np.array_equal(host(z), zr) and np.array_equal(host(y).view(np.uint16), yr)
 
 
 def bf16_matrix(shape, seed, scale=1.0):
