@@ -520,6 +520,7 @@ mpdt_status run_quantize_fp8(const char* fn, int64_t R, int64_t C, const float* 
     a.block_rows = (int)std::min<int64_t>(br, 128);
     a.fmt = fmt;
     a.shape = shape;
+    a.vec = aligned_to(X, 16) && ldx % 4 == 0 && aligned_to(Q, 4) && ldq % 4 == 0;
     return launched(mpdt::launch_quantize_fp8_blocks(a, (hipStream_t)stream), fn);
 }
 }  // namespace

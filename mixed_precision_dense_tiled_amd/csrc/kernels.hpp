@@ -114,6 +114,7 @@ struct QuantFp8Args {
     int block_rows;   // 1 or 128 (with 128 columns); or the shapes below
     int fmt;          // 0 E4M3, 1 E5M2
     int shape;        // FP8Q_* block shape
+    int vec;          // X rows 16-byte and Q rows 4-byte aligned: 4 elements per access
 };
 // Block shapes of the FP8 quantiser: 1 x 128, 128 x 128, one scale per row
 // (1 x C), per column (R x 1) or per tensor (R x C).

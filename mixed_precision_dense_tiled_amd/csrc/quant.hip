@@ -192,8 +192,22 @@ __global__ __launch_bounds__(256) void quantize_fp8_percol_kernel(QuantFp8Args g
 __global__ void fp8_tensor_clear_kernel(float* S) { S[0] = 0.0f; }
 
 constexpr int TENSOR_WGS = 1024;   // workgroups of the two grid-stride passes
+
+// Four floats from c (a multiple of 4, 16-byte aligned in a vec row): one
+// vector load inside [0, end), element loads (zeros past end) at the end.
+__device__ __forceinline__ float4 load4_bounded(const float* xr, int64_t c, int64_t end) {
+    if (c + 4 <= end) return *reinterpret_cast<const float4*>(xr + c);
+    float4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (c < end) v.x = xr[c];
+    if (c + 1 < end) v.y = xr[c + 1];
+    if (c + 2 < end) v.z = xr[c + 2];
+    return v;
+}
 constexpr int TENSOR_CH = 4096;    // columns of one work item (a row piece)
 
+// A work item is one row piece of TENSOR_CH columns; with aligned rows each
+// thread reads four 16-byte vectors of it at once (16 KiB per workgroup in
+// flight), else single elements.
 __global__ __launch_bounds__(256) void fp8_tensor_amax_kernel(QuantFp8Args g) {
     __shared__ float red[4];
     float amax = 0.0f;
@@ -201,7 +215,17 @@ __global__ __launch_bounds__(256) void fp8_tensor_amax_kernel(QuantFp8Args g) {
     for (int64_t it = blockIdx.x; it < g.R * pieces; it += gridDim.x) {
         const int64_t r = it / pieces, c0 = (it % pieces) * TENSOR_CH;
         const int64_t c1 = std::min<int64_t>(c0 + TENSOR_CH, g.C);
-        for (int64_t c = c0 + threadIdx.x; c < c1; c += 256) amax = fmaxf(amax, fabsf(g.X[r * g.ldx + c]));
+        const float* xr = g.X + r * g.ldx;
+        if (g.vec) {
+            float4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = load4_bounded(xr, c0 + 4 * (threadIdx.x + 256 * u), c1);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w))));
+        } else {
+            for (int64_t c = c0 + threadIdx.x; c < c1; c += 256) amax = fmaxf(amax, fabsf(xr[c]));
+        }
     }
     amax = block_max256(amax, red);
     if (threadIdx.x == 0) atomicMax((unsigned int*)g.S, __float_as_uint(amax));
@@ -215,8 +239,26 @@ __global__ __launch_bounds__(256) void fp8_tensor_quant_kernel(QuantFp8Args g) {
     for (int64_t it = blockIdx.x; it < g.R * pieces; it += gridDim.x) {
         const int64_t r = it / pieces, c0 = (it % pieces) * TENSOR_CH;
         const int64_t c1 = std::min<int64_t>(c0 + TENSOR_CH, g.C);
-        for (int64_t c = c0 + threadIdx.x; c < c1; c += 256)
-            g.Q[r * g.ldq + c] = to_fp8<FMT>(g.X[r * g.ldx + c] / s);
+        const float* xr = g.X + r * g.ldx;
+        uint8_t* qr = g.Q + r * g.ldq;
+        if (g.vec) {
+            float4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = load4_bounded(xr, c0 + 4 * (threadIdx.x + 256 * u), c1);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t c = c0 + 4 * (threadIdx.x + 256 * u);
+                const uint32_t q = (uint32_t)to_fp8<FMT>(v[u].x / s) | ((uint32_t)to_fp8<FMT>(v[u].y / s) << 8) |
+                                   ((uint32_t)to_fp8<FMT>(v[u].z / s) << 16) | ((uint32_t)to_fp8<FMT>(v[u].w / s) << 24);
+                if (c + 4 <= c1) {
+                    *reinterpret_cast<uint32_t*>(qr + c) = q;
+                } else {
+                    for (int e = 0; e < 4 && c + e < c1; ++e) qr[c + e] = (uint8_t)(q >> (8 * e));
+                }
+            }
+        } else {
+            for (int64_t c = c0 + threadIdx.x; c < c1; c += 256) qr[c] = to_fp8<FMT>(xr[c] / s);
+        }
     }
 }
 

@@ -104,15 +104,18 @@ SHAPES = {"row128": (1, 128), "tile128": (128, 128), "per_row": (1, None), "per_
 
 @pytest.mark.parametrize("fmt", [E4, E5])
 @pytest.mark.parametrize("shape", list(SHAPES))
-@pytest.mark.parametrize("R,C", [(257, 300), (5, 4100), (300, 7)])
-def test_quantize_fp8_bit_exact(gpu_ok, fmt, shape, R, C):
+@pytest.mark.parametrize("R,C,ld", [(257, 300, 303), (5, 4100, 4103), (300, 7, 10), (257, 300, 300),
+                                    (3, 4102, 4104), (2, 8194, 8196)])
+def test_quantize_fp8_bit_exact(gpu_ok, fmt, shape, R, C, ld):
+    # ld a multiple of 4: the 16-byte path of the per-tensor passes (with a
+    # partial last vector when C is not); otherwise the element path
     r = np.random.default_rng(R * C + fmt)
     X = (r.standard_normal((R, C)) * 2.0 ** r.integers(-12, 12, (R, 1))).astype(np.float32)
     X[min(3, R - 1)] = 0.0                                   # an all-zero row
     br, bc = SHAPES[shape]
     br = R if br is None else br
     bc = C if bc is None else bc
-    q, s = mp.quantize_fp8(dev(X, C + 3, pad=np.float32(1e30)), fmt, br, bc)
+    q, s = mp.quantize_fp8(dev(X, ld, pad=np.float32(1e30)) if ld != C else dev(X), fmt, br, bc)
     qr, sr = oracle.quantize_fp8_blocks_fmt(X, fmt, br, bc)
     assert np.array_equal(host(s), sr), shape
     assert np.array_equal(host(q), qr), shape
