@@ -548,12 +548,13 @@ void gemm_kernel(GemmArgs g) {
             };
             auto dma_piece = [&](auto P, i32x4 ra, i32x4 rb, uint32_t stage_off) {
                 constexpr int p = decltype(P)::value;
-                // (M0 changes before the first piece of each operand only)
+                // (other instructions sit between the pieces: each keeps the
+                // wait state after an M0 write)
                 if constexpr (p < C::UA)
-                    lds_dma16<p * 1024, p == 0>(ra, lds0 + stage_off + wave * C::UA * 1024, voffA,
-                                                soffA(p));
+                    lds_dma16<p * 1024, true>(ra, lds0 + stage_off + wave * C::UA * 1024, voffA,
+                                              soffA(p));
                 else
-                    lds_dma16<(p - C::UA) * 1024, p == C::UA>(
+                    lds_dma16<(p - C::UA) * 1024, true>(
                         rb, lds0 + stage_off + C::A_BYTES + wave * C::UB * 1024,
                         (p & 1) ? voffB1 : voffB0, soffB(p - C::UA));
             };
@@ -604,14 +605,29 @@ void gemm_kernel(GemmArgs g) {
             };
 
             Frags fr;
+            // The direct loads of a K tile are split in two halves: its A
+            // pieces go out in phase Y of one iteration, its B pieces in
+            // phase X of the next (both after the barrier that frees the
+            // stage), one per four MFMA slots: a 1 KiB direct load keeps the
+            // CU's address unit busy for 16 cycles, and all eight in one
+            // phase saturated it and stalled the MFMA stream.  The prologue
+            // issues tiles 0..NS-2 whole and tile NS-1's A half; iteration 0
+            // issues its B half.
+            i32x4 ra_c, rb_c;   // resources of the tile whose B half is due next
 #pragma unroll
             for (int p = 0; p < NS; ++p) {
                 const bool lastp = p == nt - 1;
                 const i32x4 ra = rsA(lastp ? kA_last : (int64_t)p * C::KT_BYTES, true);
                 const i32x4 rb = rsB(lastp ? kB_last : (int64_t)p * stepB, true);
-                static_for<0, DMA_PER_TILE>([&](auto Q) { dma_piece(Q, ra, rb, p * STAGE_BYTES); });
+                if (p < NS - 1) {
+                    static_for<0, DMA_PER_TILE>([&](auto Q) { dma_piece(Q, ra, rb, p * STAGE_BYTES); });
+                } else {
+                    static_for<0, C::UA>([&](auto Q) { dma_piece(Q, ra, rb, p * STAGE_BYTES); });
+                    ra_c = ra;
+                    rb_c = rb;
+                }
             }
-            wait_vmem<(NS - 1) * DMA_PER_TILE>();
+            wait_vmem<(NS - 2) * DMA_PER_TILE + C::UA>();
             wg_barrier();
 #pragma unroll
             for (int r = 0; r < 7; ++r) read_group(fr, 0, r, 0);
@@ -619,33 +635,39 @@ void gemm_kernel(GemmArgs g) {
             int64_t kA = (int64_t)NS * C::KT_BYTES, kB = (int64_t)NS * stepB;   // tile t+NS
             for (int t = 0; t < nt - 1; ++t) {
                 const int snext = scur + 1 == NS ? 0 : scur + 1;
+                const int sprev = scur == 0 ? NS - 1 : scur - 1;   // stage of tile t - 1 + NS
                 const uint32_t cur = (uint32_t)scur * STAGE_BYTES;
                 const uint32_t nxt = (uint32_t)snext * STAGE_BYTES;
+                const uint32_t prv = (uint32_t)sprev * STAGE_BYTES;
                 const bool live = t + NS < nt;
                 const bool lastl = t + NS == nt - 1;   // the tile loaded now is the last
                 i32x4 ra, rb;
-                // phase X
+                // phase X: the B half of tile t - 1 + NS on slots 9, 11, 13, 15
                 static_for<0, 16>([&](auto IDX) {
                     constexpr int idx = decltype(IDX)::value;
                     mma1(fr, 0, idx);
                     if constexpr (idx < 7) read_group(fr, 1, idx, cur);
                     if constexpr (idx == 8) ra = rsA(lastl ? kA_last : kA, live);
                     if constexpr (idx == 10) rb = rsB(lastl ? kB_last : kB, live);
+                    if constexpr (idx >= 9 && (idx & 1) == 1)
+                        dma_piece(std::integral_constant<int, C::UA + (idx - 9) / 2>{}, ra_c, rb_c, prv);
                     __builtin_amdgcn_sched_barrier(0);
                 });
                 wait_vmem<WAIT_AHEAD>();
                 wait_lds();
                 wg_barrier();
-                // phase Y
+                // phase Y: the A half of tile t + NS on slots 0, 4, 8, 12
                 static_for<0, 16>([&](auto IDX) {
                     constexpr int idx = decltype(IDX)::value;
                     mma1(fr, 1, idx);
-                    if constexpr ((idx & 1) == 0)
-                        dma_piece(std::integral_constant<int, idx / 2>{}, ra, rb, cur);
-                    else if constexpr (idx / 2 < 7)
+                    if constexpr ((idx & 3) == 0)
+                        dma_piece(std::integral_constant<int, idx / 4>{}, ra, rb, cur);
+                    else if constexpr ((idx & 1) == 1 && idx / 2 < 7)
                         read_group(fr, 0, idx / 2, nxt);
                     __builtin_amdgcn_sched_barrier(0);
                 });
+                ra_c = ra;
+                rb_c = rb;
                 scur = snext;
                 kA += C::KT_BYTES;
                 kB += stepB;
