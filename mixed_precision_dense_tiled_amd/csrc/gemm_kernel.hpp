@@ -798,7 +798,25 @@ void gemm_kernel(GemmArgs g) {
     const int col_base = n0_load + wn * C::WN + (int)lrow;
     constexpr int NTILE = C::TM * C::TN;
     static_assert(!BA || KD == Kind::F16 || KD == Kind::BF16, "fused epilogue: 16-bit inputs");
+    // Fused epilogue: the bias of each of the lane's columns (one per 32-column
+    // block; -0 where there is none, since x + (-0) = x for every x), read
+    // through a pointer made opaque here, after the K loop, so the loads are
+    // not hoisted into it.
+    float bcol[BA ? C::TN : 1];
     if constexpr (BA) {
+        const float* bptr = g.bias;
+        asm volatile("" : "+s"(bptr));
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+            const int col = col_base + j * 32;
+            bcol[j] = (bptr && col < g.N) ? bptr[col] : -0.0f;
+        }
+    }
+    // No activation or ReLU: the store code below, with the bias and the
+    // activation in its element conversion.  GELU and SiLU (tens of
+    // instructions per element) go through the loop over LDS here instead of
+    // code unrolled over all 256 accumulators.
+    if constexpr (BA) if (g.act == ACT_GELU || g.act == ACT_SILU) {
         // Fused epilogue, one 32-row block of the wave tile at a time:
         //   (1) v = acc + C, then v = v + bias (FP32 adds, in registers; C of
         //       the next block is read meanwhile), written straight to a
@@ -824,16 +842,7 @@ void gemm_kernel(GemmArgs g) {
         // (opaque after the K loop, so nothing below is computed early and
         // kept live through it)
         const float* cptr = (const float*)g.C;
-        const float* bptr = g.bias;
-        asm volatile("" : "+s"(cptr), "+s"(bptr));
-        // the bias of each of the lane's columns (one per 32-column block; -0
-        // where there is none, since x + (-0) = x for every x)
-        float bcol[C::TN];
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j) {
-            const int col = col_base + j * 32;
-            bcol[j] = (bptr && col < g.N) ? bptr[col] : -0.0f;
-        }
+        asm volatile("" : "+s"(cptr));
         // (on edge tiles the element is clamped into C: what is read for a
         // position outside M x N is never stored, and every lane issues the
         // same loads without branches)
@@ -895,21 +904,28 @@ void gemm_kernel(GemmArgs g) {
                     load_cblk(i + 1, cptr, cbuf[(i + 1) & 1]);
                 }
             }
-            switch (g.act) {   // uniform
-                case ACT_RELU: finish(i, std::integral_constant<int, ACT_RELU>{}); break;
-                case ACT_GELU: finish(i, std::integral_constant<int, ACT_GELU>{}); break;
-                case ACT_SILU: finish(i, std::integral_constant<int, ACT_SILU>{}); break;
-                default: finish(i, std::integral_constant<int, ACT_NONE>{}); break;
-            }
+            if (g.act == ACT_GELU) finish(i, std::integral_constant<int, ACT_GELU>{});   // uniform
+            else finish(i, std::integral_constant<int, ACT_SILU>{});
         });
     }
-    auto epilogue = [&](auto out_tag) {
+    auto epilogue = [&](auto out_tag, auto act_tag) {
         using OutT = typename decltype(out_tag)::type;
+        constexpr int ACT = decltype(act_tag)::value;
         OutT* const Dp = (OutT*)g.D;
-        // a: an accumulator element (FP32; INT32 for INT8, kept exact)
-        auto out_val = [&](auto a, CT c) -> OutT {
+        // a: an accumulator element (FP32; INT32 for INT8, kept exact); j:
+        // the 32-column block of the wave tile it belongs to
+        auto out_val = [&](auto a, CT c, int j) -> OutT {
             if constexpr (KD == Kind::FP8) return f32_to_bf16_bits(a);
-            else if constexpr (std::is_same<OutT, uint16_t>::value) {
+            else if constexpr (BA) {
+                // v = acc + C, v = v + bias, v = act(v) (none or ReLU): FP32
+                // steps, then one rounding to the output format
+                float v = a + c;
+                v = v + bcol[j];
+                v = act_apply<ACT>(v);
+                if constexpr (!std::is_same<OutT, uint16_t>::value) return v;
+                else if constexpr (KD == Kind::F16) return f32_to_f16_bits(v);
+                else return f32_to_bf16_bits(v);
+            } else if constexpr (std::is_same<OutT, uint16_t>::value) {
                 if constexpr (KD == Kind::F16) return f32_to_f16_bits(a + c);
                 else return f32_to_bf16_bits(a + c);
             } else return (OutT)(a + c);
@@ -943,7 +959,7 @@ void gemm_kernel(GemmArgs g) {
                         const uint32_t row = i * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
                         const uint32_t col = j * 32 + lrow;
                         *(MPDT_LDS uint16_t*)(reg + row * (C::WN * 2) + col * 2) =
-                            out_val(acc[i][j][r], cv[r]);
+                            out_val(acc[i][j][r], cv[r], j);
                     }
                 };
                 CT cbuf[2][16];
@@ -989,7 +1005,7 @@ void gemm_kernel(GemmArgs g) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     dp[(int64_t)(8 * (r >> 2) + (r & 3)) * g.ldd] =
-                        out_val(acc[t / C::TN][t % C::TN][r], cv[r]);
+                        out_val(acc[t / C::TN][t % C::TN][r], cv[r], t % C::TN);
             };
             if (KD != Kind::FP8 && Cp) {
                 CT cbuf[2][16];
@@ -1031,7 +1047,7 @@ void gemm_kernel(GemmArgs g) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     if (ok(t, r))
-                        Dp[at(t, r, g.ldd)] = out_val(acc[t / C::TN][t % C::TN][r], cbuf[t & 1][r]);
+                        Dp[at(t, r, g.ldd)] = out_val(acc[t / C::TN][t % C::TN][r], cbuf[t & 1][r], t % C::TN);
             });
         }
     };
@@ -1053,7 +1069,13 @@ void gemm_kernel(GemmArgs g) {
             }
         });
     }
-    if constexpr (!BA) epilogue(OutTag{});   // (the fused epilogue stored D above)
+    if constexpr (BA) {
+        if (g.act == ACT_RELU) epilogue(OutTag{}, std::integral_constant<int, ACT_RELU>{});   // uniform
+        else if (g.act == ACT_NONE) epilogue(OutTag{}, std::integral_constant<int, ACT_NONE>{});
+        // (GELU and SiLU stored D above)
+    } else {
+        epilogue(OutTag{}, std::integral_constant<int, ACT_NONE>{});
+    }
 #ifdef MPDT_CLOCK_STAMPS
     __builtin_amdgcn_s_waitcnt(0);   // this wave's stores have completed
     MPDT_STAMP(2)
