@@ -47,20 +47,29 @@ def _run(cmd, cwd):
     subprocess.run(cmd, cwd=cwd, check=True)
 
 
-def _link(out: str, sources, extra_flags=()) -> str:
-    """Compile each source to an object (in parallel, with its own options),
-    then link them into the shared library `out`."""
-    objdir = os.path.join(CSRC, "_build", os.path.basename(out))
-    os.makedirs(objdir, exist_ok=True)
-    objs = [os.path.join(objdir, s + ".o") for s in sources]
-    cmds = [[hipcc(), *HIP_FLAGS, *SOURCE_FLAGS.get(s, []), *extra_flags, "-c",
-             os.path.join(CSRC, s), "-o", o] for s, o in zip(sources, objs)]
+def _build_libs(specs):
+    """specs: (out, sources, extra_flags) per shared library.  Every source of
+    every library is compiled to its own object in one parallel pool (each
+    with its own options), then each library is linked."""
+    cmds, links = [], []
+    for out, sources, extra_flags in specs:
+        objdir = os.path.join(CSRC, "_build", os.path.basename(out))
+        os.makedirs(objdir, exist_ok=True)
+        objs = [os.path.join(objdir, s + ".o") for s in sources]
+        cmds += [[hipcc(), *HIP_FLAGS, *SOURCE_FLAGS.get(s, []), *extra_flags, "-c",
+                  os.path.join(CSRC, s), "-o", o] for s, o in zip(sources, objs)]
+        links.append((out, objs))
     with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1, 8)) as ex:
         list(ex.map(lambda c: _run(c, CSRC), cmds))
-    tmp = out + ".tmp"
-    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], cwd=CSRC)
-    os.replace(tmp, out)
-    return out
+    for out, objs in links:
+        tmp = out + ".tmp"
+        _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], cwd=CSRC)
+        os.replace(tmp, out)
+    return [out for out, _ in links]
+
+
+def _link(out: str, sources, extra_flags=()) -> str:
+    return _build_libs([(out, sources, extra_flags)])[0]
 
 
 def build_library(extra_flags=()) -> str:
@@ -93,9 +102,9 @@ def build_oracle() -> str:
 
 def build_all():
     build_oracle()
-    build_library()
-    build_probes()
-    build_clock_library()
+    # the three HIP libraries in one compile pool
+    _build_libs([(LIB, HIP_SOURCES, ()), (PROBE_LIB, ["probes.hip"], ()),
+                 (CLOCK_LIB, HIP_SOURCES, ("-DMPDT_CLOCK_STAMPS",))])
 
 
 if __name__ == "__main__":
