@@ -1088,6 +1088,190 @@ void gemm_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
+// The narrow strip at the N edge.  When N is a little over a multiple of the
+// 256-column tile (N % 256 in 1..16), the last tile column computes a whole
+// tile's K loop for at most 16 useful columns -- on 8191 x 8193 x 4099 one
+// extra round of workgroups, a fifth of the run.  Those columns go to this
+// kernel instead: a workgroup takes 16 rows (4 per wave) and stages the
+// strip of B (K rows x the strip's columns, as FP32, zero past the strip) in
+// LDS chunk by chunk; each lane walks K in 16-byte pieces of its rows of A
+// and keeps FP32 sums for every row and strip column (FMAs: each product of
+// two FP16 / BF16 values is exact in FP32); the wave then adds its lanes'
+// sums, and D = acc + C (+ bias, activation) is written as by the tiles.
+// ---------------------------------------------------------------------------
+constexpr int NSTRIP = 16;        // widest strip taken here
+constexpr int STRIP_ROWS = 16;    // rows per workgroup (4 per wave)
+
+template <Kind KD>
+__device__ __forceinline__ float half_bits_to_f32(uint32_t b) {
+    if constexpr (KD == Kind::F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+    else return __uint_as_float(b << 16);
+}
+
+template <Kind KD, bool OUT16, bool BA, int NC>
+__global__ __launch_bounds__(256) void gemm_nstrip_kernel(GemmArgs g, int j0) {
+    static_assert(KD == Kind::F16 || KD == Kind::BF16, "16-bit inputs");
+    // a 64 KiB chunk of the strip; each lane loads all of its 16-byte A
+    // pieces of a chunk (PIECES per row) before the first use
+    constexpr int STRIP_KC = 16384 / NC;
+    constexpr int PIECES = STRIP_KC / 512;
+    // row k of the strip starts at float k NC + 4 (k / 8): a lane reads the
+    // rows 8 l + e, and the 16 bytes skipped every 8 rows put consecutive
+    // lanes on consecutive 16-byte bank groups (conflict-free LDS reads)
+    __shared__ __attribute__((aligned(16))) float bs[STRIP_KC * NC + STRIP_KC / 2];
+    auto brow_lds = [&](int k) { return &bs[k * NC + (k >> 3) * 4]; };
+    const int r = g.N - j0;                       // strip columns, 1..NC
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int i0 = blockIdx.x * STRIP_ROWS + wave * 4;
+    const int64_t K = g.K;
+    const uint16_t* const B = (const uint16_t*)g.B;
+    const int64_t ldb = g.ldb_b / 2;
+    const char* arow[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) arow[q] = g.A + (int64_t)(i0 + q < g.M ? i0 + q : 0) * g.lda_b;
+    float acc[4][NC];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[q][c] = 0.0f;
+    for (int64_t k0 = 0; k0 < K; k0 += STRIP_KC) {
+        const int kc = (int)(K - k0 < STRIP_KC ? K - k0 : STRIP_KC);
+        __syncthreads();                          // the previous chunk's reads are done
+        // 8 K elements per piece and row, all in flight while the strip of B
+        // is staged: a full chunk takes plain 16-byte loads (rows need only
+        // element alignment: a 16-byte load from any byte address returns
+        // the bytes there); the last, partial chunk bounded ones (zeros past
+        // K), only for the pieces that reach into it
+        u32x4 av[PIECES][4];
+        if (kc == STRIP_KC) {
+#pragma unroll
+            for (int pc = 0; pc < PIECES; ++pc)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    av[pc][q] = *reinterpret_cast<const u32x4*>(arow[q] + (k0 + 8 * lane + 512 * pc) * 2);
+        } else {
+#pragma unroll
+            for (int pc = 0; pc < PIECES; ++pc)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    av[pc][q] = (512 * pc < kc)
+                                    ? load16_row<false>(arow[q] + (k0 + 8 * lane + 512 * pc) * 2, arow[q] + K * 2)
+                                    : u32x4{0u, 0u, 0u, 0u};
+        }
+        // the strip of B as FP32, zeros past K and past the strip: a lane
+        // takes a row (rows past K read row k0) with one load of NC
+        // elements, which on every row but B's last stays inside B; the
+        // last row is read element by element
+#pragma unroll
+        for (int k = tid; k < STRIP_KC; k += 256) {
+            const int64_t kr = k0 + (k < kc ? k : 0);
+            const uint16_t* const brow = B + kr * ldb + j0;
+            uint32_t w[NC / 2];
+            if (kr != K - 1) {
+                if constexpr (NC == 4) {
+                    const uint2 x = *reinterpret_cast<const uint2*>(brow);
+                    w[0] = x.x;
+                    w[1] = x.y;
+                } else {
+#pragma unroll
+                    for (int h = 0; h < NC / 8; ++h) {
+                        const u32x4 x = reinterpret_cast<const u32x4*>(brow)[h];
+                        w[4 * h] = x[0];
+                        w[4 * h + 1] = x[1];
+                        w[4 * h + 2] = x[2];
+                        w[4 * h + 3] = x[3];
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < NC / 2; ++c)
+                    w[c] = (uint32_t)brow[2 * c < r ? 2 * c : r - 1] |
+                           ((uint32_t)brow[2 * c + 1 < r ? 2 * c + 1 : r - 1] << 16);
+            }
+            float v[NC];
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const float x = half_bits_to_f32<KD>((w[c >> 1] >> (16 * (c & 1))) & 0xffffu);
+                v[c] = (k < kc && c < r) ? x : 0.0f;
+            }
+#pragma unroll
+            for (int c4 = 0; c4 < NC / 4; ++c4)
+                reinterpret_cast<float4*>(brow_lds(k))[c4] =
+                    float4{v[4 * c4], v[4 * c4 + 1], v[4 * c4 + 2], v[4 * c4 + 3]};
+        }
+        __syncthreads();
+#pragma unroll
+        for (int pc = 0; pc < PIECES; ++pc) {
+            if (512 * pc >= kc) break;            // (the partial chunk's empty pieces)
+            const int kk = 8 * lane + 512 * pc;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float b[NC];
+#pragma unroll
+                for (int c4 = 0; c4 < NC / 4; ++c4) {
+                    const float4 v = reinterpret_cast<const float4*>(brow_lds(kk + e))[c4];
+                    b[4 * c4] = v.x;
+                    b[4 * c4 + 1] = v.y;
+                    b[4 * c4 + 2] = v.z;
+                    b[4 * c4 + 3] = v.w;
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float a = half_bits_to_f32<KD>((av[pc][q][e >> 1] >> (16 * (e & 1))) & 0xffffu);
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) acc[q][c] = fmaf(a, b[c], acc[q][c]);
+                }
+            }
+        }
+    }
+    // the wave's 64 partial sums of every (row, column)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int m = 32; m >= 1; m >>= 1) acc[q][c] += __shfl_xor(acc[q][c], m, 64);
+    // lane c writes column c of the wave's rows: D = acc + C, then the bias and
+    // the activation of the fused epilogue, one rounding to the output format
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int i = i0 + q;
+        if (i >= g.M) break;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            if (lane != c || c >= r) continue;
+            const int j = j0 + c;
+            float v = acc[q][c] + (g.C ? ((const float*)g.C)[(int64_t)i * g.ldc + j] : 0.0f);
+            if constexpr (BA) {
+                if (g.bias) v = v + g.bias[j];
+                switch (g.act) {
+                    case ACT_RELU: v = act_apply<ACT_RELU>(v); break;
+                    case ACT_GELU: v = act_apply<ACT_GELU>(v); break;
+                    case ACT_SILU: v = act_apply<ACT_SILU>(v); break;
+                    default: break;
+                }
+            }
+            if constexpr (OUT16) {
+                ((uint16_t*)g.D)[(int64_t)i * g.ldd + j] =
+                    KD == Kind::F16 ? f32_to_f16_bits(v) : f32_to_bf16_bits(v);
+            } else {
+                ((float*)g.D)[(int64_t)i * g.ldd + j] = v;
+            }
+        }
+    }
+}
+
+template <Kind KD, bool OUT16, bool BA>
+static hipError_t launch_nstrip(const GemmArgs& a, int j0, hipStream_t stream) {
+    const dim3 grid((unsigned)((a.M + STRIP_ROWS - 1) / STRIP_ROWS)), block(256);
+    const int r = a.N - j0;
+    if (r <= 4) hipLaunchKernelGGL((gemm_nstrip_kernel<KD, OUT16, BA, 4>), grid, block, 0, stream, a, j0);
+    else if (r <= 8) hipLaunchKernelGGL((gemm_nstrip_kernel<KD, OUT16, BA, 8>), grid, block, 0, stream, a, j0);
+    else hipLaunchKernelGGL((gemm_nstrip_kernel<KD, OUT16, BA, 16>), grid, block, 0, stream, a, j0);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Host-side launchers (called by the C ABI after validation).
 // ---------------------------------------------------------------------------
 template <Kind KD, class C, bool ALIGNED, bool BA, int F8 = 0>
@@ -1127,6 +1311,19 @@ static hipError_t launch_general(GemmArgs a, bool aligned, int int_tm, int int_t
 template <Kind KD, class C1, class C8, bool BA = false>
 static hipError_t launch_mma(const GemmArgs& a0, bool aligned, hipStream_t stream) {
     static_assert(C1::BM == C8::BM && C1::BN == C8::BN, "one tile grid for both kernels");
+    if constexpr (KD == Kind::F16 || KD == Kind::BF16) {
+        // a narrow last tile column: the tiles take the whole 256-column
+        // blocks, the strip kernel the rest (see gemm_nstrip_kernel)
+        const int rem = a0.N % C1::BN;
+        if (a0.N > C1::BN && rem >= 1 && rem <= NSTRIP) {
+            GemmArgs am = a0;
+            am.N = a0.N - rem;
+            const hipError_t e = launch_mma<KD, C1, C8, BA>(am, aligned, stream);
+            if (e != hipSuccess) return e;
+            return a0.out16 ? launch_nstrip<KD, true, BA>(a0, am.N, stream)
+                            : launch_nstrip<KD, false, BA>(a0, am.N, stream);
+        }
+    }
     const int64_t kb = (int64_t)a0.K * C1::ES;
     // (the direct loads' scalar offsets take a piece's instruction offset back
     // off its row offset, which needs rows of at least one B tile row: ldb >=

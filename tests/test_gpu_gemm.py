@@ -317,3 +317,36 @@ def test_fp8_k_zero(gpu_ok):
                                 torch.zeros((0, 50), dtype=torch.uint8, device=gpu_ok),
                                 torch.zeros((1, 1), device=gpu_ok))
     assert not host(D).any()
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("M,N,K", [(300, 257, 200), (513, 520, 300), (1000, 784, 4099), (260, 265, 1),
+                                   (17, 512 + 13, 1500), (2049, 1024 + 16, 700)])
+def test_narrow_last_column_strip(gpu_ok, fmt, M, N, K):
+    """N a few columns past a multiple of 256: the tiles take the whole
+    256-column blocks and the strip kernel the rest.  Integer-valued inputs:
+    bit-exact for FP32 and for 16-bit D, C in place; random inputs: the
+    bound; bias + activation of the fused epilogue on the strip too."""
+    A, B, C = inputs.gemm16_operands(M, N, K, dist="int4", fmt=fmt, seeds=(M, N, K))
+    C = np.round(C * 8).astype(np.float32)                # integer-valued C
+    gemm = mp.gemm_f16 if fmt == "f16" else mp.gemm_bf16
+    tc = dev(C)
+    gemm(dev(A), dev(B), tc, out=tc)                       # in place
+    R, _ = (oracle.gemm_f16 if fmt == "f16" else oracle.gemm_bf16)(A, B, C)
+    assert np.array_equal(host(tc), R.astype(np.float32)), f"{fmt} {M}x{N}x{K} in place"
+    out16 = mp.gemm_f16_f16out if fmt == "f16" else mp.gemm_bf16_bf16out
+    D16 = host(out16(dev(A), dev(B), dev(C)).view(torch.int16)).view(np.uint16)
+    rnd = oracle.f32_to_f16_rne if fmt == "f16" else oracle.f32_to_bf16_rne
+    assert np.array_equal(D16, rnd(R.astype(np.float32))), f"{fmt} {M}x{N}x{K} 16-bit"
+    A, B, C = inputs.gemm16_operands(M, N, K, dist="normal", fmt=fmt, seeds=(M + 1, N + 1, K + 1))
+    D = host(gemm(dev(A), dev(B), dev(C)))
+    R, S = (oracle.gemm_f16 if fmt == "f16" else oracle.gemm_bf16)(A, B, C)
+    check_fp(D, R, S, 1e-3, f"{fmt} {M}x{N}x{K} strip")
+    bias = inputs.normal_f32((N,), N)
+    ba = mp.gemm_f16_bias_act if fmt == "f16" else mp.gemm_bf16_bias_act
+    for act in (mp.ACT_RELU, mp.ACT_GELU):
+        Dg = host(ba(dev(A), dev(B), dev(C), dev(bias), act))
+        Rg, Sg, Pg = oracle.gemm16_bias_act(fmt, A, B, C, bias, act)
+        err = np.abs(Dg - Rg)
+        bound = 1.13 * (1e-3 * Sg + 1e-6 + 2.0 ** -22 * np.abs(Pg)) + 2.0 ** -20 * (np.abs(Pg) + np.abs(Rg))
+        assert (err <= bound).all(), f"{fmt} {M}x{N}x{K} act {act}"
