@@ -130,15 +130,17 @@ hipError_t launch_gemv_w8a8(const GemvArgs& a, bool aligned, hipStream_t stream)
 //   q[m][o] = clamp(rne(( ... + bias[o]) / s_out), -127, 127)
 // With more than one token the products are a small GEMM, Z = X . W^T, whose
 // operands are both K-contiguous: a 32x32x32 INT8 MFMA takes 32 tokens
-// (rows of X, zero past M) as its A operand and 32 output channels (rows of
-// W) as its B operand, each lane reading 16 consecutive K bytes of one row
-// straight from memory -- no LDS, no transposes.  The weights are streamed
-// exactly once per 32 tokens: a workgroup owns 32 channels, its four waves
-// take interleaved 128-byte slices of K (4 MFMA steps each, so every wave
-// load covers 128 contiguous bytes of each of its 32 rows), then add their
-// partial sums through LDS.  The work stays HBM-bound: the MFMA rate is far
-// above what 32 tokens need, so the rows of the A operand past M cost nothing
-// that matters.
+// (rows of X) as its A operand and 32 output channels (rows of W) as its B
+// operand, each lane holding 16 consecutive K bytes of one row.  The weights
+// are streamed exactly once per 32 tokens: a workgroup owns 32 channels and
+// its four waves load them in long runs (one KiB of one row per load
+// instruction, the access pattern of the one-token kernel; loading the MFMA
+// fragments straight from memory instead touches 32 rows with 32 bytes each
+// per instruction, and streamed about 7 % slower), staged through LDS
+// chunk by chunk; wave w takes a quarter of each chunk's K bytes, and the
+// four partial sums meet in LDS.  The work stays HBM-bound: the MFMA rate
+// is far above what 32 tokens need, so the rows of the A operand past M
+// cost nothing that matters.
 // ---------------------------------------------------------------------------
 constexpr int TOK_WAVES = 4;                   // wavefronts per workgroup
 
@@ -169,72 +171,115 @@ __device__ __forceinline__ void w8a8_epilogue(const W8A8Args& g, const i32x16& a
         }
     }
 }
-constexpr int TOK_GROUP = 8;                   // MFMA steps (32 K bytes each) per wave slice
+constexpr int TOK_CH = 32;                     // output channels per workgroup
+constexpr int TOK_KC = 1024;                   // K bytes per LDS chunk
+constexpr int TOK_PASS = 4;                    // chunks per pass (K = 4096 in one pass)
+constexpr int TOK_PITCH = TOK_KC + 16;         // LDS row pitch: 16 bytes of padding per row
 
-__global__ __launch_bounds__(64 * TOK_WAVES) void gemm_w8a8_kernel(W8A8Args g) {
-    __shared__ int partial[TOK_WAVES - 1][16][64];
+__global__ __launch_bounds__(64 * TOK_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void gemm_w8a8_kernel(W8A8Args g) {
+    // one chunk of the workgroup's 32 weight rows, then the partial sums
+    __shared__ __attribute__((aligned(16))) char wt[TOK_CH * TOK_PITCH];
+    static_assert((TOK_WAVES - 1) * 16 * 64 * 4 <= TOK_CH * TOK_PITCH, "partial sums fit");
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int o0 = blockIdx.x * 32;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int o0 = blockIdx.x * TOK_CH;
     const int r32 = lane & 31;                 // token row (A) / channel (B) of this lane
     const int half = lane >> 5;                // which 16 bytes of a 32-byte K step
     const int64_t K = g.K;
-    const int64_t kslice = 32 * TOK_GROUP;     // K bytes per wave slice
+    constexpr int RPW = TOK_CH / TOK_WAVES;    // weight rows each wave loads
+    MPDT_LDS char* const lds = lds_cast(wt);
 
-    // this lane's rows: token r32 of X, channel o0 + r32 of W; a lane past M
-    // or N reads row 0 instead and zeroes what it read, so the loads of a full
-    // slice carry no branches (and stay in flight together)
-    const bool xrow = r32 < g.M;
-    const bool wrow = o0 + r32 < g.N;
-    const char* xp = (const char*)g.X + (int64_t)(xrow ? r32 : 0) * g.ldx;
-    const char* wp = (const char*)g.W + (int64_t)(wrow ? o0 + r32 : 0) * g.ldw;
-    const uint32_t xkeep = xrow ? ~0u : 0u, wkeep = wrow ? ~0u : 0u;
+    // the rows this wave loads (a row past N reads row N - 1: its channel's
+    // sums are never written); the token row of this lane (a row past M
+    // reads row 0: only outputs past M see it, and none is written)
+    const char* wrow[RPW];
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+        const int o = o0 + wave * RPW + j;
+        wrow[j] = (const char*)g.W + (int64_t)(o < g.N ? o : g.N - 1) * g.ldw;
+    }
+    const char* xp = (const char*)g.X + (int64_t)(r32 < g.M ? r32 : 0) * g.ldx;
 
     i32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0;
-    auto mma = [&](const u32x4 (&xv)[TOK_GROUP], const u32x4 (&wv)[TOK_GROUP]) {
+
+    // Passes of TOK_PASS chunks.  Each wave first issues the loads of its
+    // rows for the whole pass -- every instruction one contiguous KiB of one
+    // row, as in the one-token kernel, so a resident grid keeps the weight
+    // stream in flight -- then, chunk by chunk, the workgroup writes the
+    // chunk to LDS and wave w takes its K bytes 256 w .. 256 w + 255 in
+    // eight MFMA steps (operands: 16 bytes of one channel from LDS, 16
+    // bytes of one token from memory, loaded while the chunk before is
+    // written and synchronised).  A pass inside
+    // K takes plain 16-byte loads (any byte alignment is fine for them); the
+    // last, partial one bounded loads (bytes past K read as zero).
+    for (int64_t p0 = 0; p0 < K; p0 += (int64_t)TOK_PASS * TOK_KC) {
+        const bool full = p0 + (int64_t)TOK_PASS * TOK_KC <= K;
+        auto load_x = [&](int c, u32x4 (&xv)[8]) {
 #pragma unroll
-        for (int s = 0; s < TOK_GROUP; ++s)
-            acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, xv[s]),
-                                                        __builtin_bit_cast(i32x4, wv[s]), acc, 0, 0, 0);
-    };
-    int64_t k0 = (int64_t)wave * kslice;
-    // full slices: plain 16-byte loads (any byte alignment is fine for them)
-    for (; k0 + kslice <= K; k0 += (int64_t)TOK_WAVES * kslice) {
-        u32x4 wv[TOK_GROUP], xv[TOK_GROUP];
+            for (int s = 0; s < 8; ++s) {
+                const int64_t off = p0 + c * TOK_KC + wave * 256 + 32 * s + 16 * half;
+                xv[s] = full ? *reinterpret_cast<const u32x4*>(xp + off) : load16_row<false>(xp + off, xp + K);
+            }
+        };
+        // write chunk c of this wave's rows to LDS, then its eight MFMA steps
+        auto chunk = [&](int c, const u32x4 (&w)[RPW], const u32x4 (&xv)[8]) {
+            __syncthreads();                       // the previous chunk's reads are done
 #pragma unroll
-        for (int s = 0; s < TOK_GROUP; ++s) {
-            const int64_t off = k0 + 32 * s + 16 * half;
-            wv[s] = *reinterpret_cast<const u32x4*>(wp + off) & wkeep;
-            xv[s] = *reinterpret_cast<const u32x4*>(xp + off) & xkeep;
+            for (int j = 0; j < RPW; ++j)
+                lds_store16(lds, (uint32_t)((wave * RPW + j) * TOK_PITCH + 16 * lane), w[j]);
+            __syncthreads();
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const u32x4 b = lds_load16(lds, (uint32_t)(r32 * TOK_PITCH + wave * 256 + 32 * s + 16 * half));
+                acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, xv[s]),
+                                                            __builtin_bit_cast(i32x4, b), acc, 0, 0, 0);
+            }
+        };
+        u32x4 xv[8];
+        if (full) {
+            u32x4 wv[TOK_PASS][RPW];
+#pragma unroll
+            for (int c = 0; c < TOK_PASS; ++c)
+#pragma unroll
+                for (int j = 0; j < RPW; ++j)
+                    wv[c][j] = *reinterpret_cast<const u32x4*>(wrow[j] + p0 + c * TOK_KC + 16 * lane);
+            load_x(0, xv);
+#pragma unroll
+            for (int c = 0; c < TOK_PASS; ++c) {
+                chunk(c, wv[c], xv);
+                // the next chunk's tokens, once these MFMAs have read theirs
+                if (c + 1 < TOK_PASS) load_x(c + 1, xv);
+            }
+        } else {
+            // the last pass: bounded loads chunk by chunk (chunks past K skipped)
+            for (int c = 0; c < TOK_PASS && p0 + c * TOK_KC < K; ++c) {
+                u32x4 w[RPW];
+#pragma unroll
+                for (int j = 0; j < RPW; ++j)
+                    w[j] = load16_row<false>(wrow[j] + p0 + c * TOK_KC + 16 * lane, wrow[j] + K);
+                load_x(c, xv);
+                chunk(c, w, xv);
+            }
         }
-        mma(xv, wv);
-    }
-    // the one partial slice (K past it reads as zero; bounded loads)
-    if (k0 < K) {
-        u32x4 wv[TOK_GROUP], xv[TOK_GROUP];
-#pragma unroll
-        for (int s = 0; s < TOK_GROUP; ++s) {
-            const int64_t off = k0 + 32 * s + 16 * half;
-            wv[s] = load16_row<false>(wp + off, wp + K) & wkeep;
-            xv[s] = load16_row<false>(xp + off, xp + K) & xkeep;
-        }
-        mma(xv, wv);
     }
 
-    // sum the four waves' partial products (exact INT32)
+    // sum the four waves' partial products (exact INT32) through the chunk
+    // buffer, once every wave is done reading it
+    __syncthreads();
+    int* const partial = reinterpret_cast<int*>(wt);     // [3][16][64]
     if (wave > 0) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) partial[wave - 1][r][lane] = acc[r];
+        for (int r = 0; r < 16; ++r) partial[((wave - 1) * 16 + r) * 64 + lane] = acc[r];
     }
     __syncthreads();
     if (wave != 0) return;
 #pragma unroll
     for (int w = 0; w < TOK_WAVES - 1; ++w)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] += partial[w][r][lane];
+        for (int r = 0; r < 16; ++r) acc[r] += partial[(w * 16 + r) * 64 + lane];
 
     w8a8_epilogue(g, acc, o0 + r32, half);
 }
@@ -417,7 +462,7 @@ hipError_t launch_gemm_w8a8(const W8A8Args& a0, bool /*aligned*/, hipStream_t st
             hipLaunchKernelGGL(gemm_w8a8_kn_kernel, dim3((unsigned)(8 * ((nblk + 7) / 8))), dim3(256), 0,
                                stream, a);
         } else {
-            dim3 grid((unsigned)((a.N + 31) / 32)), block(64 * TOK_WAVES);
+            dim3 grid((unsigned)((a.N + TOK_CH - 1) / TOK_CH)), block(64 * TOK_WAVES);
             hipLaunchKernelGGL(gemm_w8a8_kernel, grid, block, 0, stream, a);
         }
         const hipError_t e = hipGetLastError();
