@@ -5,7 +5,7 @@ columns and the 256-boundaries of the workgroup tiles):
 
   * BF16 4096 x 4096 x 4096, N(0,1) inputs, FP32 C;
   * FP16 8191 x 8193 x 4099 with tight leading dimensions and C = 0 (and
-    C = NULL giving identical bits);
+    C = NULL giving identical bits), with every row of the last column;
   * FP8 E4M3 block-scaled 4096 x 7168 x 7168, BF16 output;
   * INT8 4096 x 4096 x 4096, bit-exact.
 (The full 4096 x 14336 W8A8 layer is compared in full in test_gpu_gemv.)"""
@@ -53,6 +53,9 @@ def test_f16_ragged_8191_8193_4099(gpu_ok):
     del Dn
     D = host(D0)
     ii, jj = sample_positions(M, N, seed=1)
+    # the whole last column: the N-edge strip kernel writes it
+    ii = np.concatenate([ii, np.arange(M)])
+    jj = np.concatenate([jj, np.full(M, N - 1)])
     R, S = oracle.gemm_f16_at(A, B, C, ii, jj)
     check_fp(D[ii, jj], R, S, 1e-5, "f16 ragged")
 

@@ -344,9 +344,14 @@ def test_narrow_last_column_strip(gpu_ok, fmt, M, N, K):
     check_fp(D, R, S, 1e-3, f"{fmt} {M}x{N}x{K} strip")
     bias = inputs.normal_f32((N,), N)
     ba = mp.gemm_f16_bias_act if fmt == "f16" else mp.gemm_bf16_bias_act
+    dec = oracle.f16_to_f64 if fmt == "f16" else oracle.bf16_to_f64
+    ulp = 2.0 ** -11 if fmt == "f16" else 2.0 ** -8
     for act in (mp.ACT_RELU, mp.ACT_GELU):
-        Dg = host(ba(dev(A), dev(B), dev(C), dev(bias), act))
         Rg, Sg, Pg = oracle.gemm16_bias_act(fmt, A, B, C, bias, act)
-        err = np.abs(Dg - Rg)
         bound = 1.13 * (1e-3 * Sg + 1e-6 + 2.0 ** -22 * np.abs(Pg)) + 2.0 ** -20 * (np.abs(Pg) + np.abs(Rg))
-        assert (err <= bound).all(), f"{fmt} {M}x{N}x{K} act {act}"
+        Dg = host(ba(dev(A), dev(B), dev(C), dev(bias), act))
+        assert (np.abs(Dg - Rg) <= bound).all(), f"{fmt} {M}x{N}x{K} act {act}"
+        # 16-bit D: the same bound plus half an ulp of the output format
+        Dh = dec(host(ba(dev(A), dev(B), dev(C), dev(bias), act, d16=True).view(torch.int16)).view(np.uint16))
+        bound16 = bound + ulp * np.maximum(np.abs(Rg), np.abs(Dh)) + 2.0 ** -25
+        assert (np.abs(Dh - Rg) <= bound16).all(), f"{fmt} {M}x{N}x{K} act {act} 16-bit"
