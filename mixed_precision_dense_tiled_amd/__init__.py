@@ -122,6 +122,9 @@ def _mat(t: torch.Tensor, itemsize: int, name: str):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
     rows, cols = t.shape
+    if rows == 0 or cols == 0:
+        # an empty operand: nothing is read or written through it
+        return t.data_ptr(), max(cols, 1)
     if cols > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} must have unit stride along its rows")
     ld = t.stride(0) if rows > 1 else max(cols, 1)

@@ -355,3 +355,40 @@ def test_narrow_last_column_strip(gpu_ok, fmt, M, N, K):
         Dh = dec(host(ba(dev(A), dev(B), dev(C), dev(bias), act, d16=True).view(torch.int16)).view(np.uint16))
         bound16 = bound + ulp * np.maximum(np.abs(Rg), np.abs(Dh)) + 2.0 ** -25
         assert (np.abs(Dh - Rg) <= bound16).all(), f"{fmt} {M}x{N}x{K} act {act} 16-bit"
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("M,N,K,pad", [(64, 64, 64, 0), (1, 1, 1, 0), (256, 256, 256, 0), (33, 200, 17, 3),
+                                       (200, 33, 255, 1), (5, 7, 16, 0), (64, 64, 0, 0), (257, 64, 64, 0)])
+def test_small_problems(gpu_ok, fmt, M, N, K, pad):
+    """M, N and K at most 256 take the small-problem kernel (one round trip
+    of loads into the MFMA fragments); 257 rows take the tiles.  Integer-
+    valued inputs: bit-exact FP32 D in place and 16-bit D, A rows not
+    16-byte aligned when padded; random inputs: the bound, also through the
+    fused bias + GELU epilogue with 16-bit D."""
+    A, B, C = inputs.gemm16_operands(M, N, K, dist="int4", fmt=fmt, seeds=(M + 7, N + 7, K + 7))
+    C = np.round(C * 8).astype(np.float32)
+    gemm = mp.gemm_f16 if fmt == "f16" else mp.gemm_bf16
+    ref = oracle.gemm_f16 if fmt == "f16" else oracle.gemm_bf16
+    tA = dev(A, K + pad, pad=0x7C00) if pad else dev(A)     # padding: never read
+    tc = dev(C)
+    gemm(tA, dev(B), tc, out=tc)
+    R, _ = ref(A, B, C)
+    assert np.array_equal(host(tc), R.astype(np.float32)), f"{fmt} {M}x{N}x{K} in place"
+    out16 = mp.gemm_f16_f16out if fmt == "f16" else mp.gemm_bf16_bf16out
+    rnd = oracle.f32_to_f16_rne if fmt == "f16" else oracle.f32_to_bf16_rne
+    D16 = host(out16(tA, dev(B), dev(C)).view(torch.int16)).view(np.uint16)
+    assert np.array_equal(D16, rnd(R.astype(np.float32))), f"{fmt} {M}x{N}x{K} 16-bit"
+    A, B, C = inputs.gemm16_operands(M, N, K, dist="normal", fmt=fmt, seeds=(M + 8, N + 8, K + 8))
+    R, S = ref(A, B, C)
+    check_fp(host(gemm(dev(A), dev(B), dev(C))), R, S, 1e-3, f"{fmt} {M}x{N}x{K} small")
+    check_fp(host(gemm(dev(A), dev(B), None)), R - C, S, 1e-3, f"{fmt} {M}x{N}x{K} no C")
+    bias = inputs.normal_f32((N,), N + 9)
+    ba = mp.gemm_f16_bias_act if fmt == "f16" else mp.gemm_bf16_bias_act
+    dec = oracle.f16_to_f64 if fmt == "f16" else oracle.bf16_to_f64
+    ulp = 2.0 ** -11 if fmt == "f16" else 2.0 ** -8
+    Rg, Sg, Pg = oracle.gemm16_bias_act(fmt, A, B, C, bias, mp.ACT_GELU)
+    Dh = dec(host(ba(dev(A), dev(B), dev(C), dev(bias), mp.ACT_GELU, d16=True).view(torch.int16)).view(np.uint16))
+    bound = (1.13 * (1e-3 * Sg + 1e-6 + 2.0 ** -22 * np.abs(Pg)) + 2.0 ** -20 * (np.abs(Pg) + np.abs(Rg))
+             + ulp * np.maximum(np.abs(Rg), np.abs(Dh)) + 2.0 ** -25)
+    assert (np.abs(Dh - Rg) <= bound).all(), f"{fmt} {M}x{N}x{K} bias + GELU 16-bit"
