@@ -1273,78 +1273,94 @@ static hipError_t launch_nstrip(const GemmArgs& a, int j0, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
-// Small FP16 / BF16 problems (M, N and K at most 256): the tiled kernels'
+// Small FP16 / BF16 / INT8 problems (M, N and K at most 256): the tiled kernels'
 // fixed costs -- LDS staging, barriers, a 256 x 256 tile for a few rows --
 // set the time there, which is then a chain of memory round trips.  This
 // kernel makes it one: a workgroup of four waves takes a 64 x 64 block of D,
 // each wave a 32 x 32 block, and every lane issues all of its operand loads
 // for the whole of K at once, straight into the MFMA fragments (A: 16 bytes
-// of one row per 32x32x16 step; B: 8 elements of one column, element
-// loads), then runs at most 16 MFMAs and the epilogue of the tiled kernels
-// (D = acc + C, then the bias and the activation, one rounding for 16-bit D).
-// Indices past M, N or K are clamped into the operands and their values
-// replaced by zero, so no load is guarded by a branch.
+// of one row per 32x32x16 or 32x32x32 step; B: the same K positions of one
+// column, element loads), then runs at most 16 (INT8: 8) MFMAs and the
+// epilogue of the tiled kernels (D = acc + C, then the bias and the
+// activation, one rounding for 16-bit D; INT8 exact in INT32).  Indices
+// past M, N or K are clamped into the operands and their values replaced by
+// zero, so no load is guarded by a branch.
 // ---------------------------------------------------------------------------
 constexpr int SMALL_MAX = 256;     // largest M, N and K taken here
 
 template <Kind KD, bool OUT16, bool BA>
 __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs g) {
-    static_assert(KD == Kind::F16 || KD == Kind::BF16, "16-bit inputs");
+    static_assert(KD == Kind::F16 || KD == Kind::BF16 || KD == Kind::I8, "16-bit or INT8 inputs");
+    static_assert(KD != Kind::I8 || (!OUT16 && !BA), "INT8: INT32 D, no fused epilogue");
     using F = Fmt<KD>;
-    constexpr int STEPS = SMALL_MAX / 16;
+    using E = typename std::conditional<KD == Kind::I8, uint8_t, uint16_t>::type;   // element bits
+    using CT = typename std::conditional<KD == Kind::I8, int32_t, float>::type;     // C and D
+    constexpr int EPL = 16 / (int)sizeof(E);          // K elements per lane and step
+    constexpr int KSTEP = 2 * EPL;                    // K elements per MFMA step
+    constexpr int PER_WORD = 4 / (int)sizeof(E);
+    constexpr int STEPS = SMALL_MAX / KSTEP;
+    constexpr uint32_t EMASK = KD == Kind::I8 ? 0xffu : 0xffffu;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lrow = lane & 31, lhalf = lane >> 5;
     const int i0 = blockIdx.y * 64 + (wave >> 1) * 32;    // the wave's 32 x 32 block
     const int j0 = blockIdx.x * 64 + (wave & 1) * 32;
     const int K = g.K;
     const int ia = i0 + lrow, jb = j0 + lrow;             // this lane's A row, B column
-    const uint16_t* const arow = (const uint16_t*)(g.A + (int64_t)(ia < g.M ? ia : g.M - 1) * g.lda_b);
-    const uint16_t* const bcol = (const uint16_t*)g.B + (jb < g.N ? jb : g.N - 1);
-    const int64_t ldb = g.ldb_b / 2;
-    const uint32_t amask = ia < g.M ? ~0u : 0u, bmask = jb < g.N ? 0xffffu : 0u;
+    const E* const arow = (const E*)(g.A + (int64_t)(ia < g.M ? ia : g.M - 1) * g.lda_b);
+    const E* const bcol = (const E*)g.B + (jb < g.N ? jb : g.N - 1);
+    const int64_t ldb = g.ldb_b / (int64_t)sizeof(E);
+    const uint32_t amask = ia < g.M ? ~0u : 0u, bmask = jb < g.N ? EMASK : 0u;
 
-    // step s covers K elements 16 s .. 16 s + 15; this lane's eight are
-    // 16 s + 8 lhalf + e
+    // step s covers K elements KSTEP s .. KSTEP s + KSTEP - 1; this lane's
+    // EPL are KSTEP s + EPL lhalf + e
     u32x4 av[STEPS], bv[STEPS];
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) {
-        const int k = 16 * s + 8 * lhalf;
+        const int k = KSTEP * s + EPL * lhalf;
         av[s] = bv[s] = u32x4{0u, 0u, 0u, 0u};
-        if (16 * s >= K) continue;
-        if (16 * s + 16 <= K) {
+        if (KSTEP * s >= K) continue;
+        if (KSTEP * s + KSTEP <= K) {
             av[s] = *reinterpret_cast<const u32x4*>(arow + k) & amask;
         } else {
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const int k0 = k + 2 * w, k1 = k0 + 1;
-                const uint32_t lo = k0 < K ? arow[k0] : 0u, hi = k1 < K ? arow[k1] : 0u;
-                av[s][w] = (lo | (hi << 16)) & amask;
+                uint32_t word = 0;
+#pragma unroll
+                for (int e = 0; e < PER_WORD; ++e) {
+                    const int ke = k + PER_WORD * w + e;
+                    word |= (ke < K ? (uint32_t)arow[ke] : 0u) << (8 * sizeof(E) * e);
+                }
+                av[s][w] = word & amask;
             }
         }
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            const int k0 = k + 2 * w, k1 = k0 + 1;
-            const uint32_t lo = bcol[(int64_t)(k0 < K ? k0 : K - 1) * ldb] & (k0 < K ? bmask : 0u);
-            const uint32_t hi = bcol[(int64_t)(k1 < K ? k1 : K - 1) * ldb] & (k1 < K ? bmask : 0u);
-            bv[s][w] = lo | (hi << 16);
+            uint32_t word = 0;
+#pragma unroll
+            for (int e = 0; e < PER_WORD; ++e) {
+                const int ke = k + PER_WORD * w + e;
+                const uint32_t x = bcol[(int64_t)(ke < K ? ke : K - 1) * ldb] & (ke < K ? bmask : 0u);
+                word |= x << (8 * sizeof(E) * e);
+            }
+            bv[s][w] = word;
         }
     }
-    f32x16 acc;
+    typename F::Acc acc;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    for (int r = 0; r < 16; ++r) acc[r] = 0;
 #pragma unroll
     for (int s = 0; s < STEPS; ++s)
-        if (16 * s < K) acc = F::mma(av[s], bv[s], acc);
+        if (KSTEP * s < K) acc = F::mma(av[s], bv[s], acc);
 
     // register r of lane l: row 8 (r / 4) + 4 lhalf + r % 4, column lrow
     const int j = jb;
     if (j >= g.N) return;
-    const float* const Cp = (const float*)g.C;
-    float cv[16];
+    const CT* const Cp = (const CT*)g.C;
+    CT cv[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int i = i0 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
-        cv[r] = Cp ? Cp[(int64_t)(i < g.M ? i : g.M - 1) * g.ldc + j] : 0.0f;
+        cv[r] = Cp ? Cp[(int64_t)(i < g.M ? i : g.M - 1) * g.ldc + j] : (CT)0;
     }
     float bj = 0.0f;
     if constexpr (BA) bj = g.bias ? g.bias[j] : 0.0f;
@@ -1352,7 +1368,7 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs g) {
     for (int r = 0; r < 16; ++r) {
         const int i = i0 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
         if (i >= g.M) continue;
-        float v = acc[r] + cv[r];
+        auto v = acc[r] + cv[r];
         if constexpr (BA) {
             if (g.bias) v = v + bj;
             switch (g.act) {
@@ -1365,7 +1381,7 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs g) {
         if constexpr (OUT16) {
             ((uint16_t*)g.D)[(int64_t)i * g.ldd + j] = KD == Kind::F16 ? f32_to_f16_bits(v) : f32_to_bf16_bits(v);
         } else {
-            ((float*)g.D)[(int64_t)i * g.ldd + j] = v;
+            ((CT*)g.D)[(int64_t)i * g.ldd + j] = v;
         }
     }
 }
@@ -1373,8 +1389,12 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs g) {
 template <Kind KD, bool BA>
 static hipError_t launch_small(const GemmArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)((a.N + 63) / 64), (unsigned)((a.M + 63) / 64)), block(256);
-    if (a.out16) hipLaunchKernelGGL((gemm_small_kernel<KD, true, BA>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((gemm_small_kernel<KD, false, BA>), grid, block, 0, stream, a);
+    if constexpr (KD == Kind::I8) {
+        hipLaunchKernelGGL((gemm_small_kernel<KD, false, false>), grid, block, 0, stream, a);
+    } else {
+        if (a.out16) hipLaunchKernelGGL((gemm_small_kernel<KD, true, BA>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((gemm_small_kernel<KD, false, BA>), grid, block, 0, stream, a);
+    }
     return hipGetLastError();
 }
 
@@ -1418,9 +1438,11 @@ static hipError_t launch_general(GemmArgs a, bool aligned, int int_tm, int int_t
 template <Kind KD, class C1, class C8, bool BA = false>
 static hipError_t launch_mma(const GemmArgs& a0, bool aligned, hipStream_t stream) {
     static_assert(C1::BM == C8::BM && C1::BN == C8::BN, "one tile grid for both kernels");
-    if constexpr (KD == Kind::F16 || KD == Kind::BF16) {
+    if constexpr (KD == Kind::F16 || KD == Kind::BF16 || KD == Kind::I8) {
         if (a0.M <= SMALL_MAX && a0.N <= SMALL_MAX && a0.K <= SMALL_MAX)
             return launch_small<KD, BA>(a0, stream);
+    }
+    if constexpr (KD == Kind::F16 || KD == Kind::BF16) {
         // a narrow last tile column: the tiles take the whole 256-column
         // blocks, the strip kernel the rest (see gemm_nstrip_kernel)
         const int rem = a0.N % C1::BN;

@@ -392,3 +392,22 @@ def test_small_problems(gpu_ok, fmt, M, N, K, pad):
     bound = (1.13 * (1e-3 * Sg + 1e-6 + 2.0 ** -22 * np.abs(Pg)) + 2.0 ** -20 * (np.abs(Pg) + np.abs(Rg))
              + ulp * np.maximum(np.abs(Rg), np.abs(Dh)) + 2.0 ** -25)
     assert (np.abs(Dh - Rg) <= bound).all(), f"{fmt} {M}x{N}x{K} bias + GELU 16-bit"
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 64, 64), (256, 256, 256), (1, 1, 1), (33, 200, 33), (200, 17, 255),
+                                   (40, 50, 0), (256, 257, 100)])
+def test_i8_small_problems_bit_exact(gpu_ok, M, N, K):
+    """INT8 problems with M, N and K at most 256 take the small-problem
+    kernel (exact INT32): extremes -128 / 127 over the whole of K, rows not
+    16-byte aligned with guard values in the padding, C NULL, K = 0, K
+    tails; 257 columns take the tiles."""
+    A = np.full((M, K), -128, np.int8)
+    B = np.full((K, N), -128, np.int8)
+    C = inputs.i8_operands(M, N, K, seeds=(M + 1, N + 1, K + 1))[2]
+    D = host(mp.gemm_i8_i32(dev(A), dev(B), dev(C)))
+    assert np.array_equal(D, oracle.gemm_i8_i32(A, B, C)), "extremes"
+    A, B, C = inputs.i8_operands(M, N, K, seeds=(M + 2, N + 2, K + 2))
+    D = host(mp.gemm_i8_i32(dev(A, K + 5, pad=99), dev(B, N + 3, pad=-99), None))
+    assert np.array_equal(D, oracle.gemm_i8_i32(A, B, None)), "unaligned, C NULL"
+    D = host(mp.gemm_i8_i32(dev(A), dev(B), dev(C)))
+    assert np.array_equal(D, oracle.gemm_i8_i32(A, B, C)), "random"
