@@ -131,11 +131,39 @@ def _mat(t: torch.Tensor, itemsize: int, name: str):
     return t.data_ptr(), int(ld)
 
 
+def _shape(t, shape, name):
+    """Raise ValueError unless tensor t (or None) has exactly this shape.
+    The C ABI sees only pointers and leading dimensions, so this is the one
+    place where a buffer too small for the problem can be caught before a
+    kernel reads or writes past it."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _same_device(ref, *ts):
+    for name, t in ts:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, the operands on {ref.device}")
+
+
+def _dims2(t, name):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    return tuple(t.shape)
+
+
+def _cdiv(a, b):
+    return -(-a // b)
+
+
 def _gemm16(fn, A, B, C, out, out_dtype=torch.float32):
-    M, K = A.shape
-    K2, N = B.shape
+    M, K = _dims2(A, "A")
+    K2, N = _dims2(B, "B")
     if K2 != K:
         raise ValueError("inner dimensions differ")
+    _shape(C, (M, N), "C")
+    _shape(out, (M, N), "out")
+    _same_device(A, ("B", B), ("C", C), ("out", out))
     pa, lda = _mat(A, 2, "A")
     pb, ldb = _mat(B, 2, "B")
     pc, ldc = (None, N) if C is None else _mat(C, 4, "C")
@@ -173,10 +201,14 @@ ACT_NONE, ACT_RELU, ACT_GELU, ACT_SILU = 0, 1, 2, 3
 
 
 def _gemm16_bias_act(fn, A, B, C, bias, act, out, out_dtype):
-    M, K = A.shape
-    K2, N = B.shape
+    M, K = _dims2(A, "A")
+    K2, N = _dims2(B, "B")
     if K2 != K:
         raise ValueError("inner dimensions differ")
+    _shape(C, (M, N), "C")
+    _shape(bias, (N,), "bias")
+    _shape(out, (M, N), "out")
+    _same_device(A, ("B", B), ("C", C), ("bias", bias), ("out", out))
     pa, lda = _mat(A, 2, "A")
     pb, ldb = _mat(B, 2, "B")
     pc, ldc = (None, N) if C is None else _mat(C, 4, "C")
@@ -211,8 +243,13 @@ def gemm_bf16_bias_act(A, B, C=None, bias=None, act=ACT_NONE, out=None, d16=Fals
 
 def gemm_i8_i32(A, B, C=None, out=None):
     """D = A . B + C; A [M,K], B [K,N] INT8, C/D [M,N] INT32 (C optional)."""
-    M, K = A.shape
-    N = B.shape[1]
+    M, K = _dims2(A, "A")
+    K2, N = _dims2(B, "B")
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    _shape(C, (M, N), "C")
+    _shape(out, (M, N), "out")
+    _same_device(A, ("B", B), ("C", C), ("out", out))
     pa, lda = _mat(A, 1, "A")
     pb, ldb = _mat(B, 1, "B")
     pc, ldc = (None, N) if C is None else _mat(C, 4, "C")
@@ -224,11 +261,24 @@ def gemm_i8_i32(A, B, C=None, out=None):
     return out
 
 
+def _fp8_blockscaled_shapes(A, scale_a, B, scale_b, out):
+    """(M, N, K) of a block-scaled FP8 call; the scale grids must be exactly
+    [M, ceil(K/128)] and [ceil(K/128), ceil(N/128)]."""
+    M, K = _dims2(A, "A")
+    K2, N = _dims2(B, "B")
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    _shape(scale_a, (M, _cdiv(K, 128)), "scale_a")
+    _shape(scale_b, (_cdiv(K, 128), _cdiv(N, 128)), "scale_b")
+    _shape(out, (M, N), "out")
+    _same_device(A, ("B", B), ("scale_a", scale_a), ("scale_b", scale_b), ("out", out))
+    return M, N, K
+
+
 def gemm_fp8_blockscaled(A, scale_a, B, scale_b, out=None):
     """BF16 D = block-scaled E4M3 A [M,K] . B [K,N]; scale_a [M, ceil(K/128)],
     scale_b [ceil(K/128), ceil(N/128)] FP32.  Returns D as a bfloat16 tensor."""
-    M, K = A.shape
-    N = B.shape[1]
+    M, N, K = _fp8_blockscaled_shapes(A, scale_a, B, scale_b, out)
     pa, lda = _mat(A, 1, "A")
     pb, ldb = _mat(B, 1, "B")
     psa, ldsa = _mat(scale_a, 4, "scale_a")
@@ -248,8 +298,7 @@ FP8_E4M3, FP8_E5M2 = 0, 1
 
 def gemm_fp8_blockscaled_fmt(A, fmt_a, scale_a, B, fmt_b, scale_b, out=None):
     """gemm_fp8_blockscaled with each operand's format (FP8_E4M3 / FP8_E5M2)."""
-    M, K = A.shape
-    N = B.shape[1]
+    M, N, K = _fp8_blockscaled_shapes(A, scale_a, B, scale_b, out)
     pa, lda = _mat(A, 1, "A")
     pb, ldb = _mat(B, 1, "B")
     psa, ldsa = _mat(scale_a, 4, "scale_a")
@@ -267,8 +316,12 @@ def gemm_fp8_rowscaled(A, fmt_a, scale_a, B, fmt_b, scale_b, out=None):
     """BF16 D = (A . B) * scale_a[i] * scale_b[j]: FP8 A [M,K], B [K,N];
     scale_a FP32 with M values (per row) or 1 (per tensor), scale_b with N
     values (per column) or 1."""
-    M, K = A.shape
-    N = B.shape[1]
+    M, K = _dims2(A, "A")
+    K2, N = _dims2(B, "B")
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    _shape(out, (M, N), "out")
+    _same_device(A, ("B", B), ("scale_a", scale_a), ("scale_b", scale_b), ("out", out))
     pa, lda = _mat(A, 1, "A")
     pb, ldb = _mat(B, 1, "B")
     inc = []
@@ -289,14 +342,24 @@ def gemv_w8a8(x, x_scale, W, w_scale, out=None, z_out=None, return_z=False):
     """Batch-1 W8A8 layer: x INT8 [K], W INT8 [N, K] (one output channel per
     row), w_scale FP32 [N]; returns y BF16 [N] (and the INT32 sums when
     return_z or z_out is given)."""
+    if x.dim() != 1:
+        raise ValueError("x must be 1-D")
     K = x.numel()
-    pw, ldw = _mat(W, 1, "W")
-    N = W.shape[0]
-    if W.shape[1] != K:
+    N, K2 = _dims2(W, "W")
+    if K2 != K:
         raise ValueError("W must be [N, K]")
+    _shape(w_scale, (N,), "w_scale")
+    _shape(out, (N,), "out")
+    _shape(z_out, (N,), "z_out")
+    _same_device(W, ("x", x), ("w_scale", w_scale), ("out", out), ("z_out", z_out))
+    if out is not None and (out.element_size() != 2 or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous 2-byte (BF16) tensor")
+    if z_out is not None and (z_out.dtype != torch.int32 or not z_out.is_contiguous()):
+        raise ValueError("z_out must be a contiguous INT32 tensor")
+    pw, ldw = _mat(W, 1, "W")
     if x.element_size() != 1 or not x.is_contiguous() or not x.is_cuda:
         raise ValueError("x must be a contiguous 1-byte GPU tensor")
-    if w_scale.dtype != torch.float32 or w_scale.numel() != N or not w_scale.is_contiguous():
+    if w_scale.dtype != torch.float32 or not w_scale.is_contiguous():
         raise ValueError("w_scale must be a contiguous FP32 tensor of N entries")
     if out is None:
         out = torch.empty(N, dtype=torch.bfloat16, device=W.device)
@@ -311,19 +374,26 @@ def gemv_w8a8(x, x_scale, W, w_scale, out=None, z_out=None, return_z=False):
 
 
 def _vec(t, n, dtype, name):
-    if t.dtype != dtype or t.numel() != n or not t.is_contiguous() or not t.is_cuda:
+    if t.dim() != 1 or t.dtype != dtype or t.numel() != n or not t.is_contiguous() or not t.is_cuda:
         raise ValueError(f"{name} must be a contiguous {dtype} GPU tensor of {n} entries")
     return t.data_ptr()
+
+
+def _w8a8_shapes(M, N, X, W, out, z_out):
+    _shape(out, (M, N), "out")
+    _shape(z_out, (M, N), "z_out")
+    _same_device(W, ("X", X), ("out", out), ("z_out", z_out))
 
 
 def gemm_w8a8(X, x_scale, W, w_scale, bias=None, out=None, z_out=None, return_z=False):
     """W8A8 layer for M tokens: X INT8 [M, K], x_scale FP32 [M], W INT8 [N, K]
     (one output channel per row), w_scale FP32 [N], bias FP32 [N] or None;
     returns Y BF16 [M, N] (and the INT32 sums when return_z or z_out is given)."""
-    M, K = X.shape
-    N = W.shape[0]
-    if W.shape[1] != K:
+    M, K = _dims2(X, "X")
+    N, K2 = _dims2(W, "W")
+    if K2 != K:
         raise ValueError("W must be [N, K]")
+    _w8a8_shapes(M, N, X, W, out, z_out)
     px, ldx = _mat(X, 1, "X")
     pw, ldw = _mat(W, 1, "W")
     psx = _vec(x_scale, M, torch.float32, "x_scale")
@@ -345,10 +415,11 @@ def gemm_w8a8(X, x_scale, W, w_scale, bias=None, out=None, z_out=None, return_z=
 def gemm_w8a8_kn(X, x_scale, W, w_scale, bias=None, out=None, z_out=None, return_z=False):
     """gemm_w8a8 with W INT8 stored [K, N] (row k holds input k of every
     output channel); returns Y BF16 [M, N] (and the INT32 sums on request)."""
-    M, K = X.shape
-    N = W.shape[1]
-    if W.shape[0] != K:
+    M, K = _dims2(X, "X")
+    K2, N = _dims2(W, "W")
+    if K2 != K:
         raise ValueError("W must be [K, N]")
+    _w8a8_shapes(M, N, X, W, out, z_out)
     px, ldx = _mat(X, 1, "X")
     pw, ldw = _mat(W, 1, "W")
     psx = _vec(x_scale, M, torch.float32, "x_scale")
@@ -372,10 +443,11 @@ def gemm_w8a8_requant(X, x_scale, W, w_scale, bias, out_scale, out=None, z_out=N
     """The W8A8 layer requantised for a next INT8 layer: as gemm_w8a8, then
     Q = clamp(rne(value / out_scale), -127, 127); returns Q INT8 [M, N] (and
     the INT32 sums when return_z or z_out is given)."""
-    M, K = X.shape
-    N = W.shape[0]
-    if W.shape[1] != K:
+    M, K = _dims2(X, "X")
+    N, K2 = _dims2(W, "W")
+    if K2 != K:
         raise ValueError("W must be [N, K]")
+    _w8a8_shapes(M, N, X, W, out, z_out)
     px, ldx = _mat(X, 1, "X")
     pw, ldw = _mat(W, 1, "W")
     psx = _vec(x_scale, M, torch.float32, "x_scale")
@@ -398,7 +470,10 @@ def gemm_w8a8_requant(X, x_scale, W, w_scale, bias, out_scale, out=None, z_out=N
 def quantize_i8_rows(X, q_out=None, scales_out=None):
     """Per-token INT8 quantisation of BF16 activations X [M, K] (any 2-byte
     dtype holding BF16 bits); returns (Q INT8 [M, K], scales FP32 [M])."""
-    M, K = X.shape
+    M, K = _dims2(X, "X")
+    _shape(q_out, (M, K), "q_out")
+    _shape(scales_out, (M,), "scales_out")
+    _same_device(X, ("q_out", q_out), ("scales_out", scales_out))
     px, ldx = _mat(X, 2, "X")
     if q_out is None:
         q_out = torch.empty((M, K), dtype=torch.int8, device=X.device)
@@ -414,9 +489,14 @@ def quantize_fp8_blocks(X, block_rows, q_out=None, scales_out=None):
     """FP8 E4M3 block quantisation of an FP32 matrix X [R, C] in
     block_rows x 128 blocks (block_rows 1 or 128); returns (Q uint8 [R, C],
     scales FP32 [ceil(R/block_rows), ceil(C/128)])."""
-    R, Cc = X.shape
-    px, ldx = _mat(X, 4, "X")
+    R, Cc = _dims2(X, "X")
+    if block_rows not in (1, 128):
+        raise ValueError("block_rows must be 1 or 128")
     nbr, nbc = -(-R // block_rows), -(-Cc // 128)
+    _shape(q_out, (R, Cc), "q_out")
+    _shape(scales_out, (nbr, nbc), "scales_out")
+    _same_device(X, ("q_out", q_out), ("scales_out", scales_out))
+    px, ldx = _mat(X, 4, "X")
     if q_out is None:
         q_out = torch.empty((R, Cc), dtype=torch.uint8, device=X.device)
     if scales_out is None:
@@ -433,9 +513,14 @@ def quantize_fp8(X, fmt, block_rows, block_cols, q_out=None, scales_out=None):
     FP8_E5M2) with block_rows x block_cols blocks: 1 x 128, 128 x 128, whole
     rows (1 x C), whole columns (R x 1) or the whole tensor (R x C); returns
     (Q uint8 [R, C], scales FP32 [ceil(R/block_rows), ceil(C/block_cols)])."""
-    R, Cc = X.shape
-    px, ldx = _mat(X, 4, "X")
+    R, Cc = _dims2(X, "X")
+    if block_rows <= 0 or block_cols <= 0:
+        raise ValueError("block_rows and block_cols must be positive")
     nbr, nbc = -(-R // block_rows), -(-Cc // block_cols)
+    _shape(q_out, (R, Cc), "q_out")
+    _shape(scales_out, (max(nbr, 1), max(nbc, 1)), "scales_out")
+    _same_device(X, ("q_out", q_out), ("scales_out", scales_out))
+    px, ldx = _mat(X, 4, "X")
     if q_out is None:
         q_out = torch.empty((R, Cc), dtype=torch.uint8, device=X.device)
     if scales_out is None:

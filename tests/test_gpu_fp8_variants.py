@@ -81,7 +81,7 @@ def test_rowscaled_per_tensor_and_mixed(gpu_ok, fa, fb):
     check_fp(bf16_values(one_b), R, S, 1e-2, "unit block", bf16_out=True)
 
 
-def test_rowscaled_k_zero_and_sampled_2048(gpu_ok):
+def test_rowscaled_k_zero_and_2048(gpu_ok):
     D = mp.gemm_fp8_rowscaled(torch.zeros((40, 0), dtype=torch.uint8, device=gpu_ok), E4,
                               dev(np.float32([2.0])), torch.zeros((0, 50), dtype=torch.uint8, device=gpu_ok),
                               E4, dev(np.float32([3.0])))
@@ -90,12 +90,10 @@ def test_rowscaled_k_zero_and_sampled_2048(gpu_ok):
     qa, sa, qb, sb = quantised(M, N, K, E4, E4, seed=5, block=False)
     D = mp.gemm_fp8_rowscaled(dev(qa), E4, dev(sa.ravel()), dev(qb), E4, dev(sb.ravel()))
     d = bf16_values(D)
-    assert np.isfinite(d).all()
-    r = np.random.default_rng(6)
-    ii = np.concatenate([r.integers(0, M, 3000), [0, M - 1]])
-    jj = np.concatenate([r.integers(0, N, 3000), [N - 1, 0]])
-    R, S = oracle.gemm_fp8_rowscaled_at(qa, E4, sa.ravel(), qb, E4, sb.ravel(), ii, jj)
-    check_fp(d[ii, jj], R, S, 1e-2, "rowscaled 2048^3 sampled", bf16_out=True)
+    # every element; at K = 2048 the bound holds as stated, the BF16
+    # rounding of D included (S is tens of times |R|)
+    R, S = oracle.gemm_fp8_rowscaled(qa, E4, sa.ravel(), qb, E4, sb.ravel())
+    check_fp(d, R, S, 1e-2, "rowscaled 2048^3")
 
 
 SHAPES = {"row128": (1, 128), "tile128": (128, 128), "per_row": (1, None), "per_col": (None, 1),

@@ -3,7 +3,8 @@ the BF16 outputs are bit-exact (the dequantisation order (float(z) * s_x) *
 s_w is fixed).  Covers the full 1 x 4096 . 4096 x 14336 layer, N not a
 multiple of the rows a workgroup owns, K not a multiple of 16 or 1024, -128
 weights and activations at the INT32 bound, misaligned x / W and a padded
-leading dimension, and K = 0."""
+leading dimension, and K = 0.  y and z are written into guard-banded buffers:
+nothing outside the N outputs may change."""
 import numpy as np
 import pytest
 import torch
@@ -15,6 +16,8 @@ from mixed_precision_dense_tiled_amd import inputs
 
 pytestmark = pytest.mark.gpu
 
+GUARD = 64
+
 
 def run(x, s_x, W, s_w, ldw=None, x_shift=0):
     N, K = W.shape
@@ -22,10 +25,19 @@ def run(x, s_x, W, s_w, ldw=None, x_shift=0):
         tx = dev(np.concatenate([np.zeros(x_shift, np.int8), x]))[x_shift:]
     else:
         tx = dev(x)
-    y, z = mp.gemv_w8a8(tx, float(s_x), dev(W, ldw, pad=77), dev(s_w), return_z=True)
+    # y and z sit inside guard bands of GUARD elements on each side, filled
+    # with a pattern no output takes; a write outside [0, N) changes them
+    ybuf = torch.full((N + 2 * GUARD,), -21846, dtype=torch.int16, device="cuda:0")   # 0xAAAA
+    zbuf = torch.full((N + 2 * GUARD,), -0x55555556, dtype=torch.int32, device="cuda:0")
+    y = ybuf[GUARD:GUARD + N].view(torch.bfloat16)
+    z = zbuf[GUARD:GUARD + N]
+    mp.gemv_w8a8(tx, float(s_x), dev(W, ldw, pad=77), dev(s_w), out=y, z_out=z)
     torch.cuda.synchronize()
+    yb, zb = host(ybuf).view(np.uint16), host(zbuf)
+    for name, b, fill in (("y", yb, 0xAAAA), ("z", zb, -0x55555556)):
+        assert (b[:GUARD] == fill).all() and (b[GUARD + N:] == fill).all(), f"{name} written outside [0, N)"
     zr, yr = oracle.gemv_w8a8(x, s_x, W, s_w)
-    return host(z), host(y).view(np.uint16), zr, yr
+    return zb[GUARD:GUARD + N], yb[GUARD:GUARD + N], zr, yr
 
 
 def test_full_layer_bit_exact(gpu_ok):
