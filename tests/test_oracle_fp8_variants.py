@@ -24,6 +24,7 @@ import pytest
 import torch
 
 import oracle
+from mixed_precision_dense_tiled_amd import inputs
 
 E4, E5 = oracle.E4M3, oracle.E5M2
 
@@ -143,3 +144,27 @@ def test_quantiser_per_row_and_per_tensor(fmt, qmax):
     assert np.abs(oracle.fp8_to_f64(Qt, fmt)).max() == qmax
     with pytest.raises(oracle.OracleError):
         oracle.quantize_fp8_blocks_fmt(X, 2, 1, Cc)
+
+
+@pytest.mark.parametrize("fa,fb", [(0, 0), (0, 1), (1, 0), (1, 1)])
+@pytest.mark.parametrize("M,N,K", [(3, 130, 131), (5, 257, 300), (2, 128, 128)])
+def test_blockscaled_full_matrix_equals_element_by_element(fa, fb, M, N, K):
+    """The whole-matrix form walks B by rows; each element must still get
+    exactly the operations of the one-element form, in the same order: bit
+    for bit the same R and S (ragged blocks, padded leading dimensions)."""
+    r = np.random.default_rng(M * 1000 + N + K)
+    qa = r.integers(0, 256, (M, K)).astype(np.uint8)
+    qb = r.integers(0, 256, (K, N)).astype(np.uint8)
+    for q, f in ((qa, fa), (qb, fb)):     # finite codes only
+        if f == 0:
+            q[(q & 0x7F) == 0x7F] = 0x38
+        else:
+            q[(q & 0x7C) == 0x7C] = 0x3C
+    kb, nb = (K + 127) // 128, (N + 127) // 128
+    sa = r.uniform(0.01, 2.0, (M, kb)).astype(np.float32)
+    sb = r.uniform(0.01, 2.0, (kb, nb)).astype(np.float32)
+    A, B, SA = inputs.with_ld(qa, K + 5), inputs.with_ld(qb, N + 3), inputs.with_ld(sa, kb + 1)
+    R, S = oracle.gemm_fp8_blockscaled_fmt(A, fa, SA, B, fb, sb)
+    ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    Rp, Sp = oracle.gemm_fp8_blockscaled_fmt_at(A, fa, SA, B, fb, sb, ii.ravel(), jj.ravel())
+    assert np.array_equal(Rp.reshape(M, N), R) and np.array_equal(Sp.reshape(M, N), S)
