@@ -26,7 +26,9 @@ __all__ = ["gemm_f16", "gemm_bf16", "gemm_f16_f16out", "gemm_bf16_bf16out", "gem
            "MpdtError", "lib", "lib_path", "version"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libmpdt.so")
+# MPDT_LIB_PATH names another build of the same library (the test-suite's
+# sanitizer build of the host code, for one); by default the in-tree one.
+_LIB_PATH = os.environ.get("MPDT_LIB_PATH") or os.path.join(_HERE, "libmpdt.so")
 _lib = None
 
 _i64 = ctypes.c_int64

@@ -17,7 +17,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# MPDT_ORACLE_LIB names another build of oracle.c (the test-suite's sanitizer
+# build); by default the in-tree one.
+LIB_PATH = os.environ.get("MPDT_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 _c_i64 = ctypes.c_int64
 _vp = ctypes.c_void_p
