@@ -46,8 +46,14 @@ def parse():
     p.add_argument("--warmup", type=int, default=300)
     p.add_argument("--only", default="all",
                    choices=["all", "bf16", "bf16out", "epi", "gemv", "w8a8_tokens", "quant", "fp8",
-                            "f16_ragged", "f16_64", "i8", "copy"])
+                            "f16_ragged", "f16_64", "i8", "copy", "ceiling", "bf16+gemv"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--procs", type=int, default=3,
+                   help="independent processes that repeat the headline BF16 GEMM and the cold "
+                        "GEMV, for the median [min, max] across processes (1: none)")
+    p.add_argument("--child", action="store_true", help=argparse.SUPPRESS)
+    p.add_argument("--no-clock", action="store_true",
+                   help="skip the clock-stamped run of the headline GEMM")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the bounded oracle sample")
     return p.parse_args()
@@ -126,6 +132,17 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
     import numpy as np
+
+    def want(name):
+        return args.only == "all" or args.only == name or (args.only == "bf16+gemv" and name in ("bf16", "gemv"))
+
+    # Independent processes first, before this one touches the GPU: each
+    # repeats the headline GEMM and the cold GEMV in a fresh process (own
+    # context, own clock ramp); their spread is reported with the median.
+    spread = None
+    if not args.child and args.procs > 1 and want("bf16"):
+        spread = process_spread(args)
+
     import torch
 
     import mixed_precision_dense_tiled_amd as mp
@@ -147,7 +164,7 @@ def main():
     result = None
 
     # ---------------- headline: BF16 4096^3 -----------------------------------
-    if args.only in ("all", "bf16"):
+    if want("bf16"):
         M = N = K = 4096
         A, B, C = inputs.gemm16_operands(M, N, K, dist="normal", fmt="bf16")
         tA, tB, tC = to_dev(A), to_dev(B), to_dev(C)
@@ -160,7 +177,8 @@ def main():
         achieved = flop / avg_s / 1e12
         digest = source_digest("gemm.hip", "gemm_kernel.hpp", "gemm_common.hpp", "device_common.hpp")
         traffic = traffic_for("gemm_bf16_4096", digest)
-        clock = gemm_clock(tA, tB, tC, tD, stream, M, N, K)
+        clock = None if (args.no_clock or args.child) else gemm_clock(tA, tB, tC, tD, stream, M, N, K)
+        smi = None if args.child else smi_clocks(lambda: mp.gemm_bf16(tA, tB, tC, out=tD), stream)
         result = {
             "metric": METRIC,
             "value": flop * args.steps / (region * 1e-3) / 1e12,
@@ -182,10 +200,16 @@ def main():
                          "kernel": "gemm_kernel<BF16,256x256,one wave per SIMD>", "launch_us": st,
                          "clock": clock},
         }
+        if smi is not None:
+            result["smi_clocks_under_load"] = smi
+        if spread is not None:
+            result["process_spread"] = spread["bf16"]
+        if not args.no_cpu_baseline and not args.child:
+            result["cpu_baseline"] = cpu_baseline_gemm16(A, B, C, "bf16", args.cpu_seconds)
         del tA, tB, tC, tD
 
     # ---------------- BF16 4096^3 with a BF16 D (16-bit-output variant) -------
-    if args.only in ("all", "bf16out"):
+    if want("bf16out"):
         M = N = K = 4096
         A, B, C = inputs.gemm16_operands(M, N, K, dist="normal", fmt="bf16")
         tA, tB, tC = to_dev(A), to_dev(B), to_dev(C)
@@ -202,7 +226,7 @@ def main():
         del tA, tB, tC, tD
 
     # ---------------- BF16 4096^3 + bias + GELU into BF16 (fused epilogue) ------
-    if args.only in ("all", "epi"):
+    if want("epi"):
         M = N = K = 4096
         A, B, C = inputs.gemm16_operands(M, N, K, dist="normal", fmt="bf16")
         bias = inputs.normal_f32((N,), inputs.SEED_BIAS)
@@ -220,8 +244,14 @@ def main():
                          "frac": tf / PEAK_BF16}}
         del tA, tB, tC, tb, tD
 
+    # ---------------- practical HBM read ceiling ------------------------------
+    ceiling = None
+    if (want("gemv") or want("ceiling")) and not args.child:
+        ceiling = read_ceiling(args, stream)
+        extra["hbm_read_ceiling"] = ceiling
+
     # ---------------- W8A8 GEMV, cold cache ------------------------------------
-    if args.only in ("all", "gemv"):
+    if want("gemv"):
         N, K = 14336, 4096
         x, s_x, W, s_w = inputs.w8a8_operands(N, K)
         copies = 8  # 8 x 58.7 MB rotated: larger than the 256 MB Infinity Cache
@@ -247,10 +277,18 @@ def main():
                          "frac": gbs / PEAK_HBM,
                          "traffic": traffic_for("gemv_w8a8_14336x4096", digest)},
         }
+        if ceiling is not None:
+            c = ceiling["same_bytes_cold_8KiB_per_wave"]["GB_s"]
+            extra["gemv_w8a8"]["roofline"]["calibrated_ceiling_GB_s"] = c
+            extra["gemv_w8a8"]["roofline"]["frac_of_calibrated_ceiling"] = gbs / c
+        if spread is not None:
+            extra["gemv_w8a8"]["process_spread"] = spread["gemv"]
+        if not args.no_cpu_baseline and not args.child:
+            extra["gemv_w8a8"]["cpu_baseline"] = cpu_baseline_gemv(x, s_x, W, s_w, nbytes)
         del tWs
 
     # ---------------- W8A8 layer for a few tokens, cold cache --------------------
-    if args.only in ("all", "w8a8_tokens"):
+    if want("w8a8_tokens"):
         N, K = 14336, 4096
         r = np.random.default_rng(12)
         copies = 8
@@ -304,7 +342,7 @@ def main():
         del tWs
 
     # ---------------- quantisers -----------------------------------------------
-    if args.only in ("all", "quant"):
+    if want("quant"):
         r = np.random.default_rng(13)
         X = r.standard_normal((16, 4096)).astype(np.float32)
         tX = to_dev((X.view(np.uint32) >> 16).astype(np.uint16))
@@ -345,7 +383,7 @@ def main():
         del tA, tq
 
     # ---------------- FP8 block-scaled 4096 x 7168 x 7168 ----------------------
-    if args.only in ("all", "fp8"):
+    if want("fp8"):
         M, N, K = 4096, 7168, 7168
         qa, sa, qb, sb = inputs.fp8_operands(M, N, K)
         ta, tsa, tb, tsb = to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb)
@@ -360,6 +398,8 @@ def main():
             "TFLOP_s": tf, "launch_us": st,
             "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP8, "unit": "TFLOP/s",
                          "frac": tf / PEAK_FP8}}
+        if not args.no_cpu_baseline and not args.child:
+            extra["gemm_fp8_blockscaled"]["cpu_baseline"] = cpu_baseline_fp8(qa, sa, qb, sb, args.cpu_seconds / 3)
         # the same operands with B read as E5M2 codes (the format of gradients)
         qb5 = qb.copy()
         qb5[(qb5 & 0x7C) == 0x7C] = 0x3C                   # no infinity / NaN codes
@@ -391,7 +431,7 @@ def main():
         del ta, tb, td, tb5
 
     # ---------------- FP16 ragged 8191 x 8193 x 4099 ---------------------------
-    if args.only in ("all", "f16_ragged"):
+    if want("f16_ragged"):
         M, N, K = 8191, 8193, 4099
         A, B, C = inputs.gemm16_operands(M, N, K, dist="uniform", fmt="f16", c_zero=True)
         tA, tB, tC = to_dev(A), to_dev(B), to_dev(C)
@@ -405,10 +445,12 @@ def main():
             "TFLOP_s": tf, "launch_us": st,
             "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP16, "unit": "TFLOP/s",
                          "frac": tf / PEAK_FP16}}
+        if not args.no_cpu_baseline and not args.child:
+            extra["gemm_f16_ragged"]["cpu_baseline"] = cpu_baseline_gemm16(A, B, C, "f16", args.cpu_seconds / 3)
         del tA, tB, tC, tD
 
     # ---------------- FP16 64^3 (latency) --------------------------------------
-    if args.only in ("all", "f16_64"):
+    if want("f16_64"):
         A, B, C = inputs.gemm16_operands(64, 64, 64, dist="uniform", fmt="f16")
         tA, tB, tC = to_dev(A), to_dev(B), to_dev(C)
         tD = torch.empty((64, 64), dtype=torch.float32, device=dev)
@@ -416,9 +458,11 @@ def main():
                             stream)
         extra["gemm_f16_64"] = {"workload": "FP16 64^3 with FP32 C (latency bound)",
                                 "launch_us": stats(per, region, args.steps)}
+        if not args.no_cpu_baseline and not args.child:
+            extra["gemm_f16_64"]["cpu_baseline"] = cpu_baseline_small(A, B, C)
 
     # ---------------- INT8 4096^3 ----------------------------------------------
-    if args.only in ("all", "i8"):
+    if want("i8"):
         M = N = K = 4096
         A, B, C = inputs.i8_operands(M, N, K)
         tA, tB, tC = to_dev(A), to_dev(B), to_dev(C)
@@ -431,6 +475,8 @@ def main():
                                 "launch_us": st,
                                 "roofline": {"bound": "mfma", "achieved": tops, "peak": PEAK_INT8,
                                              "unit": "TOP/s", "frac": tops / PEAK_INT8}}
+        if not args.no_cpu_baseline and not args.child:
+            extra["gemm_i8_i32"]["cpu_baseline"] = cpu_baseline_i8(A, B, C, args.cpu_seconds / 3)
         del tA, tB, tC, tD
 
     # ---------------- plain copy (counter calibration) -------------------------
@@ -441,10 +487,6 @@ def main():
         region, per = timed(lambda i: dst.copy_(src), args.steps, args.warmup, stream)
         extra["copy"] = {"bytes_read": n, "bytes_written": n,
                          "launch_us": stats(per, region, args.steps)}
-
-    # ---------------- CPU baseline: the oracle on a bounded sample -------------
-    if result is not None and not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
 
     if result is None:
         result = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1,
@@ -498,30 +540,190 @@ def gemm_clock(tA, tB, tC, tD, stream, M, N, K, runs=6):
             "source": "libmpdt_clock.so (same kernels + s_memtime/s_memrealtime stamps)"}
 
 
-def cpu_baseline(target_s):
-    """The CPU oracle (FP64 GEMM + bound matrix, OpenMP) timed on a row block
-    of the BF16 4096^3 workload; throughput scaled to TFLOP/s of the full
-    problem's FLOP convention (2 per multiply-add)."""
+def cpu_info():
     cores = len(os.sched_getaffinity(0))
     os.environ.setdefault("OMP_NUM_THREADS", str(cores))
-    import oracle
-    from mixed_precision_dense_tiled_amd import inputs
-    N = K = 4096
-    A, B, C = inputs.gemm16_operands(4096, N, K, dist="normal", fmt="bf16")
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return int(os.environ["OMP_NUM_THREADS"]), model
+
+
+def _grow_rows(run, total_rows, target_s):
+    """Time run(rows) on a growing leading block of rows until it takes
+    about target_s (or covers every row); returns (rows, seconds)."""
     rows = 8
-    t = 0.0
     while True:
         t0 = time.perf_counter()
-        oracle.gemm_bf16(A[:rows], B, C[:rows])
+        run(rows)
         t = time.perf_counter() - t0
-        if t * 2 > target_s or rows >= 4096:
-            break
-        rows = min(4096, max(rows * 2, int(rows * target_s / max(t, 1e-3) * 0.9)))
-    flop = 2.0 * rows * N * K
-    return {"value": flop / t / 1e12, "unit": "TFLOP/s", "cores": int(os.environ["OMP_NUM_THREADS"]),
+        if t * 2 > target_s or rows >= total_rows:
+            return rows, t
+        rows = min(total_rows, max(rows * 2, int(rows * target_s / max(t, 1e-3) * 0.9)))
+
+
+def cpu_baseline_gemm16(A, B, C, fmt, target_s):
+    """The CPU oracle (FP64 GEMM + bound matrix, OpenMP) timed on a leading
+    block of rows of a 16-bit workload; TFLOP/s of that block (2 FLOP per
+    multiply-add)."""
+    cores, model = cpu_info()
+    import oracle
+    fn = oracle.gemm_bf16 if fmt == "bf16" else oracle.gemm_f16
+    M, K = A.shape
+    N = B.shape[1]
+    rows, t = _grow_rows(lambda r: fn(A[:r], B, C[:r]), M, target_s)
+    return {"value": 2.0 * rows * N * K / t / 1e12, "unit": "TFLOP/s", "cores": cores, "cpu": model,
             "kind": "oracle",
-            "sample": f"oracle_gemm_bf16 (FP64 sum and bound matrix) on the first {rows} rows of "
-                      f"A (all 4096 columns of the 4096^3 BF16 workload), {t:.2f} s wall"}
+            "sample": f"oracle_gemm_{fmt} (FP64 sum and bound matrix) on the first {rows} of {M} rows of A "
+                      f"(all {N} columns, K = {K}), {t:.2f} s wall"}
+
+
+def cpu_baseline_i8(A, B, C, target_s):
+    cores, model = cpu_info()
+    import oracle
+    M, K = A.shape
+    N = B.shape[1]
+    rows, t = _grow_rows(lambda r: oracle.gemm_i8_i32(A[:r], B, C[:r]), M, target_s)
+    return {"value": 2.0 * rows * N * K / t / 1e12, "unit": "TOP/s", "cores": cores, "cpu": model,
+            "kind": "oracle",
+            "sample": f"oracle_gemm_i8_i32 (INT64 sums) on the first {rows} of {M} rows of A "
+                      f"(all {N} columns, K = {K}), {t:.2f} s wall"}
+
+
+def cpu_baseline_fp8(qa, sa, qb, sb, target_s):
+    cores, model = cpu_info()
+    import oracle
+    M, K = qa.shape
+    N = qb.shape[1]
+    rows, t = _grow_rows(lambda r: oracle.gemm_fp8_blockscaled(qa[:r], sa[:r], qb, sb), M, target_s)
+    return {"value": 2.0 * rows * N * K / t / 1e12, "unit": "TFLOP/s", "cores": cores, "cpu": model,
+            "kind": "oracle",
+            "sample": f"oracle_gemm_fp8_blockscaled (FP64 block sums and bound matrix) on the first {rows} "
+                      f"of {M} rows of A (all {N} columns, K = {K}), {t:.2f} s wall"}
+
+
+def cpu_baseline_small(A, B, C, runs=5):
+    """The whole 64^3 problem, median of five runs (it is latency-bound)."""
+    cores, model = cpu_info()
+    import oracle
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        oracle.gemm_f16(A, B, C)
+        ts.append(time.perf_counter() - t0)
+    t = sorted(ts)[runs // 2]
+    M, K = A.shape
+    N = B.shape[1]
+    return {"value": t * 1e6, "unit": "us per call", "gflop_s": 2.0 * M * N * K / t / 1e9, "cores": cores,
+            "cpu": model, "kind": "oracle",
+            "sample": f"oracle_gemm_f16 on the whole {M}x{N}x{K} problem, median of {runs} runs "
+                      f"[{min(ts) * 1e6:.0f}, {max(ts) * 1e6:.0f}] us"}
+
+
+def cpu_baseline_gemv(x, s_x, W, s_w, nbytes, runs=5):
+    """The whole layer, median of five runs; GB/s of the same algorithmic bytes."""
+    cores, model = cpu_info()
+    import oracle
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        oracle.gemv_w8a8(x, s_x, W, s_w)
+        ts.append(time.perf_counter() - t0)
+    t = sorted(ts)[runs // 2]
+    return {"value": nbytes / t / 1e9, "unit": "GB/s", "cores": cores, "cpu": model, "kind": "oracle",
+            "sample": f"oracle_gemv_w8a8 (INT64 sums, FP32 dequantisation) on the whole 14336 x 4096 layer, "
+                      f"median of {runs} runs {t * 1e3:.1f} ms [{min(ts) * 1e3:.1f}, {max(ts) * 1e3:.1f}]"}
+
+
+def process_spread(args):
+    """Run the headline GEMM and the cold GEMV in args.procs fresh processes
+    (this script with --child), one after the other; median and [min, max]
+    of their figures."""
+    import subprocess
+    vals = {"bf16": [], "gemv": []}
+    for _ in range(args.procs):
+        cmd = [sys.executable, os.path.abspath(__file__), "--only", "bf16+gemv", "--child",
+               "--no-cpu-baseline", "--steps", str(args.steps), "--warmup", str(args.warmup)]
+        out = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+        if out.returncode != 0:
+            sys.stderr.write(out.stdout[-2000:] + out.stderr[-2000:])
+            raise SystemExit(f"child bench process failed ({out.returncode})")
+        line = [ln for ln in out.stdout.splitlines() if ln.startswith("{")][-1]
+        r = json.loads(line)
+        vals["bf16"].append(r["value"])
+        vals["gemv"].append(r["extra"]["gemv_w8a8"]["GB_s"])
+        print(f"# child process {len(vals['bf16'])}: {r['value']:.1f} TFLOP/s, "
+              f"{vals['gemv'][-1]:.1f} GB/s", file=sys.stderr, flush=True)
+
+    def summary(v, unit):
+        s = sorted(v)
+        return {"processes": len(v), "unit": unit, "median": s[len(s) // 2], "min": s[0], "max": s[-1],
+                "values": v}
+    return {"bf16": summary(vals["bf16"], "TFLOP/s"), "gemv": summary(vals["gemv"], "GB/s")}
+
+
+def smi_clocks(launch, stream, n=4000):
+    """Clock levels rocm-smi reports while the GEMM runs: n launches are
+    queued (about half a second of work), rocm-smi is read while they run."""
+    import subprocess
+    import torch
+    for _ in range(n):
+        launch()
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                             timeout=30)
+        data = json.loads(out.stdout) if out.returncode == 0 else None
+    except (OSError, ValueError, subprocess.TimeoutExpired):
+        data = None
+    torch.cuda.synchronize()
+    if not data:
+        return None
+    card = next(iter(data.values()))
+    return {k.split(" ")[0]: v for k, v in card.items() if isinstance(v, str) and "clk" in k.lower()}
+
+
+def read_ceiling(args, stream):
+    """Practical HBM read rates on this part (libmpdt_probes.so,
+    mpdt_probe_stream_read: non-temporal 16-byte loads, all of a wave's
+    loads in flight before use): the GEMV's own byte count with 8 rotating
+    copies (cold, like the GEMV timing) at the GEMV's 8 KiB per wave and at
+    16 KiB per wave, and a long 1 GiB stream."""
+    import ctypes
+    import torch
+    L = ctypes.CDLL(os.path.join(ROOT, "mixed_precision_dense_tiled_amd", "libmpdt_probes.so"))
+    L.mpdt_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p, ctypes.c_void_p]
+    L.mpdt_probe_stream_read.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    sink = torch.zeros(16, dtype=torch.int32, device=dev)
+    out = {}
+    nbytes = 58_720_256
+    copies = [torch.ones(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(8)]
+
+    def run(buf, n, per, waves):
+        rc = L.mpdt_probe_stream_read(buf.data_ptr(), n, per, waves, sink.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"mpdt_probe_stream_read failed: {rc}")
+    for per, name in ((8, "same_bytes_cold_8KiB_per_wave"), (16, "same_bytes_cold_16KiB_per_wave")):
+        region, per_l = timed(lambda i: run(copies[i % 8], nbytes, per, 4), args.steps, args.warmup, stream)
+        st = stats(per_l, region, args.steps)
+        out[name] = {"bytes": nbytes, "GB_s": nbytes / (st["mean_us"] * 1e-6) / 1e9, "launch_us": st}
+    del copies
+    big = 1 << 30
+    buf = torch.ones(big // 4, dtype=torch.int32, device=dev)
+    steps = max(args.steps // 5, 5)
+    region, per_l = timed(lambda i: run(buf, big, 16, 4), steps, 20, stream)
+    st = stats(per_l, region, steps)
+    out["long_stream_1GiB"] = {"bytes": big, "GB_s": big / (st["mean_us"] * 1e-6) / 1e9, "launch_us": st}
+    out["note"] = ("back-to-back launches between HIP events, like the GEMV timing; the short reads "
+                   "include each launch's start and drain")
+    return out
 
 
 if __name__ == "__main__":

@@ -19,6 +19,14 @@
 //     out_dma[l]) and once with a plain 16-byte load (-> out_ld[l]); neither
 //     offset need be a multiple of 16.  With range < soff + off + 1024 it also
 //     shows which offsets the buffer range check covers.
+//   mpdt_probe_stream_read(p, bytes, per_lane, waves, out): the practical
+//     HBM read ceiling -- every 16-byte chunk of [p, p + bytes) is read once
+//     with non-temporal 16-byte loads, a wave taking per_lane KiB in a row
+//     (lane l reads chunks l, l + 64, ... of its KiB runs, all loads issued
+//     before any is used), `waves` wavefronts per workgroup; only a value no
+//     real sum takes is ever written, so the kernel moves almost nothing but
+//     the reads.  Not a probe of layout: a measuring stick for the streaming
+//     kernels (the W8A8 GEMV reads its weights this way, 8 KiB per wave).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -121,7 +129,47 @@ __global__ __launch_bounds__(64) void probe_mfma_kernel(const char* A, const cha
     }
 }
 
+// every index is checked against n16 (the 16-byte chunks of the buffer), so
+// no load leaves it whatever the grid
+template <int PER>
+__global__ __launch_bounds__(1024) void probe_stream_read_kernel(const u32x4* p, uint64_t n16, uint32_t* out) {
+    const uint64_t wave = (uint64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const uint64_t lane = threadIdx.x & 63;
+    const uint64_t base = wave * (uint64_t)(PER * 64);
+    u32x4 v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const uint64_t idx = base + (uint64_t)i * 64 + lane;
+        v[i] = idx < n16 ? __builtin_nontemporal_load(p + idx) : u32x4{0u, 0u, 0u, 0u};
+    }
+    uint32_t acc = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc ^= v[i][0] ^ v[i][1] ^ v[i][2] ^ v[i][3];
+    if (acc == 0x9E3779B9u && lane == 0) out[0] = acc;   // keeps the loads; (practically) never stores
+}
+
 }  // namespace mpdt
+
+MPDT_EXPORT int mpdt_probe_stream_read(const void* p, uint64_t bytes, int per_lane, int waves,
+                                       uint32_t* out, void* stream) {
+    if (waves < 1 || waves > 16 || !p || !out) return (int)hipErrorInvalidValue;
+    const uint64_t n16 = bytes / 16;
+    if (n16 == 0) return 0;
+    const uint64_t per_wave = (uint64_t)per_lane * 64;
+    const uint64_t nwaves = (n16 + per_wave - 1) / per_wave;
+    const uint64_t grid = (nwaves + waves - 1) / waves;
+    if (grid > 0x7fffffffull) return (int)hipErrorInvalidValue;
+    const dim3 g((unsigned)grid), b((unsigned)(64 * waves));
+    hipStream_t s = (hipStream_t)stream;
+    const mpdt::u32x4* q = (const mpdt::u32x4*)p;
+    switch (per_lane) {
+        case 4: hipLaunchKernelGGL(mpdt::probe_stream_read_kernel<4>, g, b, 0, s, q, n16, out); break;
+        case 8: hipLaunchKernelGGL(mpdt::probe_stream_read_kernel<8>, g, b, 0, s, q, n16, out); break;
+        case 16: hipLaunchKernelGGL(mpdt::probe_stream_read_kernel<16>, g, b, 0, s, q, n16, out); break;
+        default: return (int)hipErrorInvalidValue;
+    }
+    return (int)hipGetLastError();
+}
 
 MPDT_EXPORT int mpdt_probe_tr(int bits, const void* image, const uint32_t* offsets, void* out,
                               void* stream) {
