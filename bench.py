@@ -126,6 +126,12 @@ def stats(per, region_ms=None, steps=None):
     return out
 
 
+def note(msg):
+    """One progress line on stderr per finished section (stdout keeps the
+    single JSON line)."""
+    print(f"# bench: section {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -163,6 +169,7 @@ def main():
     extra = {}
     result = None
 
+    note("headline: BF16 4096^3")
     # ---------------- headline: BF16 4096^3 -----------------------------------
     if want("bf16"):
         M = N = K = 4096
@@ -208,6 +215,7 @@ def main():
             result["cpu_baseline"] = cpu_baseline_gemm16(A, B, C, "bf16", args.cpu_seconds)
         del tA, tB, tC, tD
 
+    note("BF16 4096^3 with a BF16 D (16-bit-output variant)")
     # ---------------- BF16 4096^3 with a BF16 D (16-bit-output variant) -------
     if want("bf16out"):
         M = N = K = 4096
@@ -225,6 +233,7 @@ def main():
                          "frac": tf / PEAK_BF16}}
         del tA, tB, tC, tD
 
+    note("BF16 4096^3 + bias + GELU into BF16 (fused epilogue)")
     # ---------------- BF16 4096^3 + bias + GELU into BF16 (fused epilogue) ------
     if want("epi"):
         M = N = K = 4096
@@ -244,12 +253,14 @@ def main():
                          "frac": tf / PEAK_BF16}}
         del tA, tB, tC, tb, tD
 
+    note("practical HBM read ceiling")
     # ---------------- practical HBM read ceiling ------------------------------
     ceiling = None
     if (want("gemv") or want("ceiling")) and not args.child:
         ceiling = read_ceiling(args, stream)
         extra["hbm_read_ceiling"] = ceiling
 
+    note("W8A8 GEMV, cold cache")
     # ---------------- W8A8 GEMV, cold cache ------------------------------------
     if want("gemv"):
         N, K = 14336, 4096
@@ -287,6 +298,7 @@ def main():
             extra["gemv_w8a8"]["cpu_baseline"] = cpu_baseline_gemv(x, s_x, W, s_w, nbytes)
         del tWs
 
+    note("W8A8 layer for a few tokens, cold cache")
     # ---------------- W8A8 layer for a few tokens, cold cache --------------------
     if want("w8a8_tokens"):
         N, K = 14336, 4096
@@ -341,6 +353,7 @@ def main():
                                  "frac": gbs / PEAK_HBM}}
         del tWs
 
+    note("quantisers")
     # ---------------- quantisers -----------------------------------------------
     if want("quant"):
         r = np.random.default_rng(13)
@@ -382,6 +395,7 @@ def main():
                          "frac": gbs / PEAK_HBM}}
         del tA, tq
 
+    note("FP8 block-scaled 4096 x 7168 x 7168")
     # ---------------- FP8 block-scaled 4096 x 7168 x 7168 ----------------------
     if want("fp8"):
         M, N, K = 4096, 7168, 7168
@@ -430,6 +444,7 @@ def main():
                          "frac": tf / PEAK_FP8}}
         del ta, tb, td, tb5
 
+    note("FP16 ragged 8191 x 8193 x 4099")
     # ---------------- FP16 ragged 8191 x 8193 x 4099 ---------------------------
     if want("f16_ragged"):
         M, N, K = 8191, 8193, 4099
@@ -449,6 +464,7 @@ def main():
             extra["gemm_f16_ragged"]["cpu_baseline"] = cpu_baseline_gemm16(A, B, C, "f16", args.cpu_seconds / 3)
         del tA, tB, tC, tD
 
+    note("FP16 64^3 (latency)")
     # ---------------- FP16 64^3 (latency) --------------------------------------
     if want("f16_64"):
         A, B, C = inputs.gemm16_operands(64, 64, 64, dist="uniform", fmt="f16")
@@ -461,6 +477,7 @@ def main():
         if not args.no_cpu_baseline and not args.child:
             extra["gemm_f16_64"]["cpu_baseline"] = cpu_baseline_small(A, B, C)
 
+    note("INT8 4096^3")
     # ---------------- INT8 4096^3 ----------------------------------------------
     if want("i8"):
         M = N = K = 4096
@@ -479,6 +496,7 @@ def main():
             extra["gemm_i8_i32"]["cpu_baseline"] = cpu_baseline_i8(A, B, C, args.cpu_seconds / 3)
         del tA, tB, tC, tD
 
+    note("plain copy (counter calibration)")
     # ---------------- plain copy (counter calibration) -------------------------
     if args.only == "copy":
         n = 256 << 20
