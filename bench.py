@@ -703,7 +703,7 @@ def smi_clocks(launch, stream, n=4000):
     if not data:
         return None
     card = next(iter(data.values()))
-    return {k.split(" ")[0]: v for k, v in card.items() if isinstance(v, str) and "clk" in k.lower()}
+    return {k.rstrip(":").strip(): v for k, v in card.items() if isinstance(v, str) and "clk" in k.lower()}
 
 
 def read_ceiling(args, stream):
