@@ -116,6 +116,36 @@ def timed(fn, steps, warmup, stream):
     return region, [a.elapsed_time(b) for a, b in ev]
 
 
+def timed_graph(fn, period, reps, warmup, stream, before_replay=None):
+    """The calls fn(0) .. fn(period - 1) (one rotation over the rotating
+    inputs) captured once into a HIP graph, which is replayed `warmup` times
+    untimed and then `reps` times between two HIP events: the kernels run
+    back to back at the GPU's own pace, with no host launch cost between
+    them (a short kernel launched one call at a time from Python waits on
+    the host).  Returns (region_ms, steps = reps * period)."""
+    import torch
+    for i in range(period):                 # eager calls first (lazy set-up outside the capture)
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(period):
+            fn(i)
+    if before_replay is not None:           # (e.g. clear the outputs, so a check after
+        before_replay()                     #  the replays sees only what they wrote)
+        torch.cuda.synchronize()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    r1.record(stream)
+    torch.cuda.synchronize()
+    return r0.elapsed_time(r1), reps * period
+
+
 def stats(per, region_ms=None, steps=None):
     s = sorted(per)
     n = len(s)
@@ -271,9 +301,18 @@ def main():
         ty = torch.empty(N, dtype=torch.bfloat16, device=dev)
         region, per = timed(lambda i: mp.gemv_w8a8(tx, float(s_x), tWs[i % copies], tsw, out=ty),
                             args.steps, args.warmup, stream)
+        y_eager = ty.clone()
         st = stats(per, region, args.steps)
         nbytes = N * K + K + 4 * N + 4 + 2 * N      # W + x + s_w + s_x + y (algorithmic)
         gbs = nbytes / (st["mean_us"] * 1e-6) / 1e9
+        # the same rotation replayed from a HIP graph (no host cost between
+        # launches; checked against the eager result)
+        reps = max(args.steps // copies, 4)
+        region_g, gsteps = timed_graph(lambda i: mp.gemv_w8a8(tx, float(s_x), tWs[i % copies], tsw, out=ty),
+                                       copies, reps, max(args.warmup // copies, 8), stream,
+                                       before_replay=lambda: ty.fill_(-1.0))
+        assert torch.equal(ty, y_eager), "graph replays must give the eager result"
+        graph_us = 1e3 * region_g / gsteps
         region_w, per_w = timed(lambda i: mp.gemv_w8a8(tx, float(s_x), tWs[0], tsw, out=ty),
                                 args.steps, args.warmup, stream)
         stw = stats(per_w, region_w, args.steps)
@@ -282,14 +321,17 @@ def main():
             "workload": "batch-1 W8A8 linear, x int8 [4096], W int8 [14336 x 4096] (stored N x K), "
                         "BF16 out; cold: 8 rotating W copies",
             "GB_s": gbs, "algorithmic_bytes": nbytes, "launch_us": st,
-            "region_ms_per_step": region / args.steps,
+            "timing": f"{args.steps} back-to-back launches over {copies} rotating weight copies, "
+                      "between HIP events",
+            "graph_replay": {"mean_us": graph_us, "GB_s": nbytes / (graph_us * 1e-6) / 1e9,
+                             "launches": gsteps},
             "warm_same_W_GB_s": nbytes / (stw["mean_us"] * 1e-6) / 1e9,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s",
                          "frac": gbs / PEAK_HBM,
                          "traffic": traffic_for("gemv_w8a8_14336x4096", digest)},
         }
         if ceiling is not None:
-            c = ceiling["same_bytes_cold_8KiB_per_wave"]["GB_s"]
+            c = max(v["GB_s"] for k, v in ceiling.items() if k.startswith("same_bytes_cold"))
             extra["gemv_w8a8"]["roofline"]["calibrated_ceiling_GB_s"] = c
             extra["gemv_w8a8"]["roofline"]["frac_of_calibrated_ceiling"] = gbs / c
         if spread is not None:
@@ -514,12 +556,17 @@ def main():
 
 
 def gemm_clock(tA, tB, tC, tD, stream, M, N, K, runs=6):
-    """Shader clock the BF16 GEMM runs at, read from the instrumented build of
-    the same kernels (libmpdt_clock.so: per-workgroup s_memtime and
-    s_memrealtime stamps at entry, after the K loop and after the last store),
-    run back-to-back right after the timed region.  Medians over workgroups of
-    the last runs; the clock-adjusted peak scales the 2.5 PFLOP/s spec (quoted
-    at 2.4 GHz) to that clock."""
+    """Where the BF16 GEMM's time goes, read from the instrumented build of the
+    same kernels (libmpdt_clock.so: per-workgroup s_memtime and s_memrealtime
+    stamps at entry, after the K loop and after the last store), run
+    back-to-back right after the timed region.  The workgroups of the last
+    launch are those whose entry stamps lie within a millisecond of the
+    latest.  Reported (medians over the last runs): the shader clock, K-loop
+    and epilogue cycles per workgroup (for each half of the grid when two
+    workgroups share a CU: the first half issues ahead), and the exposed
+    epilogue -- from the last K loop's end to the last store, the part of the
+    kernel no MFMA work overlaps.  The clock-adjusted peak scales the 2.5
+    PFLOP/s spec (quoted at 2.4 GHz) to the measured clock."""
     import ctypes
     import numpy as np
     import torch
@@ -532,30 +579,48 @@ def gemm_clock(tA, tB, tC, tD, stream, M, N, K, runs=6):
     L.gemm_bf16.restype = ctypes.c_int
     L.mpdt_clock_stamps.argtypes = [vp, ctypes.c_int]
     L.mpdt_clock_stamps.restype = ctypes.c_int
-    wgs = (M // 256) * (N // 256)
-    buf = np.zeros(wgs * 6, dtype=np.uint64)
-    clk, loop, epi, wg_us = [], [], [], []
+    cap = 4096
+    buf = np.zeros(cap * 6, dtype=np.uint64)
+    rec = {k: [] for k in ("clk", "loop", "epi", "loop_a", "epi_a", "loop_b", "epi_b", "span", "exposed", "wgs")}
     for r in range(runs):
         rc = L.gemm_bf16(M, N, K, tA.data_ptr(), K, tB.data_ptr(), N, tC.data_ptr(), N,
                          tD.data_ptr(), N, stream.cuda_stream)
         torch.cuda.synchronize()
-        if rc != 0 or L.mpdt_clock_stamps(buf.ctypes.data, wgs) != 0:
+        if rc != 0 or L.mpdt_clock_stamps(buf.ctypes.data, cap) != 0:
             return None
         if r < runs // 2:
             continue
-        q = buf.reshape(wgs, 6).astype(np.float64)
+        q = buf.reshape(cap, 6).astype(np.float64)
+        live = q[:, 3] >= q[:, 3].max() - 100e3          # entry within 1 ms of the latest
+        wgs = int(live.sum())
+        q = q[:wgs] if live[:wgs].all() else q[live]
         real_s = (q[:, 5] - q[:, 3]) / 100e6
-        clk.append(np.median((q[:, 2] - q[:, 0]) / real_s) / 1e9)
-        loop.append(np.median(q[:, 1] - q[:, 0]))
-        epi.append(np.median(q[:, 2] - q[:, 1]))
-        wg_us.append(np.median(real_s) * 1e6)
-    ghz = float(np.median(clk))
-    return {"shader_clock_ghz": ghz, "k_loop_cycles": float(np.median(loop)),
-            "epilogue_cycles": float(np.median(epi)), "workgroup_us": float(np.median(wg_us)),
-            # MFMA-bound K loop: 2MNK FLOP over the workgroups' SIMDs at 1024 FLOP/clk
-            "k_loop_cycles_mfma_bound": 2.0 * M * N * K / 1024.0 / (wgs * 4),
-            "clock_adjusted_peak_tflops": PEAK_BF16 * ghz / 2.4,
-            "source": "libmpdt_clock.so (same kernels + s_memtime/s_memrealtime stamps)"}
+        ghz = np.median((q[:, 2] - q[:, 0]) / real_s) / 1e9
+        rec["clk"].append(ghz)
+        rec["loop"].append(np.median(q[:, 1] - q[:, 0]))
+        rec["epi"].append(np.median(q[:, 2] - q[:, 1]))
+        h = wgs // 2
+        rec["loop_a"].append(np.median(q[:h, 1] - q[:h, 0]))
+        rec["epi_a"].append(np.median(q[:h, 2] - q[:h, 1]))
+        rec["loop_b"].append(np.median(q[h:, 1] - q[h:, 0]))
+        rec["epi_b"].append(np.median(q[h:, 2] - q[h:, 1]))
+        rec["span"].append((q[:, 5].max() - q[:, 3].min()) / 100e6 * 1e6)
+        rec["exposed"].append((q[:, 5].max() - q[:, 4].max()) / 100e6 * ghz * 1e9)
+        rec["wgs"].append(wgs)
+    med = {k: float(np.median(v)) for k, v in rec.items()}
+    wgs = int(med["wgs"])
+    out = {"shader_clock_ghz": med["clk"], "workgroups": wgs,
+           "k_loop_cycles": med["loop"], "epilogue_cycles": med["epi"],
+           "kernel_span_us": med["span"], "exposed_epilogue_cycles": med["exposed"],
+           # MFMA-bound work: 2MNK FLOP at 1024 FLOP per clock and SIMD
+           "mfma_cycles_per_simd": 2.0 * M * N * K / 1024.0 / (256 * 4),
+           "k_loop_cycles_mfma_bound_per_workgroup": 2.0 * M * N * K / 1024.0 / (wgs * 4),
+           "clock_adjusted_peak_tflops": PEAK_BF16 * med["clk"] / 2.4,
+           "source": "libmpdt_clock.so (same kernels + s_memtime/s_memrealtime stamps)"}
+    if wgs > 256:
+        out["first_half"] = {"k_loop_cycles": med["loop_a"], "epilogue_cycles": med["epi_a"]}
+        out["second_half"] = {"k_loop_cycles": med["loop_b"], "epilogue_cycles": med["epi_b"]}
+    return out
 
 
 def cpu_info():
@@ -725,13 +790,16 @@ def read_ceiling(args, stream):
     copies = [torch.ones(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(8)]
 
     def run(buf, n, per, waves):
-        rc = L.mpdt_probe_stream_read(buf.data_ptr(), n, per, waves, sink.data_ptr(), stream.cuda_stream)
+        # torch's current stream: the capture stream while a graph is recorded
+        rc = L.mpdt_probe_stream_read(buf.data_ptr(), n, per, waves, sink.data_ptr(),
+                                      torch.cuda.current_stream().cuda_stream)
         if rc != 0:
             raise RuntimeError(f"mpdt_probe_stream_read failed: {rc}")
-    for per, name in ((8, "same_bytes_cold_8KiB_per_wave"), (16, "same_bytes_cold_16KiB_per_wave")):
-        region, per_l = timed(lambda i: run(copies[i % 8], nbytes, per, 4), args.steps, args.warmup, stream)
-        st = stats(per_l, region, args.steps)
-        out[name] = {"bytes": nbytes, "GB_s": nbytes / (st["mean_us"] * 1e-6) / 1e9, "launch_us": st}
+    for per, waves, name in ((8, 4, "same_bytes_cold_8KiB_per_wave"), (16, 4, "same_bytes_cold_16KiB_per_wave"),
+                             (4, 1, "same_bytes_cold_4KiB_per_wave_1_wave_groups")):
+        region, _ = timed(lambda i: run(copies[i % 8], nbytes, per, waves), args.steps, args.warmup, stream)
+        us = 1e3 * region / args.steps
+        out[name] = {"bytes": nbytes, "GB_s": nbytes / (us * 1e-6) / 1e9, "mean_us": us}
     del copies
     big = 1 << 30
     buf = torch.ones(big // 4, dtype=torch.int32, device=dev)
@@ -739,8 +807,8 @@ def read_ceiling(args, stream):
     region, per_l = timed(lambda i: run(buf, big, 16, 4), steps, 20, stream)
     st = stats(per_l, region, steps)
     out["long_stream_1GiB"] = {"bytes": big, "GB_s": big / (st["mean_us"] * 1e-6) / 1e9, "launch_us": st}
-    out["note"] = ("back-to-back launches between HIP events, like the GEMV timing; the short reads "
-                   "include each launch's start and drain")
+    out["note"] = ("back-to-back launches between HIP events, timed like the GEMV (each launch's start "
+                   "and drain included); short reads rotate 8 copies")
     return out
 
 

@@ -44,8 +44,13 @@ __device__ __forceinline__ int wave_sum(int v) {
     return v;
 }
 
-template <bool ALIGNED>
+// FULL: x and every row of W are 16-byte aligned and K is a whole number of
+// passes (K % 4096 == 0; the host checks it): no chunk is partial, so the
+// loads of a pass carry no bounds, and the weight loads go out first.  The
+// wave's rows past N (only in the last wave) still take the bounded form.
+template <bool ALIGNED, bool FULL = false>
 __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_w8a8_kernel(GemvArgs g) {
+    static_assert(!FULL || ALIGNED, "whole passes need aligned rows");
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int row0 = (blockIdx.x * GEMV_WAVES + wave) * GEMV_ROWS;
@@ -58,6 +63,23 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_w8a8_kernel(GemvArgs g) 
 #pragma unroll
     for (int r = 0; r < GEMV_ROWS; ++r) acc[r] = 0;
 
+    if (FULL && row0 + GEMV_ROWS <= g.N) {
+        for (int64_t kb = 0; kb < kbytes; kb += 64 * 16 * GEMV_U) {
+            u32x4 wv[GEMV_ROWS][GEMV_U], xv[GEMV_U];
+#pragma unroll
+            for (int r = 0; r < GEMV_ROWS; ++r)
+#pragma unroll
+                for (int u = 0; u < GEMV_U; ++u)
+                    wv[r][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                        (const char*)g.W + (int64_t)(row0 + r) * g.ldw + kb + 16 * (lane + 64 * u)));
+#pragma unroll
+            for (int u = 0; u < GEMV_U; ++u) xv[u] = load16_fast(x + kb + 16 * (lane + 64 * u));
+#pragma unroll
+            for (int r = 0; r < GEMV_ROWS; ++r)
+#pragma unroll
+                for (int u = 0; u < GEMV_U; ++u) acc[r] = dot16(wv[r][u], xv[u], acc[r]);
+        }
+    } else
     for (int64_t kb = 0; kb < kbytes; kb += 64 * 16 * GEMV_U) {
         u32x4 xv[GEMV_U];
         u32x4 wv[GEMV_ROWS][GEMV_U];
@@ -112,7 +134,9 @@ hipError_t launch_gemv_w8a8(const GemvArgs& a, bool aligned, hipStream_t stream)
     if (a.N <= 0) return hipSuccess;
     const int rows_per_wg = GEMV_WAVES * GEMV_ROWS;
     dim3 grid((unsigned)((a.N + rows_per_wg - 1) / rows_per_wg)), block(64 * GEMV_WAVES);
-    if (aligned)
+    if (aligned && a.K % (64 * 16 * GEMV_U) == 0)
+        hipLaunchKernelGGL((gemv_w8a8_kernel<true, true>), grid, block, 0, stream, a);
+    else if (aligned)
         hipLaunchKernelGGL(gemv_w8a8_kernel<true>, grid, block, 0, stream, a);
     else
         hipLaunchKernelGGL(gemv_w8a8_kernel<false>, grid, block, 0, stream, a);
