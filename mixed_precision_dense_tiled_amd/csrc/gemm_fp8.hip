@@ -385,11 +385,11 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
     // column j*32 + 8*r4 + 4*lhalf + q: four consecutive columns per r4, one
     // 8-byte LDS write.  Each wave stages its 64 x 128 tile row-major (256
     // bytes per row, 16-byte chunks XOR-swizzled by row) and writes it out in
-    // 16-byte pieces of whole rows.  Rows 16-31 of each 32-row group keep
-    // the two 8-byte halves of a chunk in swapped places, so the 32 lanes of
-    // a half-wave (rows r and r + 16 share a chunk position) write 32
-    // distinct 8-byte slots -- all 64 banks once, no conflict; the reads
-    // swap them back.
+    // 16-byte pieces of whole rows.  The LDS serves 128 bytes (32 banks of
+    // 4 bytes) per pass, 16 lanes of an 8-byte write: rows r and r + 8 of
+    // those 16 lanes share a chunk position modulo 8, so rows whose bit 3 is
+    // set keep the two 8-byte halves of a chunk in swapped places and the 16
+    // lanes cover all 32 banks once (no conflict); the reads swap them back.
     if constexpr (ROWS) {
         // one scale per row of A and per column of B (increments ld_sa,
         // ld_sb: 1, or 0 for one scale per tensor); full tiles only here
@@ -423,7 +423,7 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
                 v[1] = (uint32_t)f32_to_bf16_bits(acc[i][j][4 * r4 + 2]) |
                        ((uint32_t)f32_to_bf16_bits(acc[i][j][4 * r4 + 3]) << 16);
                 *reinterpret_cast<MPDT_LDS u32x2*>(reg + row * 256 + ((c ^ (row & 15)) << 4) +
-                                                   8 * (lhalf ^ ((row >> 4) & 1))) = v;
+                                                   8 * (lhalf ^ ((row >> 3) & 1))) = v;
             }
     uint16_t* const dbase = (uint16_t*)g.D + (int64_t)(m0 + wm * C::WM) * g.ldd + n0 + wn * C::WN;
 #pragma unroll 4
@@ -431,7 +431,7 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
         const int idx = q * 64 + lane;
         const int row = idx >> 4, c = idx & 15;
         u32x4 v = lds_load16(reg, (uint32_t)(row * 256 + ((c ^ (row & 15)) << 4)));
-        if ((row >> 4) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+        if ((row >> 3) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
         *reinterpret_cast<u32x4*>(dbase + (int64_t)row * g.ldd + c * 8) = v;
     }
 #ifdef MPDT_CLOCK_STAMPS
