@@ -34,6 +34,7 @@ PEAK_INT8 = 5000.0      # TOP/s
 PEAK_HBM = 8000.0       # GB/s
 
 METRIC = "TFLOP/s & % MFMA peak (BF16 4096³); GB/s & % HBM peak (W8A8 GEMV)"
+GEMM_SOURCES = ("gemm.hip", "gemm_kernel.hpp", "gemm_common.hpp", "device_common.hpp")
 
 
 def parse():
@@ -212,8 +213,7 @@ def main():
         flop = 2.0 * M * N * K
         avg_s = st["mean_us"] * 1e-6
         achieved = flop / avg_s / 1e12
-        digest = source_digest("gemm.hip", "gemm_kernel.hpp", "gemm_common.hpp", "device_common.hpp")
-        traffic = traffic_for("gemm_bf16_4096", digest)
+        traffic = traffic_for("gemm_bf16_4096", source_digest(*GEMM_SOURCES))
         clock = None if (args.no_clock or args.child) else gemm_clock(tA, tB, tC, tD, stream, M, N, K)
         smi = None if args.child else smi_clocks(lambda: mp.gemm_bf16(tA, tB, tC, out=tD), stream)
         result = {
@@ -501,10 +501,22 @@ def main():
             "workload": "FP16 8191x8193x4099 tight leading dims, C=0, FP32 out",
             "TFLOP_s": tf, "launch_us": st,
             "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP16, "unit": "TFLOP/s",
-                         "frac": tf / PEAK_FP16}}
+                         "frac": tf / PEAK_FP16,
+                         "traffic": traffic_for("gemm_f16_ragged", source_digest(*GEMM_SOURCES))}}
         if not args.no_cpu_baseline and not args.child:
             extra["gemm_f16_ragged"]["cpu_baseline"] = cpu_baseline_gemm16(A, B, C, "f16", args.cpu_seconds / 3)
         del tA, tB, tC, tD
+        if not args.child:
+            # the same tiles and rounds with aligned rows (8192 x 8192 x 4096):
+            # what the tight, 2-byte-aligned leading dimensions cost
+            Aa, Ba, Ca = inputs.gemm16_operands(8192, 8192, 4096, dist="uniform", fmt="f16", c_zero=True)
+            tA, tB, tC = to_dev(Aa), to_dev(Ba), to_dev(Ca)
+            tD = torch.empty((8192, 8192), dtype=torch.float32, device=dev)
+            region, per = timed(lambda i: mp.gemm_f16(tA, tB, tC, out=tD), steps, args.warmup, stream)
+            sta = stats(per, region, steps)
+            extra["gemm_f16_ragged"]["aligned_8192x8192x4096_same_tiles"] = {
+                "launch_us": sta, "TFLOP_s": 2.0 * 8192 * 8192 * 4096 / (sta["mean_us"] * 1e-6) / 1e12}
+            del tA, tB, tC, tD
 
     note("FP16 64^3 (latency)")
     # ---------------- FP16 64^3 (latency) --------------------------------------
@@ -533,7 +545,8 @@ def main():
         extra["gemm_i8_i32"] = {"workload": "INT8 4096^3, INT32 C/D", "TOP_s": tops,
                                 "launch_us": st,
                                 "roofline": {"bound": "mfma", "achieved": tops, "peak": PEAK_INT8,
-                                             "unit": "TOP/s", "frac": tops / PEAK_INT8}}
+                                             "unit": "TOP/s", "frac": tops / PEAK_INT8,
+                                             "traffic": traffic_for("gemm_i8_4096", source_digest(*GEMM_SOURCES))}}
         if not args.no_cpu_baseline and not args.child:
             extra["gemm_i8_i32"]["cpu_baseline"] = cpu_baseline_i8(A, B, C, args.cpu_seconds / 3)
         del tA, tB, tC, tD

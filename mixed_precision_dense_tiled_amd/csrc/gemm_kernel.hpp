@@ -912,6 +912,22 @@ void gemm_kernel(GemmArgs g) {
         using OutT = typename decltype(out_tag)::type;
         constexpr int ACT = decltype(act_tag)::value;
         OutT* const Dp = (OutT*)g.D;
+        // Edge tiles: buffer resources over C and D from the wave's first row
+        // (wrow0) to the last element of each (none past M: empty); the
+        // buffer form is taken while every range stays below 2^31 bytes and
+        // every scalar row offset below 2^30.
+        const int wrow0 = m0 + wm * C::WM;
+        const int64_t rows_left = (int64_t)g.M - wrow0;
+        const int64_t spanD = rows_left > 0 ? ((rows_left - 1) * g.ldd + g.N) * (int64_t)sizeof(OutT) : 0;
+        const int64_t spanC = (rows_left > 0 && Cp) ? ((rows_left - 1) * g.ldc + g.N) * (int64_t)sizeof(CT) : 0;
+        const bool edge_buf = !full_mn && spanD < (int64_t(1) << 31) && spanC < (int64_t(1) << 31) &&
+                              (int64_t)C::WM * g.ldd * (int64_t)sizeof(OutT) < (int64_t(1) << 30) &&
+                              (int64_t)C::WM * g.ldc * (int64_t)sizeof(CT) < (int64_t(1) << 30);
+        const __amdgpu_buffer_rsrc_t rs_d =
+            buffer_rsrc(Dp + (rows_left > 0 ? (int64_t)wrow0 * g.ldd : 0), (uint32_t)(edge_buf ? spanD : 0));
+        const __amdgpu_buffer_rsrc_t rs_c =
+            buffer_rsrc(Cp ? (const void*)(Cp + (rows_left > 0 ? (int64_t)wrow0 * g.ldc : 0)) : (const void*)Dp,
+                        (uint32_t)(edge_buf ? spanC : 0));
         // a: an accumulator element (FP32; INT32 for INT8, kept exact); j:
         // the 32-column block of the wave tile it belongs to
         auto out_val = [&](auto a, CT c, int j) -> OutT {
@@ -1021,10 +1037,61 @@ void gemm_kernel(GemmArgs g) {
                 for (int r = 0; r < 16; ++r) zero[r] = (CT)0;
                 static_for<0, NTILE>([&](auto T) { store_t(decltype(T)::value, zero); });
             }
+        } else if (edge_buf) {
+            // Edge tile through buffer loads and stores, streamed like an
+            // interior tile: each resource starts at the wave's first row and
+            // ends at the last element of C / D, so rows at or past M fall
+            // outside it and the hardware drops their stores (their loads read
+            // zero) with no branch; a column outside [n0, N) gets a lane
+            // offset of 0xC0000000, far past any range (edge_buf guarantees
+            // ranges below 2^31 and scalar offsets below 2^30, so the sum
+            // never wraps).  Lane offset: 4 lhalf rows plus the column; scalar
+            // offset: the row within the wave tile, wave-uniform.
+            constexpr uint32_t OUT_B = sizeof(OutT), C_B = sizeof(CT);
+            uint32_t voD[C::TN], voC[C::TN];
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j) {
+                const int col = col_base + j * 32;
+                const bool cok = col < g.N && col >= n0;
+                voD[j] = cok ? (uint32_t)(4 * (int)lhalf * g.ldd + col) * OUT_B : 0xC0000000u;
+                voC[j] = cok ? (uint32_t)(4 * (int)lhalf * g.ldc + col) * C_B : 0xC0000000u;
+            }
+            auto so = [&](int t, int r, int64_t ld, uint32_t esz) {
+                return (uint32_t)(((t / C::TN) * 32 + 8 * (r >> 2) + (r & 3)) * ld) * esz;
+            };
+            auto load_c = [&](int t, CT (&cv)[16]) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    if constexpr (KD != Kind::FP8) {
+                        const uint32_t bits = __builtin_amdgcn_raw_buffer_load_b32(rs_c, voC[t % C::TN],
+                                                                                    so(t, r, g.ldc, C_B), 0);
+                        cv[r] = __builtin_bit_cast(CT, bits);
+                    } else {
+                        cv[r] = (CT)0;
+                    }
+                }
+            };
+            CT cbuf[2][16];
+            load_c(0, cbuf[0]);
+            static_for<0, NTILE>([&](auto T) {
+                constexpr int t = decltype(T)::value;
+                if constexpr (t + 1 < NTILE) load_c(t + 1, cbuf[(t + 1) & 1]);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const OutT o = out_val(acc[t / C::TN][t % C::TN][r], cbuf[t & 1][r], t % C::TN);
+                    if constexpr (sizeof(OutT) == 4)
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o), rs_d, voD[t % C::TN],
+                                                              so(t, r, g.ldd, OUT_B), 0);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)o, rs_d, voD[t % C::TN],
+                                                              so(t, r, g.ldd, OUT_B), 0);
+                }
+            });
         } else {
-            // Edge tile: every element checked; as above, C of the next 32x32
-            // tile is read (masked) before this one is stored, so the reads
-            // are not one round trip per element.
+            // Edge tile with offsets too large for the buffer form: every
+            // element checked; as above, C of the next 32x32 tile is read
+            // (masked) before this one is stored, so the reads are not one
+            // round trip per element.
             auto ok = [&](int t, int r) {
                 const int row = row_base + (t / C::TN) * 32 + 8 * (r >> 2) + (r & 3);
                 const int col = col_base + (t % C::TN) * 32;
