@@ -134,6 +134,9 @@ void gemm_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(NS > 3 ? 1024 : 16))) char sB3[NS > 3 ? C::B_BYTES : 16];
     __shared__ __attribute__((aligned(NS > 4 ? 1024 : 16))) char sA4[NS > 4 ? C::A_BYTES + C::SA_BYTES : 16];
     __shared__ __attribute__((aligned(NS > 4 ? 1024 : 16))) char sB4[NS > 4 ? C::B_BYTES : 16];
+    // One-wave kernel: each wave's 32 x 32 block of C on its way into the
+    // accumulators during the K loop (4 KiB per wave).
+    __shared__ __attribute__((aligned(1024))) char sCf[ONE_WAVE ? (C::NT / 64) * 4096 : 16];
     // FP8 keeps the A-row scales of a stage's K tile right after its A tile.
     auto scales_of = [&](char* a) -> MPDT_LDS float* {
         if constexpr (C::SA_BYTES > 0) return (MPDT_LDS float*)(lds_cast(a) + C::A_BYTES);
@@ -187,8 +190,11 @@ void gemm_kernel(GemmArgs g) {
     } else {
         tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
     }
-    const int m0 = tm * C::BM;
-    const int n0 = tn * C::BN;
+    // (the tile indices come out of VALU integer divisions; taken back to
+    // scalar registers here, so that everything derived from them -- the
+    // buffer resources of the direct loads above all -- stays scalar)
+    const int m0 = __builtin_amdgcn_readfirstlane(tm) * C::BM;
+    const int n0 = __builtin_amdgcn_readfirstlane(tn) * C::BN;
     // One-wave kernel: the last tile column of a problem whose B rows end
     // inside a 16-byte chunk is loaded from column N - BN, so that no 16-byte
     // load runs past B's end, and stores only its own columns [n0, N).
@@ -463,6 +469,9 @@ void gemm_kernel(GemmArgs g) {
     };
 
     // ---- K loop -------------------------------------------------------------
+    // c_folded: C was added to the accumulators inside the K loop (one-wave
+    // interior tiles), so the epilogue only writes D.
+    bool c_folded = false;
     const bool direct = ALIGNED && full_mn && g.lda_b < (int64_t(1) << 31) / C::BM &&
                         g.ldb_b < (int64_t(1) << 31) / C::KROWS;
     if constexpr (ONE_WAVE) {
@@ -614,6 +623,55 @@ void gemm_kernel(GemmArgs g) {
             // issues tiles 0..NS-2 whole and tile NS-1's A half; iteration 0
             // issues its B half.
             i32x4 ra_c, rb_c;   // resources of the tile whose B half is due next
+
+            // C inside the K loop.  On a full interior tile with C, C's reads
+            // need not wait for the last MFMA: every CU would otherwise read
+            // its 256 KiB of C at the same moment after its K loop, with the
+            // memory idle before.  Each wave brings its sixteen 32 x 32
+            // blocks of C into its own 4 KiB of LDS, one block every c_step K
+            // tiles (four 1 KiB direct loads at the end of an iteration), and
+            // adds the block to its accumulators c_step iterations later:
+            // by then the block has landed, since the barrier wait of the
+            // third iteration after its loads retires every older load of
+            // this wave (reads retire in order).  The loads of the next block
+            // go out only after the previous block's LDS reads are complete.
+            // The sum is taken in a different order than with C added last
+            // (C joins after the first partial sums) -- the same FP32 adds
+            // otherwise, exact for INT32.
+            constexpr int CB = (int)sizeof(typename std::conditional<KD == Kind::I8, int32_t, float>::type);
+            const int64_t ldc_b = g.ldc * (int64_t)CB;
+            const int c_step = (nt - 2) / 16;
+            c_folded = full_mn && g.C != nullptr && c_step >= 3 && ldc_b >= 128 &&
+                       ldc_b < (int64_t(1) << 31) / 32;
+            MPDT_LDS char* const sCw = lds_cast(sCf) + wave * 4096;
+            // lane l of piece u: row 8 u + l / 8 of the block, bytes 16 (l % 8)
+            const uint32_t voffC = (uint32_t)(lane >> 3) * (uint32_t)ldc_b + (uint32_t)(lane & 7) * 16u;
+            auto c_load = [&](int q) __attribute__((always_inline)) {
+                const int64_t row = m0 + wm * C::WM + 32 * (q >> 2), col = n0 + wn * C::WN + 32 * (q & 3);
+                const i32x4 rc = rsrc_words((uint64_t)(uintptr_t)g.C + (uint64_t)((row * g.ldc + col) * CB),
+                                            (uint32_t)(32 * ldc_b));
+                // the previous block's LDS reads have completed before its
+                // buffer is refilled
+                asm volatile("" ::: "memory");
+                wait_lds();
+                lds_dma16<0, true>(rc, sCw, voffC, 0u);
+                lds_dma16<0, true>(rc, sCw + 1024, voffC, (uint32_t)(8 * ldc_b));
+                lds_dma16<0, true>(rc, sCw + 2048, voffC, (uint32_t)(16 * ldc_b));
+                lds_dma16<0, true>(rc, sCw + 3072, voffC, (uint32_t)(24 * ldc_b));
+            };
+            // add block q (accumulator tile q / 4, q % 4) from LDS: lane
+            // element r is row 8 (r / 4) + 4 lhalf + r % 4, column lrow
+            auto c_add = [&](auto Q) __attribute__((always_inline)) {
+                constexpr int q = decltype(Q)::value;
+                Acc cv;
+                static_for<0, 16>([&](auto R) __attribute__((always_inline)) {
+                    constexpr int r = decltype(R)::value;
+                    const uint32_t off = (uint32_t)(8 * (r >> 2) + 4 * (int)lhalf + (r & 3)) * 128u + lrow * 4u;
+                    if constexpr (KD == Kind::I8) cv[r] = *(const MPDT_LDS int32_t*)(sCw + off);
+                    else cv[r] = *(const MPDT_LDS float*)(sCw + off);
+                });
+                acc[q / C::TN][q % C::TN] += cv;
+            };
 #pragma unroll
             for (int p = 0; p < NS; ++p) {
                 const bool lastp = p == nt - 1;
@@ -633,7 +691,8 @@ void gemm_kernel(GemmArgs g) {
             for (int r = 0; r < 7; ++r) read_group(fr, 0, r, 0);
             int scur = 0;
             int64_t kA = (int64_t)NS * C::KT_BYTES, kB = (int64_t)NS * stepB;   // tile t+NS
-            for (int t = 0; t < nt - 1; ++t) {
+            // one K-loop iteration (K tile t)
+            auto iter = [&](int t) __attribute__((always_inline)) {
                 const int snext = scur + 1 == NS ? 0 : scur + 1;
                 const int sprev = scur == 0 ? NS - 1 : scur - 1;   // stage of tile t - 1 + NS
                 const uint32_t cur = (uint32_t)scur * STAGE_BYTES;
@@ -671,6 +730,23 @@ void gemm_kernel(GemmArgs g) {
                 scur = snext;
                 kA += C::KT_BYTES;
                 kB += stepB;
+            };
+            if (c_folded) {
+                // event q after iteration q * c_step: add block q - 1, load
+                // block q; the loop is cut at the events, so each event names
+                // its accumulator tile at compile time
+                int t = 0;
+                static_for<0, C::TM * C::TN + 1>([&](auto Q) __attribute__((always_inline)) {
+                    constexpr int q = decltype(Q)::value;
+                    for (; t <= q * c_step; ++t) iter(t);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (q > 0) c_add(std::integral_constant<int, q - 1>{});
+                    if constexpr (q < C::TM * C::TN) c_load(q);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+                for (; t < nt - 1; ++t) iter(t);
+            } else {
+                for (int t = 0; t < nt - 1; ++t) iter(t);
             }
             // last K tile; if it is partial, only the window bytes [shift,
             // shift + last_bytes) are new K: the fragment bytes outside (the
@@ -793,7 +869,7 @@ void gemm_kernel(GemmArgs g) {
     // the output format: FP32 / INT32, or FP16 / BF16 (one round to nearest
     // even) for the 16-bit-output entry points; FP8 writes BF16.
     using CT = typename std::conditional<KD == Kind::I8, int32_t, float>::type;
-    const CT* const Cp = (const CT*)g.C;
+    const CT* const Cp = c_folded ? nullptr : (const CT*)g.C;
     const int row_base = m0 + wm * C::WM + 4 * (int)lhalf;
     const int col_base = n0_load + wn * C::WN + (int)lrow;
     constexpr int NTILE = C::TM * C::TN;
@@ -841,7 +917,7 @@ void gemm_kernel(GemmArgs g) {
         }
         // (opaque after the K loop, so nothing below is computed early and
         // kept live through it)
-        const float* cptr = (const float*)g.C;
+        const float* cptr = (const float*)Cp;
         asm volatile("" : "+s"(cptr));
         // (on edge tiles the element is clamped into C: what is read for a
         // position outside M x N is never stored, and every lane issues the
