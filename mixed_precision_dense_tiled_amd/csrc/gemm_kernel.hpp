@@ -630,11 +630,12 @@ void gemm_kernel(GemmArgs g) {
             // memory idle before.  Each wave brings its sixteen 32 x 32
             // blocks of C into its own 4 KiB of LDS, one block every c_step K
             // tiles (four 1 KiB direct loads at the end of an iteration), and
-            // adds the block to its accumulators c_step iterations later:
-            // by then the block has landed, since the barrier wait of the
-            // third iteration after its loads retires every older load of
-            // this wave (reads retire in order).  The loads of the next block
-            // go out only after the previous block's LDS reads are complete.
+            // adds the block to its accumulators in phase Y of the iteration
+            // c_step (>= 3) later: by then the block has landed, since the
+            // barrier wait of the third iteration after its loads retires
+            // every older load of this wave (reads retire in order).  The
+            // loads of the next block go out at the end of that iteration,
+            // after the block's LDS reads are complete.
             // The sum is taken in a different order than with C added last
             // (C joins after the first partial sums) -- the same FP32 adds
             // otherwise, exact for INT32.
@@ -659,18 +660,15 @@ void gemm_kernel(GemmArgs g) {
                 lds_dma16<0, true>(rc, sCw + 2048, voffC, (uint32_t)(16 * ldc_b));
                 lds_dma16<0, true>(rc, sCw + 3072, voffC, (uint32_t)(24 * ldc_b));
             };
-            // add block q (accumulator tile q / 4, q % 4) from LDS: lane
-            // element r is row 8 (r / 4) + 4 lhalf + r % 4, column lrow
-            auto c_add = [&](auto Q) __attribute__((always_inline)) {
-                constexpr int q = decltype(Q)::value;
-                Acc cv;
+            // the wave's block of C from LDS: lane element r is row 8 (r / 4) +
+            // 4 lhalf + r % 4, column lrow
+            auto c_read = [&](Acc& cv) __attribute__((always_inline)) {
                 static_for<0, 16>([&](auto R) __attribute__((always_inline)) {
                     constexpr int r = decltype(R)::value;
                     const uint32_t off = (uint32_t)(8 * (r >> 2) + 4 * (int)lhalf + (r & 3)) * 128u + lrow * 4u;
                     if constexpr (KD == Kind::I8) cv[r] = *(const MPDT_LDS int32_t*)(sCw + off);
                     else cv[r] = *(const MPDT_LDS float*)(sCw + off);
                 });
-                acc[q / C::TN][q % C::TN] += cv;
             };
 #pragma unroll
             for (int p = 0; p < NS; ++p) {
@@ -691,8 +689,15 @@ void gemm_kernel(GemmArgs g) {
             for (int r = 0; r < 7; ++r) read_group(fr, 0, r, 0);
             int scur = 0;
             int64_t kA = (int64_t)NS * C::KT_BYTES, kB = (int64_t)NS * stepB;   // tile t+NS
-            // one K-loop iteration (K tile t)
-            auto iter = [&](int t) __attribute__((always_inline)) {
+            // One K-loop iteration (K tile t).  FP >= 0: C's block FP, read
+            // from LDS at the start of phase Y, joins accumulator tile FP on
+            // an MFMA slot of phase Y away from that tile's own MFMA in slot
+            // FP (two slots after it for FP < 8, four before it otherwise):
+            // the adds then run while other tiles' MFMAs execute.
+            auto iter = [&](int t, auto FPc) __attribute__((always_inline)) {
+                constexpr int FP = decltype(FPc)::value;
+                constexpr int FS = FP < 8 ? FP + 2 : FP - 4;   // first slot of the adds
+                Acc cv;
                 const int snext = scur + 1 == NS ? 0 : scur + 1;
                 const int sprev = scur == 0 ? NS - 1 : scur - 1;   // stage of tile t - 1 + NS
                 const uint32_t cur = (uint32_t)scur * STAGE_BYTES;
@@ -719,6 +724,10 @@ void gemm_kernel(GemmArgs g) {
                 static_for<0, 16>([&](auto IDX) {
                     constexpr int idx = decltype(IDX)::value;
                     mma1(fr, 1, idx);
+                    if constexpr (FP >= 0) {
+                        if constexpr (idx == 0) c_read(cv);
+                        if constexpr (idx == FS) acc[FP / C::TN][FP % C::TN] += cv;
+                    }
                     if constexpr ((idx & 3) == 0)
                         dma_piece(std::integral_constant<int, idx / 4>{}, ra, rb, cur);
                     else if constexpr ((idx & 1) == 1 && idx / 2 < 7)
@@ -735,18 +744,22 @@ void gemm_kernel(GemmArgs g) {
                 // event q after iteration q * c_step: add block q - 1, load
                 // block q; the loop is cut at the events, so each event names
                 // its accumulator tile at compile time
+                using NoFold = std::integral_constant<int, -1>;
                 int t = 0;
                 static_for<0, C::TM * C::TN + 1>([&](auto Q) __attribute__((always_inline)) {
                     constexpr int q = decltype(Q)::value;
-                    for (; t <= q * c_step; ++t) iter(t);
-                    __builtin_amdgcn_sched_barrier(0);
-                    if constexpr (q > 0) c_add(std::integral_constant<int, q - 1>{});
-                    if constexpr (q < C::TM * C::TN) c_load(q);
-                    __builtin_amdgcn_sched_barrier(0);
+                    for (; t < q * c_step; ++t) iter(t, NoFold{});
+                    iter(t, std::integral_constant<int, q - 1>{});   // (q = 0: no block yet)
+                    ++t;
+                    if constexpr (q < C::TM * C::TN) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        c_load(q);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 });
-                for (; t < nt - 1; ++t) iter(t);
+                for (; t < nt - 1; ++t) iter(t, NoFold{});
             } else {
-                for (int t = 0; t < nt - 1; ++t) iter(t);
+                for (int t = 0; t < nt - 1; ++t) iter(t, std::integral_constant<int, -1>{});
             }
             // last K tile; if it is partial, only the window bytes [shift,
             // shift + last_bytes) are new K: the fragment bytes outside (the
