@@ -22,7 +22,9 @@
 // In both:
 //   * WG tile BM x BN of D; wave tile (BM / WAVES_M) x (BN / WAVES_N) held in
 //     MFMA accumulators for the whole K loop (acc starts at zero; C is added
-//     once in the epilogue).
+//     once in the epilogue, except on one-wave full tiles with at least 50 K
+//     tiles, where each wave's blocks of C join the accumulators inside the
+//     K loop so that C's reads overlap the MFMAs).
 //   * K is walked in K tiles of KT_BYTES bytes per row (32 FP16/BF16 or 64
 //     INT8 elements; 128 FP8 elements, exactly one scale block).
 //   * Interior tiles with 16-byte aligned rows: buffer loads that write LDS
@@ -54,7 +56,8 @@ namespace mpdt {
 // OUT16 (FP16 / BF16 inputs): D is written in the input format; a separate
 // instantiation, so the two output forms are distinct kernels.
 // BA (FP16 / BF16 inputs): the fused epilogue -- a bias per output column and
-// an activation (GemmArgs::bias, ::act) after C is added.
+// an activation (GemmArgs::bias, ::act) after C is added (in the epilogue, or
+// already inside the K loop).
 // exp(y) through the hardware base-2 exponential (about 1 ulp, plus the
 // rounding of y log2 e: a relative error near |y| 2^-24).
 __device__ __forceinline__ float exp_hw(float y) {
