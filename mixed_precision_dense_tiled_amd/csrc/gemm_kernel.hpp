@@ -1148,15 +1148,21 @@ void gemm_kernel(GemmArgs g) {
                 voD[j] = cok ? (uint32_t)(4 * (int)lhalf * g.ldd + col) * OUT_B : 0xC0000000u;
                 voC[j] = cok ? (uint32_t)(4 * (int)lhalf * g.ldc + col) * C_B : 0xC0000000u;
             }
-            auto so = [&](int t, int r, int64_t ld, uint32_t esz) {
-                return (uint32_t)(((t / C::TN) * 32 + 8 * (r >> 2) + (r & 3)) * ld) * esz;
+            // row pitches in bytes, taken to scalar registers: a scalar
+            // offset the compiler cannot prove uniform becomes a loop over
+            // the lanes' values around every store (edge_buf keeps
+            // WM * pitch below 2^30, so 32 bits hold every offset)
+            const uint32_t pitch_d = __builtin_amdgcn_readfirstlane((uint32_t)(g.ldd * (int64_t)OUT_B));
+            const uint32_t pitch_c = __builtin_amdgcn_readfirstlane((uint32_t)(g.ldc * (int64_t)C_B));
+            auto so = [&](int t, int r, uint32_t pitch) {
+                return (uint32_t)((t / C::TN) * 32 + 8 * (r >> 2) + (r & 3)) * pitch;
             };
             auto load_c = [&](int t, CT (&cv)[16]) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     if constexpr (KD != Kind::FP8) {
                         const uint32_t bits = __builtin_amdgcn_raw_buffer_load_b32(rs_c, voC[t % C::TN],
-                                                                                    so(t, r, g.ldc, C_B), 0);
+                                                                                    so(t, r, pitch_c), 0);
                         cv[r] = __builtin_bit_cast(CT, bits);
                     } else {
                         cv[r] = (CT)0;
@@ -1173,10 +1179,10 @@ void gemm_kernel(GemmArgs g) {
                     const OutT o = out_val(acc[t / C::TN][t % C::TN][r], cbuf[t & 1][r], t % C::TN);
                     if constexpr (sizeof(OutT) == 4)
                         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o), rs_d, voD[t % C::TN],
-                                                              so(t, r, g.ldd, OUT_B), 0);
+                                                              so(t, r, pitch_d), 0);
                     else
                         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)o, rs_d, voD[t % C::TN],
-                                                              so(t, r, g.ldd, OUT_B), 0);
+                                                              so(t, r, pitch_d), 0);
                 }
             });
         } else {
