@@ -1274,7 +1274,8 @@ __device__ __forceinline__ float half_bits_to_f32(uint32_t b) {
 }
 
 template <Kind KD, bool OUT16, bool BA, int NC>
-__global__ __launch_bounds__(256) void gemm_nstrip_kernel(GemmArgs g, int j0) {
+// (two workgroups per CU: at most 256 registers per lane)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gemm_nstrip_kernel(GemmArgs g, int j0) {
     static_assert(KD == Kind::F16 || KD == Kind::BF16, "16-bit inputs");
     // a 64 KiB chunk of the strip; each lane loads all of its 16-byte A
     // pieces of a chunk (PIECES per row) before the first use
@@ -1302,11 +1303,10 @@ __global__ __launch_bounds__(256) void gemm_nstrip_kernel(GemmArgs g, int j0) {
     for (int64_t k0 = 0; k0 < K; k0 += STRIP_KC) {
         const int kc = (int)(K - k0 < STRIP_KC ? K - k0 : STRIP_KC);
         __syncthreads();                          // the previous chunk's reads are done
-        // 8 K elements per piece and row, all in flight while the strip of B
-        // is staged: a full chunk takes plain 16-byte loads (rows need only
-        // element alignment: a 16-byte load from any byte address returns
-        // the bytes there); the last, partial chunk bounded ones (zeros past
-        // K), only for the pieces that reach into it
+        // 8 K elements per piece and row: a full chunk takes plain 16-byte
+        // loads (rows need only element alignment: a 16-byte load from any
+        // byte address returns the bytes there); the last, partial chunk
+        // bounded ones (zeros past K), only for the pieces that reach into it
         u32x4 av[PIECES][4];
         if (kc == STRIP_KC) {
 #pragma unroll
@@ -1323,41 +1323,61 @@ __global__ __launch_bounds__(256) void gemm_nstrip_kernel(GemmArgs g, int j0) {
                                     ? load16_row<false>(arow[q] + (k0 + 8 * lane + 512 * pc) * 2, arow[q] + K * 2)
                                     : u32x4{0u, 0u, 0u, 0u};
         }
-        // the strip of B as FP32, zeros past K and past the strip: a lane
-        // takes a row (rows past K read row k0) with one load of NC
-        // elements, which on every row but B's last stays inside B; the
-        // last row is read element by element
+        // Then the strip of B, every load of the chunk issued before the
+        // first one is used, so that A's and B's round trips overlap.  B: a
+        // thread takes rows tid + 256 it (rows past the chunk read row k0)
+        // with one load of NC elements each, which stays inside B on every
+        // row but B's last; that row is read as row K - 2 in the batch (no
+        // branch between the loads) and element by element beside it, its
+        // elements used by the one thread that holds the row.
+        // (with K = 1 the batch reads row 0 NC columns to the left of the
+        // strip instead -- inside B, since the strip starts at column 256 or
+        // later -- and only the last row's own elements are used)
+        constexpr int BIT = STRIP_KC / 256;
+        uint32_t wb[BIT][NC / 2];
+        const int64_t jb = K >= 2 ? j0 : j0 - NC;
 #pragma unroll
-        for (int it = 0; it < STRIP_KC / 256; ++it) {
+        for (int it = 0; it < BIT; ++it) {
             const int k = tid + 256 * it;
-            const int64_t kr = k0 + (k < kc ? k : 0);
-            const uint16_t* const brow = B + kr * ldb + j0;
-            uint32_t w[NC / 2];
-            if (kr != K - 1) {
-                if constexpr (NC == 4) {
-                    const uint2 x = *reinterpret_cast<const uint2*>(brow);
-                    w[0] = x.x;
-                    w[1] = x.y;
-                } else {
-#pragma unroll
-                    for (int h = 0; h < NC / 8; ++h) {
-                        const u32x4 x = reinterpret_cast<const u32x4*>(brow)[h];
-                        w[4 * h] = x[0];
-                        w[4 * h + 1] = x[1];
-                        w[4 * h + 2] = x[2];
-                        w[4 * h + 3] = x[3];
-                    }
-                }
+            int64_t kr = k0 + (k < kc ? k : 0);
+            kr = (kr == K - 1 && K >= 2) ? K - 2 : kr;
+            const uint16_t* const brow = B + kr * ldb + jb;
+            if constexpr (NC == 4) {
+                const uint2 x = *reinterpret_cast<const uint2*>(brow);
+                wb[it][0] = x.x;
+                wb[it][1] = x.y;
             } else {
 #pragma unroll
-                for (int c = 0; c < NC / 2; ++c)
-                    w[c] = (uint32_t)brow[2 * c < r ? 2 * c : r - 1] |
-                           ((uint32_t)brow[2 * c + 1 < r ? 2 * c + 1 : r - 1] << 16);
+                for (int h = 0; h < NC / 8; ++h) {
+                    const u32x4 x = reinterpret_cast<const u32x4*>(brow)[h];
+                    wb[it][4 * h] = x[0];
+                    wb[it][4 * h + 1] = x[1];
+                    wb[it][4 * h + 2] = x[2];
+                    wb[it][4 * h + 3] = x[3];
+                }
             }
+        }
+        // B's last row: its r elements, read by every thread (the same
+        // addresses for all, no branch); only the thread that holds the row
+        // in this chunk uses them
+        const int64_t kl = K - 1 - k0;   // its index in the chunk
+        const bool own_last = kl < kc && (int)(kl & 255) == tid;
+        uint16_t wl[NC];
+        {
+            const uint16_t* const brow = B + (K - 1) * ldb + j0;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) wl[c] = brow[c < r ? c : r - 1];
+        }
+        // the strip of B in LDS as FP32, zeros past K and past the strip
+#pragma unroll
+        for (int it = 0; it < BIT; ++it) {
+            const int k = tid + 256 * it;
+            const bool last = own_last && (int)(kl >> 8) == it;
             float v[NC];
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                const float x = half_bits_to_f32<KD>((w[c >> 1] >> (16 * (c & 1))) & 0xffffu);
+                const uint32_t bits = last ? (uint32_t)wl[c] : (wb[it][c >> 1] >> (16 * (c & 1))) & 0xffffu;
+                const float x = half_bits_to_f32<KD>(bits);
                 v[c] = (k < kc && c < r) ? x : 0.0f;
             }
 #pragma unroll
