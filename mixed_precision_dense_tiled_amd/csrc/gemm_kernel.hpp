@@ -1085,7 +1085,7 @@ void gemm_kernel(GemmArgs g) {
                     const int idx = q * 64 + lane;
                     const int row = idx / CPR, c = idx % CPR;
                     const u32x4 v = lds_load16(reg, (uint32_t)(row * (C::WN * 2) + c * 16));
-                    *reinterpret_cast<u32x4*>(dbase + (int64_t)row * g.ldd + c * 8) = v;
+                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dbase + (int64_t)row * g.ldd + c * 8));
                 }
                 return;
             }
@@ -1111,9 +1111,11 @@ void gemm_kernel(GemmArgs g) {
             auto store_t = [&](int t, const CT (&cv)[16]) {
                 OutT* dp = dtile(t);
 #pragma unroll
+                // (D is written once and never read here: non-temporal
+                // stores, which keep it from displacing A and B in L2)
                 for (int r = 0; r < 16; ++r)
-                    dp[(int64_t)(8 * (r >> 2) + (r & 3)) * g.ldd] =
-                        out_val(acc[t / C::TN][t % C::TN][r], cv[r], t % C::TN);
+                    __builtin_nontemporal_store(out_val(acc[t / C::TN][t % C::TN][r], cv[r], t % C::TN),
+                                                &dp[(int64_t)(8 * (r >> 2) + (r & 3)) * g.ldd]);
             };
             if (KD != Kind::FP8 && Cp) {
                 CT cbuf[2][16];
