@@ -432,7 +432,7 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
         const int row = idx >> 4, c = idx & 15;
         u32x4 v = lds_load16(reg, (uint32_t)(row * 256 + ((c ^ (row & 15)) << 4)));
         if ((row >> 3) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-        *reinterpret_cast<u32x4*>(dbase + (int64_t)row * g.ldd + c * 8) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dbase + (int64_t)row * g.ldd + c * 8));   // D: written once
     }
 #ifdef MPDT_CLOCK_STAMPS
     __builtin_amdgcn_s_waitcnt(0);
