@@ -426,13 +426,18 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
                                                    8 * (lhalf ^ ((row >> 3) & 1))) = v;
             }
     uint16_t* const dbase = (uint16_t*)g.D + (int64_t)(m0 + wm * C::WM) * g.ldd + n0 + wn * C::WN;
+    const bool d_lines = ((uintptr_t)g.D % 128 == 0) && ((g.ldd * 2) % 128 == 0);
 #pragma unroll 4
     for (int q = 0; q < C::WM * 16 / 64; ++q) {
         const int idx = q * 64 + lane;
         const int row = idx >> 4, c = idx & 15;
         u32x4 v = lds_load16(reg, (uint32_t)(row * 256 + ((c ^ (row & 15)) << 4)));
         if ((row >> 3) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dbase + (int64_t)row * g.ldd + c * 8));   // D: written once
+        // D is written once: non-temporal stores when its rows start on
+        // 128-byte lines (streamed partial lines cost more than they save)
+        u32x4* const dq = reinterpret_cast<u32x4*>(dbase + (int64_t)row * g.ldd + c * 8);
+        if (d_lines) __builtin_nontemporal_store(v, dq);
+        else *dq = v;
     }
 #ifdef MPDT_CLOCK_STAMPS
     __builtin_amdgcn_s_waitcnt(0);

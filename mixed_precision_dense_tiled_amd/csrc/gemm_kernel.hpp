@@ -1004,6 +1004,8 @@ void gemm_kernel(GemmArgs g) {
         using OutT = typename decltype(out_tag)::type;
         constexpr int ACT = decltype(act_tag)::value;
         OutT* const Dp = (OutT*)g.D;
+        // D's rows start on 128-byte lines (base and pitch)
+        const bool d_lines = ((uintptr_t)g.D % 128 == 0) && ((g.ldd * (int64_t)sizeof(OutT)) % 128 == 0);
         // Edge tiles: buffer resources over C and D from the wave's first row
         // (wrow0) to the last element of each (none past M: empty); the
         // buffer form is taken while every range stays below 2^31 bytes and
@@ -1085,7 +1087,9 @@ void gemm_kernel(GemmArgs g) {
                     const int idx = q * 64 + lane;
                     const int row = idx / CPR, c = idx % CPR;
                     const u32x4 v = lds_load16(reg, (uint32_t)(row * (C::WN * 2) + c * 16));
-                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dbase + (int64_t)row * g.ldd + c * 8));
+                    u32x4* const dq = reinterpret_cast<u32x4*>(dbase + (int64_t)row * g.ldd + c * 8);
+                    if (d_lines) __builtin_nontemporal_store(v, dq);   // (as in the FP32 form below)
+                    else *dq = v;
                 }
                 return;
             }
@@ -1110,12 +1114,22 @@ void gemm_kernel(GemmArgs g) {
             };
             auto store_t = [&](int t, const CT (&cv)[16]) {
                 OutT* dp = dtile(t);
+                // D is written once and never read here: with whole 128-byte
+                // lines per row segment (D and its row pitch on 128 bytes),
+                // non-temporal stores, which keep D from displacing A and B in
+                // L2; rows off line boundaries take plain stores (streamed
+                // partial lines cost far more than they save)
+                if (d_lines) {
 #pragma unroll
-                // (D is written once and never read here: non-temporal
-                // stores, which keep it from displacing A and B in L2)
-                for (int r = 0; r < 16; ++r)
-                    __builtin_nontemporal_store(out_val(acc[t / C::TN][t % C::TN][r], cv[r], t % C::TN),
-                                                &dp[(int64_t)(8 * (r >> 2) + (r & 3)) * g.ldd]);
+                    for (int r = 0; r < 16; ++r)
+                        __builtin_nontemporal_store(out_val(acc[t / C::TN][t % C::TN][r], cv[r], t % C::TN),
+                                                    &dp[(int64_t)(8 * (r >> 2) + (r & 3)) * g.ldd]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        dp[(int64_t)(8 * (r >> 2) + (r & 3)) * g.ldd] =
+                            out_val(acc[t / C::TN][t % C::TN][r], cv[r], t % C::TN);
+                }
             };
             if (KD != Kind::FP8 && Cp) {
                 CT cbuf[2][16];
