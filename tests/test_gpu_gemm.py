@@ -321,7 +321,10 @@ def test_fp8_k_zero(gpu_ok):
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
 @pytest.mark.parametrize("M,N,K", [(300, 257, 200), (513, 520, 300), (1000, 784, 4099), (260, 265, 1),
-                                   (17, 512 + 13, 1500), (2049, 1024 + 16, 700)])
+                                   (17, 512 + 13, 1500), (2049, 1024 + 16, 700),
+                                   # the 4-column strip with K = 1, with a last chunk of B's
+                                   # final row alone (4097 = 4096 + 1), over three chunks
+                                   (300, 258, 1), (260, 257, 4097), (130, 259, 8193), (64, 261, 2049)])
 def test_narrow_last_column_strip(gpu_ok, fmt, M, N, K):
     """N a few columns past a multiple of 256: the tiles take the whole
     256-column blocks and the strip kernel the rest.  Integer-valued inputs:
