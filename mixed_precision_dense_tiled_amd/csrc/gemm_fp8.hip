@@ -1,6 +1,7 @@
-// gemm_fp8.hip -- the FP8 E4M3 block-scaled GEMM on full 128 x 256 tiles
-// with one wavefront per SIMD (the general kernel in gemm_kernel.hpp covers edge
-// tiles, unaligned rows and K that is not a whole number of scale blocks).
+// gemm_fp8.hip -- the FP8 E4M3 block-scaled GEMM on 128 x 256 tiles with one
+// wavefront per SIMD (the general kernel in gemm_kernel.hpp covers unaligned
+// rows, K that is not a whole number of scale blocks, M below 128 and N not a
+// multiple of 16).
 //
 // D = sum over 128-wide K blocks of (scale_a[row][kb] * scale_b[kb][col/128])
 // times the FP8 block product, accumulated in FP32 and written as BF16: the
@@ -15,7 +16,7 @@
 namespace mpdt {
 
 // ---------------------------------------------------------------------------
-// FP8 block-scaled GEMM, one wavefront per SIMD, interior tiles.
+// FP8 block-scaled GEMM, one wavefront per SIMD.
 // ---------------------------------------------------------------------------
 // The FP8 path of gemm_kernel (eight wavefronts, 64 x 64 wave tiles, 256
 // registers per lane) reads all fragments of a K tile, then runs its MFMAs,
@@ -95,10 +96,15 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
     int tm, tn;
     tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
-    const int m0 = tm * C::BM, n0 = tn * C::BN;
+    // Edge tiles: the last row tile of a problem whose M is not a multiple of
+    // 128 moves up to end at row M - 1 (M >= 128; rows it shares with the tile
+    // above are computed twice and stored once, from row_lo on); columns past
+    // N read zeros (masked B loads) and are not stored.
+    const int row_lo = __builtin_amdgcn_readfirstlane(tm) * C::BM;
+    const int m0 = min(row_lo, g.M - C::BM), n0 = __builtin_amdgcn_readfirstlane(tn) * C::BN;
     const int nt = g.K / C::KT_BYTES;
-    // (the host launches this kernel over full tiles with whole K tiles only)
-    if (m0 + C::BM > g.M || n0 + C::BN > g.N || g.K % C::KT_BYTES != 0 || nt < NS) return;
+    // (the host launches this kernel with M >= 128 and whole K tiles only)
+    if (m0 < 0 || g.K % C::KT_BYTES != 0 || nt < NS) return;
 
     const uint32_t lrow = lane & 31, lhalf = lane >> 5, grp = lane >> 4, gp = lane & 15;
 
@@ -108,9 +114,11 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
     // the B swizzle every 8 K rows, so even and odd pieces have one lane offset
     // each.  Pieces sharing an M0 value move through the instruction offset,
     // which the scalar offset takes back off the global address.  Each buffer
-    // resource starts at the K tile's first byte and spans exactly the bytes
-    // the tile reads (all inside the operand for a full tile), or nothing
-    // past the last tile.
+    // resource starts at the K tile's first byte and spans the bytes the tile
+    // reads, or nothing past the last tile.  A lane whose 16 B columns lie at
+    // or past N gets a lane offset of 2^31, past every range (whether or not
+    // the range check counts the scalar offset): it reads zeros and touches
+    // no memory.  N is a multiple of 16 here, so a chunk is all in or all out.
     constexpr int RPA = 1024 / C::KT_BYTES, RPB = 1024 / C::B_ROW;
     const uint32_t lda = (uint32_t)g.lda_b, ldb = (uint32_t)g.ldb_b;
     const int lra = lane / C::CPR_A, lrb = lane / C::CPR_B;
@@ -119,8 +127,8 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
     for (int p = 0; p < 2; ++p) {
         voffA[p] = (uint32_t)lra * lda +
                    (((uint32_t)(lane % C::CPR_A) ^ swz_a<C::CPR_A>(p * RPA + lra)) << 4);
-        voffB[p] = (uint32_t)lrb * ldb +
-                   (((uint32_t)(lane % C::CPR_B) ^ swz_b<1>(p * RPB + lrb)) << 4);
+        const uint32_t gc = (uint32_t)(lane % C::CPR_B) ^ swz_b<1>(p * RPB + lrb);
+        voffB[p] = (int)(gc * 16) < g.N - n0 ? (uint32_t)lrb * ldb + (gc << 4) : 0x80000000u;
     }
     auto soffA = [&](int u) __attribute__((always_inline)) {
         return (uint32_t)((wave * C::UA + u) * RPA) * lda - (uint32_t)(u & 3) * 1024u;
@@ -129,7 +137,9 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
         return (uint32_t)((wave * C::UB + u) * RPB) * ldb - (uint32_t)(u & 3) * 1024u;
     };
     const uint32_t rangeA = (uint32_t)(C::BM - 1) * lda + C::KT_BYTES;
-    const uint32_t rangeB = (uint32_t)(C::KROWS - 1) * ldb + C::B_ROW;
+    // (+4 KiB: every live lane's offset stays inside the range also when the
+    // check leaves out the scalar offset and B rows are narrow)
+    const uint32_t rangeB = (uint32_t)(C::KROWS - 1) * ldb + C::B_ROW + 4096u;
     const uint64_t baseA = (uint64_t)(uintptr_t)g.A + (uint64_t)((int64_t)m0 * g.lda_b);
     const uint64_t baseB = (uint64_t)(uintptr_t)g.B + (uint64_t)n0;
     const uint64_t stepB = (uint64_t)C::KROWS * (uint64_t)g.ldb_b;
@@ -142,7 +152,7 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
     const uint32_t ldsa4 = (uint32_t)g.ld_sa * 4u;
     const uint32_t voffS = scaleA ? (uint32_t)((lane >> 1) + 32 * (lane & 1)) * ldsa4
                                   : (uint32_t)(lane & 1) * 4u;
-    const uint32_t rangeS = ROWS ? 0u : scaleA ? 63u * ldsa4 + 4u : 8u;
+    const uint32_t rangeS = ROWS ? 0u : scaleA ? 63u * ldsa4 + 4u : (n0 + 128 < g.N ? 8u : 4u);
     const uint64_t baseS = scaleA ? (uint64_t)(uintptr_t)g.sA + (uint64_t)((int64_t)(m0 + wave * 64) * ldsa4)
                             : (uint64_t)(uintptr_t)g.sB + (uint64_t)(n0 / 128) * 4u;
     const uint64_t stepS = scaleA ? 4u : (uint64_t)g.ld_sb * 4u;
@@ -427,17 +437,50 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
             }
     uint16_t* const dbase = (uint16_t*)g.D + (int64_t)(m0 + wm * C::WM) * g.ldd + n0 + wn * C::WN;
     const bool d_lines = ((uintptr_t)g.D % 128 == 0) && ((g.ldd * 2) % 128 == 0);
+    // rows from row_lo and 8-column pieces left of N (N is a multiple of 16);
+    // the tile's place is worked out again here rather than kept through the
+    // K loop, where every register is taken
+    // (row-scaled problems come here with full tiles only)
+    int row_skip = 0, cols_left = C::WN;
+    if constexpr (!ROWS) {
+        int wg = blockIdx.x, etm, etn;
+        asm volatile("" : "+s"(wg));
+        tile_of(wg, g.tiles_m, g.tiles_n, etm, etn);
+        row_skip = etm * C::BM - (m0 + wm * C::WM);
+        cols_left = g.N - (etn * C::BN + wn * C::WN);
+    }
+    if constexpr (ROWS) {
 #pragma unroll 4
-    for (int q = 0; q < C::WM * 16 / 64; ++q) {
-        const int idx = q * 64 + lane;
-        const int row = idx >> 4, c = idx & 15;
-        u32x4 v = lds_load16(reg, (uint32_t)(row * 256 + ((c ^ (row & 15)) << 4)));
-        if ((row >> 3) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-        // D is written once: non-temporal stores when its rows start on
-        // 128-byte lines (streamed partial lines cost more than they save)
-        u32x4* const dq = reinterpret_cast<u32x4*>(dbase + (int64_t)row * g.ldd + c * 8);
-        if (d_lines) __builtin_nontemporal_store(v, dq);
-        else *dq = v;
+        for (int q = 0; q < C::WM * 16 / 64; ++q) {
+            const int idx = q * 64 + lane;
+            const int row = idx >> 4, c = idx & 15;
+            u32x4 v = lds_load16(reg, (uint32_t)(row * 256 + ((c ^ (row & 15)) << 4)));
+            if ((row >> 3) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+            // D is written once: non-temporal stores when its rows start on
+            // 128-byte lines (streamed partial lines cost more than they save)
+            u32x4* const dq = reinterpret_cast<u32x4*>(dbase + (int64_t)row * g.ldd + c * 8);
+            if (d_lines) __builtin_nontemporal_store(v, dq);
+            else *dq = v;
+        }
+    } else {
+        // Buffer stores over the wave's 64 rows of D: a lane whose piece is
+        // above row_lo or at or past N gets an offset past the range, and its
+        // store is dropped (no branch around the stores).
+        const __amdgpu_buffer_rsrc_t drs = buffer_rsrc(dbase, (uint32_t)(C::WM * 2) * (uint32_t)g.ldd);
+#pragma unroll 4
+        for (int q = 0; q < C::WM * 16 / 64; ++q) {
+            const int idx = q * 64 + lane;
+            const int row = idx >> 4, c = idx & 15;
+            u32x4 v = lds_load16(reg, (uint32_t)(row * 256 + ((c ^ (row & 15)) << 4)));
+            if ((row >> 3) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+            const uint32_t off = (row >= row_skip && c * 8 < cols_left)
+                                     ? ((uint32_t)row * (uint32_t)g.ldd + (uint32_t)(c * 8)) * 2u
+                                     : 0x80000000u;
+            // D is written once: non-temporal stores when its rows start on
+            // 128-byte lines (streamed partial lines cost more than they save)
+            if (d_lines) __builtin_amdgcn_raw_buffer_store_b128(v, drs, off, 0, 2 /* nt */);
+            else __builtin_amdgcn_raw_buffer_store_b128(v, drs, off, 0, 0);
+        }
     }
 #ifdef MPDT_CLOCK_STAMPS
     __builtin_amdgcn_s_waitcnt(0);
@@ -454,11 +497,19 @@ void gemm_fp8_1w_kernel(GemmArgs g) {
 // one wavefront per SIMD: 128 x 256 tiles, 2 x 2 waves, three stages
 using CfgFP8W = Cfg<Kind::FP8, FP8_TILE_M, FP8_TILE_N, 2, 2, 128, 3>;
 
-bool fp8_1w_eligible(const GemmArgs& a, bool aligned) {
+int fp8_1w_mode(const GemmArgs& a, bool aligned) {
     using C = CfgFP8W;
-    return aligned && a.K % C::KT_BYTES == 0 && a.K >= C::STAGES * C::KT_BYTES &&
-           a.lda_b < (int64_t(1) << 31) / C::BM && a.ldb_b < (int64_t(1) << 31) / C::KROWS &&
-           a.ld_sa < (int64_t(1) << 31) / (4 * C::WM) && ((uintptr_t)a.D % 16) == 0 && a.ldd % 8 == 0;
+    const bool full = aligned && a.K % C::KT_BYTES == 0 && a.K >= C::STAGES * C::KT_BYTES &&
+                      a.lda_b < (int64_t(1) << 31) / C::BM && a.ldb_b < (int64_t(1) << 31) / C::KROWS &&
+                      a.ld_sa < (int64_t(1) << 31) / (4 * C::WM) && ((uintptr_t)a.D % 16) == 0 &&
+                      a.ldd % 8 == 0 && a.ldd < (int64_t(1) << 31) / (2 * C::WM);
+    // (B rows of at least 256 bytes: the scalar offsets of the B pieces,
+    // K-row offsets less the 1 KiB steps of the instruction offset, stay
+    // non-negative)
+    if (!full || a.ldb_b < C::B_ROW) return 0;
+    // (the row-scaled variants take full tiles only: their epilogue leaves
+    // no registers for the edge masks)
+    return (a.M >= C::BM && a.N % 16 == 0 && !a.row_scaled) ? 2 : 1;
 }
 
 template <int F8>

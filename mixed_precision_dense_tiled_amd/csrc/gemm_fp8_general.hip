@@ -1,17 +1,21 @@
 // gemm_fp8_general.hip -- host entry of the FP8 GEMMs (block-scaled or
-// row-scaled, E4M3 or E5M2 operands, BF16 D): the full tiles of a problem the
-// one-wave kernel takes (gemm_fp8.hip) go to it, the edge tiles and every
-// other problem to the general kernel (gemm_kernel.hpp), both instantiated
-// for the operand formats and the scaling variant of the call.
+// row-scaled, E4M3 or E5M2 operands, BF16 D): a problem the one-wave kernel
+// takes whole (gemm_fp8.hip) goes to it in one launch; where it takes only
+// the full tiles, the edge tiles go to the general kernel (gemm_kernel.hpp),
+// and so does every other problem; both kernels are instantiated for the
+// operand formats and the scaling variant of the call.
 #include "gemm_kernel.hpp"
 
 namespace mpdt {
 
 template <int F8>
 static hipError_t launch_fp8_t(const GemmArgs& a0, bool aligned, hipStream_t stream) {
-    const bool one = fp8_1w_eligible(a0, aligned);
-    const int int_tm = one ? a0.M / FP8_TILE_M : 0;
-    const int int_tn = one ? a0.N / FP8_TILE_N : 0;
+    const int mode = fp8_1w_mode(a0, aligned);
+    if (mode == 2)
+        return launch_fp8_1w(a0, (a0.M + FP8_TILE_M - 1) / FP8_TILE_M, (a0.N + FP8_TILE_N - 1) / FP8_TILE_N,
+                             stream);
+    const int int_tm = mode ? a0.M / FP8_TILE_M : 0;
+    const int int_tn = mode ? a0.N / FP8_TILE_N : 0;
     if (int_tm > 0 && int_tn > 0) {
         const hipError_t e = launch_fp8_1w(a0, int_tm, int_tn, stream);
         if (e != hipSuccess) return e;

@@ -40,16 +40,19 @@ enum : int { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2, ACT_SILU = 3 };
 
 // aligned: every row start of A and B is 16-byte aligned.
 hipError_t launch_gemm(Kind kind, const GemmArgs& a, bool aligned, hipStream_t stream);
-// The FP8 GEMMs (gemm_fp8_general.hip): full tiles of an eligible problem
-// on the one-wave kernel, the rest on the general kernel.
+// The FP8 GEMMs (gemm_fp8_general.hip): every tile of an eligible problem
+// (or its full tiles only) on the one-wave kernel, the rest on the general
+// kernel.
 hipError_t launch_fp8(const GemmArgs& a, bool aligned, hipStream_t stream);
 // FP16 / BF16 with the fused bias / activation epilogue (gemm_epi.hip).
 hipError_t launch_gemm_epi(Kind kind, const GemmArgs& a, bool aligned, hipStream_t stream);
 
-// FP8 one-wavefront kernel (gemm_fp8.hip) over the full FP8_TILE_M x
-// FP8_TILE_N tiles of a problem it takes (fp8_1w_eligible).
+// FP8 one-wavefront kernel (gemm_fp8.hip) over the FP8_TILE_M x FP8_TILE_N
+// tiles of a problem it takes.  fp8_1w_mode: 0 -- not at all; 1 -- its full
+// tiles only; 2 -- every tile, edge tiles included (M >= FP8_TILE_M and N a
+// multiple of 16 besides what mode 1 needs).
 constexpr int FP8_TILE_M = 128, FP8_TILE_N = 256;
-bool fp8_1w_eligible(const GemmArgs& a, bool aligned);
+int fp8_1w_mode(const GemmArgs& a, bool aligned);
 hipError_t launch_fp8_1w(const GemmArgs& a, int tiles_m, int tiles_n, hipStream_t stream);
 
 struct GemvArgs {

@@ -6,7 +6,7 @@ scales folded in, and relative Frobenius error <= 1e-2.
 
 Operands are quantised from N(0, 1) FP32 data by the oracle's quantiser (the
 E5M2 codes therefore cover about three binades below the block maximum, as
-scaled gradients do); shapes cover full one-wave tiles, edge tiles and a K
+scaled gradients do); shapes cover full one-wave tiles, edge tiles on either kernel and a K
 tail on the general kernel, unaligned rows, per-tensor and per-row scales,
 and a 2048^3 problem checked at sampled outputs."""
 import numpy as np
@@ -43,7 +43,8 @@ def bf16_values(D):
 
 
 @pytest.mark.parametrize("fa,fb", FORMATS)
-@pytest.mark.parametrize("M,N,K,pad", [(256, 512, 512, 0), (300, 520, 260, 0), (200, 300, 333, 3)])
+@pytest.mark.parametrize("M,N,K,pad", [(256, 512, 512, 0), (300, 520, 260, 0), (200, 300, 333, 3),
+                                       (300, 528, 384, 0)])
 def test_blockscaled_formats(gpu_ok, fa, fb, M, N, K, pad):
     qa, sa, qb, sb = quantised(M, N, K, fa, fb, seed=M + N + K + 10 * fa + 20 * fb)
     ta = dev(qa, K + pad) if pad else dev(qa)

@@ -267,9 +267,11 @@ def run_fp8(qa, sa, qb, sb, lda=None, ldb=None):
 
 
 # Full 128 x 256 tiles with whole 128-wide K blocks (at least three) go to the
-# one-wavefront kernel, the rest (edge tiles, short or ragged K) to the
-# general one: (256, 512, 384) and (384, 768, 512) are all one-wave tiles with
-# the fewest K blocks it takes, (300, 600, 768) mixes both kernels in one call.
+# one-wavefront kernel, and so do the edge tiles when N is a multiple of 16
+# and M >= 128; the rest (short or ragged K, edge tiles of other shapes) go to
+# the general one: (256, 512, 384) and (384, 768, 512) are all one-wave tiles
+# with the fewest K blocks it takes, (300, 600, 768) mixes both kernels in one
+# call (N = 600 is not a multiple of 16).
 @pytest.mark.parametrize("M,N,K", [(128, 256, 256), (300, 520, 400), (129, 130, 131),
                                    (1, 1, 1), (256, 512, 1024), (256, 512, 384),
                                    (384, 768, 512), (300, 600, 768)])
@@ -277,6 +279,40 @@ def test_fp8_parity(gpu_ok, M, N, K):
     qa, sa, qb, sb = inputs.fp8_operands(M, N, K, seeds=(M, N))
     got, R, S = run_fp8(qa, sa, qb, sb)
     check_fp(got, R, S, 1e-2, f"fp8 {M}x{N}x{K}", bf16_out=True)
+
+
+# Edge tiles on the one-wavefront kernel: with M >= 128, N a multiple of 16 and
+# whole 128-wide K blocks (at least three), every tile of a block-scaled
+# problem runs there in one launch -- the last row tile moves up to end at row
+# M - 1 (its rows shared with the tile above are stored once), B's columns past
+# N read zeros and D's are not stored.  (129, 272): one stored row and 16
+# columns in the edge tiles; (1000, 1040): a last column tile with 16 columns
+# and no second B scale block; (128, 48) with B rows padded to 256 bytes: a
+# single tile 48 columns wide; (128, 16) with tight B rows (16 bytes, under
+# the 256 the one-wave kernel's B loads need): the general kernel.
+@pytest.mark.parametrize("M,N,K,ldb", [(200, 400, 1024, None), (1000, 1040, 384, None),
+                                       (129, 272, 512, None), (128, 48, 384, 256), (128, 16, 384, None),
+                                       (2000, 2000, 2048, None)])
+def test_fp8_edge_tiles_one_wave(gpu_ok, M, N, K, ldb):
+    qa, sa, qb, sb = inputs.fp8_operands(M, N, K, seeds=(M + 1, N + 2))
+    got, R, S = run_fp8(qa, sa, qb, sb, ldb=ldb)
+    check_fp(got, R, S, 1e-2, f"fp8 edge tiles {M}x{N}x{K} ldb={ldb}", bf16_out=True)
+
+
+def test_fp8_edge_tiles_guard_band(gpu_ok):
+    """Edge tiles with padded rows everywhere: A and B padded with E4M3 NaN
+    codes, D inside a larger buffer.  No NaN reaches D, and nothing right of
+    column N or below row M of the buffer is written."""
+    M, N, K = 200, 400, 768
+    qa, sa, qb, sb = inputs.fp8_operands(M, N, K, seeds=(41, 42))
+    R, S = oracle.gemm_fp8_blockscaled(qa, sa, qb, sb)
+    buf = torch.full((M + 3, N + 16), -1, dtype=torch.int16, device=gpu_ok).view(torch.bfloat16)
+    mp.gemm_fp8_blockscaled(dev(qa, K + 16, pad=0x7F), dev(sa), dev(qb, N + 16, pad=0x7F), dev(sb),
+                            out=buf[:M, :N])
+    torch.cuda.synchronize()
+    whole = host(buf).view(np.uint16)
+    assert (whole[:, N:] == 0xFFFF).all() and (whole[M:] == 0xFFFF).all(), "D written outside M x N"
+    check_fp(oracle.bf16_to_f64(whole[:M, :N]), R, S, 1e-2, "fp8 edge tiles, padded", bf16_out=True)
 
 
 def test_fp8_unaligned_and_unit_scales(gpu_ok):
