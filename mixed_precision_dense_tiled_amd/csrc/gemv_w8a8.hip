@@ -224,6 +224,20 @@ __global__ __launch_bounds__(64 * TOK_WAVES) __attribute__((amdgpu_waves_per_eu(
         wrow[j] = (const char*)g.W + (int64_t)(o < g.N ? o : g.N - 1) * g.ldw;
     }
     const char* xp = (const char*)g.X + (int64_t)(r32 < g.M ? r32 : 0) * g.ldx;
+    // Full passes read the weights through one buffer resource over this
+    // wave's rows: a row's offset goes in a scalar register and one lane
+    // offset serves every load (64-bit per-row lane addresses took 16
+    // registers, which the token loads need).
+    const int row0 = o0 + wave * RPW;
+    const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc((const char*)g.W + (int64_t)min(row0, g.N - 1) * g.ldw, 0xffffffffu);
+    uint32_t wsoff[RPW];
+#pragma unroll
+    for (int j = 0; j < RPW; ++j)
+        wsoff[j] = (uint32_t)((int64_t)(min(row0 + j, g.N - 1) - min(row0, g.N - 1)) * g.ldw);
+    const uint32_t lane16 = 16u * (uint32_t)lane;
+    // (the lane and scalar offsets are added in 32 bits: passes take this
+    // path only while the largest sum stays below 2^32)
+    const bool wbuf = (int64_t)(RPW - 1) * g.ldw + K + 4096 < (int64_t(1) << 32);
 
     i32x16 acc;
 #pragma unroll
@@ -235,12 +249,12 @@ __global__ __launch_bounds__(64 * TOK_WAVES) __attribute__((amdgpu_waves_per_eu(
     // stream in flight -- then, chunk by chunk, the workgroup writes the
     // chunk to LDS and wave w takes its K bytes 256 w .. 256 w + 255 in
     // eight MFMA steps (operands: 16 bytes of one channel from LDS, 16
-    // bytes of one token from memory, loaded while the chunk before is
-    // written and synchronised).  A pass inside
+    // bytes of one token from memory, loaded up to two chunks ahead).  A
+    // pass inside
     // K takes plain 16-byte loads (any byte alignment is fine for them); the
     // last, partial one bounded loads (bytes past K read as zero).
     for (int64_t p0 = 0; p0 < K; p0 += (int64_t)TOK_PASS * TOK_KC) {
-        const bool full = p0 + (int64_t)TOK_PASS * TOK_KC <= K;
+        const bool full = wbuf && p0 + (int64_t)TOK_PASS * TOK_KC <= K;
         auto load_x = [&](int c, u32x4 (&xv)[8]) {
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
@@ -262,23 +276,38 @@ __global__ __launch_bounds__(64 * TOK_WAVES) __attribute__((amdgpu_waves_per_eu(
                                                             __builtin_bit_cast(i32x4, b), acc, 0, 0, 0);
             }
         };
-        u32x4 xv[8];
         if (full) {
-            u32x4 wv[TOK_PASS][RPW];
+            // Issue order: the tokens of chunks 0 and 1, the pass's weights,
+            // then the tokens of chunk c + 2 once chunk c's MFMAs have read
+            // that register set.  Loads retire in issue order, so a chunk
+            // waits only for what was issued up to its own operands: chunk 0
+            // for its weights, not for the whole pass (token loads issued
+            // after the weights held every chunk until the pass had landed,
+            // and each chunk then waited for its tokens in turn).
+            static_assert(TOK_PASS == 4, "two token register sets over four chunks");
+            u32x4 xa[8], xb[8], wv[TOK_PASS][RPW];
+            load_x(0, xa);
+            load_x(1, xb);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int c = 0; c < TOK_PASS; ++c)
 #pragma unroll
                 for (int j = 0; j < RPW; ++j)
-                    wv[c][j] = *reinterpret_cast<const u32x4*>(wrow[j] + p0 + c * TOK_KC + 16 * lane);
-            load_x(0, xv);
-#pragma unroll
-            for (int c = 0; c < TOK_PASS; ++c) {
-                chunk(c, wv[c], xv);
-                // the next chunk's tokens, once these MFMAs have read theirs
-                if (c + 1 < TOK_PASS) load_x(c + 1, xv);
-            }
+                    wv[c][j] = __builtin_bit_cast(
+                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, (uint32_t)p0 + c * TOK_KC + lane16, wsoff[j], 0));
+            __builtin_amdgcn_sched_barrier(0);
+            chunk(0, wv[0], xa);
+            __builtin_amdgcn_sched_barrier(0);
+            load_x(2, xa);
+            chunk(1, wv[1], xb);
+            __builtin_amdgcn_sched_barrier(0);
+            load_x(3, xb);
+            chunk(2, wv[2], xa);
+            chunk(3, wv[3], xb);
         } else {
-            // the last pass: bounded loads chunk by chunk (chunks past K skipped)
+            u32x4 xv[8];
+            // the last pass (or any, past the buffer path's offsets): bounded
+            // loads chunk by chunk (chunks past K skipped)
             for (int c = 0; c < TOK_PASS && p0 + c * TOK_KC < K; ++c) {
                 u32x4 w[RPW];
 #pragma unroll
