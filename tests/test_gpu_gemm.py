@@ -315,6 +315,32 @@ def test_fp8_edge_tiles_guard_band(gpu_ok):
     check_fp(oracle.bf16_to_f64(whole[:M, :N]), R, S, 1e-2, "fp8 edge tiles, padded", bf16_out=True)
 
 
+def test_fp8_shape_sweep(gpu_ok):
+    """Seeded random shapes around the one-wave kernel's conditions: M on
+    both sides of 128, N multiples of 16 (one-wave edge tiles) and not (edge
+    tiles on the general kernel), K whole scale blocks from three up, and
+    padded leading dimensions (A and B rows padded with E4M3 NaN codes, D
+    inside a buffer whose padding must stay untouched)."""
+    r = np.random.default_rng(4242)
+    for case in range(24):
+        M = int(r.integers(100, 700))
+        N = int(r.integers(1, 50)) * 16 + (0 if case % 4 else int(r.integers(1, 16)))
+        K = 128 * int(r.integers(3, 12))
+        lda = K + 16 * int(r.integers(0, 3))
+        ldb = N + (16 * int(r.integers(0, 3)) if N % 16 == 0 else int(r.integers(0, 9)))
+        ldd = N + 8 * int(r.integers(0, 3))
+        qa, sa, qb, sb = inputs.fp8_operands(M, N, K, seeds=(case, M + N + K))
+        R, S = oracle.gemm_fp8_blockscaled(qa, sa, qb, sb)
+        buf = torch.full((M + 2, ldd), -1, dtype=torch.int16, device=gpu_ok).view(torch.bfloat16)
+        mp.gemm_fp8_blockscaled(dev(qa, lda, pad=0x7F), dev(sa), dev(qb, ldb, pad=0x7F), dev(sb),
+                                out=buf[:M, :N])
+        torch.cuda.synchronize()
+        whole = host(buf).view(np.uint16)
+        what = f"fp8 sweep case {case}: {M}x{N}x{K} lda={lda} ldb={ldb} ldd={ldd}"
+        assert (whole[:, N:] == 0xFFFF).all() and (whole[M:] == 0xFFFF).all(), what + ": padding written"
+        check_fp(oracle.bf16_to_f64(whole[:M, :N]), R, S, 1e-2, what, bf16_out=True)
+
+
 def test_fp8_unaligned_and_unit_scales(gpu_ok):
     M, N, K = 200, 300, 333
     qa, sa, qb, sb = inputs.fp8_operands(M, N, K, seeds=(21, 22))
