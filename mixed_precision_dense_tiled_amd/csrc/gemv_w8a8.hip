@@ -162,9 +162,12 @@ hipError_t launch_gemv_w8a8(const GemvArgs& a, bool aligned, hipStream_t stream)
 // fragments straight from memory instead touches 32 rows with 32 bytes each
 // per instruction, and streamed about 7 % slower), staged through LDS
 // chunk by chunk; wave w takes a quarter of each chunk's K bytes, and the
-// four partial sums meet in LDS.  The work stays HBM-bound: the MFMA rate
-// is far above what 32 tokens need, so the rows of the A operand past M
-// cost nothing that matters.
+// four partial sums meet in LDS.  Up to 16 tokens their rows take the same
+// road (one KiB of one row per load, staged beside the weights): loaded as
+// per-lane fragments, 32 rows x 32 bytes per instruction, they took a sixth
+// of the layer's time at 16 tokens.  The work stays HBM-bound: the
+// MFMA rate is far above what 32 tokens need, so the rows of the A operand
+// past M cost nothing that matters.
 // ---------------------------------------------------------------------------
 constexpr int TOK_WAVES = 4;                   // wavefronts per workgroup
 
@@ -200,9 +203,16 @@ constexpr int TOK_KC = 1024;                   // K bytes per LDS chunk
 constexpr int TOK_PASS = 4;                    // chunks per pass (K = 4096 in one pass)
 constexpr int TOK_PITCH = TOK_KC + 16;         // LDS row pitch: 16 bytes of padding per row
 
+// XL (at most 16 tokens): token rows staged through LDS, each a contiguous
+// KiB per chunk loaded once per workgroup; otherwise (at most 32 tokens; the
+// staged form's registers would not fit) every lane loads its own MFMA
+// fragments of the tokens (32 rows x 32 bytes per load instruction).
+template <bool XL>
 __global__ __launch_bounds__(64 * TOK_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void gemm_w8a8_kernel(W8A8Args g) {
-    // one chunk of the workgroup's 32 weight rows, then the partial sums
+    // one chunk of the workgroup's 32 weight rows (then the partial sums),
+    // and the same chunk of the token rows
     __shared__ __attribute__((aligned(16))) char wt[TOK_CH * TOK_PITCH];
+    __shared__ __attribute__((aligned(16))) char xt[XL ? 16 * TOK_PITCH : 16];
     static_assert((TOK_WAVES - 1) * 16 * 64 * 4 <= TOK_CH * TOK_PITCH, "partial sums fit");
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -212,32 +222,40 @@ __global__ __launch_bounds__(64 * TOK_WAVES) __attribute__((amdgpu_waves_per_eu(
     const int half = lane >> 5;                // which 16 bytes of a 32-byte K step
     const int64_t K = g.K;
     constexpr int RPW = TOK_CH / TOK_WAVES;    // weight rows each wave loads
+    constexpr int XPW = XL ? 16 / TOK_WAVES : 8;   // token rows each wave loads / fragments per lane
     MPDT_LDS char* const lds = lds_cast(wt);
+    MPDT_LDS char* const xl = lds_cast(xt);
 
     // the rows this wave loads (a row past N reads row N - 1: its channel's
-    // sums are never written); the token row of this lane (a row past M
-    // reads row 0: only outputs past M see it, and none is written)
+    // sums are never written)
     const char* wrow[RPW];
 #pragma unroll
     for (int j = 0; j < RPW; ++j) {
         const int o = o0 + wave * RPW + j;
         wrow[j] = (const char*)g.W + (int64_t)(o < g.N ? o : g.N - 1) * g.ldw;
     }
-    const char* xp = (const char*)g.X + (int64_t)(r32 < g.M ? r32 : 0) * g.ldx;
-    // Full passes read the weights through one buffer resource over this
-    // wave's rows: a row's offset goes in a scalar register and one lane
-    // offset serves every load (64-bit per-row lane addresses took 16
-    // registers, which the token loads need).
+    // XL: token rows wave, wave + 4, ... below M, each a contiguous KiB per
+    // chunk, staged through LDS beside the weights; the MFMA's rows past M
+    // read whatever the token buffer holds there (rows 16..31 read rows
+    // 0..15 again).  Otherwise the token row of this lane (a row past M reads
+    // row 0).  Only outputs past M see those rows, and none is written.
+    const int xrows = g.M > wave ? (g.M - wave + TOK_WAVES - 1) / TOK_WAVES : 0;
+    const char* const xp = (const char*)g.X + (int64_t)(r32 < g.M ? r32 : 0) * g.ldx;
+    // Full passes read the weights and the tokens through buffer resources:
+    // a row's offset goes in a scalar register and one lane offset serves
+    // every load (64-bit per-row lane addresses would take 16 registers).
     const int row0 = o0 + wave * RPW;
     const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc((const char*)g.W + (int64_t)min(row0, g.N - 1) * g.ldw, 0xffffffffu);
+    const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc((const char*)g.X + (int64_t)wave * g.ldx, 0xffffffffu);
     uint32_t wsoff[RPW];
 #pragma unroll
     for (int j = 0; j < RPW; ++j)
         wsoff[j] = (uint32_t)((int64_t)(min(row0 + j, g.N - 1) - min(row0, g.N - 1)) * g.ldw);
     const uint32_t lane16 = 16u * (uint32_t)lane;
     // (the lane and scalar offsets are added in 32 bits: passes take this
-    // path only while the largest sum stays below 2^32)
-    const bool wbuf = (int64_t)(RPW - 1) * g.ldw + K + 4096 < (int64_t(1) << 32);
+    // path only while the largest sums stay below 2^32)
+    const bool wbuf = (int64_t)(RPW - 1) * g.ldw + K + 4096 < (int64_t(1) << 32) &&
+                      (int64_t)(16 - TOK_WAVES) * g.ldx + K + 4096 < (int64_t(1) << 32);
 
     i32x16 acc;
 #pragma unroll
@@ -247,54 +265,91 @@ __global__ __launch_bounds__(64 * TOK_WAVES) __attribute__((amdgpu_waves_per_eu(
     // rows for the whole pass -- every instruction one contiguous KiB of one
     // row, as in the one-token kernel, so a resident grid keeps the weight
     // stream in flight -- then, chunk by chunk, the workgroup writes the
-    // chunk to LDS and wave w takes its K bytes 256 w .. 256 w + 255 in
-    // eight MFMA steps (operands: 16 bytes of one channel from LDS, 16
-    // bytes of one token from memory, loaded up to two chunks ahead).  A
-    // pass inside
-    // K takes plain 16-byte loads (any byte alignment is fine for them); the
+    // chunk's weight and token rows to LDS and wave w takes its K bytes
+    // 256 w .. 256 w + 255 in eight MFMA steps (operands: 16 bytes of one
+    // token and 16 bytes of one channel, both from LDS).  A pass inside K
+    // takes plain 16-byte loads (any byte alignment is fine for them); the
     // last, partial one bounded loads (bytes past K read as zero).
     for (int64_t p0 = 0; p0 < K; p0 += (int64_t)TOK_PASS * TOK_KC) {
         const bool full = wbuf && p0 + (int64_t)TOK_PASS * TOK_KC <= K;
-        auto load_x = [&](int c, u32x4 (&xv)[8]) {
+        auto load_x = [&](int c, u32x4 (&xr)[XPW]) {
+            if constexpr (!XL) {
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const int64_t off = p0 + c * TOK_KC + wave * 256 + 32 * s + 16 * half;
-                xv[s] = full ? *reinterpret_cast<const u32x4*>(xp + off) : load16_row<false>(xp + off, xp + K);
+                for (int s = 0; s < 8; ++s) {
+                    const int64_t off = p0 + c * TOK_KC + wave * 256 + 32 * s + 16 * half;
+                    xr[s] = full ? *reinterpret_cast<const u32x4*>(xp + off) : load16_row<false>(xp + off, xp + K);
+                }
+                return;
+            }
+#pragma unroll
+            for (int i = 0; i < XPW; ++i) {
+                if (i < xrows) {
+                    const int64_t off = p0 + c * TOK_KC;
+                    if (full) {
+                        xr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                              xrs, (uint32_t)off + lane16,
+                                                              (uint32_t)(TOK_WAVES * i) * (uint32_t)g.ldx, 0));
+                    } else {
+                        const char* xq = (const char*)g.X + (int64_t)(wave + TOK_WAVES * i) * g.ldx;
+                        xr[i] = load16_row<false>(xq + off + lane16, xq + K);
+                    }
+                }
             }
         };
-        // write chunk c of this wave's rows to LDS, then its eight MFMA steps
-        auto chunk = [&](int c, const u32x4 (&w)[RPW], const u32x4 (&xv)[8]) {
+        // write chunk c of this wave's weight and token rows to LDS, then
+        // its eight MFMA steps
+        auto chunk = [&](int c, const u32x4 (&w)[RPW], const u32x4 (&xr)[XPW]) {
             __syncthreads();                       // the previous chunk's reads are done
 #pragma unroll
             for (int j = 0; j < RPW; ++j)
                 lds_store16(lds, (uint32_t)((wave * RPW + j) * TOK_PITCH + 16 * lane), w[j]);
+            if constexpr (XL) {
+#pragma unroll
+                for (int i = 0; i < XPW; ++i)
+                    if (i < xrows) lds_store16(xl, (uint32_t)((wave + TOK_WAVES * i) * TOK_PITCH + 16 * lane), xr[i]);
+            }
             __syncthreads();
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                const u32x4 b = lds_load16(lds, (uint32_t)(r32 * TOK_PITCH + wave * 256 + 32 * s + 16 * half));
-                acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, xv[s]),
+                const uint32_t ko = (uint32_t)(wave * 256 + 32 * s + 16 * half);
+                const u32x4 a = XL ? lds_load16(xl, (uint32_t)((r32 & 15) * TOK_PITCH) + ko) : xr[s];
+                const u32x4 b = lds_load16(lds, (uint32_t)(r32 * TOK_PITCH) + ko);
+                acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
                                                             __builtin_bit_cast(i32x4, b), acc, 0, 0, 0);
             }
         };
-        if (full) {
-            // Issue order: the tokens of chunks 0 and 1, the pass's weights,
-            // then the tokens of chunk c + 2 once chunk c's MFMAs have read
-            // that register set.  Loads retire in issue order, so a chunk
-            // waits only for what was issued up to its own operands: chunk 0
-            // for its weights, not for the whole pass (token loads issued
-            // after the weights held every chunk until the pass had landed,
-            // and each chunk then waited for its tokens in turn).
-            static_assert(TOK_PASS == 4, "two token register sets over four chunks");
-            u32x4 xa[8], xb[8], wv[TOK_PASS][RPW];
-            load_x(0, xa);
-            load_x(1, xb);
-            __builtin_amdgcn_sched_barrier(0);
+        auto load_w = [&](u32x4 (&wv)[TOK_PASS][RPW]) {
 #pragma unroll
             for (int c = 0; c < TOK_PASS; ++c)
 #pragma unroll
                 for (int j = 0; j < RPW; ++j)
                     wv[c][j] = __builtin_bit_cast(
                         u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, (uint32_t)p0 + c * TOK_KC + lane16, wsoff[j], 0));
+        };
+        static_assert(TOK_PASS == 4, "four chunks per pass");
+        if (full && XL) {
+            // Issue order: the pass's tokens (a few KiB-long rows per wave),
+            // then its weights.  Loads retire in issue order, so chunk c
+            // waits for what was issued up to its own weights and no token
+            // load's latency is left exposed between chunks.
+            u32x4 xs[TOK_PASS][XPW], wv[TOK_PASS][RPW];
+#pragma unroll
+            for (int c = 0; c < TOK_PASS; ++c) load_x(c, xs[c]);
+            __builtin_amdgcn_sched_barrier(0);
+            load_w(wv);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int c = 0; c < TOK_PASS; ++c) chunk(c, wv[c], xs[c]);
+        } else if (full) {
+            // Issue order: the token fragments of chunks 0 and 1, the pass's
+            // weights, then the fragments of chunk c + 2 once chunk c's MFMAs
+            // have read that register set: chunk 0 waits for its weights, not
+            // for the whole pass.
+            u32x4 xa[XPW], xb[XPW], wv[TOK_PASS][RPW];
+            load_x(0, xa);
+            load_x(1, xb);
+            __builtin_amdgcn_sched_barrier(0);
+            load_w(wv);
             __builtin_amdgcn_sched_barrier(0);
             chunk(0, wv[0], xa);
             __builtin_amdgcn_sched_barrier(0);
@@ -305,7 +360,7 @@ __global__ __launch_bounds__(64 * TOK_WAVES) __attribute__((amdgpu_waves_per_eu(
             chunk(2, wv[2], xa);
             chunk(3, wv[3], xb);
         } else {
-            u32x4 xv[8];
+            u32x4 xr[XPW];
             // the last pass (or any, past the buffer path's offsets): bounded
             // loads chunk by chunk (chunks past K skipped)
             for (int c = 0; c < TOK_PASS && p0 + c * TOK_KC < K; ++c) {
@@ -313,8 +368,8 @@ __global__ __launch_bounds__(64 * TOK_WAVES) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
                 for (int j = 0; j < RPW; ++j)
                     w[j] = load16_row<false>(wrow[j] + p0 + c * TOK_KC + 16 * lane, wrow[j] + K);
-                load_x(c, xv);
-                chunk(c, w, xv);
+                load_x(c, xr);
+                chunk(c, w, xr);
             }
         }
     }
@@ -516,7 +571,8 @@ hipError_t launch_gemm_w8a8(const W8A8Args& a0, bool /*aligned*/, hipStream_t st
                                stream, a);
         } else {
             dim3 grid((unsigned)((a.N + TOK_CH - 1) / TOK_CH)), block(64 * TOK_WAVES);
-            hipLaunchKernelGGL(gemm_w8a8_kernel, grid, block, 0, stream, a);
+            if (a.M <= 16) hipLaunchKernelGGL(gemm_w8a8_kernel<true>, grid, block, 0, stream, a);
+            else hipLaunchKernelGGL(gemm_w8a8_kernel<false>, grid, block, 0, stream, a);
         }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
