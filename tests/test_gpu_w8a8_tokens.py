@@ -59,7 +59,7 @@ def test_w8a8_tokens_bit_exact(gpu_ok, M, with_bias):
 
 @pytest.mark.parametrize("M,N,K,ldx,ldw,shift", [(4, 333, 1000, 1003, 1001, 0), (6, 17, 64, None, 80, 3),
                                                  (16, 9, 8193, None, None, 0), (2, 1, 1, None, None, 1),
-                                                 (5, 40, 4196, 4099, 4101, 1), (20, 70, 8192, 8195, None, 2)])
+                                                 (5, 40, 4196, None, 4211, 1), (20, 70, 8192, None, None, 2)])
 def test_w8a8_tokens_shapes_padded_unaligned(gpu_ok, M, N, K, ldx, ldw, shift):
     X, sx, W, sw, bias = w8a8_inputs(M, N, K, seed=N + K)
     z, y, zr, yr = run_w8a8(X, sx, W, sw, bias, ldx=ldx, ldw=ldw, shift=shift)
