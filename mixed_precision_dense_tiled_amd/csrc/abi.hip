@@ -561,6 +561,7 @@ MPDT_EXPORT mpdt_status quantize_fp8_blocks(int64_t R, int64_t C, const float* X
     a.block_rows = (int)block_rows;
     a.fmt = 0;
     a.shape = block_rows == 1 ? mpdt::FP8Q_ROW128 : mpdt::FP8Q_TILE128;
+    a.vec = aligned_to(X, 16) && ldx % 4 == 0 && aligned_to(Q, 4) && ldq % 4 == 0;
     return launched(mpdt::launch_quantize_fp8_blocks(a, (hipStream_t)stream), fn);
 }
 

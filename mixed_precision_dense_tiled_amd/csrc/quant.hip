@@ -81,10 +81,31 @@ __device__ __forceinline__ uint8_t to_fp8(float v) {
 }
 template <int FMT> constexpr float QMAX = FMT == 0 ? 448.0f : 57344.0f;
 
-// 1 x 128 blocks: a wavefront takes FP8_RB consecutive blocks of one row,
-// two elements per lane per block (each load instruction reads 512
-// consecutive bytes); all loads are issued before the first reduction.
+// Four floats from c (a multiple of 4, 16-byte aligned in a vec row): one
+// vector load inside [0, end), element loads (zeros past end) at the end.
+__device__ __forceinline__ float4 load4_bounded(const float* xr, int64_t c, int64_t end) {
+    if (c + 4 <= end) return *reinterpret_cast<const float4*>(xr + c);
+    float4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (c < end) v.x = xr[c];
+    if (c + 1 < end) v.y = xr[c + 1];
+    if (c + 2 < end) v.z = xr[c + 2];
+    return v;
+}
+// 1 x 128 blocks: a wavefront takes FP8_RB = 4 consecutive blocks of one
+// row.  With vec rows, lane l takes elements 4 l .. 4 l + 3 of each
+// 256-element half (one 16-byte load; lanes 0-31 cover one block, 32-63
+// the next), the maximum runs over each half-wave, and the four FP8 codes go
+// out as one 4-byte store; otherwise two elements per lane and block, loaded
+// and stored one at a time.  All loads are issued before the first
+// reduction.
 constexpr int FP8_RB = 4;
+
+// four FP8 codes of v / s, element 0 in the low byte
+template <int FMT>
+__device__ __forceinline__ uint32_t fp8x4(float4 v, float s) {
+    return (uint32_t)to_fp8<FMT>(v.x / s) | ((uint32_t)to_fp8<FMT>(v.y / s) << 8) |
+           ((uint32_t)to_fp8<FMT>(v.z / s) << 16) | ((uint32_t)to_fp8<FMT>(v.w / s) << 24);
+}
 
 template <int FMT>
 __global__ __launch_bounds__(256) void quantize_fp8_rowblocks_kernel(QuantFp8Args g) {
@@ -96,6 +117,29 @@ __global__ __launch_bounds__(256) void quantize_fp8_rowblocks_kernel(QuantFp8Arg
     const int64_t r = w / groups, bj0 = (w % groups) * FP8_RB;
     const float* xr = g.X + r * g.ldx;
     uint8_t* qr = g.Q + r * g.ldq;
+    if (g.vec) {
+        float4 v[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) v[h] = load4_bounded(xr, bj0 * 128 + 256 * h + 4 * lane, g.C);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t bj = bj0 + 2 * h + (lane >> 5);   // this half-wave's block
+            float amax = fmaxf(fmaxf(fabsf(v[h].x), fabsf(v[h].y)), fmaxf(fabsf(v[h].z), fabsf(v[h].w)));
+#pragma unroll
+            for (int m = 16; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+            if (bj >= nbc) continue;
+            const float s = amax > 0.0f ? amax / QMAX<FMT> : 1.0f;
+            if ((lane & 31) == 0) g.S[r * g.lds + bj] = s;
+            const int64_t c = bj0 * 128 + 256 * h + 4 * lane;
+            const uint32_t q = fp8x4<FMT>(v[h], s);
+            if (c + 4 <= g.C) {
+                *reinterpret_cast<uint32_t*>(qr + c) = q;
+            } else {
+                for (int e = 0; e < 4 && c + e < g.C; ++e) qr[c + e] = (uint8_t)(q >> (8 * e));
+            }
+        }
+        return;
+    }
     float v[FP8_RB][2];
 #pragma unroll
     for (int b = 0; b < FP8_RB; ++b) {
@@ -115,18 +159,51 @@ __global__ __launch_bounds__(256) void quantize_fp8_rowblocks_kernel(QuantFp8Arg
     }
 }
 
-// 128 x 128 blocks: one workgroup per block; thread t covers column t % 128
-// of the block's rows t / 128, t / 128 + 2, ... (each wave instruction reads
-// 256 consecutive bytes of one row).
+// 128 x 128 blocks: one workgroup per block.  With vec rows thread t covers
+// columns 4 (t % 32) .. +3 of the block's rows t / 32, t / 32 + 8, ... (one
+// 16-byte load per row; a wave instruction reads 512 consecutive bytes of
+// each of two rows) and stores four codes at once; otherwise column t % 128
+// of rows t / 128, t / 128 + 2, ..., element by element.  The thread's 64
+// values stay in registers between the two passes.
 template <int FMT>
 __global__ __launch_bounds__(256) void quantize_fp8_tileblocks_kernel(QuantFp8Args g) {
     __shared__ float red[4];
     const int64_t nbc = (g.C + 127) / 128;
     const int64_t bi = blockIdx.x / nbc, bj = blockIdx.x % nbc;
+    if (g.vec) {
+        const int64_t c = bj * 128 + 4 * (threadIdx.x & 31);
+        const int64_t r0 = bi * 128 + (threadIdx.x >> 5);
+        float4 v[16];
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int64_t r = r0 + 8 * i;
+            v[i] = r < g.R ? load4_bounded(g.X + r * g.ldx, c, g.C) : float4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+        amax = block_max256(amax, red);
+        const float s = amax > 0.0f ? amax / QMAX<FMT> : 1.0f;
+        if (threadIdx.x == 0) g.S[bi * g.lds + bj] = s;
+        if (c >= g.C) return;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int64_t r = r0 + 8 * i;
+            if (r >= g.R) break;
+            uint8_t* qr = g.Q + r * g.ldq;
+            const uint32_t q = fp8x4<FMT>(v[i], s);
+            if (c + 4 <= g.C) {
+                *reinterpret_cast<uint32_t*>(qr + c) = q;
+            } else {
+                for (int e = 0; e < 4 && c + e < g.C; ++e) qr[c + e] = (uint8_t)(q >> (8 * e));
+            }
+        }
+        return;
+    }
     const int64_t c = bj * 128 + (threadIdx.x & 127);
     const int64_t r0 = bi * 128 + (threadIdx.x >> 7);
     const bool col_ok = c < g.C;
-    // the thread's 64 values stay in registers between the two passes
     float v[64];
     float amax = 0.0f;
 #pragma unroll
@@ -193,16 +270,6 @@ __global__ void fp8_tensor_clear_kernel(float* S) { S[0] = 0.0f; }
 
 constexpr int TENSOR_WGS = 1024;   // workgroups of the two grid-stride passes
 
-// Four floats from c (a multiple of 4, 16-byte aligned in a vec row): one
-// vector load inside [0, end), element loads (zeros past end) at the end.
-__device__ __forceinline__ float4 load4_bounded(const float* xr, int64_t c, int64_t end) {
-    if (c + 4 <= end) return *reinterpret_cast<const float4*>(xr + c);
-    float4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (c < end) v.x = xr[c];
-    if (c + 1 < end) v.y = xr[c + 1];
-    if (c + 2 < end) v.z = xr[c + 2];
-    return v;
-}
 constexpr int TENSOR_CH = 4096;    // columns of one work item (a row piece)
 
 // A work item is one row piece of TENSOR_CH columns; with aligned rows each
