@@ -474,6 +474,7 @@ MPDT_EXPORT mpdt_status quantize_i8_rows(int64_t M, int64_t K, const uint16_t* X
     a.S = scales;
     a.K = K;
     a.M = (int)M;
+    a.vec = aligned_to(X, 16) && ldx % 8 == 0 && aligned_to(Q, 8) && ldq % 8 == 0;
     return launched(mpdt::launch_quantize_i8_rows(a, (hipStream_t)stream), fn);
 }
 

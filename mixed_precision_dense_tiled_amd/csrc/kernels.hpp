@@ -102,6 +102,7 @@ struct QuantI8Args {
     float* S;
     int64_t K;
     int M;
+    int vec;          // X rows 16-byte and Q rows 8-byte aligned: 8 elements per access
 };
 hipError_t launch_quantize_i8_rows(const QuantI8Args& a, hipStream_t stream);
 

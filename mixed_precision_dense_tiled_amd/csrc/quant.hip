@@ -50,21 +50,67 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
 }
 
 // ---- per-token INT8 quantisation: one workgroup per token ------------------
+// With vec rows up to I8_VK elements long, each thread loads its 16-byte
+// pieces of the row once (all loads in flight together), keeps them in
+// registers for the second pass and stores eight codes at once; otherwise
+// the row is read twice, element by element.
+constexpr int I8_VU = 4;                       // 16-byte pieces per thread
+constexpr int64_t I8_VK = 256 * 8 * I8_VU;     // 8192 elements
+
+__device__ __forceinline__ int8_t q_i8(float x, float s) {
+    const float r = __builtin_rintf(x / s);
+    return (int8_t)(int)fminf(fmaxf(r, -127.0f), 127.0f);
+}
+
 __global__ __launch_bounds__(256) void quantize_i8_rows_kernel(QuantI8Args g) {
     __shared__ float red[4];
     const int m = blockIdx.x;
     const uint16_t* xr = g.X + (int64_t)m * g.ldx;
     int8_t* qr = g.Q + (int64_t)m * g.ldq;
+    if (g.vec && g.K <= I8_VK) {
+        u32x4 v[I8_VU];
+#pragma unroll
+        for (int u = 0; u < I8_VU; ++u) {
+            const int64_t k = 8 * (threadIdx.x + 256 * u);
+            if (k + 8 <= g.K) {
+                v[u] = *reinterpret_cast<const u32x4*>(xr + k);
+            } else {
+                v[u] = u32x4{0u, 0u, 0u, 0u};
+                for (int e = 0; e < 8 && k + e < g.K; ++e) v[u][e >> 1] |= (uint32_t)xr[k + e] << (16 * (e & 1));
+            }
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int u = 0; u < I8_VU; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(bf16_bits_to_f32((uint16_t)(v[u][e >> 1] >> (16 * (e & 1))))));
+        amax = block_max256(amax, red);
+        const float s = amax > 0.0f ? amax / 127.0f : 1.0f;
+        if (threadIdx.x == 0) g.S[m] = s;
+#pragma unroll
+        for (int u = 0; u < I8_VU; ++u) {
+            const int64_t k = 8 * (threadIdx.x + 256 * u);
+            if (k >= g.K) break;
+            uint32_t w[2] = {0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = bf16_bits_to_f32((uint16_t)(v[u][e >> 1] >> (16 * (e & 1))));
+                w[e >> 2] |= (uint32_t)(uint8_t)q_i8(x, s) << (8 * (e & 3));
+            }
+            if (k + 8 <= g.K) {
+                *reinterpret_cast<u32x2*>(qr + k) = u32x2{w[0], w[1]};
+            } else {
+                for (int e = 0; k + e < g.K; ++e) qr[k + e] = (int8_t)(w[e >> 2] >> (8 * (e & 3)));
+            }
+        }
+        return;
+    }
     float amax = 0.0f;
     for (int64_t k = threadIdx.x; k < g.K; k += 256) amax = fmaxf(amax, fabsf(bf16_bits_to_f32(xr[k])));
     amax = block_max256(amax, red);
     const float s = amax > 0.0f ? amax / 127.0f : 1.0f;
     if (threadIdx.x == 0) g.S[m] = s;
-    for (int64_t k = threadIdx.x; k < g.K; k += 256) {
-        float r = __builtin_rintf(bf16_bits_to_f32(xr[k]) / s);
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-        qr[k] = (int8_t)(int)r;
-    }
+    for (int64_t k = threadIdx.x; k < g.K; k += 256) qr[k] = q_i8(bf16_bits_to_f32(xr[k]), s);
 }
 
 hipError_t launch_quantize_i8_rows(const QuantI8Args& a, hipStream_t stream) {

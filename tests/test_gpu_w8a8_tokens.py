@@ -166,6 +166,23 @@ def test_quantize_i8_rows_ties_zero_rows_padding(gpu_ok):
     assert (full[:, 8:] == 77).all()                 # padding of Q untouched
 
 
+@pytest.mark.parametrize("M,K,ldx,ldq", [(5, 1003, 1008, 1016), (3, 8192, 8192, 8192), (2, 8193, 8200, 8200),
+                                         (4, 17, 24, 24)])
+def test_quantize_i8_rows_aligned_padded_tails(gpu_ok, M, K, ldx, ldq):
+    """Rows 16-byte aligned (X) and 8-byte aligned (Q), with a partial last
+    group of eight at the end of K, padding that holds BF16 NaN codes in X and
+    a marker in Q (neither may be read or written), and K past the 8192
+    elements one pass of registers holds."""
+    X = bf16_matrix((M, K), seed=M + K, scale=2.0)
+    tX = dev(X, ldx, pad=0x7FC0)
+    q_out = dev(np.zeros((M, K), np.int8), ldq, pad=77)
+    q, s = mp.quantize_i8_rows(tX, q_out=q_out)
+    qr, sr = oracle.quantize_i8_rows(X)
+    assert np.array_equal(host(q), qr) and np.array_equal(host(s), sr)
+    full = host(q_out.as_strided((M, ldq), (ldq, 1)))
+    assert (full[:, K:] == 77).all()
+
+
 @pytest.mark.parametrize("R,C,br", [(256, 384, 128), (130, 200, 128), (5, 300, 1), (129, 257, 1),
                                     (1, 1, 1), (1, 1, 128)])
 def test_quantize_fp8_blocks_bit_exact(gpu_ok, R, C, br):
