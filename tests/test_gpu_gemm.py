@@ -476,3 +476,47 @@ def test_i8_small_problems_bit_exact(gpu_ok, M, N, K):
     assert np.array_equal(D, oracle.gemm_i8_i32(A, B, None)), "unaligned, C NULL"
     D = host(mp.gemm_i8_i32(dev(A), dev(B), dev(C)))
     assert np.array_equal(D, oracle.gemm_i8_i32(A, B, C)), "random"
+
+
+def test_random_shape_sweep_bit_exact(gpu_ok):
+    """Seeded random shapes up to ~1100 x 1100 x 3300 through every 16-bit
+    and INT8 path (small-problem, tile, strip and general kernels, K tails,
+    the in-loop C of long K), with padded leading dimensions (NaN or marker
+    padding), C absent, given or overwritten in place, and a guard band
+    around D.  Integer-valued 16-bit inputs keep every FP32 partial sum
+    exact, so D must equal the oracle bit for bit in every case."""
+    r = np.random.default_rng(777)
+    for case in range(60):
+        fmt = ("f16", "bf16", "i8")[case % 3]
+        M, N = int(r.integers(1, 1100)), int(r.integers(1, 1100))
+        K = int(r.integers(1, 3300)) if case % 5 else int(r.integers(1600, 3300))
+        pa, pb, pd = (int(x) for x in r.integers(0, 9, 3))
+        cmode = ("none", "given", "inplace")[int(r.integers(0, 3))]
+        what = f"case {case}: {fmt} {M}x{N}x{K} pads {pa},{pb},{pd} C {cmode}"
+        if fmt == "i8":
+            A, B, C = inputs.i8_operands(M, N, K, seeds=(case, M, N))
+            if cmode == "none":
+                C = None
+            want = oracle.gemm_i8_i32(A, B, C)
+            tA, tB = dev(A, K + pa, pad=-128), dev(B, N + pb, pad=127)
+            gpu, dt, marker = mp.gemm_i8_i32, np.int32, -7
+        else:
+            A, B, _ = inputs.gemm16_operands(M, N, K, dist="int4", fmt=fmt, with_c=False, seeds=(case, M, N))
+            C = None if cmode == "none" else np.round(inputs.uniform_f32((M, N), case + 99) * 16.0).astype(np.float32)
+            want, _ = FN16[fmt][1](A, B, C)
+            tA, tB = dev(A, K + pa, pad=NAN16[fmt]), dev(B, N + pb, pad=NAN16[fmt])
+            gpu, dt, marker = FN16[fmt][0], np.float32, -7.0
+        buf = dev(np.zeros((M + 2, N + pd), dt), pad=0)
+        buf.fill_(marker)
+        if cmode == "inplace":
+            buf[:M, :N] = torch.from_numpy(C).to(buf.device)
+            out = buf[:M, :N]
+            D = gpu(tA, tB, out, out=out)
+        else:
+            out = buf[:M, :N]
+            D = gpu(tA, tB, None if C is None else dev(C), out=out)
+        torch.cuda.synchronize()
+        assert D.data_ptr() == out.data_ptr(), what
+        whole = host(buf)
+        assert np.array_equal(whole[:M, :N].astype(np.float64), np.asarray(want, np.float64)), what + ": D differs"
+        assert (whole[:, N:] == marker).all() and (whole[M:] == marker).all(), what + ": guard band written"
