@@ -299,6 +299,15 @@ def test_fp8_edge_tiles_one_wave(gpu_ok, M, N, K, ldb):
     check_fp(got, R, S, 1e-2, f"fp8 edge tiles {M}x{N}x{K} ldb={ldb}", bf16_out=True)
 
 
+# Wide one-wave grids with a partly filled last round (8 x 33 and 8 x 34
+# tiles on 256 CUs); (1000, 8432): the row shift and a partial last column.
+@pytest.mark.parametrize("M,N,K", [(1024, 8448, 384), (1024, 8576, 512), (1000, 8432, 768)])
+def test_fp8_wide_grids(gpu_ok, M, N, K):
+    qa, sa, qb, sb = inputs.fp8_operands(M, N, K, seeds=(M + 3, N + 4))
+    got, R, S = run_fp8(qa, sa, qb, sb)
+    check_fp(got, R, S, 1e-2, f"fp8 wide grid {M}x{N}x{K}", bf16_out=True)
+
+
 def test_fp8_edge_tiles_guard_band(gpu_ok):
     """Edge tiles with padded rows everywhere: A and B padded with E4M3 NaN
     codes, D inside a larger buffer.  No NaN reaches D, and nothing right of
