@@ -154,3 +154,39 @@ def test_full_size_bf16_gelu_sampled(gpu_ok):
     jj = np.concatenate([r.integers(0, N, 4000), [0, 0, N - 1, N - 1]])
     R, S, P = oracle.gemm16_bias_act_at("bf16", A, B, C, bias, mp.ACT_GELU, ii, jj)
     check_act(d[ii, jj], R, S, P, mp.ACT_GELU, "bf16", True, 1e-2, "4096^3 sampled")
+
+
+def test_random_shape_sweep(gpu_ok):
+    """Seeded random shapes through the fused epilogue: with no activation
+    or ReLU, integer-valued inputs and D checked bit for bit (FP32 or 16-bit,
+    long K included, where C joins inside the K loop, and unaligned A rows);
+    with GELU or SiLU, random inputs against the bound above."""
+    r = np.random.default_rng(31337)
+    for case in range(36):
+        fmt = ("f16", "bf16")[case % 2]
+        d16 = bool((case // 2) % 2)
+        M, N = int(r.integers(1, 900)), int(r.integers(1, 900))
+        K = int(r.integers(1, 2100)) if case % 3 else int(r.integers(1600, 2100))
+        pad = int(r.integers(0, 4))
+        name = f"case {case}: {fmt} {M}x{N}x{K} d16={d16} pad={pad}"
+        if case < 24:
+            act = (mp.ACT_NONE, mp.ACT_RELU)[(case // 4) % 2]
+            A, B, C, bias = int_operands(M, N, K, fmt, seed=case * 10)
+            tA = dev(A, K + pad, pad=0x7C00) if pad else dev(A)
+            D = GPU[fmt](tA, dev(B), dev(C), dev(bias), act, d16=d16)
+            torch.cuda.synchronize()
+            R, _, _ = oracle.gemm16_bias_act(fmt, A, B, C, bias, act)
+            r32 = R.astype(np.float32)
+            if d16:
+                assert np.array_equal(host(D.view(torch.int16)).view(np.uint16), ROUND[fmt](r32)), name
+            else:
+                assert np.array_equal(host(D), r32), name
+        else:
+            act = (mp.ACT_GELU, mp.ACT_SILU)[case % 2]
+            A, B, C = inputs.gemm16_operands(M, N, K, dist="normal", fmt=fmt, seeds=(case, M, N))
+            C = (C * 4.0).astype(np.float32)
+            bias = inputs.normal_f32((N,), case + 5)
+            D = GPU[fmt](dev(A), dev(B), dev(C), dev(bias), act, d16=d16)
+            R, S, P = oracle.gemm16_bias_act(fmt, A, B, C, bias, act)
+            frob = 1e-2 if (d16 and fmt == "bf16") else 1e-3
+            check_act(out_values(D, fmt, d16), R, S, P, act, fmt, d16, frob, f"{name} act {act}")
