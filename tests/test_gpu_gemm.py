@@ -296,7 +296,8 @@ def test_fp8_parity(gpu_ok, M, N, K):
 def test_fp8_edge_tiles_one_wave(gpu_ok, M, N, K, ldb):
     qa, sa, qb, sb = inputs.fp8_operands(M, N, K, seeds=(M + 1, N + 2))
     got, R, S = run_fp8(qa, sa, qb, sb, ldb=ldb)
-    check_fp(got, R, S, 1e-2, f"fp8 edge tiles {M}x{N}x{K} ldb={ldb}", bf16_out=True)
+    # (the output's rounding is admitted on top of the bound only up to K = 1024)
+    check_fp(got, R, S, 1e-2, f"fp8 edge tiles {M}x{N}x{K} ldb={ldb}", bf16_out=K <= 1024)
 
 
 # Wide one-wave grids with a partly filled last round (8 x 33 and 8 x 34
@@ -347,7 +348,7 @@ def test_fp8_shape_sweep(gpu_ok):
         whole = host(buf).view(np.uint16)
         what = f"fp8 sweep case {case}: {M}x{N}x{K} lda={lda} ldb={ldb} ldd={ldd}"
         assert (whole[:, N:] == 0xFFFF).all() and (whole[M:] == 0xFFFF).all(), what + ": padding written"
-        check_fp(oracle.bf16_to_f64(whole[:M, :N]), R, S, 1e-2, what, bf16_out=True)
+        check_fp(oracle.bf16_to_f64(whole[:M, :N]), R, S, 1e-2, what, bf16_out=K <= 1024)
 
 
 def test_fp8_unaligned_and_unit_scales(gpu_ok):
