@@ -111,7 +111,15 @@ def _check(fn: str, status: int):
         raise MpdtError(fn, status, lib().mpdt_last_error().decode())
 
 
+# torch's current stream on a device, as the raw HIP stream handle: the
+# direct accessor where this torch has it (a tenth of the public route's host
+# time), else the public one.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(t: torch.Tensor) -> int:
+    if _raw_stream is not None:
+        return _raw_stream(t.get_device())
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
@@ -127,10 +135,10 @@ def _mat(t: torch.Tensor, itemsize: int, name: str):
     if rows == 0 or cols == 0:
         # an empty operand: nothing is read or written through it
         return t.data_ptr(), max(cols, 1)
-    if cols > 1 and t.stride(1) != 1:
+    s0, s1 = t.stride()
+    if cols > 1 and s1 != 1:
         raise ValueError(f"{name} must have unit stride along its rows")
-    ld = t.stride(0) if rows > 1 else max(cols, 1)
-    return t.data_ptr(), int(ld)
+    return t.data_ptr(), s0 if rows > 1 else max(cols, 1)
 
 
 def _shape(t, shape, name):
@@ -143,8 +151,9 @@ def _shape(t, shape, name):
 
 
 def _same_device(ref, *ts):
+    d = ref.get_device()
     for name, t in ts:
-        if t is not None and t.device != ref.device:
+        if t is not None and t.get_device() != d:
             raise ValueError(f"{name} is on {t.device}, the operands on {ref.device}")
 
 
