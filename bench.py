@@ -239,6 +239,10 @@ def main():
         }
         if smi is not None:
             result["smi_clocks_under_load"] = smi
+        if not args.child:
+            ceil = mfma_ceiling(args, stream, inputs)
+            result["roofline"]["mfma_ceiling"] = ceil
+            result["roofline"]["frac_of_mfma_ceiling"] = achieved / ceil["TFLOP_s"]
         if spread is not None:
             result["process_spread"] = spread["bf16"]
         if not args.no_cpu_baseline and not args.child:
@@ -782,6 +786,48 @@ def smi_clocks(launch, stream, n=4000):
         return None
     card = next(iter(data.values()))
     return {k.rstrip(":").strip(): v for k, v in card.items() if isinstance(v, str) and "clk" in k.lower()}
+
+
+def mfma_ceiling(args, stream, inputs):
+    """Practical BF16 MFMA rate on this part under sustained load
+    (libmpdt_probes.so, mpdt_probe_mfma_peak: one wavefront per SIMD on every
+    CU, each issuing the 4096 32x32x16 BF16 MFMAs of the 4096^3 GEMM back to
+    back from registers and nothing else), with operands drawn like the
+    headline's (N(0,1) as BF16) and with all-zero operands; timed like the
+    GEMM (back-to-back launches after the same warm-up), shader clock from
+    the probe's own s_memtime / s_memrealtime stamps."""
+    import ctypes
+    import numpy as np
+    import torch
+    L = ctypes.CDLL(os.path.join(ROOT, "mixed_precision_dense_tiled_amd", "libmpdt_probes.so"))
+    L.mpdt_probe_mfma_peak.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    L.mpdt_probe_mfma_peak.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    iters, wgs = 32, 256
+    flop = wgs * 4 * iters * 128 * 2.0 * 32 * 32 * 16
+    out = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+    stamps = torch.zeros(wgs * 4, dtype=torch.int64, device=dev)
+    res = {"note": "one wavefront per SIMD on every CU, 4096 back-to-back 32x32x16 BF16 MFMAs each "
+                   "(the 4096^3 GEMM's MFMA work) from registers, nothing else"}
+    normal = inputs.to_bf16_bits(inputs.normal_f32((1024 * 8,), 11))
+    for name, bits in (("normal", normal), ("zero", np.zeros(1024 * 8, np.uint16))):
+        data = torch.from_numpy(bits.view(np.int16)).to(dev)
+
+        def run(i):
+            rc = L.mpdt_probe_mfma_peak(data.data_ptr(), iters, out.data_ptr(), stamps.data_ptr(),
+                                        torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"mpdt_probe_mfma_peak failed: {rc}")
+        region, per = timed(run, args.steps, args.warmup, stream)
+        st = stats(per, region, args.steps)
+        q = stamps.cpu().numpy().reshape(wgs, 4).astype(np.float64)
+        ghz = float(np.median((q[:, 1] - q[:, 0]) / ((q[:, 3] - q[:, 2]) / 100e6)) / 1e9)
+        key = "" if name == "normal" else "zero_data_"
+        res[key + "TFLOP_s"] = flop / (st["mean_us"] * 1e-6) / 1e12
+        res[key + "mean_us"] = st["mean_us"]
+        res[key + "shader_clock_ghz"] = ghz
+    return res
 
 
 def read_ceiling(args, stream):

@@ -27,6 +27,17 @@
 //     real sum takes is ever written, so the kernel moves almost nothing but
 //     the reads.  Not a probe of layout: a measuring stick for the streaming
 //     kernels (the W8A8 GEMV reads its weights this way, 8 KiB per wave).
+//   mpdt_probe_mfma_peak(data, iters, out, stamps): the practical MFMA
+//     ceiling -- 256 workgroups of four wavefronts (one per SIMD, as the
+//     one-wave GEMM kernel runs), each wavefront 16 independent 32 x 32 FP32
+//     accumulators and eight register-held pairs of BF16 operand fragments
+//     taken from `data` (1024 16-byte vectors), then iters x 128 back-to-back
+//     32x32x16 BF16 MFMAs whose B operand changes at every instruction, and
+//     nothing else.  At iters = 32 a wavefront issues the 4096 MFMAs of the
+//     BF16 4096^3 GEMM.  out[workgroup * 256 + thread] = the sum of the
+//     thread's accumulators (keeps every MFMA); stamps[workgroup * 4 ..] =
+//     s_memtime and s_memrealtime (100 MHz) at the start and the end of
+//     workgroup's first wavefront, for the shader clock under this load.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -148,7 +159,60 @@ __global__ __launch_bounds__(1024) void probe_stream_read_kernel(const u32x4* p,
     if (acc == 0x9E3779B9u && lane == 0) out[0] = acc;   // keeps the loads; (practically) never stores
 }
 
+constexpr int PEAK_WGS = 256;
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void probe_mfma_peak_kernel(const u32x4* data, int iters, float* out, uint64_t* stamps) {
+    const int lane = threadIdx.x & 63;
+    u32x4 a[8], b[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        a[s] = data[s * 64 + lane];
+        b[s] = data[512 + s * 64 + lane];
+    }
+    f32x16 acc[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[k][r] = 0.0f;
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+    __builtin_amdgcn_sched_barrier(0);
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[s]),
+                                                                 __builtin_bit_cast(bf16x8, b[(s + k) & 7]),
+                                                                 acc[k], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float sum = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum += acc[k][r];
+    const uint64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+    out[blockIdx.x * 256 + threadIdx.x] = sum;
+    if (threadIdx.x == 0) {
+        uint64_t* q = stamps + blockIdx.x * 4;
+        q[0] = t0; q[1] = t1; q[2] = r0; q[3] = r1;
+    }
+}
+
 }  // namespace mpdt
+
+// data: 1024 x 16 bytes of BF16 operand bits; out: 256 x 256 floats;
+// stamps: 256 x 4 values.
+MPDT_EXPORT int mpdt_probe_mfma_peak(const void* data, int iters, float* out, uint64_t* stamps,
+                                     void* stream) {
+    if (!data || !out || !stamps || iters < 0 || iters > (1 << 20)) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(mpdt::probe_mfma_peak_kernel, dim3(mpdt::PEAK_WGS), dim3(256), 0, (hipStream_t)stream,
+                       (const mpdt::u32x4*)data, iters, out, stamps);
+    return (int)hipGetLastError();
+}
 
 MPDT_EXPORT int mpdt_probe_stream_read(const void* p, uint64_t bytes, int per_lane, int waves,
                                        uint32_t* out, void* stream) {

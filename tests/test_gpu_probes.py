@@ -8,6 +8,7 @@ import torch
 
 import oracle
 from helpers import dev, host, probes
+from mixed_precision_dense_tiled_amd import inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -172,3 +173,26 @@ def test_buffer_range_check_covers(gpu_ok):
     print("scalar offset inside the range check:", not got[16:32].any())
     assert np.array_equal(got[:16].ravel(), src[256:512])
     assert not got[32:].any()
+
+
+def test_mfma_peak_probe_runs_and_accumulates(gpu_ok):
+    """The MFMA ceiling probe (a measuring stick, not a layout probe): every
+    thread's accumulator sum is finite, the same on a second run, and zero
+    for zero operands; the clock stamps advance."""
+    L = probes()
+    data = dev(inputs.to_bf16_bits(inputs.normal_f32((1024 * 8,), 11)))
+    out = torch.empty(256 * 256, dtype=torch.float32, device=gpu_ok)
+    stamps = torch.zeros(256 * 4, dtype=torch.int64, device=gpu_ok)
+    assert L.mpdt_probe_mfma_peak(data.data_ptr(), 2, out.data_ptr(), stamps.data_ptr(), _stream()) == 0
+    torch.cuda.synchronize()
+    first = host(out)
+    assert np.isfinite(first).all() and np.abs(first).max() > 0
+    assert L.mpdt_probe_mfma_peak(data.data_ptr(), 2, out.data_ptr(), stamps.data_ptr(), _stream()) == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out), first)
+    q = host(stamps).reshape(256, 4)
+    assert (q[:, 1] > q[:, 0]).all() and (q[:, 3] >= q[:, 2]).all()
+    zero = dev(np.zeros(1024 * 8, np.uint16))
+    assert L.mpdt_probe_mfma_peak(zero.data_ptr(), 2, out.data_ptr(), stamps.data_ptr(), _stream()) == 0
+    torch.cuda.synchronize()
+    assert not host(out).any()
