@@ -240,7 +240,7 @@ def main():
         if smi is not None:
             result["smi_clocks_under_load"] = smi
         if not args.child:
-            ceil = mfma_ceiling(args, stream, inputs)
+            ceil = mfma_ceiling(args, stream, inputs, "bf16")
             result["roofline"]["mfma_ceiling"] = ceil
             result["roofline"]["frac_of_mfma_ceiling"] = achieved / ceil["TFLOP_s"]
         if spread is not None:
@@ -458,6 +458,10 @@ def main():
             "TFLOP_s": tf, "launch_us": st,
             "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP8, "unit": "TFLOP/s",
                          "frac": tf / PEAK_FP8}}
+        if not args.child:
+            ceil = mfma_ceiling(args, stream, inputs, "fp8")
+            extra["gemm_fp8_blockscaled"]["roofline"]["mfma_ceiling"] = ceil
+            extra["gemm_fp8_blockscaled"]["roofline"]["frac_of_mfma_ceiling"] = tf / ceil["TFLOP_s"]
         if not args.no_cpu_baseline and not args.child:
             extra["gemm_fp8_blockscaled"]["cpu_baseline"] = cpu_baseline_fp8(qa, sa, qb, sb, args.cpu_seconds / 3)
         # the same operands with B read as E5M2 codes (the format of gradients)
@@ -551,6 +555,10 @@ def main():
                                 "roofline": {"bound": "mfma", "achieved": tops, "peak": PEAK_INT8,
                                              "unit": "TOP/s", "frac": tops / PEAK_INT8,
                                              "traffic": traffic_for("gemm_i8_4096", source_digest(*GEMM_SOURCES))}}
+        if not args.child:
+            ceil = mfma_ceiling(args, stream, inputs, "i8")
+            extra["gemm_i8_i32"]["roofline"]["mfma_ceiling"] = ceil
+            extra["gemm_i8_i32"]["roofline"]["frac_of_mfma_ceiling"] = tops / ceil["TOP_s"]
         if not args.no_cpu_baseline and not args.child:
             extra["gemm_i8_i32"]["cpu_baseline"] = cpu_baseline_i8(A, B, C, args.cpu_seconds / 3)
         del tA, tB, tC, tD
@@ -788,34 +796,45 @@ def smi_clocks(launch, stream, n=4000):
     return {k.rstrip(":").strip(): v for k, v in card.items() if isinstance(v, str) and "clk" in k.lower()}
 
 
-def mfma_ceiling(args, stream, inputs):
-    """Practical BF16 MFMA rate on this part under sustained load
+def mfma_ceiling(args, stream, inputs, kind="bf16"):
+    """Practical MFMA rate on this part under sustained load
     (libmpdt_probes.so, mpdt_probe_mfma_peak: one wavefront per SIMD on every
-    CU, each issuing the 4096 32x32x16 BF16 MFMAs of the 4096^3 GEMM back to
-    back from registers and nothing else), with operands drawn like the
-    headline's (N(0,1) as BF16) and with all-zero operands; timed like the
-    GEMM (back-to-back launches after the same warm-up), shader clock from
-    the probe's own s_memtime / s_memrealtime stamps."""
+    CU, each issuing back-to-back MFMAs of one kind from registers and
+    nothing else -- for BF16 the 4096 32x32x16 MFMAs of the 4096^3 GEMM, for
+    FP8 and INT8 the same number of cycles of 32x32x64 / 32x32x32 MFMAs),
+    with operands drawn like the workloads' (N(0,1) as BF16, N(0,1)
+    block-quantised to E4M3, uniform INT8) and with all-zero operands; timed
+    like the GEMMs (back-to-back launches after the same warm-up), shader
+    clock from the probe's own s_memtime / s_memrealtime stamps."""
     import ctypes
     import numpy as np
     import torch
     L = ctypes.CDLL(os.path.join(ROOT, "mixed_precision_dense_tiled_amd", "libmpdt_probes.so"))
-    L.mpdt_probe_mfma_peak.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
-                                       ctypes.c_void_p]
+    L.mpdt_probe_mfma_peak.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p]
     L.mpdt_probe_mfma_peak.restype = ctypes.c_int
     dev = torch.device("cuda:0")
-    iters, wgs = 32, 256
-    flop = wgs * 4 * iters * 128 * 2.0 * 32 * 32 * 16
+    wgs = 256
+    code, iters, per_mfma = {"bf16": (0, 32, 2.0 * 32 * 32 * 16), "fp8": (1, 16, 2.0 * 32 * 32 * 64),
+                             "i8": (2, 32, 2.0 * 32 * 32 * 32)}[kind]
+    flop = wgs * 4 * iters * 128 * per_mfma
     out = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
     stamps = torch.zeros(wgs * 4, dtype=torch.int64, device=dev)
-    res = {"note": "one wavefront per SIMD on every CU, 4096 back-to-back 32x32x16 BF16 MFMAs each "
-                   "(the 4096^3 GEMM's MFMA work) from registers, nothing else"}
-    normal = inputs.to_bf16_bits(inputs.normal_f32((1024 * 8,), 11))
-    for name, bits in (("normal", normal), ("zero", np.zeros(1024 * 8, np.uint16))):
-        data = torch.from_numpy(bits.view(np.int16)).to(dev)
+    if kind == "bf16":
+        bits = inputs.to_bf16_bits(inputs.normal_f32((2048 * 8,), 11)).view(np.uint8)
+    elif kind == "fp8":
+        bits = inputs.fp8_quantize_rows(inputs.normal_f32((64, 512), 11))[0].reshape(-1)
+    else:
+        bits = inputs.int_uniform((2048 * 16,), 11, -128, 127, np.int8).view(np.uint8)
+    res = {"note": "one wavefront per SIMD on every CU, back-to-back MFMAs from registers "
+                   "(" + {"bf16": "4096 32x32x16 BF16 each, the 4096^3 GEMM's MFMA work",
+                          "fp8": "2048 32x32x64 FP8 E4M3 each", "i8": "4096 32x32x32 INT8 each"}[kind]
+                   + "), nothing else"}
+    for name, b in (("data", bits), ("zero", np.zeros_like(bits))):
+        data = torch.from_numpy(np.ascontiguousarray(b)).to(dev)
 
         def run(i):
-            rc = L.mpdt_probe_mfma_peak(data.data_ptr(), iters, out.data_ptr(), stamps.data_ptr(),
+            rc = L.mpdt_probe_mfma_peak(code, data.data_ptr(), iters, out.data_ptr(), stamps.data_ptr(),
                                         torch.cuda.current_stream().cuda_stream)
             if rc != 0:
                 raise RuntimeError(f"mpdt_probe_mfma_peak failed: {rc}")
@@ -823,8 +842,9 @@ def mfma_ceiling(args, stream, inputs):
         st = stats(per, region, args.steps)
         q = stamps.cpu().numpy().reshape(wgs, 4).astype(np.float64)
         ghz = float(np.median((q[:, 1] - q[:, 0]) / ((q[:, 3] - q[:, 2]) / 100e6)) / 1e9)
-        key = "" if name == "normal" else "zero_data_"
-        res[key + "TFLOP_s"] = flop / (st["mean_us"] * 1e-6) / 1e12
+        key = "" if name == "data" else "zero_data_"
+        unit = "TOP_s" if kind == "i8" else "TFLOP_s"
+        res[key + unit] = flop / (st["mean_us"] * 1e-6) / 1e12
         res[key + "mean_us"] = st["mean_us"]
         res[key + "shader_clock_ghz"] = ghz
     return res

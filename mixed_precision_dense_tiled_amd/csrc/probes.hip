@@ -27,19 +27,20 @@
 //     real sum takes is ever written, so the kernel moves almost nothing but
 //     the reads.  Not a probe of layout: a measuring stick for the streaming
 //     kernels (the W8A8 GEMV reads its weights this way, 8 KiB per wave).
-//   mpdt_probe_mfma_peak(data, iters, out, stamps): the practical MFMA
+//   mpdt_probe_mfma_peak(kind, data, iters, out, stamps): the practical MFMA
 //     ceiling -- 256 workgroups of four wavefronts (one per SIMD, as the
-//     one-wave GEMM kernel runs), each wavefront 16 independent 32 x 32 FP32
-//     accumulators and eight register-held pairs of BF16 operand fragments
-//     taken from `data` (1024 16-byte vectors), then iters x 128 back-to-back
-//     32x32x16 BF16 MFMAs whose B operand changes at every instruction, and
-//     nothing else.  At iters = 32 a wavefront issues the 4096 MFMAs of the
-//     BF16 4096^3 GEMM.  out[workgroup * 256 + thread] = the sum of the
+//     one-wave GEMM kernels run), each wavefront 16 independent 32 x 32
+//     accumulators and eight register-held pairs of operand fragments taken
+//     from `data`, then iters x 128 back-to-back MFMAs of one kind (BF16
+//     32x32x16, FP8 E4M3 32x32x64 with unit scales, INT8 32x32x32) whose B
+//     operand changes at every instruction, and nothing else.  BF16 at iters
+//     = 32: a wavefront issues the 4096 MFMAs of the BF16 4096^3 GEMM.  out[workgroup * 256 + thread] = the sum of the
 //     thread's accumulators (keeps every MFMA); stamps[workgroup * 4 ..] =
 //     s_memtime and s_memrealtime (100 MHz) at the start and the end of
 //     workgroup's first wavefront, for the shader clock under this load.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 #include "device_common.hpp"
 
@@ -161,20 +162,27 @@ __global__ __launch_bounds__(1024) void probe_stream_read_kernel(const u32x4* p,
 
 constexpr int PEAK_WGS = 256;
 
+// KIND 0: 32x32x16 BF16 (operands 16 bytes a lane); 1: 32x32x64 FP8 E4M3
+// with unit block scales (32 bytes); 2: 32x32x32 INT8 (16 bytes).
+template <int KIND>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void probe_mfma_peak_kernel(const u32x4* data, int iters, float* out, uint64_t* stamps) {
+    constexpr int V = KIND == 1 ? 2 : 1;         // 16-byte pieces per operand fragment
+    using Acc = typename std::conditional<KIND == 2, i32x16, f32x16>::type;
     const int lane = threadIdx.x & 63;
-    u32x4 a[8], b[8];
+    u32x4 a[8][V], b[8][V];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        a[s] = data[s * 64 + lane];
-        b[s] = data[512 + s * 64 + lane];
-    }
-    f32x16 acc[16];
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            a[s][v] = data[(s * V + v) * 64 + lane];
+            b[s][v] = data[512 + (s * V + v) * 64 + lane];
+        }
+    Acc acc[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[k][r] = 0.0f;
+        for (int r = 0; r < 16; ++r) acc[k][r] = 0;
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_sched_barrier(0);
     const uint64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
@@ -183,17 +191,33 @@ void probe_mfma_peak_kernel(const u32x4* data, int iters, float* out, uint64_t* 
 #pragma unroll
         for (int s = 0; s < 8; ++s)
 #pragma unroll
-            for (int k = 0; k < 16; ++k)
-                acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[s]),
-                                                                 __builtin_bit_cast(bf16x8, b[(s + k) & 7]),
-                                                                 acc[k], 0, 0, 0);
+            for (int k = 0; k < 16; ++k) {
+                const int t = (s + k) & 7;
+                if constexpr (KIND == 0) {
+                    acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[s][0]),
+                                                                     __builtin_bit_cast(bf16x8, b[t][0]),
+                                                                     acc[k], 0, 0, 0);
+                } else if constexpr (KIND == 1) {
+                    i32x8 a8, b8;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        a8[e] = (int32_t)a[s][e >> 2][e & 3];
+                        b8[e] = (int32_t)b[t][e >> 2][e & 3];
+                    }
+                    acc[k] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc[k], 0, 0, 0, 127, 0, 127);
+                } else {
+                    acc[k] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a[s][0]),
+                                                                   __builtin_bit_cast(i32x4, b[t][0]),
+                                                                   acc[k], 0, 0, 0);
+                }
+            }
     }
     __builtin_amdgcn_sched_barrier(0);
     float sum = 0.0f;
 #pragma unroll
     for (int k = 0; k < 16; ++k)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sum += acc[k][r];
+        for (int r = 0; r < 16; ++r) sum += (float)acc[k][r];
     const uint64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
     out[blockIdx.x * 256 + threadIdx.x] = sum;
     if (threadIdx.x == 0) {
@@ -204,13 +228,21 @@ void probe_mfma_peak_kernel(const u32x4* data, int iters, float* out, uint64_t* 
 
 }  // namespace mpdt
 
-// data: 1024 x 16 bytes of BF16 operand bits; out: 256 x 256 floats;
-// stamps: 256 x 4 values.
-MPDT_EXPORT int mpdt_probe_mfma_peak(const void* data, int iters, float* out, uint64_t* stamps,
+// kind 0 BF16, 1 FP8 E4M3, 2 INT8; data: 2048 x 16 bytes of operand bits
+// (BF16 and INT8 read the first 1024 and 512 + the next 512, FP8 all);
+// out: 256 x 256 floats; stamps: 256 x 4 values.
+MPDT_EXPORT int mpdt_probe_mfma_peak(int kind, const void* data, int iters, float* out, uint64_t* stamps,
                                      void* stream) {
     if (!data || !out || !stamps || iters < 0 || iters > (1 << 20)) return (int)hipErrorInvalidValue;
-    hipLaunchKernelGGL(mpdt::probe_mfma_peak_kernel, dim3(mpdt::PEAK_WGS), dim3(256), 0, (hipStream_t)stream,
-                       (const mpdt::u32x4*)data, iters, out, stamps);
+    const dim3 g(mpdt::PEAK_WGS), b(256);
+    hipStream_t s = (hipStream_t)stream;
+    const mpdt::u32x4* d = (const mpdt::u32x4*)data;
+    switch (kind) {
+        case 0: hipLaunchKernelGGL(mpdt::probe_mfma_peak_kernel<0>, g, b, 0, s, d, iters, out, stamps); break;
+        case 1: hipLaunchKernelGGL(mpdt::probe_mfma_peak_kernel<1>, g, b, 0, s, d, iters, out, stamps); break;
+        case 2: hipLaunchKernelGGL(mpdt::probe_mfma_peak_kernel<2>, g, b, 0, s, d, iters, out, stamps); break;
+        default: return (int)hipErrorInvalidValue;
+    }
     return (int)hipGetLastError();
 }
 

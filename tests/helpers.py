@@ -64,8 +64,8 @@ def check_fp(D, R, S, frob_max, what="", bf16_out=False, f16_out=False):
 
 def probes():
     L = ctypes.CDLL(os.path.join(ROOT, "mixed_precision_dense_tiled_amd", "libmpdt_probes.so"))
-    L.mpdt_probe_mfma_peak.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
-                                       ctypes.c_void_p]
+    L.mpdt_probe_mfma_peak.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p]
     L.mpdt_probe_mfma_peak.restype = ctypes.c_int
     L.mpdt_probe_tr.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                 ctypes.c_void_p]

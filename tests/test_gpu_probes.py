@@ -175,24 +175,31 @@ def test_buffer_range_check_covers(gpu_ok):
     assert not got[32:].any()
 
 
-def test_mfma_peak_probe_runs_and_accumulates(gpu_ok):
-    """The MFMA ceiling probe (a measuring stick, not a layout probe): every
-    thread's accumulator sum is finite, the same on a second run, and zero
-    for zero operands; the clock stamps advance."""
+@pytest.mark.parametrize("kind", [0, 1, 2])
+def test_mfma_peak_probe_runs_and_accumulates(gpu_ok, kind):
+    """The MFMA ceiling probe (a measuring stick, not a layout probe), BF16,
+    FP8 and INT8: every thread's accumulator sum is finite, the same on a
+    second run, and zero for zero operands; the clock stamps advance."""
     L = probes()
-    data = dev(inputs.to_bf16_bits(inputs.normal_f32((1024 * 8,), 11)))
+    if kind == 0:
+        bits = inputs.to_bf16_bits(inputs.normal_f32((2048 * 8,), 11)).view(np.uint8)
+    elif kind == 1:
+        bits = inputs.fp8_quantize_rows(inputs.normal_f32((64, 512), 11))[0].reshape(-1)
+    else:
+        bits = inputs.int_uniform((2048 * 16,), 11, -128, 127, np.int8).view(np.uint8)
+    data = dev(np.ascontiguousarray(bits))
     out = torch.empty(256 * 256, dtype=torch.float32, device=gpu_ok)
     stamps = torch.zeros(256 * 4, dtype=torch.int64, device=gpu_ok)
-    assert L.mpdt_probe_mfma_peak(data.data_ptr(), 2, out.data_ptr(), stamps.data_ptr(), _stream()) == 0
+    assert L.mpdt_probe_mfma_peak(kind, data.data_ptr(), 2, out.data_ptr(), stamps.data_ptr(), _stream()) == 0
     torch.cuda.synchronize()
     first = host(out)
     assert np.isfinite(first).all() and np.abs(first).max() > 0
-    assert L.mpdt_probe_mfma_peak(data.data_ptr(), 2, out.data_ptr(), stamps.data_ptr(), _stream()) == 0
+    assert L.mpdt_probe_mfma_peak(kind, data.data_ptr(), 2, out.data_ptr(), stamps.data_ptr(), _stream()) == 0
     torch.cuda.synchronize()
     assert np.array_equal(host(out), first)
     q = host(stamps).reshape(256, 4)
     assert (q[:, 1] > q[:, 0]).all() and (q[:, 3] >= q[:, 2]).all()
-    zero = dev(np.zeros(1024 * 8, np.uint16))
-    assert L.mpdt_probe_mfma_peak(zero.data_ptr(), 2, out.data_ptr(), stamps.data_ptr(), _stream()) == 0
+    zero = dev(np.zeros_like(bits))
+    assert L.mpdt_probe_mfma_peak(kind, zero.data_ptr(), 2, out.data_ptr(), stamps.data_ptr(), _stream()) == 0
     torch.cuda.synchronize()
     assert not host(out).any()
