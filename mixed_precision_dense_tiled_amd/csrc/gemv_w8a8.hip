@@ -15,10 +15,12 @@
 //     shared by all waves through L2);
 //   * all R * (K / 1024) loads of a wave are issued before the first use, so
 //     a resident grid keeps the whole weight stream in flight (R = 2 keeps
-//     the register count at 72, seven waves per SIMD: the 14336-row layer
-//     fits the chip in one round);
+//     the register count under 72, seven waves per SIMD: the 14336-row layer
+//     fits the chip in one round, two 14-wave workgroups per CU);
+//   * the rows' weight scales are requested before the weights, so no
+//     memory round trip is left for the end of the wave;
 //   * v_dot4 accumulates 4 byte products per instruction into INT32;
-//   * a butterfly over the 64 lanes reduces each row; lane r writes row r.
+//   * DPP moves reduce each row over the 64 lanes; lane r writes row r.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -27,8 +29,9 @@
 
 namespace mpdt {
 
-constexpr int GEMV_WAVES = 4;        // wavefronts per workgroup
-constexpr int GEMV_ROWS = 2;         // output rows per wavefront (72 VGPRs: 7 waves per SIMD,
+constexpr int GEMV_WAVES = 14;       // wavefronts per workgroup (896 threads; two workgroups
+                                     // fill a CU at 7 waves per SIMD)
+constexpr int GEMV_ROWS = 2;         // output rows per wavefront (<= 72 VGPRs: 7 waves per SIMD,
                                      // so the whole 14336-row layer is resident at once)
 constexpr int GEMV_U = 4;            // 16-byte chunks per lane per row per pass (K = 4096 in one pass)
 
@@ -38,10 +41,19 @@ __device__ __forceinline__ int dot16(u32x4 w, u32x4 x, int acc) {
     return acc;
 }
 
+// Sum over the 64 lanes of a fully active wavefront, returned wave-uniform
+// (scalar registers): DPP moves inside each row of 16 lanes (quad swaps, then
+// the half-row and row mirrors), then the four row sums read into scalar
+// registers.  No LDS round trip: a shuffle per step (ds_bpermute) costs an
+// LDS latency each, six times over at the end of every wave.  Integer adds,
+// so the order does not change the result.
 __device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
+    v += __builtin_amdgcn_update_dpp(0, v, 0xb1, 0xf, 0xf, false);    // quad_perm [1, 0, 3, 2]
+    v += __builtin_amdgcn_update_dpp(0, v, 0x4e, 0xf, 0xf, false);    // quad_perm [2, 3, 0, 1]
+    v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xf, 0xf, false);   // row_half_mirror
+    v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xf, 0xf, false);   // row_mirror
+    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+           __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
 }
 
 // FULL: x and every row of W are 16-byte aligned and K is a whole number of
@@ -52,9 +64,17 @@ template <bool ALIGNED, bool FULL = false>
 __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_w8a8_kernel(GemvArgs g) {
     static_assert(!FULL || ALIGNED, "whole passes need aligned rows");
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int row0 = (blockIdx.x * GEMV_WAVES + wave) * GEMV_ROWS;
     if (row0 >= g.N) return;                      // whole wave past the end: nothing to do
+    // the rows' weight scales, requested before the weights (a row past N
+    // reads row N - 1 and is not written): fetched after the reduction they
+    // would add a memory round trip to the end of every wave.  (Relaxed
+    // atomic loads, so the compiler does not sink them to their use.)
+    float sw[GEMV_ROWS];
+#pragma unroll
+    for (int r = 0; r < GEMV_ROWS; ++r)
+        sw[r] = __hip_atomic_load(&g.w_scale[min(row0 + r, g.N - 1)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
 
     const int64_t kbytes = g.K;
     const char* x = (const char*)g.x;
@@ -116,17 +136,24 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_w8a8_kernel(GemvArgs g) 
 #pragma unroll
     for (int r = 0; r < GEMV_ROWS; ++r) z[r] = wave_sum(acc[r]);
 
+    // lane r writes row r: one store instruction for all the wave's rows
+    if (lane < GEMV_ROWS && row0 + lane < g.N) {
+        int zr = z[0];
+        float swr = sw[0];
 #pragma unroll
-    for (int r = 0; r < GEMV_ROWS; ++r) {
-        const int row = row0 + r;
-        if (lane == r && row < g.N) {
-            if (g.z) g.z[row] = z[r];
-            // dequantise: two FP32 products, activation scale first
-            float v = (float)z[r];
-            v = v * g.x_scale;
-            v = v * g.w_scale[row];
-            g.y[row] = f32_to_bf16_bits(v);
+        for (int r = 1; r < GEMV_ROWS; ++r) {
+            if (lane == r) {
+                zr = z[r];
+                swr = sw[r];
+            }
         }
+        const int row = row0 + lane;
+        if (g.z) g.z[row] = zr;
+        // dequantise: two FP32 products, activation scale first
+        float v = (float)zr;
+        v = v * g.x_scale;
+        v = v * swr;
+        g.y[row] = f32_to_bf16_bits(v);
     }
 }
 

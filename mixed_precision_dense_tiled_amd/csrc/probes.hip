@@ -23,7 +23,8 @@
 //     HBM read ceiling -- every 16-byte chunk of [p, p + bytes) is read once
 //     with non-temporal 16-byte loads, a wave taking per_lane KiB in a row
 //     (lane l reads chunks l, l + 64, ... of its KiB runs, all loads issued
-//     before any is used), `waves` wavefronts per workgroup; only a value no
+//     before any is used; bytes must hold at least one wave's per_lane KiB),
+//     `waves` wavefronts per workgroup; only a value no
 //     real sum takes is ever written, so the kernel moves almost nothing but
 //     the reads.  Not a probe of layout: a measuring stick for the streaming
 //     kernels (the W8A8 GEMV reads its weights this way, 8 KiB per wave).
@@ -141,22 +142,31 @@ __global__ __launch_bounds__(64) void probe_mfma_kernel(const char* A, const cha
     }
 }
 
-// every index is checked against n16 (the 16-byte chunks of the buffer), so
-// no load leaves it whatever the grid
+// The wave's window of PER * 64 chunks is moved back to end at the buffer's
+// last chunk when it would pass it (the host launches only buffers of at
+// least one window), so no load leaves the buffer whatever the grid and the
+// loads carry no branches: a conditional load lets the compiler place a wait
+// between two loads, which leaves most of a wave's bytes unrequested until
+// the first ones arrive.  Chunks that the moved window shares with the wave
+// before it are left out of the sum.
 template <int PER>
 __global__ __launch_bounds__(1024) void probe_stream_read_kernel(const u32x4* p, uint64_t n16, uint32_t* out) {
-    const uint64_t wave = (uint64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const uint64_t wave = (uint64_t)blockIdx.x * (blockDim.x >> 6) +
+                          (uint64_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint64_t lane = threadIdx.x & 63;
-    const uint64_t base = wave * (uint64_t)(PER * 64);
+    constexpr uint64_t SPAN = (uint64_t)PER * 64;
+    const uint64_t first = wave * SPAN;
+    const uint64_t base = first + SPAN <= n16 ? first : n16 - SPAN;
+    const u32x4* q = p + base + lane;
     u32x4 v[PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const uint64_t idx = base + (uint64_t)i * 64 + lane;
-        v[i] = idx < n16 ? __builtin_nontemporal_load(p + idx) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < PER; ++i) v[i] = __builtin_nontemporal_load(q + 64 * i);
+    // every load of the wave is issued before the first wait
+    __builtin_amdgcn_sched_barrier(0);
     uint32_t acc = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) acc ^= v[i][0] ^ v[i][1] ^ v[i][2] ^ v[i][3];
+    for (int i = 0; i < PER; ++i)
+        if (base + (uint64_t)i * 64 + lane >= first) acc ^= v[i][0] ^ v[i][1] ^ v[i][2] ^ v[i][3];
     if (acc == 0x9E3779B9u && lane == 0) out[0] = acc;   // keeps the loads; (practically) never stores
 }
 
@@ -252,6 +262,7 @@ MPDT_EXPORT int mpdt_probe_stream_read(const void* p, uint64_t bytes, int per_la
     const uint64_t n16 = bytes / 16;
     if (n16 == 0) return 0;
     const uint64_t per_wave = (uint64_t)per_lane * 64;
+    if (n16 < per_wave) return (int)hipErrorInvalidValue;   // smaller than one wave's window
     const uint64_t nwaves = (n16 + per_wave - 1) / per_wave;
     const uint64_t grid = (nwaves + waves - 1) / waves;
     if (grid > 0x7fffffffull) return (int)hipErrorInvalidValue;
