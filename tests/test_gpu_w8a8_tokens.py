@@ -10,7 +10,10 @@ sum or a fixed sequence of IEEE FP32 operations, then one rounding):
     32 per launch),
     N not a multiple of a workgroup's 32 channels, K not a multiple of the
     wave slices, with and without bias, padded and misaligned operands, -128 at the
-    INT32 bound, K = 0, and the full 4096 x 14336 layer for 4 tokens;
+    INT32 bound, K = 0, and the full 4096 x 14336 layer for 4 tokens; the
+    streaming path of up to 16 tokens over whole 4096-byte passes (ragged N
+    around its 28-channel workgroups, one to three passes, guard-banded
+    outputs, the full layer at 16 tokens, requantised);
   * quantize_i8_rows: random BF16 rows, exact ties, zero rows, K tails;
   * quantize_fp8_blocks: 1 x 128 and 128 x 128 blocks, ragged edges, a zero
     block, the FP8 workload's operand sizes, and the result fed to
@@ -84,6 +87,44 @@ def test_w8a8_tokens_int32_bound_full_layer_and_k_zero(gpu_ok):
                         dev(bias), return_z=True)
     assert not host(z).any()
     assert np.array_equal(host(y).view(np.uint16), np.tile(oracle.f32_to_bf16_rne(bias), (5, 1)))
+
+
+# Up to 16 tokens over whole 4096-byte passes with 16-byte aligned rows: the
+# streaming kernel (14 waves of two weight rows, 28 channels per workgroup,
+# the sums of several passes carried through LDS).  N around and across the
+# 28-channel workgroups, padded rows, one to three passes, the full layer at
+# 16 tokens; Y and Z written into guard-banded buffers that must keep their
+# padding.
+@pytest.mark.parametrize("M,N,K,ldx,ldw", [(1, 1, 4096, None, None), (2, 27, 4096, 4112, None),
+                                           (5, 28, 8192, None, 8208), (8, 29, 4096, None, None),
+                                           (13, 57, 12288, 12304, 12320), (14, 1000, 4096, None, None),
+                                           (15, 85, 8192, None, None), (16, 300, 4096, 4160, 4128),
+                                           (16, 14336, 4096, None, None)])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_w8a8_stream_path_bit_exact_guarded(gpu_ok, M, N, K, ldx, ldw, with_bias):
+    X, sx, W, sw, bias = w8a8_inputs(M, N, K, seed=7 * M + N)
+    b = bias if with_bias else None
+    ybuf = torch.empty((M + 1, N + 9), dtype=torch.bfloat16, device=gpu_ok)
+    ybuf.view(torch.int16).fill_(0x7FC1)
+    zbuf = torch.full((M + 1, N + 9), -7, dtype=torch.int32, device=gpu_ok)
+    mp.gemm_w8a8(dev(X, ldx, pad=55), dev(sx), dev(W, ldw, pad=-66), dev(sw), None if b is None else dev(b),
+                 out=ybuf[:M, :N], z_out=zbuf[:M, :N])
+    torch.cuda.synchronize()
+    zr, yr = oracle.gemm_w8a8(X, sx, W, sw, b)
+    y, z = host(ybuf).view(np.uint16), host(zbuf)
+    assert np.array_equal(z[:M, :N], zr) and np.array_equal(y[:M, :N], yr)
+    assert (z[M:] == -7).all() and (z[:, N:] == -7).all()
+    assert (y[M:] == 0x7FC1).all() and (y[:, N:] == 0x7FC1).all()
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 100, 4096), (3, 57, 8192)])
+def test_w8a8_stream_path_requant_bit_exact(gpu_ok, M, N, K):
+    X, sx, W, sw, bias = w8a8_inputs(M, N, K, seed=M + N + K)
+    s_out = np.float32(0.6)
+    Q, Z = mp.gemm_w8a8_requant(dev(X), dev(sx), dev(W), dev(sw), dev(bias), float(s_out), return_z=True)
+    torch.cuda.synchronize()
+    Zr, Qr = oracle.gemm_w8a8_requant(X, sx, W, sw, bias, s_out)
+    assert np.array_equal(host(Z), Zr) and np.array_equal(host(Q), Qr)
 
 
 @pytest.mark.parametrize("M", [1, 3, 17, 33, 40])
