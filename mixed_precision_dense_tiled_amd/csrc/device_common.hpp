@@ -88,6 +88,18 @@ __device__ __forceinline__ void lds_dma4(i32x4 r, MPDT_LDS char* dst, uint32_t v
                      : "{m0}"((uint32_t)(uintptr_t)dst), "v"(voff), "s"(r), "s"(soff), "n"(OFF));
 }
 
+// s_waitcnt vmcnt(N): at most N vector-memory operations of this wave
+// (direct-to-LDS loads included) are still in flight.  Memory reads retire in
+// issue order, so this waits for all but the N most recent.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// s_waitcnt lgkmcnt(0): this wave's LDS reads and writes have completed.
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // Keep the bytes [0, nbytes) of an 8-byte piece, zero the rest (nbytes 0..8).
 __device__ __forceinline__ u32x2 mask_tail8(u32x2 v, int nbytes) {
 #pragma unroll

@@ -184,18 +184,6 @@ struct Stage {
     MPDT_LDS float* S;   // FP8: per-row A scales of the staged K tile
 };
 
-// s_waitcnt vmcnt(N): at most N vector-memory operations of this wave
-// (direct-to-LDS loads included) are still in flight.  Memory reads retire in
-// issue order, so this waits for all but the N most recent.
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
-// s_waitcnt lgkmcnt(0): this wave's LDS reads and writes have completed.
-__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
 // Workgroup barrier without a memory fence.  (A fence would make the compiler
 // drain every direct-to-LDS load in flight, defeating the multi-stage
 // pipeline.)  LDS visibility is managed explicitly: a wave waits for its own

@@ -422,47 +422,50 @@ __global__ __launch_bounds__(64 * TOK_WAVES) __attribute__((amdgpu_waves_per_eu(
 // ---------------------------------------------------------------------------
 // Up to 16 tokens over whole passes (K a multiple of 4096, X and W rows 16-byte
 // aligned): the weights stream as in the one-token kernel, every load one
-// contiguous KiB of one row, all of a wave's loads issued at once and
-// non-temporal.  A workgroup of 14 wavefronts owns 56 channels, four weight
-// rows (16 KiB per pass) per wave, so the 14336-channel layer is 256
+// contiguous KiB of one row, all of a wave's loads issued at once, row after
+// row, non-temporal.  A workgroup of 14 wavefronts owns 56 channels, four
+// weight rows (16 KiB per pass) per wave, so the 14336-channel layer is 256
 // workgroups, one per CU, all resident from the start.  Measured against
 // this shape: eight rows per wave in four-wave workgroups (the kernel above)
 // streams the same bytes about a third slower, and two 28-channel workgroups
 // per CU do not fit side by side at this register count, so half of them
-// started only when the first half ended, each half then paying the chunk
-// phases' tail after its last weights arrived.
+// started only when the first half ended.
 //
-// The pass's 64 token pieces (16 rows x 4 chunks of one KiB; rows past M
-// skipped) are spread over the 14 waves, at most five each, and issued
-// before the weights, so a chunk waits only for its own weights.  At chunk c
-// every wave writes its four weight rows and its token pieces of that chunk
-// to LDS; then eight waves run 16x16x64 INT8 MFMAs (16 tokens x 16 channels),
-// wave w on channel block w / 2 (channels 16 (w / 2) .. +15 of the
-// workgroup; operand rows 56..63 are dead rows whose sums are never written)
-// and on K bytes 512 (w % 2) .. +511 of the chunk, eight steps of 64 bytes.
-// The two K halves of a block meet in LDS.
+// The pass's token rows go straight to LDS first (direct loads, 16 rows x 4
+// KiB), and each MFMA wave takes its K part of them into registers.  Then
+// four phases: in phase j every wave writes its j-th weight row (4 KiB) to
+// LDS, so the 14 rows staged are channels 4 w + j (w = 0..13) of the
+// workgroup, the block of a 16x16x64 INT8 MFMA (16 tokens x 16 channels;
+// operand rows 14 and 15 are dead rows whose sums are never written).  Eight
+// waves take 512 K bytes each, eight steps of 64 bytes, into one register
+// quad per phase.  The phases alternate between two LDS buffers (the second
+// is the token buffer once the MFMA waves hold their tokens), so one barrier
+// per phase suffices, and a phase waits only for the weight row it stages,
+// which each wave requested as one contiguous run before the next.  Every
+// phase waits for the slowest wave's row, so phases start late in the
+// stream; what a phase costs is then its LDS traffic, which holding the
+// tokens in registers halves.  The eight K parts of each block meet in LDS
+// at the end.
 // ---------------------------------------------------------------------------
 constexpr int TS_WAVES = 14;                                  // wavefronts per workgroup
-constexpr int TS_RPW = 4;                                     // weight rows per wave
+constexpr int TS_RPW = 4;                                     // weight rows per wave (= phases)
 constexpr int TS_CH = TS_RPW * TS_WAVES;                      // live channels per workgroup (56)
-constexpr int TS_ROWS = 64;                                   // operand rows in LDS (four 16-channel blocks)
-constexpr int TS_XP = (16 * TOK_PASS + TS_WAVES - 1) / TS_WAVES;   // token pieces per wave
-constexpr int TS_MW = 8;                                      // MFMA waves: 4 channel blocks x 2 K halves
+constexpr int TS_PITCH = TOK_PASS * TOK_KC + 16;              // LDS row pitch: a pass + 16 bytes
+constexpr int TS_XP = (16 + TS_WAVES - 1) / TS_WAVES;         // token rows per wave (direct loads)
+constexpr int TS_MW = 8;                                      // MFMA waves: 8 K parts of 512 bytes
 
 __global__ __launch_bounds__(64 * TS_WAVES) void gemm_w8a8_stream_kernel(W8A8Args g) {
-    __shared__ __attribute__((aligned(16))) char wt[TS_ROWS * TOK_PITCH];
-    __shared__ __attribute__((aligned(16))) char xt[16 * TOK_PITCH];
-    // the MFMA waves' sums between passes (kept in registers across the pass
-    // loop, they would be live while the loads are in flight)
-    __shared__ int carry[TS_MW * 4 * 64];
-    // the epilogue's weight scales, bias and token scales per channel block
-    __shared__ float esc[TS_ROWS / 16][3][64];
-    static_assert(TS_CH <= TS_ROWS && (TS_MW / 2) * 4 * 64 * 4 <= TS_ROWS * TOK_PITCH, "layout");
+    // two buffers of 16 rows of a pass: the token rows, then the weight rows
+    // of odd phases; the weight rows of even phases
+    __shared__ __attribute__((aligned(16))) char st[2][16 * TS_PITCH];
+    // the epilogue's weight scales, bias and token scales per phase block
+    __shared__ float esc[TS_RPW][3][64];
+    static_assert(TS_MW * TS_RPW * 4 * 64 * 4 <= 16 * TS_PITCH, "partial sums fit");
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int o0 = blockIdx.x * TS_CH;
-    MPDT_LDS char* const wl = lds_cast(wt);
-    MPDT_LDS char* const xl = lds_cast(xt);
+    MPDT_LDS char* const sl = lds_cast(&st[0][0]);
+    MPDT_LDS char* const xl = sl + 16 * TS_PITCH;   // the token rows (buffer 1)
 
     // Buffer resources with scalar bases and offsets and one lane offset for
     // every load (the host checks that the offset sums stay below 2^32).
@@ -474,120 +477,128 @@ __global__ __launch_bounds__(64 * TS_WAVES) void gemm_w8a8_stream_kernel(W8A8Arg
     for (int j = 0; j < TS_RPW; ++j)
         wro[j] = (uint32_t)((int64_t)(min(o0 + TS_RPW * wave + j, g.N - 1) - wr0) * g.ldw);
     const __amdgpu_buffer_rsrc_t wrs = buffer_rsrc((const char*)g.W + (int64_t)wr0 * g.ldw, 0xffffffffu);
-    const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(g.X, 0xffffffffu);
+    const i32x4 xrs = rsrc_words((uint64_t)(uintptr_t)g.X, 0xffffffffu);
     const uint32_t lane16 = 16u * (uint32_t)lane;
     const uint32_t ldx = (uint32_t)g.ldx;
-    // MFMA operands: token row / channel lane % 16 of the block, 16 K bytes
-    // at 16 (lane / 16) of each 64-byte step
-    const int blk = wave >> 1, kh = wave & 1;
-    const uint32_t la = (uint32_t)((lane & 15) * TOK_PITCH + 512 * kh + 16 * (lane >> 4));
-    const uint32_t lb = la + (uint32_t)(16 * blk * TOK_PITCH);
+    // MFMA operands: token row / staged row lane % 16, 16 K bytes at
+    // 16 (lane / 16) of each 64-byte step of this wave's K part
+    const uint32_t lo = (uint32_t)((lane & 15) * TS_PITCH + 512 * (wave & (TS_MW - 1)) + 16 * (lane >> 4));
 
     // The epilogue's scales and bias, fetched straight into LDS before any
     // other load (fetched at the end, they would add a memory round trip
-    // after the last weights arrive), by the wave of each channel block that
-    // writes it: lane l takes channel 16 blk + l % 16 of the workgroup and
-    // token l % 16.  Channels past N and tokens past M fall outside the
-    // buffers' ranges and read zero without touching memory.  (These loads
-    // retire before the weights' and tokens', which every wave waits for
-    // before its first barrier.)
-    if (wave < TS_MW && kh == 0) {
-        const int c0 = o0 + 16 * blk;
-        const uint32_t nch = (uint32_t)min((int64_t)(g.N - c0) * 4, (int64_t)0xffffffff);
+    // after the last weights arrive), by the wave that writes block j: lane l
+    // takes channel 4 (l % 16) + j of the workgroup and token l % 16.
+    // Channels past N and tokens past M fall outside the buffers' ranges and
+    // read zero without touching memory.
+    if (wave < TS_RPW) {
+        const int j = wave;
+        const uint32_t nch = (uint32_t)min((int64_t)(g.N - o0) * 4, (int64_t)0xffffffff);
+        const uint32_t lc = 4u * (uint32_t)(TS_RPW * (lane & 15) + j);
         const uint32_t l4 = 4u * (uint32_t)(lane & 15);
-        lds_dma4(rsrc_words((uint64_t)(uintptr_t)(g.w_scale + c0), c0 < g.N ? nch : 0u),
-                 lds_cast(&esc[blk][0][0]), l4, 0u);
-        if (g.bias)
-            lds_dma4(rsrc_words((uint64_t)(uintptr_t)(g.bias + c0), c0 < g.N ? nch : 0u),
-                     lds_cast(&esc[blk][1][0]), l4, 0u);
-        lds_dma4(rsrc_words((uint64_t)(uintptr_t)g.x_scale, 4u * (uint32_t)g.M), lds_cast(&esc[blk][2][0]), l4, 0u);
+        lds_dma4(rsrc_words((uint64_t)(uintptr_t)(g.w_scale + o0), nch), lds_cast(&esc[j][0][0]), lc, 0u);
+        if (g.bias) lds_dma4(rsrc_words((uint64_t)(uintptr_t)(g.bias + o0), nch), lds_cast(&esc[j][1][0]), lc, 0u);
+        lds_dma4(rsrc_words((uint64_t)(uintptr_t)g.x_scale, 4u * (uint32_t)g.M), lds_cast(&esc[j][2][0]), l4, 0u);
     }
 
-    i32x4 acc;
+    i32x4 acc[TS_RPW];
+#pragma unroll
+    for (int j = 0; j < TS_RPW; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[j][r] = 0;
     for (int64_t p0 = 0; p0 < g.K; p0 += (int64_t)TOK_PASS * TOK_KC) {
         const uint32_t pk = (uint32_t)p0;
-        // token piece q = wave + 14 j: chunk q / 16 of token row q % 16
-        u32x4 xs[TS_XP];
+        if (p0 > 0) __syncthreads();           // the previous pass's reads are done
+        // The pass's token rows straight into LDS (no registers held): wave w
+        // loads rows w and w + 14 (below M), four KiB each.  Issued before the
+        // weights, so they have landed once a wave has waited for all but its
+        // weight loads (loads retire in issue order).
 #pragma unroll
-        for (int j = 0; j < TS_XP; ++j) {
-            const int q = wave + TS_WAVES * j;
-            if (q < 16 * TOK_PASS && (q & 15) < g.M)
-                xs[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                      xrs, lane16, (uint32_t)(q & 15) * ldx + pk + (uint32_t)(q >> 4) * TOK_KC, 0));
+        for (int i = 0; i < TS_XP; ++i) {
+            const int m = wave + TS_WAVES * i;
+            if (m < 16 && m < g.M) {
+#pragma unroll
+                for (int c = 0; c < TOK_PASS; ++c)
+                    lds_dma16(xrs, xl + m * TS_PITCH + c * TOK_KC, lane16,
+                              (uint32_t)m * ldx + pk + (uint32_t)(c * TOK_KC));
+            }
         }
-        // the weights in chunk order (loads retire in issue order), non-temporal (aux 2)
-        u32x4 wv[TOK_PASS][TS_RPW];
+        // the weights, row after row (each row one contiguous run of four
+        // KiB), non-temporal (aux 2)
+        u32x4 wv[TS_RPW][TOK_PASS];
 #pragma unroll
-        for (int c = 0; c < TOK_PASS; ++c) {
+        for (int j = 0; j < TS_RPW; ++j) {
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int j = 0; j < TS_RPW; ++j)
-                wv[c][j] = __builtin_bit_cast(
+            for (int c = 0; c < TOK_PASS; ++c)
+                wv[j][c] = __builtin_bit_cast(
                     u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, lane16, wro[j] + pk + c * TOK_KC, 2));
         }
         __builtin_amdgcn_sched_barrier(0);
+        wait_vmem<TS_RPW * TOK_PASS>();            // this wave's token rows have landed
+        __syncthreads();                           // everyone's
+        // this MFMA wave's tokens for the pass: its K part, eight steps
+        u32x4 xa[8];
+        if (wave < TS_MW) {
 #pragma unroll
-        for (int c = 0; c < TOK_PASS; ++c) {
-            __syncthreads();                       // the previous chunk's reads are done
+            for (int s = 0; s < 8; ++s) xa[s] = lds_load16(xl, lo + 64 * s);
+        }
 #pragma unroll
-            for (int j = 0; j < TS_RPW; ++j)
-                lds_store16(wl, (uint32_t)((TS_RPW * wave + j) * TOK_PITCH) + lane16, wv[c][j]);
+        for (int j = 0; j < TS_RPW; ++j) {
+            // phase j stages in buffer j % 2; the waves' reads of that buffer
+            // (the tokens, or phase j - 2) ended before the previous barrier
+            MPDT_LDS char* const wl = sl + (j & 1) * 16 * TS_PITCH;
 #pragma unroll
-            for (int j = 0; j < TS_XP; ++j) {
-                const int q = wave + TS_WAVES * j;
-                if (q < 16 * TOK_PASS && (q >> 4) == c && (q & 15) < g.M)
-                    lds_store16(xl, (uint32_t)((q & 15) * TOK_PITCH) + lane16, xs[j]);
-            }
+            for (int c = 0; c < TOK_PASS; ++c)
+                lds_store16(wl, (uint32_t)(wave * TS_PITCH + c * TOK_KC) + lane16, wv[j][c]);
             __syncthreads();
             if (wave < TS_MW) {
+                // weight operands read two steps ahead of their MFMA
+                u32x4 b0 = lds_load16(wl, lo), b1 = lds_load16(wl, lo + 64);
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
-                    const u32x4 a = lds_load16(xl, la + 64 * s);
-                    const u32x4 b = lds_load16(wl, lb + 64 * s);
-                    const i32x4 zero = {};
-                    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a),
-                                                                __builtin_bit_cast(i32x4, b),
-                                                                (c == 0 && s == 0) ? zero : acc, 0, 0, 0);
+                    u32x4 b2 = b1;
+                    if (s + 2 < 8) b2 = lds_load16(wl, lo + 64 * (s + 2));
+                    acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, xa[s]),
+                                                                   __builtin_bit_cast(i32x4, b0), acc[j], 0, 0, 0);
+                    b0 = b1;
+                    b1 = b2;
                 }
-            }
-        }
-        if (wave < TS_MW) {
-            if (p0 > 0) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] += carry[(wave * 4 + r) * 64 + lane];
-            }
-            if (p0 + (int64_t)TOK_PASS * TOK_KC < g.K) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) carry[(wave * 4 + r) * 64 + lane] = acc[r];
             }
         }
     }
 
-    // the second K half of each block (exact INT32) through the weight
-    // buffer, once every wave is done reading it; the first adds it and writes
+    // the eight K parts of each block (exact INT32) through the even-phase
+    // buffer, once every wave is done reading it; wave j adds block j's and
+    // writes its 14 channels
     __syncthreads();
-    int* const partial = reinterpret_cast<int*>(wt);     // [4 blocks][4][64]
-    if (wave < TS_MW && kh == 1) {
+    int* const partial = reinterpret_cast<int*>(&st[0][0]);   // [8 K parts][4 blocks][4][64]
+    if (wave < TS_MW) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) partial[(blk * 4 + r) * 64 + lane] = acc[r];
+        for (int j = 0; j < TS_RPW; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) partial[((wave * TS_RPW + j) * 4 + r) * 64 + lane] = acc[j][r];
     }
     __syncthreads();
-    if (wave >= TS_MW || kh != 0) return;
+    if (wave >= TS_RPW) return;
+    const int j = wave;
+    i32x4 z4 = {0, 0, 0, 0};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] += partial[(blk * 4 + r) * 64 + lane];
-    const int ch = 16 * blk + (lane & 15);
-    const int o = o0 + ch;
-    if (ch >= TS_CH || o >= g.N) return;       // dead operand rows, channels past N
-    const float sw = esc[blk][0][lane & 15];
-    const float bo = esc[blk][1][lane & 15];
+    for (int w = 0; w < TS_MW; ++w)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) z4[r] += partial[((w * TS_RPW + j) * 4 + r) * 64 + lane];
+    const int row = lane & 15;                 // staged row: channel 4 row + j of the workgroup
+    const int o = o0 + TS_RPW * row + j;
+    if (row >= TS_WAVES || o >= g.N) return;   // dead operand rows, channels past N
+    const float sw = esc[j][0][row];
+    const float bo = esc[j][1][row];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int m = 4 * (lane >> 4) + r;    // sum r of lane l: token 4 (l / 16) + r
         if (m < g.M) {
-            const int z = acc[r];
+            const int z = z4[r];
             if (g.Z) g.Z[(int64_t)m * g.ldz + o] = z;
             // three separately rounded FP32 operations (no fused multiply-add)
-            float v = mul_rn((float)z, esc[blk][2][m]);
+            float v = mul_rn((float)z, esc[j][2][m]);
             v = mul_rn(v, sw);
             if (g.bias) v = add_rn(v, bo);
             if (g.Q) {
