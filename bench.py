@@ -368,7 +368,10 @@ def main():
                             "cold: 8 rotating W copies",
                 "GB_s": gbs, "algorithmic_bytes": nbytes, "launch_us": st,
                 "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM, "unit": "GB/s",
-                             "frac": gbs / PEAK_HBM}}
+                             "frac": gbs / PEAK_HBM,
+                             "traffic": traffic_for("gemm_w8a8_stream_16x14336x4096",
+                                                    source_digest("gemv_w8a8.hip", "device_common.hpp"))
+                             if M == 16 else None}}
             if M == 16:
                 # the same layer with the weights stored K x N
                 tWkn = [tW.t().contiguous() for tW in tWs[:4]]
