@@ -455,8 +455,8 @@ constexpr int TS_XP = (16 + TS_WAVES - 1) / TS_WAVES;         // token rows per 
 constexpr int TS_MW = 8;                                      // MFMA waves: 8 K parts of 512 bytes
 
 __global__ __launch_bounds__(64 * TS_WAVES) void gemm_w8a8_stream_kernel(W8A8Args g) {
-    // two buffers of 16 rows of a pass: the token rows, then the weight rows
-    // of odd phases; the weight rows of even phases
+    // two buffers of 16 rows of a pass: st[0] holds the weight rows of even
+    // phases, st[1] the token rows and then the weight rows of odd phases
     __shared__ __attribute__((aligned(16))) char st[2][16 * TS_PITCH];
     // the epilogue's weight scales, bias and token scales per phase block
     __shared__ float esc[TS_RPW][3][64];
