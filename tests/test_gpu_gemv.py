@@ -48,7 +48,9 @@ def test_full_layer_bit_exact(gpu_ok):
 
 
 @pytest.mark.parametrize("N,K", [(1, 1), (17, 4096), (1000, 4095), (333, 1000), (20, 5000),
-                                 (4097, 64), (15, 8193)])
+                                 (4097, 64), (15, 8193),
+                                 # around the 28 rows of a workgroup, whole passes of 4096 bytes
+                                 (27, 8192), (28, 4096), (29, 12288), (57, 4096), (85, 8192)])
 def test_shapes_bit_exact(gpu_ok, N, K):
     x, s_x, W, s_w = inputs.w8a8_operands(N, K, seeds=(N, K, 3, 4))
     z, y, zr, yr = run(x, s_x, W, s_w)
