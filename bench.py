@@ -240,9 +240,10 @@ def main():
         if smi is not None:
             result["smi_clocks_under_load"] = smi
         if not args.child:
-            ceil = mfma_ceiling(args, stream, inputs, "bf16")
+            ceil = optional(mfma_ceiling, args, stream, inputs, "bf16")
             result["roofline"]["mfma_ceiling"] = ceil
-            result["roofline"]["frac_of_mfma_ceiling"] = achieved / ceil["TFLOP_s"]
+            if "TFLOP_s" in ceil:
+                result["roofline"]["frac_of_mfma_ceiling"] = achieved / ceil["TFLOP_s"]
         if spread is not None:
             result["process_spread"] = spread["bf16"]
         if not args.no_cpu_baseline and not args.child:
@@ -291,7 +292,7 @@ def main():
     # ---------------- practical HBM read ceiling ------------------------------
     ceiling = None
     if (want("gemv") or want("ceiling")) and not args.child:
-        ceiling = read_ceiling(args, stream)
+        ceiling = optional(read_ceiling, args, stream)
         extra["hbm_read_ceiling"] = ceiling
 
     note("W8A8 GEMV, cold cache")
@@ -334,7 +335,7 @@ def main():
                          "frac": gbs / PEAK_HBM,
                          "traffic": traffic_for("gemv_w8a8_14336x4096", digest)},
         }
-        if ceiling is not None:
+        if ceiling is not None and "error" not in ceiling:
             c = max(v["GB_s"] for k, v in ceiling.items() if k.startswith("same_bytes_cold"))
             extra["gemv_w8a8"]["roofline"]["calibrated_ceiling_GB_s"] = c
             extra["gemv_w8a8"]["roofline"]["frac_of_calibrated_ceiling"] = gbs / c
@@ -462,9 +463,10 @@ def main():
             "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP8, "unit": "TFLOP/s",
                          "frac": tf / PEAK_FP8}}
         if not args.child:
-            ceil = mfma_ceiling(args, stream, inputs, "fp8")
+            ceil = optional(mfma_ceiling, args, stream, inputs, "fp8")
             extra["gemm_fp8_blockscaled"]["roofline"]["mfma_ceiling"] = ceil
-            extra["gemm_fp8_blockscaled"]["roofline"]["frac_of_mfma_ceiling"] = tf / ceil["TFLOP_s"]
+            if "TFLOP_s" in ceil:
+                extra["gemm_fp8_blockscaled"]["roofline"]["frac_of_mfma_ceiling"] = tf / ceil["TFLOP_s"]
         if not args.no_cpu_baseline and not args.child:
             extra["gemm_fp8_blockscaled"]["cpu_baseline"] = cpu_baseline_fp8(qa, sa, qb, sb, args.cpu_seconds / 3)
         # the same operands with B read as E5M2 codes (the format of gradients)
@@ -559,9 +561,10 @@ def main():
                                              "unit": "TOP/s", "frac": tops / PEAK_INT8,
                                              "traffic": traffic_for("gemm_i8_4096", source_digest(*GEMM_SOURCES))}}
         if not args.child:
-            ceil = mfma_ceiling(args, stream, inputs, "i8")
+            ceil = optional(mfma_ceiling, args, stream, inputs, "i8")
             extra["gemm_i8_i32"]["roofline"]["mfma_ceiling"] = ceil
-            extra["gemm_i8_i32"]["roofline"]["frac_of_mfma_ceiling"] = tops / ceil["TOP_s"]
+            if "TOP_s" in ceil:
+                extra["gemm_i8_i32"]["roofline"]["frac_of_mfma_ceiling"] = tops / ceil["TOP_s"]
         if not args.no_cpu_baseline and not args.child:
             extra["gemm_i8_i32"]["cpu_baseline"] = cpu_baseline_i8(A, B, C, args.cpu_seconds / 3)
         del tA, tB, tC, tD
@@ -797,6 +800,15 @@ def smi_clocks(launch, stream, n=4000):
         return None
     card = next(iter(data.values()))
     return {k.rstrip(":").strip(): v for k, v in card.items() if isinstance(v, str) and "clk" in k.lower()}
+
+
+def optional(fn, *a):
+    """A context measurement (probe ceilings): its failure to load or run is
+    reported in the line instead of ending the benchmark."""
+    try:
+        return fn(*a)
+    except (OSError, RuntimeError) as e:
+        return {"error": f"{type(e).__name__}: {e}"}
 
 
 def mfma_ceiling(args, stream, inputs, kind="bf16"):
